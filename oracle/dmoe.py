@@ -1,0 +1,450 @@
+"""CPU oracle for the dropless-MoE (dMoE) expert layer -- TEST INFRASTRUCTURE.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this module.  The product path (the HIP library and its Python
+binding) never calls it; the two share no code.
+
+Everything here is plain numpy in float64.  Inputs are converted to float64
+exactly (bf16 and fp32 values are exact in fp64), so the oracle sees the very
+values the GPU sees and rounds nowhere.
+
+Sources (the pages are the authority on what the layer computes):
+
+* [MB] "02 · dropless MoE 与 block-sparse 重构", the MegaBlocks chapter on
+  ai-reference-codex: §2 (round each expert's count up to 128, one expert
+  per 128-row block, at most 127 pad rows per expert), §3 (the sdd/dsd
+  pair), §4.1 (sort / histogram / cumsum, round_up, bins and padded_bins),
+  §4.2 (padded_gather / padded_scatter index arithmetic, the A_TO_B switch,
+  the routing-weight gradient, the gather <-> scatter backward pairing),
+  §4.3 (row block -> expert column blocks), §4.5 (the forward sketch),
+  §5 (GLU variant shares the topology, ffn % 128, pad rows are zero and
+  dropped on scatter).
+* [FL] Fast-LLM issue "[feat] Support sparse copy for a large number of
+  experts": the layer is gated with activation SiLU, no biases.
+
+Readings where the pages are silent or garbled (each is used below):
+
+* R1/R2: ``bins[e-1]`` and ``padded_bins[e-1]`` at e = 0 mean 0 (the
+  exclusive start), not Python's wrap-around to the last element.
+* R3: the sketch's ``rows`` are flattened (token, slot) entries
+  ``a = t*k + j``; the source token is ``a // k`` (the kernel of §4.2
+  divides by TOP_K) and the weight is ``weights.flat[a]``.
+* R4/R5: the activation is gated SiLU, ``silu(x@w1) * (x@w3)`` then ``@w2``
+  (the sketch's ungated gelu is replaced by [FL]'s gated silu).
+* R6: the sort is stable: ties keep ascending ``a``.
+* R7: ``round_up(0) = 0``: an empty expert gets no rows and no tile.
+* R9: the top-k reduction is a plain sum over j (the oracle does not round).
+* w1, w3 are stored ``[E,H,F]`` and w2 ``[E,F,H]``.
+
+Pins (tests/test_oracle_*.py): hand-derived metadata fixtures, a pure-Python
+counting sort against the library sort, the padding invariants of §2, the
+gather-then-unit-scatter identity, a dense gated-SiLU MLP (E=1, k=1) and
+identical experts, closed forms, loop vs. padded-pipeline agreement, and
+central finite differences for every gradient.
+"""
+from __future__ import annotations
+
+from typing import Dict, Iterable, Optional, Sequence, Tuple
+
+import numpy as np
+
+BLOCK = 128
+
+__all__ = [
+    "BLOCK", "round_up", "max_tiles", "metadata", "metadata_counting_sort",
+    "padded_gather", "padded_scatter", "silu", "sigmoid", "forward_loop",
+    "backward_loop", "forward_padded", "backward_padded", "sampled_rows",
+    "sampled_dw",
+]
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# Metadata  ([MB] §4.1, §4.2, §4.3)
+# --------------------------------------------------------------------------
+
+def round_up(c, block: int = BLOCK):
+    """Round a count up to a multiple of ``block`` ([MB] §4.1).  round_up(0)=0."""
+    c = np.asarray(c, dtype=np.int64)
+    return ((c + block - 1) // block) * block
+
+
+def max_tiles(T: int, k: int, E: int) -> int:
+    """Host bound on the number of 128-row tiles.
+
+    Every non-empty expert wastes at most 127 rows ([MB] §2), so
+    ``P <= T*k + 127*min(E, T*k)``; P is a multiple of 128.
+    """
+    n = T * k
+    return (n + 127 * min(E, n)) // BLOCK
+
+
+def metadata(top_experts, num_experts: int, n_tiles: Optional[int] = None
+             ) -> Dict[str, np.ndarray]:
+    """Routing metadata from top-k expert ids, with library primitives.
+
+    [MB] §4.1: a stable sort of the flattened entries by expert, a histogram
+    (tokens per expert), its inclusive cumsum ``bins``, the per-expert counts
+    rounded up to 128, and their inclusive cumsum ``padded_bins``.
+    [MB] §4.2: entry ``indices[s]`` lands on padded row
+    ``(s - bins[e-1]) + padded_bins[e-1]`` with e its expert (R1: the start of
+    expert 0 is 0).  [MB] §2/§4.3: each 128-row block belongs to one expert;
+    ``tile_expert[r]`` names it, -1 past the last padded row.
+    """
+    ids = np.asarray(top_experts).reshape(-1).astype(np.int64)
+    E = int(num_experts)
+    if ids.size and (ids.min() < 0 or ids.max() >= E):
+        raise ValueError("expert id out of range")
+    n = ids.size
+    counts = np.bincount(ids, minlength=E).astype(np.int64)
+    indices = np.argsort(ids, kind="stable").astype(np.int64)   # R6
+    bin_ids = ids[indices]
+    bins = np.cumsum(counts)
+    padded = round_up(counts)
+    padded_bins = np.cumsum(padded)
+    bins_start = bins - counts              # R1: exclusive starts
+    padded_start = padded_bins - padded
+    s = np.arange(n, dtype=np.int64)
+    row_of_entry = np.empty(n, dtype=np.int64)
+    row_of_entry[indices] = padded_start[bin_ids] + (s - bins_start[bin_ids])
+    P = int(padded_bins[-1]) if E else 0
+    if n_tiles is None:
+        n_tiles = P // BLOCK
+    tile_expert = np.full(n_tiles, -1, dtype=np.int64)
+    live = np.arange(min(n_tiles, P // BLOCK))
+    tile_expert[live] = np.searchsorted(padded_bins, live * BLOCK, side="right")
+    return dict(tokens_per_expert=counts, bins=bins, padded_bins=padded_bins,
+                indices=indices, bin_ids=bin_ids, row_of_entry=row_of_entry,
+                tile_expert=tile_expert, P=P)
+
+
+def metadata_counting_sort(top_experts, num_experts: int,
+                           n_tiles: Optional[int] = None):
+    """The same metadata with nothing but Python loops (small inputs only).
+
+    A counting sort: count, take running starts, then place the entries in
+    ascending flattened order, which is what makes it stable.
+    """
+    ids = [int(v) for v in np.asarray(top_experts).reshape(-1)]
+    E = int(num_experts)
+    counts = [0] * E
+    for e in ids:
+        counts[e] += 1
+    bins, padded_bins = [], []
+    run = prun = 0
+    for e in range(E):
+        run += counts[e]
+        prun += ((counts[e] + BLOCK - 1) // BLOCK) * BLOCK
+        bins.append(run)
+        padded_bins.append(prun)
+    start = [bins[e] - counts[e] for e in range(E)]
+    pstart = [padded_bins[e] - ((counts[e] + BLOCK - 1) // BLOCK) * BLOCK
+              for e in range(E)]
+    fill = [0] * E
+    indices = [0] * len(ids)
+    bin_ids = [0] * len(ids)
+    row_of_entry = [0] * len(ids)
+    for a, e in enumerate(ids):
+        s = start[e] + fill[e]
+        indices[s] = a
+        bin_ids[s] = e
+        row_of_entry[a] = pstart[e] + fill[e]
+        fill[e] += 1
+    P = padded_bins[-1] if E else 0
+    if n_tiles is None:
+        n_tiles = P // BLOCK
+    tile_expert = []
+    for r in range(n_tiles):
+        owner = -1
+        for e in range(E):
+            if pstart[e] <= r * BLOCK < padded_bins[e]:
+                owner = e
+        tile_expert.append(owner)
+    as_arr = lambda v: np.asarray(v, dtype=np.int64)
+    return dict(tokens_per_expert=as_arr(counts), bins=as_arr(bins),
+                padded_bins=as_arr(padded_bins), indices=as_arr(indices),
+                bin_ids=as_arr(bin_ids), row_of_entry=as_arr(row_of_entry),
+                tile_expert=as_arr(tile_expert), P=P)
+
+
+# --------------------------------------------------------------------------
+# Permutation  ([MB] §4.2, §4.5, §5)
+# --------------------------------------------------------------------------
+
+def padded_gather(x, md, k: int) -> np.ndarray:
+    """Copy token rows into the expert-sorted, 128-padded layout.
+
+    [MB] §4.2 gather direction: ``out[index_b] = x[index_a // TOP_K]``; every
+    other row of the ``padded_bins[-1]``-row output is zero ([MB] §4.5, §5).
+    """
+    x = _f64(x)
+    out = np.zeros((md["P"], x.shape[1]), dtype=np.float64)
+    a = np.arange(md["row_of_entry"].size)
+    out[md["row_of_entry"]] = x[a // k]
+    return out
+
+
+def padded_scatter(y_perm, md, weights, T: int, k: int) -> np.ndarray:
+    """Weighted un-permute with top-k reduction ([MB] §4.2 scatter direction,
+    §4.5 last loop).  Only real rows are read back ([MB] §5); R9: plain sum
+    over the k slots of a token."""
+    y_perm = _f64(y_perm)
+    w = _f64(weights).reshape(-1)
+    rows = y_perm[md["row_of_entry"]] * w[:, None]        # entry a's term
+    return rows.reshape(T, k, -1).sum(axis=1)
+
+
+# --------------------------------------------------------------------------
+# Expert FFN: gated SiLU  ([FL] gated + silu; [MB] §3, §5 GLU variant)
+# --------------------------------------------------------------------------
+
+def sigmoid(z):
+    z = _f64(z)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def silu(z):
+    """silu(z) = z * sigmoid(z) = z / (1 + exp(-z))."""
+    z = _f64(z)
+    return z / (1.0 + np.exp(-z))
+
+
+def forward_loop(x, top_experts, weights, w1, w3, w2):
+    """The layer's definition, one (token, slot) entry at a time.
+
+    For token t and slot j with e = top_experts[t, j]:
+    u1 = x[t] w1[e], u3 = x[t] w3[e], act = silu(u1) * u3, o = act w2[e],
+    y[t] = sum_j weights[t, j] * o.  No token is dropped ([MB] §1, §4.5).
+    Returns y and the per-entry (u1, u3, act, o), entry a = t*k + j.
+    """
+    x, w = _f64(x), _f64(weights)
+    ids = np.asarray(top_experts)
+    T, k = ids.shape
+    F, H = np.shape(w2)[1], x.shape[1]
+    y = np.zeros((T, H))
+    u1s, u3s, acts, outs = (np.zeros((T * k, F)), np.zeros((T * k, F)),
+                            np.zeros((T * k, F)), np.zeros((T * k, H)))
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            u1 = x[t] @ _f64(w1[e])
+            u3 = x[t] @ _f64(w3[e])
+            act = silu(u1) * u3
+            o = act @ _f64(w2[e])
+            y[t] += w[t, j] * o
+            a = t * k + j
+            u1s[a], u3s[a], acts[a], outs[a] = u1, u3, act, o
+    return y, dict(u1=u1s, u3=u3s, act=acts, o=outs)
+
+
+def backward_loop(x, top_experts, weights, w1, w3, w2, dy):
+    """Gradients of sum(y * dy), one entry at a time (chain rule of
+    ``forward_loop``; the routing-weight gradient is the dot product of dy
+    with the expert output, [MB] §4.2 wgrad kernel).
+
+    With s = sigmoid(u1): d silu(u1)/du1 = s * (1 + u1 * (1 - s)).
+    """
+    x, w, dy = _f64(x), _f64(weights), _f64(dy)
+    ids = np.asarray(top_experts)
+    T, k = ids.shape
+    E = np.shape(w1)[0]
+    dx = np.zeros_like(x)
+    dw1 = np.zeros(np.shape(w1))
+    dw3 = np.zeros(np.shape(w3))
+    dw2 = np.zeros(np.shape(w2))
+    dwts = np.zeros((T, k))
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            W1, W3, W2 = _f64(w1[e]), _f64(w3[e]), _f64(w2[e])
+            u1 = x[t] @ W1
+            u3 = x[t] @ W3
+            s = sigmoid(u1)
+            g = u1 * s
+            act = g * u3
+            o = act @ W2
+            dwts[t, j] = dy[t] @ o
+            do = w[t, j] * dy[t]
+            dw2[e] += np.outer(act, do)
+            da = W2 @ do
+            du3 = da * g
+            du1 = da * u3 * s * (1.0 + u1 * (1.0 - s))
+            dw1[e] += np.outer(x[t], du1)
+            dw3[e] += np.outer(x[t], du3)
+            dx[t] += W1 @ du1 + W3 @ du3
+    assert dw1.shape[0] == E
+    return dict(dx=dx, dw1=dw1, dw3=dw3, dw2=dw2, d_weights=dwts)
+
+
+# --------------------------------------------------------------------------
+# The pages' pipeline in the padded layout  ([MB] §3, §4.5)
+# --------------------------------------------------------------------------
+
+def _expert_rows(md, e):
+    """Padded row range [start, end) of expert e (R1)."""
+    end = int(md["padded_bins"][e])
+    start = end - int(round_up(md["tokens_per_expert"][e]))
+    return start, end
+
+
+def forward_padded(x, top_experts, weights, w1, w3, w2, md=None):
+    """Forward through the padded layout, as in [MB] §4.5.
+
+    metadata -> padded gather -> for each expert, the products over its
+    padded row range (the row blocks of one expert touch only that expert's
+    weight columns, [MB] §3) -> gated SiLU -> down projection -> weighted
+    scatter.  Returns y and the padded intermediates.
+    """
+    ids = np.asarray(top_experts)
+    T, k = ids.shape
+    E = np.shape(w1)[0]
+    if md is None:
+        md = metadata(ids, E)
+    xp = padded_gather(x, md, k)
+    P, F, H = md["P"], np.shape(w1)[2], np.shape(x)[1]
+    h1, h3, act, yp = (np.zeros((P, F)), np.zeros((P, F)), np.zeros((P, F)),
+                       np.zeros((P, H)))
+    for e in range(E):
+        r0, r1 = _expert_rows(md, e)
+        if r1 == r0:
+            continue
+        h1[r0:r1] = xp[r0:r1] @ _f64(w1[e])
+        h3[r0:r1] = xp[r0:r1] @ _f64(w3[e])
+        act[r0:r1] = silu(h1[r0:r1]) * h3[r0:r1]
+        yp[r0:r1] = act[r0:r1] @ _f64(w2[e])
+    y = padded_scatter(yp, md, weights, T, k)
+    return y, dict(md=md, x_perm=xp, h1=h1, h3=h3, act=act, y_perm=yp)
+
+
+def backward_padded(x, top_experts, weights, w1, w3, w2, dy, saved=None):
+    """Backward through the padded layout.
+
+    [MB] §4.2: the scatter's backward is a gather of dy times the routing
+    weight plus the routing-weight gradient; the gather's backward is a
+    scatter (unit weights, summed over the k slots).  In between, per expert:
+    dA = dY w2^T, the gated-SiLU derivative, dw2 = A^T dY, dw1 = X^T dH1,
+    dw3 = X^T dH3, dX = dH1 w1^T + dH3 w3^T.  An expert with no rows gets
+    zero weight gradients.
+    """
+    ids = np.asarray(top_experts)
+    T, k = ids.shape
+    E = np.shape(w1)[0]
+    if saved is None:
+        _, saved = forward_padded(x, ids, weights, w1, w3, w2)
+    md = saved["md"]
+    w = _f64(weights).reshape(-1)
+    dy = _f64(dy)
+    P, H = md["P"], dy.shape[1]
+    F = np.shape(w1)[2]
+    a = np.arange(T * k)
+    rows = md["row_of_entry"]
+    dyp = np.zeros((P, H))
+    dyp[rows] = dy[a // k] * w[:, None]
+    d_weights = np.einsum("ah,ah->a", dy[a // k], saved["y_perm"][rows]
+                          ).reshape(T, k)
+    dh1, dh3, dxp = np.zeros((P, F)), np.zeros((P, F)), np.zeros((P, H))
+    dw1 = np.zeros(np.shape(w1))
+    dw3 = np.zeros(np.shape(w3))
+    dw2 = np.zeros(np.shape(w2))
+    xp, h1, h3, act = saved["x_perm"], saved["h1"], saved["h3"], saved["act"]
+    for e in range(E):
+        r0, r1 = _expert_rows(md, e)
+        if r1 == r0:
+            continue
+        W1, W3, W2 = _f64(w1[e]), _f64(w3[e]), _f64(w2[e])
+        da = dyp[r0:r1] @ W2.T
+        s = sigmoid(h1[r0:r1])
+        dh3[r0:r1] = da * h1[r0:r1] * s
+        dh1[r0:r1] = da * h3[r0:r1] * s * (1.0 + h1[r0:r1] * (1.0 - s))
+        dw2[e] = act[r0:r1].T @ dyp[r0:r1]
+        dw1[e] = xp[r0:r1].T @ dh1[r0:r1]
+        dw3[e] = xp[r0:r1].T @ dh3[r0:r1]
+        dxp[r0:r1] = dh1[r0:r1] @ W1.T + dh3[r0:r1] @ W3.T
+    dx = dxp[rows].reshape(T, k, H).sum(axis=1)
+    return dict(dx=dx, dw1=dw1, dw3=dw3, dw2=dw2, d_weights=d_weights,
+                dy_perm=dyp, dh1=dh1, dh3=dh3, dx_perm=dxp)
+
+
+# --------------------------------------------------------------------------
+# Sampled outputs at full size, each from the per-entry definition
+# --------------------------------------------------------------------------
+
+def sampled_rows(x, top_experts, weights, w1, w3, w2, dy,
+                 tokens: Iterable[int]):
+    """y[t], dx[t] and d_weights[t, :] for a few tokens, by the per-entry
+    definition of ``forward_loop``/``backward_loop`` (no other token is
+    needed for these rows)."""
+    ids = np.asarray(top_experts)
+    k = ids.shape[1]
+    out = {}
+    for t in tokens:
+        xt, dyt = _f64(x[t]), _f64(dy[t])
+        y = np.zeros_like(xt)
+        dx = np.zeros_like(xt)
+        dw = np.zeros(k)
+        for j in range(k):
+            e = int(ids[t, j])
+            W1, W3, W2 = _f64(w1[e]), _f64(w3[e]), _f64(w2[e])
+            u1, u3 = xt @ W1, xt @ W3
+            s = sigmoid(u1)
+            g = u1 * s
+            o = (g * u3) @ W2
+            wt = float(weights[t, j])
+            y += wt * o
+            dw[j] = dyt @ o
+            da = W2 @ (wt * dyt)
+            du1 = da * u3 * s * (1.0 + u1 * (1.0 - s))
+            du3 = da * g
+            dx += W1 @ du1 + W3 @ du3
+        out[int(t)] = dict(y=y, dx=dx, d_weights=dw)
+    return out
+
+
+def sampled_dw(x, top_experts, weights, w1, w3, w2, dy,
+               picks: Sequence[Tuple[str, int, int, int]]):
+    """Single elements of dw1/dw3/dw2, each summed over the entries routed to
+    its expert, by the per-entry definition of ``backward_loop``.
+
+    ``picks`` holds (name, e, i, j) with name in {"dw1","dw3","dw2"}:
+    dw1[e][h, f] and dw3[e][h, f] (i = h, j = f), dw2[e][f, h] (i = f, j = h).
+    """
+    ids = np.asarray(top_experts)
+    T, k = ids.shape
+    flat = ids.reshape(-1)
+    wflat = _f64(weights).reshape(-1)
+    res = []
+    cache = {}
+    for name, e, i, j in picks:
+        if e not in cache:
+            ent = np.nonzero(flat == e)[0]           # entries of expert e
+            cache[e] = ent
+        ent = cache[e]
+        if ent.size == 0:
+            res.append(0.0)
+            continue
+        xe = _f64(x[ent // k])                        # [n_e, H]
+        do = _f64(dy[ent // k]) * wflat[ent][:, None]  # [n_e, H]
+        if name == "dw2":
+            f, h = i, j
+            u1 = xe @ _f64(w1[e][:, f])
+            u3 = xe @ _f64(w3[e][:, f])
+            act = silu(u1) * u3
+            res.append(float(act @ do[:, h]))
+        else:
+            h, f = i, j
+            u1 = xe @ _f64(w1[e][:, f])
+            u3 = xe @ _f64(w3[e][:, f])
+            s = sigmoid(u1)
+            da = do @ _f64(w2[e][f, :])
+            if name == "dw1":
+                du = da * u3 * s * (1.0 + u1 * (1.0 - s))
+            elif name == "dw3":
+                du = da * u1 * s
+            else:
+                raise ValueError(name)
+            res.append(float(xe[:, h] @ du))
+    return np.asarray(res)
+
