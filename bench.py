@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the dropless-MoE expert layer on one MI355X.
+
+One step = routing metadata + forward + backward of the whole layer (every
+kernel of the path) on one batch of seeded synthetic input already resident
+in HBM.  Default workload: the fine-grained layer T=4096 (2x2048 tokens),
+H=2048, F=1024, E=64, top-8, bf16, Gaussian router.
+
+Prints ONE JSON line with tokens/s, the per-kernel times measured live with
+HIP events recorded by the library between its kernels in the timed region,
+the roofline of the dominant kernel and the CPU oracle's rate on the host.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 matrix / vector
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+METRIC = "dMoE fwd+bwd tokens/s and useful TFLOP/s (% bf16 MFMA peak), E=64 k=8"
+
+META_KERNELS = ["meta_hist", "meta_scan", "meta_place"]
+FWD_KERNELS = ["padded_gather", "gemm_up_gate", "gemm_down", "padded_scatter"]
+BWD_KERNELS = ["scatter_backward", "gemm_down_dgrad_gate", "gemm_wgrad_down",
+               "gemm_up_dgrad", "gemm_wgrad_up", "gather_backward"]
+
+
+def kernel_work(cfg, P):
+    """Algorithmic FLOPs and bytes of each kernel for P padded rows.
+
+    Bytes are unique reads plus writes; weights are counted once per kernel
+    for the experts that have rows.  GEMM FLOPs are the executed (padded)
+    multiply-adds x2."""
+    s = 4 if cfg.dtype == "f32" else 2
+    T, H, F, E, k = cfg.T, cfg.H, cfg.F, cfg.E, cfg.k
+    N = T * k
+    Ea = E  # every expert is active in the timed workloads
+    w = {}
+    w["meta_hist"] = (0, 4 * N + 4 * E)
+    w["meta_scan"] = (0, 16 * E)
+    w["meta_place"] = (0, 4 * N + 12 * N)
+    w["padded_gather"] = (0, (T * H + P * H) * s)
+    w["gemm_up_gate"] = (4 * P * H * F, (P * H + 2 * Ea * H * F + 3 * P * F) * s)
+    w["gemm_down"] = (2 * P * F * H, (P * F + Ea * F * H + P * H) * s)
+    w["padded_scatter"] = (0, (N * H + T * H) * s + 4 * N)
+    w["scatter_backward"] = (0, (T * H + N * H + P * H) * s + 8 * N)
+    w["gemm_down_dgrad_gate"] = (2 * P * H * F, (P * H + Ea * F * H + 4 * P * F) * s)
+    w["gemm_wgrad_down"] = (2 * P * F * H, (P * F + P * H + Ea * F * H) * s)
+    w["gemm_up_dgrad"] = (4 * P * H * F, (2 * P * F + 2 * Ea * H * F + P * H) * s)
+    w["gemm_wgrad_up"] = (4 * P * H * F, (P * H + 2 * P * F + 2 * Ea * H * F) * s)
+    w["gather_backward"] = (0, (N * H + T * H) * s)
+    return w
+
+
+def cpu_baseline(inp, budget_s=30.0):
+    """Time the fp64 CPU oracle (metadata + forward + backward) on the host."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    y, saved = oracle.forward_padded(inp.x, inp.top_experts, inp.weights,
+                                     inp.w1, inp.w3, inp.w2)
+    g = oracle.backward_padded(inp.x, inp.top_experts, inp.weights, inp.w1,
+                               inp.w3, inp.w2, inp.dy, saved)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(y).all() and np.isfinite(g["dx"]).all()
+    T = inp.cfg.T
+    return {"value": T / dt, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"one full step (metadata + forward + backward, fp64 numpy, "
+                       f"expert-batched) of the same {T}-token workload: {dt:.2f} s; "
+                       f"host os.cpu_count()={os.cpu_count()}")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="fine_e64")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--kernels", action="store_true",
+                    help="also print the per-kernel table on stderr")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if world != 1:
+        print("bench.py is single-process: WORLD_SIZE must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dropless_mixture_experts_amd as dm
+    from dropless_mixture_experts_amd.hip_events import EventArray
+    from workloads import CONFIGS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs an MI355X GPU", file=sys.stderr)
+        sys.exit(1)
+    dm.load_library()   # fail loudly if the HIP library is not built
+    dev = torch.device("cuda:0")
+    cfg = CONFIGS[args.workload]
+    t_gen = time.perf_counter()
+    inp = make_inputs(cfg)
+    t_gen = time.perf_counter() - t_gen
+    dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+    up = lambda a, d=dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(d)
+    x, dy = up(inp.x), up(inp.dy)
+    ids = up(inp.top_experts, torch.int32)
+    w = up(inp.weights, torch.float32)
+    w1, w3, w2 = up(inp.w1), up(inp.w3), up(inp.w2)
+    D = dm.Dims(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k,
+                dm.DMOE_F32 if cfg.dtype == "f32" else dm.DMOE_BF16)
+    layer = dm.DMoELayer(D, dev)
+    y = torch.empty(cfg.T, cfg.H, dtype=dt, device=dev)
+    grads = dict(dx=torch.empty(cfg.T, cfg.H, dtype=dt, device=dev),
+                 dw1=torch.empty_like(w1), dw3=torch.empty_like(w3),
+                 dw2=torch.empty_like(w2),
+                 d_weights=torch.empty(cfg.T, cfg.k, dtype=torch.float32, device=dev))
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        layer.metadata(ids, stream, ev[0] if ev else None)
+        layer.forward(x, ids, w, w1, w3, w2, y=y, stream=stream, run_metadata=False,
+                      events=ev[1] if ev else None)
+        layer.backward(dy, w, w1, w3, w2, grads=grads, stream=stream,
+                       events=ev[2] if ev else None)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    P = int(layer.buf.meta.num_padded_rows.item())
+    assert int(layer.buf.meta.status.item()) == 0
+
+    K = args.steps
+    evs = [(EventArray(4), EventArray(5), EventArray(7)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    names = META_KERNELS + FWD_KERNELS + BWD_KERNELS
+    per = {n: 0.0 for n in names}
+    for ev in evs:
+        for arr, ks in zip(ev, (META_KERNELS, FWD_KERNELS, BWD_KERNELS)):
+            for j, n in enumerate(ks):
+                per[n] += arr.elapsed_ms(j, j + 1) / K
+    for ev in evs:
+        for arr in ev:
+            arr.close()
+
+    ms = elapsed * 1e3 / K
+    tokens_s = cfg.T / (ms * 1e-3)
+    useful_flop = 18.0 * cfg.T * cfg.k * cfg.H * cfg.F
+    executed_flop = 18.0 * P * cfg.H * cfg.F
+    peak = PEAK_F32_TFLOPS if cfg.dtype == "f32" else PEAK_BF16_TFLOPS
+    useful_tf = useful_flop / (ms * 1e-3) / 1e12
+    work = kernel_work(cfg, P)
+    table = {}
+    for n in names:
+        fl, by = work[n]
+        t = per[n] * 1e-3
+        table[n] = {"ms": round(per[n], 4),
+                    "tflops": round(fl / t / 1e12, 1) if fl and t > 0 else None,
+                    "gbs": round(by / t / 1e9, 1) if t > 0 else None}
+    gemms = [n for n in names if n.startswith("gemm")]
+    gemm_ms = sum(per[n] for n in gemms)
+    gs = ["padded_gather", "padded_scatter", "scatter_backward", "gather_backward"]
+    gs_ms = sum(per[n] for n in gs)
+    gs_bytes = sum(work[n][1] for n in gs)
+    dom = max(names, key=lambda n: per[n])
+    fl, by = work[dom]
+    if fl:
+        achieved = fl / (per[dom] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": None}
+    else:
+        achieved = by / (per[dom] * 1e-3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    roof["algorithmic_per_launch"] = fl if fl else by
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded; Gaussian router logits, top-k + softmax)",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "F": cfg.F,
+                   "E": cfg.E, "k": cfg.k, "routing": cfg.routing, "P": P},
+        "useful_tflops": round(useful_tf, 1),
+        "useful_frac_peak": round(useful_tf / peak, 4),
+        "gemm_executed_frac_peak": round(executed_flop / (gemm_ms * 1e-3) / 1e12 / peak, 4),
+        "gather_scatter_frac_hbm": round(gs_bytes / (gs_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "metadata_us": round(1e3 * sum(per[n] for n in META_KERNELS), 1),
+        "roofline": roof,
+        "kernels": table,
+    }
+    if args.kernels:
+        for n in names:
+            print(f"{n:22s} {table[n]}", file=sys.stderr)
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(inp)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,470 @@
+"""Dropless mixture-of-experts (dMoE) expert layer for MI355X (gfx950).
+
+Thin Python binding of the C ABI in ``include/dmoe.h`` (``libdmoe.so``).
+It only marshals arguments: torch tensors supply device pointers and the
+current HIP stream; every step of the layer runs in the HIP kernels.  There is
+no CPU fallback: if the library is missing, importing works but every call
+raises ``DMoELibraryMissing``.
+
+Entry points mirror the C names::
+
+    dmoe_max_tiles(dims)            -> int
+    dmoe_workspace_bytes(dims)      -> int
+    dmoe_metadata(dims, top_experts, meta, ws)
+    dmoe_forward(dims, x, weights, w1, w3, w2, meta, saved, y)
+    dmoe_backward(dims, dy, weights, w1, w3, w2, meta, saved, scratch,
+                  dx, dw1, dw3, dw2, d_weights)
+    dmoe_padded_gather(dims, x, meta, x_perm)
+    dmoe_padded_scatter(dims, src_perm, weights_or_None, meta, out)
+
+``allocate(dims, device)`` creates every caller-owned buffer with torch, and
+``DMoELayer`` / ``dmoe_autograd`` wrap the three calls for convenience.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+__all__ = [
+    "DMOE_F32", "DMOE_BF16", "DMoEError", "DMoELibraryMissing", "Dims",
+    "Meta", "Saved", "GradScratch", "library_path", "load_library",
+    "dmoe_max_tiles", "dmoe_workspace_bytes", "dmoe_metadata", "dmoe_forward",
+    "dmoe_backward", "dmoe_padded_gather", "dmoe_padded_scatter",
+    "dmoe_status_string", "allocate", "allocate_meta", "DMoELayer",
+    "dmoe_autograd",
+]
+
+DMOE_F32 = 0
+DMOE_BF16 = 1
+_DTYPES = {torch.float32: DMOE_F32, torch.bfloat16: DMOE_BF16}
+_TORCH = {v: k for k, v in _DTYPES.items()}
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+
+
+class DMoEError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {dmoe_status_string(code)} (status {code})")
+
+
+class DMoELibraryMissing(ImportError):
+    pass
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("F", ctypes.c_int64), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class _Meta(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "tokens_per_expert", "bins", "padded_bins", "indices", "bin_ids",
+        "row_of_entry", "tile_expert", "num_padded_rows", "status")]
+
+
+class _Saved(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("x_perm", "h1", "h3", "act", "y_perm")]
+
+
+class _Scratch(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("dy_perm", "dh1", "dh3", "dx_perm")]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.environ.get("DMOE_LIBRARY", os.path.join(_PKG, "libdmoe.so"))
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libdmoe.so once; raise DMoELibraryMissing if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise DMoELibraryMissing(
+            f"{path} is not built; run `python -m dropless_mixture_experts_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    vp = ctypes.c_void_p
+    lib.dmoe_max_tiles.argtypes = [P(_Dims)]
+    lib.dmoe_max_tiles.restype = ctypes.c_int64
+    lib.dmoe_workspace_bytes.argtypes = [P(_Dims)]
+    lib.dmoe_workspace_bytes.restype = ctypes.c_int64
+    lib.dmoe_metadata.argtypes = [P(_Dims), vp, P(_Meta), vp, vp]
+    lib.dmoe_metadata.restype = ctypes.c_int
+    lib.dmoe_forward.argtypes = [P(_Dims), vp, vp, vp, vp, vp, P(_Meta),
+                                 P(_Saved), vp, vp]
+    lib.dmoe_forward.restype = ctypes.c_int
+    lib.dmoe_backward.argtypes = [P(_Dims), vp, vp, vp, vp, vp, P(_Meta),
+                                  P(_Saved), P(_Scratch), vp, vp, vp, vp, vp, vp]
+    lib.dmoe_backward.restype = ctypes.c_int
+    lib.dmoe_padded_gather.argtypes = [P(_Dims), vp, P(_Meta), vp, vp]
+    lib.dmoe_padded_gather.restype = ctypes.c_int
+    lib.dmoe_padded_scatter.argtypes = [P(_Dims), vp, vp, P(_Meta), vp, vp]
+    lib.dmoe_padded_scatter.restype = ctypes.c_int
+    lib.dmoe_metadata_timed.argtypes = [P(_Dims), vp, P(_Meta), vp, vp, vp]
+    lib.dmoe_metadata_timed.restype = ctypes.c_int
+    lib.dmoe_forward_timed.argtypes = [P(_Dims), vp, vp, vp, vp, vp, P(_Meta),
+                                       P(_Saved), vp, vp, vp]
+    lib.dmoe_forward_timed.restype = ctypes.c_int
+    lib.dmoe_backward_timed.argtypes = [P(_Dims), vp, vp, vp, vp, vp, P(_Meta),
+                                        P(_Saved), P(_Scratch), vp, vp, vp, vp,
+                                        vp, vp, vp]
+    lib.dmoe_backward_timed.restype = ctypes.c_int
+    lib.dmoe_status_string.argtypes = [ctypes.c_int]
+    lib.dmoe_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+@dataclasses.dataclass(frozen=True)
+class Dims:
+    T: int
+    H: int
+    F: int
+    E: int
+    k: int
+    dtype: int = DMOE_BF16
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return _TORCH[self.dtype]
+
+    def _c(self) -> _Dims:
+        return _Dims(self.T, self.H, self.F, self.E, self.k, self.dtype)
+
+
+@dataclasses.dataclass
+class Meta:
+    tokens_per_expert: torch.Tensor
+    bins: torch.Tensor
+    padded_bins: torch.Tensor
+    indices: torch.Tensor
+    bin_ids: torch.Tensor
+    row_of_entry: torch.Tensor
+    tile_expert: torch.Tensor
+    num_padded_rows: torch.Tensor
+    status: torch.Tensor
+
+    def _c(self) -> _Meta:
+        return _Meta(*[_ptr(getattr(self, f.name), torch.int32, f.name)
+                       for f in dataclasses.fields(self)])
+
+
+@dataclasses.dataclass
+class Saved:
+    x_perm: torch.Tensor
+    h1: torch.Tensor
+    h3: torch.Tensor
+    act: torch.Tensor
+    y_perm: torch.Tensor
+
+    def _c(self, dt) -> _Saved:
+        return _Saved(*[_ptr(getattr(self, f.name), dt, f.name)
+                        for f in dataclasses.fields(self)])
+
+
+@dataclasses.dataclass
+class GradScratch:
+    dy_perm: torch.Tensor
+    dh1: torch.Tensor
+    dh3: torch.Tensor
+    dx_perm: torch.Tensor
+
+    def _c(self, dt) -> _Scratch:
+        return _Scratch(*[_ptr(getattr(self, f.name), dt, f.name)
+                          for f in dataclasses.fields(self)])
+
+
+def _ptr(t: Optional[torch.Tensor], dtype: Optional[torch.dtype], name: str):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a device tensor, got {t.device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, numel: int):
+    if t.numel() < numel:
+        raise ValueError(f"{name}: needs at least {numel} elements, has {t.numel()}")
+
+
+def _stream(t: torch.Tensor, stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream")
+                           else int(stream))
+
+
+def _check(code: int, where: str):
+    if code != 0:
+        raise DMoEError(code, where)
+
+
+def dmoe_status_string(code: int) -> str:
+    try:
+        return load_library().dmoe_status_string(int(code)).decode()
+    except DMoELibraryMissing:
+        return f"status {code}"
+
+
+def dmoe_max_tiles(dims: Dims) -> int:
+    v = load_library().dmoe_max_tiles(ctypes.byref(dims._c()))
+    _check(v if v < 0 else 0, "dmoe_max_tiles")
+    return int(v)
+
+
+def dmoe_workspace_bytes(dims: Dims) -> int:
+    v = load_library().dmoe_workspace_bytes(ctypes.byref(dims._c()))
+    _check(v if v < 0 else 0, "dmoe_workspace_bytes")
+    return int(v)
+
+
+def _check_meta(dims: Dims, meta: Meta):
+    n = dims.T * dims.k
+    for name, size in (("tokens_per_expert", dims.E), ("bins", dims.E),
+                       ("padded_bins", dims.E), ("indices", n), ("bin_ids", n),
+                       ("row_of_entry", n), ("tile_expert", dmoe_max_tiles(dims)),
+                       ("num_padded_rows", 1), ("status", 1)):
+        _need(getattr(meta, name), name, size)
+
+
+def _ev(events, n):
+    """None, or an EventArray of at least n+1 events (see hip_events)."""
+    if events is None:
+        return None
+    if len(events) < n + 1:
+        raise ValueError(f"timing needs {n + 1} events, got {len(events)}")
+    return events.pointer()
+
+
+def dmoe_metadata(dims: Dims, top_experts: torch.Tensor, meta: Meta,
+                  ws: torch.Tensor, stream=None, events=None) -> None:
+    """Routing metadata; see include/dmoe.h.  `events`: optional EventArray
+    of 4 events for per-kernel timing (dmoe_metadata_timed)."""
+    lib = load_library()
+    _need(top_experts, "top_experts", dims.T * dims.k)
+    _check_meta(dims, meta)
+    _need(ws, "ws", dmoe_workspace_bytes(dims) // ws.element_size())
+    _check(lib.dmoe_metadata_timed(ctypes.byref(dims._c()),
+                                   _ptr(top_experts, torch.int32, "top_experts"),
+                                   ctypes.byref(meta._c()), _ptr(ws, None, "ws"),
+                                   _stream(top_experts, stream), _ev(events, 3)),
+           "dmoe_metadata")
+
+
+def _pmax(dims: Dims) -> int:
+    return 128 * dmoe_max_tiles(dims)
+
+
+def dmoe_forward(dims: Dims, x, weights, w1, w3, w2, meta: Meta, saved: Saved,
+                 y, stream=None, events=None) -> None:
+    """Forward of the layer; see include/dmoe.h.  `events`: optional
+    EventArray of 5 events for per-kernel timing (dmoe_forward_timed)."""
+    lib = load_library()
+    dt = dims.torch_dtype
+    T, H, F, E, k = dims.T, dims.H, dims.F, dims.E, dims.k
+    pm = _pmax(dims)
+    for t, n, s in ((x, "x", T * H), (weights, "weights", T * k),
+                    (w1, "w1", E * H * F), (w3, "w3", E * H * F),
+                    (w2, "w2", E * F * H), (y, "y", T * H),
+                    (saved.x_perm, "x_perm", pm * H), (saved.h1, "h1", pm * F),
+                    (saved.h3, "h3", pm * F), (saved.act, "act", pm * F),
+                    (saved.y_perm, "y_perm", pm * H)):
+        _need(t, n, s)
+    _check_meta(dims, meta)
+    _check(lib.dmoe_forward_timed(
+        ctypes.byref(dims._c()), _ptr(x, dt, "x"),
+        _ptr(weights, torch.float32, "weights"), _ptr(w1, dt, "w1"),
+        _ptr(w3, dt, "w3"), _ptr(w2, dt, "w2"), ctypes.byref(meta._c()),
+        ctypes.byref(saved._c(dt)), _ptr(y, dt, "y"), _stream(x, stream),
+        _ev(events, 4)), "dmoe_forward")
+
+
+def dmoe_backward(dims: Dims, dy, weights, w1, w3, w2, meta: Meta, saved: Saved,
+                  scratch: GradScratch, dx, dw1, dw3, dw2, d_weights,
+                  stream=None, events=None) -> None:
+    """Backward of the layer; see include/dmoe.h.  `events`: optional
+    EventArray of 7 events for per-kernel timing (dmoe_backward_timed)."""
+    lib = load_library()
+    dt = dims.torch_dtype
+    T, H, F, E, k = dims.T, dims.H, dims.F, dims.E, dims.k
+    pm = _pmax(dims)
+    for t, n, s in ((dy, "dy", T * H), (weights, "weights", T * k),
+                    (w1, "w1", E * H * F), (w3, "w3", E * H * F),
+                    (w2, "w2", E * F * H), (dx, "dx", T * H),
+                    (dw1, "dw1", E * H * F), (dw3, "dw3", E * H * F),
+                    (dw2, "dw2", E * F * H), (d_weights, "d_weights", T * k),
+                    (scratch.dy_perm, "dy_perm", pm * H),
+                    (scratch.dh1, "dh1", pm * F), (scratch.dh3, "dh3", pm * F),
+                    (scratch.dx_perm, "dx_perm", pm * H)):
+        _need(t, n, s)
+    _check_meta(dims, meta)
+    _check(lib.dmoe_backward_timed(
+        ctypes.byref(dims._c()), _ptr(dy, dt, "dy"),
+        _ptr(weights, torch.float32, "weights"), _ptr(w1, dt, "w1"),
+        _ptr(w3, dt, "w3"), _ptr(w2, dt, "w2"), ctypes.byref(meta._c()),
+        ctypes.byref(saved._c(dt)), ctypes.byref(scratch._c(dt)),
+        _ptr(dx, dt, "dx"), _ptr(dw1, dt, "dw1"), _ptr(dw3, dt, "dw3"),
+        _ptr(dw2, dt, "dw2"), _ptr(d_weights, torch.float32, "d_weights"),
+        _stream(dy, stream), _ev(events, 6)), "dmoe_backward")
+
+
+def dmoe_padded_gather(dims: Dims, x, meta: Meta, x_perm, stream=None) -> None:
+    """padded_gather alone; see include/dmoe.h."""
+    lib = load_library()
+    dt = dims.torch_dtype
+    _need(x, "x", dims.T * dims.H)
+    _need(x_perm, "x_perm", _pmax(dims) * dims.H)
+    _check_meta(dims, meta)
+    _check(lib.dmoe_padded_gather(ctypes.byref(dims._c()), _ptr(x, dt, "x"),
+                                  ctypes.byref(meta._c()), _ptr(x_perm, dt, "x_perm"),
+                                  _stream(x, stream)), "dmoe_padded_gather")
+
+
+def dmoe_padded_scatter(dims: Dims, src_perm, weights, meta: Meta, out,
+                        stream=None) -> None:
+    """padded_scatter alone (weights=None: unit weights); see include/dmoe.h."""
+    lib = load_library()
+    dt = dims.torch_dtype
+    _need(src_perm, "src_perm", _pmax(dims) * dims.H)
+    _need(out, "out", dims.T * dims.H)
+    if weights is not None:
+        _need(weights, "weights", dims.T * dims.k)
+    _check_meta(dims, meta)
+    _check(lib.dmoe_padded_scatter(
+        ctypes.byref(dims._c()), _ptr(src_perm, dt, "src_perm"),
+        _ptr(weights, torch.float32, "weights"), ctypes.byref(meta._c()),
+        _ptr(out, dt, "out"), _stream(out, stream)), "dmoe_padded_scatter")
+
+
+# --------------------------------------------------------------------------
+# Buffer plumbing (torch allocates; the library never does)
+# --------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class Buffers:
+    dims: Dims
+    meta: Meta
+    ws: torch.Tensor
+    saved: Saved
+    scratch: Optional[GradScratch]
+
+
+def allocate_meta(dims: Dims, device):
+    """The metadata arrays and the metadata workspace for `dims`."""
+    n, E = dims.T * dims.k, dims.E
+    nt = dmoe_max_tiles(dims)
+    i32 = dict(dtype=torch.int32, device=device)
+    meta = Meta(torch.empty(E, **i32), torch.empty(E, **i32), torch.empty(E, **i32),
+                torch.empty(n, **i32), torch.empty(n, **i32), torch.empty(n, **i32),
+                torch.empty(nt, **i32), torch.empty(1, **i32), torch.empty(1, **i32))
+    ws = torch.empty(dmoe_workspace_bytes(dims), dtype=torch.uint8, device=device)
+    return meta, ws
+
+
+def allocate(dims: Dims, device, with_backward: bool = True,
+             lean: bool = False) -> Buffers:
+    """Allocate every caller-owned buffer for `dims` on `device`.
+
+    lean=True lets the backward scratch alias the saved activations where
+    include/dmoe.h permits it (dh1 -> h1, dh3 -> h3, dx_perm -> dy_perm)."""
+    pm = 128 * dmoe_max_tiles(dims)
+    meta, ws = allocate_meta(dims, device)
+    fl = dict(dtype=dims.torch_dtype, device=device)
+    saved = Saved(torch.empty(pm, dims.H, **fl), torch.empty(pm, dims.F, **fl),
+                  torch.empty(pm, dims.F, **fl), torch.empty(pm, dims.F, **fl),
+                  torch.empty(pm, dims.H, **fl))
+    scratch = None
+    if with_backward:
+        dyp = torch.empty(pm, dims.H, **fl)
+        if lean:
+            scratch = GradScratch(dyp, saved.h1, saved.h3, dyp)
+        else:
+            scratch = GradScratch(dyp, torch.empty(pm, dims.F, **fl),
+                                  torch.empty(pm, dims.F, **fl),
+                                  torch.empty(pm, dims.H, **fl))
+    return Buffers(dims, meta, ws, saved, scratch)
+
+
+class DMoELayer:
+    """Runs metadata + forward + backward on preallocated buffers."""
+
+    def __init__(self, dims: Dims, device="cuda", lean: bool = False):
+        self.dims = dims
+        self.buf = allocate(dims, device, True, lean)
+        self.device = torch.device(device)
+
+    def metadata(self, top_experts, stream=None, events=None):
+        dmoe_metadata(self.dims, top_experts, self.buf.meta, self.buf.ws, stream,
+                      events)
+
+    def forward(self, x, top_experts, weights, w1, w3, w2, y=None,
+                stream=None, run_metadata=True, events=None):
+        if run_metadata:
+            self.metadata(top_experts, stream)
+        if y is None:
+            y = torch.empty(self.dims.T, self.dims.H, dtype=self.dims.torch_dtype,
+                            device=self.device)
+        dmoe_forward(self.dims, x, weights, w1, w3, w2, self.buf.meta,
+                     self.buf.saved, y, stream, events)
+        return y
+
+    def backward(self, dy, weights, w1, w3, w2, grads=None, stream=None,
+                 events=None):
+        d = self.dims
+        if grads is None:
+            fl = dict(dtype=d.torch_dtype, device=self.device)
+            grads = dict(dx=torch.empty(d.T, d.H, **fl),
+                         dw1=torch.empty(d.E, d.H, d.F, **fl),
+                         dw3=torch.empty(d.E, d.H, d.F, **fl),
+                         dw2=torch.empty(d.E, d.F, d.H, **fl),
+                         d_weights=torch.empty(d.T, d.k, dtype=torch.float32,
+                                               device=self.device))
+        dmoe_backward(d, dy, weights, w1, w3, w2, self.buf.meta, self.buf.saved,
+                      self.buf.scratch, grads["dx"], grads["dw1"], grads["dw3"],
+                      grads["dw2"], grads["d_weights"], stream, events)
+        return grads
+
+
+class _DMoEFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, top_experts, weights, w1, w3, w2):
+        T, H = x.shape
+        E, _, F = w1.shape
+        dims = Dims(T, H, F, E, top_experts.shape[1], _DTYPES[x.dtype])
+        layer = DMoELayer(dims, x.device)
+        args = [a.contiguous() for a in (x, top_experts.to(torch.int32),
+                                         weights.float(), w1, w3, w2)]
+        y = layer.forward(*args)
+        ctx.layer = layer
+        ctx.save_for_backward(*args[2:])
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        weights, w1, w3, w2 = ctx.saved_tensors
+        g = ctx.layer.backward(dy.contiguous(), weights, w1, w3, w2)
+        return g["dx"], None, g["d_weights"], g["dw1"], g["dw3"], g["dw2"]
+
+
+def dmoe_autograd(x, top_experts, weights, w1, w3, w2):
+    """y = dMoE(x) with autograd support (gradients for x, weights, w1/w3/w2)."""
+    return _DMoEFunction.apply(x, top_experts, weights, w1, w3, w2)

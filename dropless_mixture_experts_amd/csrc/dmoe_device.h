@@ -1,0 +1,85 @@
+// Device-side helpers shared by the dMoE kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dmoe {
+
+constexpr int kBlock = 128;          // rows per padded block (MegaBlocks §2)
+constexpr int kWave = 64;
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return static_cast<float>(v); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+// Round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) {
+  return static_cast<bf16>(v);
+}
+
+// 16 bytes as 8 bf16 or 4 fp32, converted to fp32 lanes.
+template <typename T> struct Vec16;
+template <> struct Vec16<float> {
+  static constexpr int N = 4;
+  __device__ __forceinline__ static void unpack(const u32x4& v, float* out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(v[i]);
+  }
+  __device__ __forceinline__ static u32x4 pack(const float* in) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(in[i]);
+    return v;
+  }
+};
+template <> struct Vec16<bf16> {
+  static constexpr int N = 8;
+  __device__ __forceinline__ static void unpack(const u32x4& v, float* out) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(v[i] << 16);
+      out[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+  }
+  __device__ __forceinline__ static u32x4 pack(const float* in) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t lo = __builtin_bit_cast(uint16_t, from_f32<bf16>(in[2 * i]));
+      uint32_t hi = __builtin_bit_cast(uint16_t, from_f32<bf16>(in[2 * i + 1]));
+      v[i] = lo | (hi << 16);
+    }
+    return v;
+  }
+};
+
+// Non-temporal 16-byte global load/store (streamed once).
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void st16(void* p, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+__device__ __forceinline__ void st16_nt(void* p, const u32x4& v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int round_up_block(int c) {
+  return ((c + kBlock - 1) / kBlock) * kBlock;
+}
+
+}  // namespace dmoe

@@ -1,0 +1,65 @@
+// Host-side declarations shared by the C-ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dmoe {
+
+constexpr int kMaxExperts = 256;
+constexpr int kErrExpertId = -5;   // matches DMOE_ERR_EXPERT_ID
+
+struct MetaPtrs {
+  int32_t *tokens_per_expert, *bins, *padded_bins;
+  int32_t *indices, *bin_ids, *row_of_entry;
+  int32_t *tile_expert, *num_padded_rows, *status;
+};
+
+struct Shape {
+  int64_t T, H, F;
+  int E, k;
+  int64_t max_tiles;
+  bool bf16;
+};
+
+// meta.hip
+int64_t meta_chunk(int64_t n);
+int meta_nchunks(int64_t n);
+int64_t meta_workspace_bytes(int64_t n, int E);
+hipError_t launch_metadata(int64_t n, int E, int64_t max_tiles,
+                           const int32_t* ids, const MetaPtrs& m, void* ws,
+                           hipStream_t stream, hipEvent_t* ev);
+
+// permute.hip
+hipError_t launch_padded_gather(const Shape& s, const void* x, const MetaPtrs& m,
+                                void* x_perm, hipStream_t stream);
+hipError_t launch_padded_scatter(const Shape& s, const void* src_perm,
+                                 const float* weights, const MetaPtrs& m,
+                                 void* out, hipStream_t stream);
+hipError_t launch_scatter_backward(const Shape& s, const void* dy,
+                                   const void* y_perm, const float* weights,
+                                   const MetaPtrs& m, void* dy_perm,
+                                   float* d_weights, hipStream_t stream);
+
+// gemm.hip
+hipError_t launch_gemm_up(const Shape& s, const void* x_perm, const void* w1,
+                          const void* w3, const MetaPtrs& m, void* h1, void* h3,
+                          void* act, hipStream_t stream);
+hipError_t launch_gemm_down(const Shape& s, const void* act, const void* w2,
+                            const MetaPtrs& m, void* y_perm, hipStream_t stream);
+hipError_t launch_gemm_down_dgrad(const Shape& s, const void* dy_perm,
+                                  const void* w2, const void* h1, const void* h3,
+                                  const MetaPtrs& m, void* dh1, void* dh3,
+                                  hipStream_t stream);
+hipError_t launch_gemm_up_dgrad(const Shape& s, const void* dh1, const void* dh3,
+                                const void* w1, const void* w3, const MetaPtrs& m,
+                                void* dx_perm, hipStream_t stream);
+hipError_t launch_gemm_wgrad_down(const Shape& s, const void* act,
+                                  const void* dy_perm, const MetaPtrs& m,
+                                  void* dw2, hipStream_t stream);
+hipError_t launch_gemm_wgrad_up(const Shape& s, const void* x_perm,
+                                const void* dh1, const void* dh3,
+                                const MetaPtrs& m, void* dw1, void* dw3,
+                                hipStream_t stream);
+
+}  // namespace dmoe

@@ -1,0 +1,260 @@
+// Routing metadata for the dropless MoE layer (gfx950).
+//
+// MegaBlocks chapter "02 · dropless MoE 与 block-sparse 重构": §4.1 asks for a
+// sort of the (token, expert) entries by expert, a histogram, its inclusive
+// cumsum `bins`, the counts rounded up to 128 and their inclusive cumsum
+// `padded_bins`; §4.2 places sorted entry s of expert e on padded row
+// (s - bins[e-1]) + padded_bins[e-1]; §2/§4.3 give each 128-row block one
+// expert.  The Fast-LLM issue "[feat] Support sparse copy for a large number
+// of experts" reports a metadata kernel whose on-chip footprint grew with the
+// token count and overflowed shared memory at 64 experts; here on-chip memory
+// is O(E) (at most ~5 KB at E = 256) whatever T is.
+//
+// Three launches, stream-ordered, no host synchronisation:
+//   meta_hist   one wave per chunk of entries: expert histogram of the chunk
+//               (LDS counters) and an invalid-id flag.
+//   meta_scan   one workgroup: per-expert totals, bins / padded_bins / P,
+//               each chunk's starting sorted position per expert, the
+//               block -> expert table, the status word.
+//   meta_place  one wave per chunk: stable rank of every entry among the
+//               chunk's entries of the same expert (64-lane ballots on the
+//               bits of the id + mbcnt), then writes indices, bin_ids and
+//               row_of_entry.  Ties keep ascending entry order, so the
+//               result is unique and bit-identical on every run.
+#include "dmoe_device.h"
+#include "dmoe_internal.h"
+
+namespace dmoe {
+
+constexpr int kMetaWaves = 4;  // waves (chunks) per workgroup
+constexpr int kScanThreads = 1024;
+
+__global__ void __launch_bounds__(kMetaWaves * kWave)
+meta_hist_kernel(const int32_t* __restrict__ ids, int64_t n, int64_t chunk,
+                 int nchunks, int E, int32_t* __restrict__ hist,
+                 int32_t* __restrict__ err) {
+  __shared__ int32_t cnt[kMetaWaves][kMaxExperts];
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int c = blockIdx.x * kMetaWaves + w;
+  for (int i = lane; i < E; i += kWave) cnt[w][i] = 0;
+  __syncthreads();
+  int bad = 0;
+  if (c < nchunks) {
+    const int64_t beg = c * chunk;
+    const int64_t end = min(n, beg + chunk);
+    for (int64_t a = beg + lane; a < end; a += kWave) {
+      const int e = ids[a];
+      if (e >= 0 && e < E)
+        atomicAdd(&cnt[w][e], 1);   // integer count: order does not matter
+      else
+        bad = 1;
+    }
+  }
+  __syncthreads();
+  if (c < nchunks) {
+    for (int i = lane; i < E; i += kWave) hist[(int64_t)c * E + i] = cnt[w][i];
+    const unsigned long long any_bad = __ballot(bad);
+    if (lane == 0) err[c] = any_bad ? 1 : 0;
+  }
+}
+
+// One workgroup of 1024 threads.  Thread (e, seg) owns expert e over the
+// seg-th range of chunks; Ecap (a power of two >= E) experts x S segments.
+__global__ void __launch_bounds__(kScanThreads)
+meta_scan_kernel(int32_t* __restrict__ hist, const int32_t* __restrict__ err,
+                 int nchunks, int E, int Ecap, int max_tiles,
+                 int32_t* __restrict__ tokens_per_expert,
+                 int32_t* __restrict__ bins, int32_t* __restrict__ padded_bins,
+                 int32_t* __restrict__ tile_expert,
+                 int32_t* __restrict__ num_padded_rows,
+                 int32_t* __restrict__ status) {
+  __shared__ int32_t seg_tot[kScanThreads];
+  __shared__ int32_t count_s[kMaxExperts];
+  __shared__ int32_t start_s[kMaxExperts];
+  __shared__ int32_t pend_s[kMaxExperts];
+  __shared__ int32_t P_s, bad_s;
+  const int tid = threadIdx.x;
+  const int S = kScanThreads / Ecap;
+  const int e = tid % Ecap, seg = tid / Ecap;
+  const int seg_len = (nchunks + S - 1) / S;
+  const int c0 = min(nchunks, seg * seg_len);
+  const int c1 = min(nchunks, c0 + seg_len);
+
+  int sum = 0;
+  if (e < E)
+    for (int c = c0; c < c1; ++c) sum += hist[(int64_t)c * E + e];
+  seg_tot[tid] = sum;
+  if (tid == 0) bad_s = 0;
+  __syncthreads();
+  for (int c = tid; c < nchunks; c += kScanThreads)
+    if (err[c]) bad_s = 1;                 // every writer stores the same 1
+  if (tid < E) {
+    int tot = 0;
+    for (int s = 0; s < S; ++s) tot += seg_tot[s * Ecap + tid];
+    count_s[tid] = tot;
+  }
+  __syncthreads();
+
+  // Inclusive scans over experts of the counts and the rounded-up counts:
+  // wave 0, four consecutive experts per lane, then a 64-lane shuffle scan.
+  if (tid < kWave) {
+    int c[4], pc[4], cs = 0, ps = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ee = tid * 4 + i;
+      c[i] = ee < E ? count_s[ee] : 0;
+      pc[i] = round_up_block(c[i]);
+      cs += c[i];
+      ps += pc[i];
+    }
+    int ci = cs, pi = ps;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int cu = __shfl_up(ci, off, kWave);
+      const int pu = __shfl_up(pi, off, kWave);
+      if (tid >= off) { ci += cu; pi += pu; }
+    }
+    int crun = ci - cs, prun = pi - ps;    // exclusive starts of this lane
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ee = tid * 4 + i;
+      if (ee < E) {
+        start_s[ee] = crun;
+        crun += c[i];
+        prun += pc[i];
+        pend_s[ee] = prun;
+        tokens_per_expert[ee] = c[i];
+        bins[ee] = crun;
+        padded_bins[ee] = prun;
+      }
+    }
+    if (tid == kWave - 1) {
+      P_s = pi;
+      *num_padded_rows = pi;
+    }
+  }
+  __syncthreads();
+
+  // Each chunk's first sorted position per expert (exclusive, global).
+  if (e < E) {
+    int run = start_s[e];
+    for (int s = 0; s < seg; ++s) run += seg_tot[s * Ecap + e];
+    for (int c = c0; c < c1; ++c) {
+      const int64_t i = (int64_t)c * E + e;
+      const int v = hist[i];
+      hist[i] = run;
+      run += v;
+    }
+  }
+  // 128-row block r -> its expert: the first e with padded_bins[e] > 128 r.
+  const int P = P_s;
+  for (int r = tid; r < max_tiles; r += kScanThreads) {
+    const int row = r * kBlock;
+    int owner = -1;
+    if (row < P) {
+      int lo = 0, hi = E - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (pend_s[mid] > row) hi = mid; else lo = mid + 1;
+      }
+      owner = lo;
+    }
+    tile_expert[r] = owner;
+  }
+  if (tid == 0) *status = bad_s ? kErrExpertId : 0;
+}
+
+__global__ void __launch_bounds__(kMetaWaves * kWave)
+meta_place_kernel(const int32_t* __restrict__ ids, int64_t n, int64_t chunk,
+                  int nchunks, int E, int nbits,
+                  const int32_t* __restrict__ chunk_start,
+                  const int32_t* __restrict__ tokens_per_expert,
+                  const int32_t* __restrict__ bins,
+                  const int32_t* __restrict__ padded_bins,
+                  int32_t* __restrict__ indices, int32_t* __restrict__ bin_ids,
+                  int32_t* __restrict__ row_of_entry) {
+  __shared__ int32_t run[kMetaWaves][kMaxExperts];
+  __shared__ int32_t shift_s[kMaxExperts];   // padded start - sorted start
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int c = blockIdx.x * kMetaWaves + w;
+  for (int i = threadIdx.x; i < E; i += blockDim.x) {
+    const int cnt = tokens_per_expert[i];
+    shift_s[i] = (padded_bins[i] - round_up_block(cnt)) - (bins[i] - cnt);
+  }
+  if (c < nchunks)
+    for (int i = lane; i < E; i += kWave) run[w][i] = chunk_start[(int64_t)c * E + i];
+  __syncthreads();
+  if (c >= nchunks) return;
+
+  const int64_t beg = c * chunk;
+  const int64_t end = min(n, beg + chunk);
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  for (int64_t base = beg; base < end; base += kWave) {
+    const int64_t a = base + lane;
+    const bool in = a < end;
+    const int e = in ? ids[a] : -1;
+    const bool ok = in && e >= 0 && e < E;
+    // Lanes holding the same expert id: intersect ballots over its bits.
+    unsigned long long same = __ballot(ok);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = ok && ((e >> b) & 1);
+      const unsigned long long on = __ballot(bit);
+      same &= ((e >> b) & 1) ? on : ~on;
+    }
+    if (ok) {
+      const int rank = __popcll(same & lt);
+      const int pos = run[w][e] + rank;
+      indices[pos] = (int32_t)a;
+      bin_ids[pos] = e;
+      row_of_entry[a] = pos + shift_s[e];
+      if ((same & lt) == 0ull) run[w][e] = pos + __popcll(same);  // group leader
+    } else if (in) {
+      row_of_entry[a] = -1;
+    }
+  }
+}
+
+int64_t meta_chunk(int64_t n) {
+  // >= 1024 entries per wave, and at most 4096 chunks.
+  int64_t c = (n + 4095) / 4096;
+  c = ((c + kWave - 1) / kWave) * kWave;
+  return c < 1024 ? 1024 : c;
+}
+
+int meta_nchunks(int64_t n) { return (int)((n + meta_chunk(n) - 1) / meta_chunk(n)); }
+
+int64_t meta_workspace_bytes(int64_t n, int E) {
+  const int64_t nc = meta_nchunks(n);
+  return ((nc * E + nc) * (int64_t)sizeof(int32_t) + 255) / 256 * 256;
+}
+
+hipError_t launch_metadata(int64_t n, int E, int64_t max_tiles,
+                           const int32_t* ids, const MetaPtrs& m, void* ws,
+                           hipStream_t stream, hipEvent_t* ev) {
+  const int64_t chunk = meta_chunk(n);
+  const int nchunks = meta_nchunks(n);
+  int32_t* hist = static_cast<int32_t*>(ws);
+  int32_t* err = hist + (int64_t)nchunks * E;
+  int Ecap = 1;
+  while (Ecap < E) Ecap <<= 1;
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const int blocks = (nchunks + kMetaWaves - 1) / kMetaWaves;
+  if (ev) hipEventRecord(ev[0], stream);
+  hipLaunchKernelGGL(meta_hist_kernel, dim3(blocks), dim3(kMetaWaves * kWave), 0,
+                     stream, ids, n, chunk, nchunks, E, hist, err);
+  if (ev) hipEventRecord(ev[1], stream);
+  hipLaunchKernelGGL(meta_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream,
+                     hist, err, nchunks, E, Ecap, (int)max_tiles,
+                     m.tokens_per_expert, m.bins, m.padded_bins, m.tile_expert,
+                     m.num_padded_rows, m.status);
+  if (ev) hipEventRecord(ev[2], stream);
+  hipLaunchKernelGGL(meta_place_kernel, dim3(blocks), dim3(kMetaWaves * kWave), 0,
+                     stream, ids, n, chunk, nchunks, E, nbits, hist,
+                     m.tokens_per_expert, m.bins, m.padded_bins, m.indices,
+                     m.bin_ids, m.row_of_entry);
+  if (ev) hipEventRecord(ev[3], stream);
+  return hipGetLastError();
+}
+
+}  // namespace dmoe

@@ -1,0 +1,209 @@
+/*
+ * dmoe.h -- C ABI of the dropless mixture-of-experts (dMoE) expert layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer, as the MegaBlocks chapter "02 · dropless MoE 与 block-sparse 重构"
+ * describes it: every (token, slot) entry chosen by the router is kept (no
+ * capacity, no dropping, §1); the entries are sorted by expert, each
+ * expert's count is rounded up to a multiple of 128 so that every 128-row
+ * block belongs to one expert (§2, §4.1); token rows are copied into that
+ * padded layout (padded_gather, §4.2); each expert's FFN runs on its row
+ * blocks only (the sdd/dsd pair of §3, here gated SiLU as in the Fast-LLM
+ * issue "[feat] Support sparse copy for a large number of experts"); the
+ * results are copied back, scaled by the routing weight and summed over the
+ * k slots (padded_scatter, §4.2).  The backward pairs gather with scatter
+ * and adds the routing-weight gradient (§4.2).
+ *
+ *   y[t] = sum_j weights[t,j] * ( silu(x[t] w1[e]) * (x[t] w3[e]) ) w2[e],
+ *          e = top_experts[t,j],  silu(z) = z / (1 + exp(-z)).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers.  Every array argument is a DEVICE pointer owned by the caller.
+ *   The library allocates nothing, frees nothing and never synchronises
+ *   the host: all work is enqueued on `stream` (a hipStream_t; NULL is the
+ *   default stream).  No state is kept between calls; calls on different
+ *   streams with disjoint buffers may run concurrently.
+ * - Layouts.  Row-major and contiguous.  x, dy, dx, y: [T,H].
+ *   top_experts: int32 [T,k].  weights, d_weights: fp32 [T,k] for every
+ *   dtype.  w1, w3, dw1, dw3: [E,H,F].  w2, dw2: [E,F,H].  The floating
+ *   arrays other than weights/d_weights are all of `dims->dtype`.
+ * - Entry numbering.  Entry a = t*k + j is slot j of token t.
+ * - Padded rows.  P = padded_bins[E-1] is known only on the device
+ *   (meta.num_padded_rows).  Buffers with padded rows are sized for
+ *   P_max = 128 * dmoe_max_tiles(dims) rows.  Rows in [P, P_max) are left
+ *   untouched.  Pad rows inside [0, P) are written as exact zeros.
+ * - Precision.  bf16 inputs are multiplied on the matrix cores with fp32
+ *   accumulation; every stored intermediate (x_perm, h1, h3, act, y_perm,
+ *   dy_perm, dh1, dh3, dx_perm) and every output is rounded once to the
+ *   I/O dtype (round to nearest even).  The top-k sums run in fp32 in slot
+ *   order.  fp32 runs in full fp32.
+ * - Determinism.  No reduction uses atomics; results are bitwise
+ *   reproducible run to run.
+ * - Errors.  Argument and shape errors are detected on the host before any
+ *   launch and returned as a negative dmoe_status; nothing is enqueued then.
+ *   An expert id outside [0,E) is a data error found on the device:
+ *   dmoe_metadata stores DMOE_ERR_EXPERT_ID in meta.status (0 otherwise),
+ *   the offending entries get row_of_entry = -1 and contribute nothing;
+ *   other outputs are then unspecified.  The caller reads meta.status after
+ *   its own synchronisation.  A failed launch returns DMOE_ERR_HIP.
+ */
+#ifndef DMOE_H
+#define DMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DMOE_BLOCK 128       /* rows per padded block (MegaBlocks §2) */
+#define DMOE_MAX_EXPERTS 256
+
+typedef enum {
+  DMOE_OK = 0,
+  DMOE_ERR_ARG = -1,         /* null pointer, non-positive size, k > E, T*k >= 2^31 */
+  DMOE_ERR_SHAPE = -2,       /* F % 128 != 0 (MegaBlocks §5) or H % 128 != 0 */
+  DMOE_ERR_UNSUPPORTED = -3, /* E > 256, an unknown dtype, H or F > 2^24, or
+                                (forward/backward) more than 65535 row blocks */
+  DMOE_ERR_HIP = -4,         /* a kernel launch failed */
+  DMOE_ERR_EXPERT_ID = -5    /* device-side: an expert id outside [0,E) */
+} dmoe_status;
+
+typedef enum { DMOE_F32 = 0, DMOE_BF16 = 1 } dmoe_dtype;
+
+/* Problem sizes.  T tokens, hidden size H, per-expert ffn size F, E experts,
+ * top-k slots per token, element type of the floating arrays. */
+typedef struct {
+  int64_t T, H, F;
+  int32_t E, k;
+  int32_t dtype;             /* a dmoe_dtype */
+} dmoe_dims;
+
+/* Routing metadata, written by dmoe_metadata and read by the other calls
+ * (MegaBlocks §4.1-§4.3).  All device int32 arrays owned by the caller.
+ *   tokens_per_expert[E]  histogram of the expert ids
+ *   bins[E]               inclusive cumsum of tokens_per_expert
+ *   padded_bins[E]        inclusive cumsum of round_up(tokens_per_expert, 128)
+ *   indices[T*k]          stable sort of the entries by expert: indices[s] = a
+ *   bin_ids[T*k]          expert of the s-th sorted entry
+ *   row_of_entry[T*k]     padded row of entry a:
+ *                         (s - bins[e-1]) + padded_bins[e-1], both starts 0 at e=0
+ *   tile_expert[max_tiles] expert owning 128-row block r; -1 for r >= P/128
+ *   num_padded_rows[1]    P = padded_bins[E-1]
+ *   status[1]             0, or DMOE_ERR_EXPERT_ID                        */
+typedef struct {
+  int32_t *tokens_per_expert, *bins, *padded_bins;
+  int32_t *indices, *bin_ids, *row_of_entry;
+  int32_t *tile_expert;
+  int32_t *num_padded_rows;
+  int32_t *status;
+} dmoe_meta;
+
+/* Activations kept from forward for backward, each [P_max, H] or [P_max, F]
+ * of dtype: x_perm [.,H] (padded_gather output), h1 = x_perm w1, h3 = x_perm w3,
+ * act = silu(h1)*h3 [.,F], y_perm = act w2 [.,H]. */
+typedef struct {
+  void *x_perm, *h1, *h3, *act, *y_perm;
+} dmoe_saved;
+
+/* Backward intermediates, caller-owned: dy_perm [.,H], dh1, dh3 [.,F],
+ * dx_perm [.,H], all [P_max, .] of dtype.  dh1 may alias saved.h1, dh3 may
+ * alias saved.h3 and dx_perm may alias dy_perm (each element is read before
+ * it is overwritten); no other aliasing is allowed. */
+typedef struct {
+  void *dy_perm, *dh1, *dh3, *dx_perm;
+} dmoe_grad_scratch;
+
+/* Number of 128-row blocks that bound P:
+ * floor((T*k + 127*min(E, T*k)) / 128), since each non-empty expert adds at
+ * most 127 pad rows (MegaBlocks §2).  Returns a negative dmoe_status on bad
+ * dims. */
+int64_t dmoe_max_tiles(const dmoe_dims* dims);
+
+/* Bytes of device workspace `ws` that dmoe_metadata needs (per-chunk
+ * expert histograms and error flags).  The other entry points take no
+ * workspace.  Returns a negative dmoe_status on bad dims. */
+int64_t dmoe_workspace_bytes(const dmoe_dims* dims);
+
+/* Routing metadata (MegaBlocks §4.1 sort / histogram / cumsum and round_up,
+ * §4.2 padded row of each entry, §4.3 row block -> expert).
+ * top_experts: int32 [T,k] device.  Writes every array of *meta.
+ * ws: device scratch of dmoe_workspace_bytes(dims) bytes; contents on entry
+ * are ignored.  LDS use is O(E) and independent of T. */
+int dmoe_metadata(const dmoe_dims* dims, const int32_t* top_experts,
+                  const dmoe_meta* meta, void* ws, hipStream_t stream);
+
+/* Forward: padded_gather (MegaBlocks §4.2) -> per-128-row-block gated-SiLU
+ * up projection (the sdd of §3, GLU variant of §5) -> down projection (the
+ * dsd of §3) -> padded_scatter with the routing weights and the top-k sum
+ * (§4.2, §4.5).  Reads x, weights, w1, w3, w2 and *meta (from
+ * dmoe_metadata); writes every buffer of *saved and y [T,H]. */
+int dmoe_forward(const dmoe_dims* dims, const void* x, const float* weights,
+                 const void* w1, const void* w3, const void* w2,
+                 const dmoe_meta* meta, const dmoe_saved* saved, void* y,
+                 hipStream_t stream);
+
+/* Backward of dmoe_forward for upstream gradient dy [T,H] (MegaBlocks §4.2:
+ * the scatter's backward is a gather of dy times the routing weight plus the
+ * routing-weight gradient d_weights[a] = <dy[a/k], y_perm[row_of_entry[a]]>;
+ * the gather's backward is a scatter summing the k slots).  Reads *saved
+ * from the forward of the same inputs.  Writes dx [T,H], dw1, dw3 [E,H,F],
+ * dw2 [E,F,H] (overwritten, not accumulated; experts with no rows get
+ * zeros), d_weights fp32 [T,k] and every buffer of *scratch. */
+int dmoe_backward(const dmoe_dims* dims, const void* dy, const float* weights,
+                  const void* w1, const void* w3, const void* w2,
+                  const dmoe_meta* meta, const dmoe_saved* saved,
+                  const dmoe_grad_scratch* scratch, void* dx, void* dw1,
+                  void* dw3, void* dw2, float* d_weights, hipStream_t stream);
+
+/* padded_gather alone (MegaBlocks §4.2, gather direction): for every real
+ * padded row p of entry a, x_perm[p] = x[a / k]; pad rows below P are zero.
+ * x [T,H], x_perm [P_max,H] of dtype; *meta from dmoe_metadata. */
+int dmoe_padded_gather(const dmoe_dims* dims, const void* x, const dmoe_meta* meta,
+                       void* x_perm, hipStream_t stream);
+
+/* padded_scatter alone (MegaBlocks §4.2, scatter direction, and the top-k
+ * sum of §4.5): out[t] = sum_j w[t,j] * src_perm[row_of_entry[t*k+j]], in
+ * fp32 in slot order, rounded once.  weights may be NULL for unit weights
+ * (the gather's backward).  src_perm [P_max,H], out [T,H] of dtype. */
+int dmoe_padded_scatter(const dmoe_dims* dims, const void* src_perm,
+                        const float* weights, const dmoe_meta* meta, void* out,
+                        hipStream_t stream);
+
+/* The same three calls with per-kernel timing.  `events` is NULL or an array
+ * of n+1 caller-created hipEvent_t; event i is recorded on `stream` just
+ * before kernel i and event n after the last kernel, so the elapsed time
+ * between events i and i+1 is kernel i's duration on the stream.
+ *   metadata (n = 3): histogram, scan, placement.
+ *   forward  (n = 4): padded_gather, up projection + SiLU gate, down
+ *                     projection, padded_scatter.
+ *   backward (n = 6): scatter backward (dy_perm, d_weights), down dgrad +
+ *                     gate backward, dw2, up dgrad (dx_perm), dw1 + dw3,
+ *                     gather backward (dx).
+ * Results are identical to the untimed calls. */
+int dmoe_metadata_timed(const dmoe_dims* dims, const int32_t* top_experts,
+                        const dmoe_meta* meta, void* ws, hipStream_t stream,
+                        hipEvent_t* events);
+int dmoe_forward_timed(const dmoe_dims* dims, const void* x, const float* weights,
+                       const void* w1, const void* w3, const void* w2,
+                       const dmoe_meta* meta, const dmoe_saved* saved, void* y,
+                       hipStream_t stream, hipEvent_t* events);
+int dmoe_backward_timed(const dmoe_dims* dims, const void* dy, const float* weights,
+                        const void* w1, const void* w3, const void* w2,
+                        const dmoe_meta* meta, const dmoe_saved* saved,
+                        const dmoe_grad_scratch* scratch, void* dx, void* dw1,
+                        void* dw3, void* dw2, float* d_weights, hipStream_t stream,
+                        hipEvent_t* events);
+
+/* Static text for a dmoe_status value. */
+const char* dmoe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMOE_H */

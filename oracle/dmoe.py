@@ -376,30 +376,33 @@ def sampled_rows(x, top_experts, weights, w1, w3, w2, dy,
                  tokens: Iterable[int]):
     """y[t], dx[t] and d_weights[t, :] for a few tokens, by the per-entry
     definition of ``forward_loop``/``backward_loop`` (no other token is
-    needed for these rows)."""
+    needed for these rows).  Entries are visited expert by expert so that
+    each expert's weights are converted to fp64 once."""
     ids = np.asarray(top_experts)
     k = ids.shape[1]
-    out = {}
+    tokens = [int(t) for t in tokens]
+    H = np.shape(x)[1]
+    out = {t: dict(y=np.zeros(H), dx=np.zeros(H), d_weights=np.zeros(k))
+           for t in tokens}
+    by_expert: Dict[int, list] = {}
     for t in tokens:
-        xt, dyt = _f64(x[t]), _f64(dy[t])
-        y = np.zeros_like(xt)
-        dx = np.zeros_like(xt)
-        dw = np.zeros(k)
         for j in range(k):
-            e = int(ids[t, j])
-            W1, W3, W2 = _f64(w1[e]), _f64(w3[e]), _f64(w2[e])
+            by_expert.setdefault(int(ids[t, j]), []).append((t, j))
+    for e, ents in sorted(by_expert.items()):
+        W1, W3, W2 = _f64(w1[e]), _f64(w3[e]), _f64(w2[e])
+        for t, j in ents:
+            xt, dyt = _f64(x[t]), _f64(dy[t])
             u1, u3 = xt @ W1, xt @ W3
             s = sigmoid(u1)
             g = u1 * s
             o = (g * u3) @ W2
             wt = float(weights[t, j])
-            y += wt * o
-            dw[j] = dyt @ o
+            out[t]["y"] += wt * o
+            out[t]["d_weights"][j] = dyt @ o
             da = W2 @ (wt * dyt)
             du1 = da * u3 * s * (1.0 + u1 * (1.0 - s))
             du3 = da * g
-            dx += W1 @ du1 + W3 @ du3
-        out[int(t)] = dict(y=y, dx=dx, d_weights=dw)
+            out[t]["dx"] += W1 @ du1 + W3 @ du3
     return out
 
 
@@ -420,13 +423,16 @@ def sampled_dw(x, top_experts, weights, w1, w3, w2, dy,
     for name, e, i, j in picks:
         if e not in cache:
             ent = np.nonzero(flat == e)[0]           # entries of expert e
-            cache[e] = ent
-        ent = cache[e]
+            if ent.size:
+                xe = _f64(x[ent // k])                         # [n_e, H]
+                do = _f64(dy[ent // k]) * wflat[ent][:, None]  # [n_e, H]
+            else:
+                xe = do = None
+            cache[e] = (ent, xe, do)
+        ent, xe, do = cache[e]
         if ent.size == 0:
             res.append(0.0)
             continue
-        xe = _f64(x[ent // k])                        # [n_e, H]
-        do = _f64(dy[ent // k]) * wflat[ent][:, None]  # [n_e, H]
         if name == "dw2":
             f, h = i, j
             u1 = xe @ _f64(w1[e][:, f])
@@ -447,4 +453,3 @@ def sampled_dw(x, top_experts, weights, w1, w3, w2, dy,
                 raise ValueError(name)
             res.append(float(xe[:, h] @ du))
     return np.asarray(res)
-

@@ -1,0 +1,111 @@
+"""The C-ABI library loads and exports every entry point include/dmoe.h
+declares; host-side argument checks return their status codes before any
+launch (no GPU needed: nothing is enqueued when a check fails)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dropless_mixture_experts_amd as dm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dmoe.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dmoe_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dm.library_path()):
+        pytest.fail("libdmoe.so is not built: run __graft_entry__.build()")
+    return dm.load_library()
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("dmoe_metadata", "dmoe_forward", "dmoe_backward", "dmoe_max_tiles",
+              "dmoe_workspace_bytes", "dmoe_padded_gather", "dmoe_padded_scatter",
+              "dmoe_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def _dims(**kw):
+    d = dict(T=512, H=128, F=256, E=8, k=2, dtype=dm.DMOE_F32)
+    d.update(kw)
+    return dm._Dims(d["T"], d["H"], d["F"], d["E"], d["k"], d["dtype"])
+
+
+def test_max_tiles_and_workspace(lib):
+    d = _dims()
+    # floor((1024 + 127*8)/128) = floor(2040/128) = 15
+    assert lib.dmoe_max_tiles(ctypes.byref(d)) == 15
+    assert lib.dmoe_workspace_bytes(ctypes.byref(d)) > 0
+    d = _dims(T=16384, H=1536, F=256, E=256, k=8)
+    assert lib.dmoe_max_tiles(ctypes.byref(d)) == (131072 + 127 * 256) // 128
+    d = _dims(T=1, k=1, E=256)           # min(E, T*k) = 1
+    assert lib.dmoe_max_tiles(ctypes.byref(d)) == 1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(F=200), -2), (dict(H=100), -2), (dict(E=257, k=2), -3),
+    (dict(k=9, E=8), -1), (dict(T=0), -1), (dict(E=0), -1), (dict(k=0), -1),
+    (dict(dtype=7), -3), (dict(T=1 << 29, k=8, E=8), -1)])
+def test_bad_dims_rejected(lib, kw, code):
+    d = _dims(**kw)
+    assert lib.dmoe_max_tiles(ctypes.byref(d)) == code
+    assert lib.dmoe_workspace_bytes(ctypes.byref(d)) == code
+    meta = dm._Meta(*([ctypes.c_void_p(0x1000)] * 9))
+    assert lib.dmoe_metadata(ctypes.byref(d), ctypes.c_void_p(0x1000),
+                             ctypes.byref(meta), ctypes.c_void_p(0x1000), None) == code
+
+
+def test_null_pointers_rejected_before_launch(lib):
+    d = _dims()
+    meta = dm._Meta(*([ctypes.c_void_p(0x1000)] * 9))
+    assert lib.dmoe_metadata(ctypes.byref(d), None, ctypes.byref(meta),
+                             ctypes.c_void_p(0x1000), None) == -1
+    assert lib.dmoe_metadata(ctypes.byref(d), ctypes.c_void_p(0x1000),
+                             ctypes.byref(meta), None, None) == -1
+    bad = dm._Meta(*([ctypes.c_void_p(0x1000)] * 8 + [None]))
+    assert lib.dmoe_metadata(ctypes.byref(d), ctypes.c_void_p(0x1000),
+                             ctypes.byref(bad), ctypes.c_void_p(0x1000), None) == -1
+    saved = dm._Saved(*([ctypes.c_void_p(0x1000)] * 4 + [None]))
+    p = ctypes.c_void_p(0x1000)
+    assert lib.dmoe_forward(ctypes.byref(d), p, p, p, p, p, ctypes.byref(meta),
+                            ctypes.byref(saved), p, None) == -1
+    saved = dm._Saved(*([p] * 5))
+    scratch = dm._Scratch(p, p, None, p)
+    assert lib.dmoe_backward(ctypes.byref(d), p, p, p, p, p, ctypes.byref(meta),
+                             ctypes.byref(saved), ctypes.byref(scratch), p, p, p,
+                             p, p, None) == -1
+    assert lib.dmoe_padded_gather(ctypes.byref(d), None, ctypes.byref(meta), p,
+                                  None) == -1
+    assert lib.dmoe_padded_scatter(ctypes.byref(d), p, None, ctypes.byref(meta),
+                                   None, None) == -1
+    assert lib.dmoe_forward(None, p, p, p, p, p, ctypes.byref(meta),
+                            ctypes.byref(saved), p, None) == -1
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5, 42):
+        assert len(lib.dmoe_status_string(code)) > 0
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    D = dm.Dims(8, 128, 128, 2, 1, dm.DMOE_F32)
+    with pytest.raises(ValueError):
+        dm._ptr(torch.zeros(4), torch.float32, "x")
+    assert dm.dmoe_max_tiles(D) == (8 + 127 * 2) // 128
+    with pytest.raises(dm.DMoEError):
+        dm.dmoe_max_tiles(dm.Dims(8, 100, 128, 2, 1, dm.DMOE_F32))

@@ -1,0 +1,154 @@
+"""Forward + backward of the whole layer on the GPU vs the fp64 oracle.
+
+Small cases (several 128-row tiles, ragged tails, empty experts) compare
+every output and every intermediate element by element.  Full-size cases run
+the exact call sequence the benchmark times and compare sampled outputs that
+the oracle computes one by one from the per-entry definition."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import CONFIGS, make_inputs, shrink
+
+from gpu_helpers import TOL, Run, assert_close, down
+
+pytestmark = pytest.mark.gpu
+
+OUTS = ("dx", "dw1", "dw3", "dw2", "d_weights")
+
+SMALL = [
+    CONFIGS["tiny_f32"],
+    shrink(CONFIGS["fine_e64"], T=512, H=256, F=256),
+    shrink(CONFIGS["zipf_e64"], T=1024, H=256, F=256),
+    shrink(CONFIGS["zipf_e64_empty"], T=1024, H=128, F=256),
+    shrink(CONFIGS["coarse_e8"], T=1024, H=512, F=1024),
+    shrink(CONFIGS["sparse_e256"], T=2048, H=384, F=256),
+    # edge cases
+    shrink(CONFIGS["fine_e64"], T=5, H=128, F=128, E=1, k=1),      # one expert, ragged
+    shrink(CONFIGS["fine_e64"], T=1, H=256, F=128, E=4, k=2),      # one token
+    shrink(CONFIGS["fine_e64"], T=200, H=128, F=128, E=4, k=4),    # k = E
+    shrink(CONFIGS["fine_e64"], T=128, H=256, F=384, E=1, k=1),    # exactly one tile
+    shrink(CONFIGS["sparse_e256"], T=16, H=128, F=128),            # most experts empty
+    shrink(CONFIGS["tiny_f32"], T=129, H=384, F=384, E=3, k=1),    # fp32, 2 tiles + tail
+]
+
+
+def _check_small(cfg, lean=False):
+    inp = make_inputs(cfg)
+    print(f"layer {cfg.name} lean={lean}", flush=True)
+    r = Run(inp, lean=lean)
+    tol = TOL[cfg.dtype]
+    ref_y, sv = oracle.forward_padded(inp.x, inp.top_experts, inp.weights,
+                                      inp.w1, inp.w3, inp.w2)
+    ref_g = oracle.backward_padded(inp.x, inp.top_experts, inp.weights, inp.w1,
+                                   inp.w3, inp.w2, inp.dy, sv)
+    md = sv["md"]
+    got_md = r.meta_np()
+    np.testing.assert_array_equal(got_md["row_of_entry"], md["row_of_entry"])
+    P = md["P"]
+    assert r.P == P
+    # the gather is a copy: bit-exact, pad rows exactly zero
+    assert np.array_equal(down(r.saved.x_perm[:P]), sv["x_perm"])
+    pad = np.ones(P, dtype=bool)
+    pad[md["row_of_entry"]] = False
+    assert_close(down(r.y), ref_y, tol, "y")
+    for key in OUTS:
+        assert_close(down(r.g[key]), ref_g[key], tol, key)
+    inter = {"act": (r.saved.act, sv["act"]), "y_perm": (r.saved.y_perm, sv["y_perm"]),
+             "dh1": (r.scratch.dh1, ref_g["dh1"]), "dh3": (r.scratch.dh3, ref_g["dh3"]),
+             "dx_perm": (r.scratch.dx_perm, ref_g["dx_perm"])}
+    if not lean:
+        # in lean mode h1/h3 hold dh1/dh3 and dy_perm holds dx_perm afterwards
+        inter.update({"h1": (r.saved.h1, sv["h1"]), "h3": (r.saved.h3, sv["h3"]),
+                      "dy_perm": (r.scratch.dy_perm, ref_g["dy_perm"])})
+    for key, (t, ref) in inter.items():
+        got = down(t[:P])
+        assert_close(got, ref, tol, key)
+        assert np.all(got[pad] == 0.0), f"{key}: pad rows not zero"
+    return r
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_small_case_against_oracle(cfg):
+    _check_small(cfg)
+
+
+def test_lean_buffers_match_and_runs_are_bitwise_identical():
+    cfg = shrink(CONFIGS["zipf_e64_empty"], T=600, H=256, F=256)
+    a = _check_small(cfg, lean=False)
+    b = _check_small(cfg, lean=True)
+    assert torch.equal(a.y, b.y)
+    for key in OUTS:
+        assert torch.equal(a.g[key], b.g[key]), key
+    c = Run(make_inputs(cfg))
+    assert torch.equal(a.y, c.y)
+    for key in OUTS:
+        assert torch.equal(a.g[key], c.g[key]), key
+
+
+def _picks(inp, md, rng, n=24):
+    cfg = inp.cfg
+    counts = md["tokens_per_expert"]
+    big = int(np.argmax(counts))
+    experts = [big] + list(rng.integers(0, cfg.E, n - 1))
+    empty = np.nonzero(counts == 0)[0]
+    if empty.size:
+        experts[1] = int(empty[0])
+    picks = []
+    for i, e in enumerate(experts):
+        e = int(e)
+        picks.append(("dw1", e, int(rng.integers(cfg.H)), int(rng.integers(cfg.F))))
+        picks.append(("dw3", e, int(rng.integers(cfg.H)), int(rng.integers(cfg.F))))
+        picks.append(("dw2", e, int(rng.integers(cfg.F)), int(rng.integers(cfg.H))))
+    return picks
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "fine_e64", "zipf_e64",
+                                  "zipf_e64_empty", "coarse_e8", "sparse_e256"])
+def test_full_size_sampled(name):
+    cfg = CONFIGS[name]
+    inp = make_inputs(cfg)
+    print(f"full {name}", flush=True)
+    r = Run(inp)
+    tol = TOL[cfg.dtype]
+    md = oracle.metadata(inp.top_experts, cfg.E, len(r.meta.tile_expert))
+    got_md = r.meta_np()
+    for key in ("tokens_per_expert", "bins", "padded_bins", "indices", "bin_ids",
+                "row_of_entry", "tile_expert"):
+        np.testing.assert_array_equal(got_md[key], md[key], err_msg=key)
+    P = md["P"]
+    assert r.P == P
+    # x_perm: every real row is the token row, every pad row zero
+    a = np.arange(cfg.T * cfg.k)
+    rows = torch.from_numpy(md["row_of_entry"]).to(r.dev)
+    src = torch.from_numpy(a // cfg.k).to(r.dev)
+    assert torch.equal(r.saved.x_perm[rows], r.x[src])
+    pad = torch.ones(P, dtype=torch.bool, device=r.dev)
+    pad[rows] = False
+    for t in (r.saved.x_perm, r.saved.h1, r.saved.h3, r.saved.act, r.saved.y_perm,
+              r.scratch.dy_perm, r.scratch.dh1, r.scratch.dh3, r.scratch.dx_perm):
+        assert int(torch.count_nonzero(t[:P][pad])) == 0
+    for t in (r.y, r.g["dx"], r.g["dw1"], r.g["dw3"], r.g["dw2"], r.g["d_weights"]):
+        assert bool(torch.isfinite(t).all())
+    rng = np.random.default_rng(17)
+    toks = sorted(set([0, cfg.T - 1] + list(rng.integers(0, cfg.T, 22))))
+    ref = oracle.sampled_rows(inp.x, inp.top_experts, inp.weights, inp.w1, inp.w3,
+                              inp.w2, inp.dy, toks)
+    idx = torch.tensor(toks, device=r.dev)
+    for key, got in (("y", r.y), ("dx", r.g["dx"]), ("d_weights", r.g["d_weights"])):
+        g = down(got[idx])
+        want = np.stack([ref[t][key] for t in toks])
+        assert_close(g, want, tol, f"{name} {key}")
+    picks = _picks(inp, md, rng)
+    want = oracle.sampled_dw(inp.x, inp.top_experts, inp.weights, inp.w1, inp.w3,
+                             inp.w2, inp.dy, picks)
+    for nm in ("dw1", "dw3", "dw2"):
+        sel = [i for i, p in enumerate(picks) if p[0] == nm]
+        got = np.array([float(r.g[nm][p[1], p[2], p[3]]) for p in
+                        (picks[i] for i in sel)])
+        scale = float(np.max(np.abs(want[sel])))
+        err = float(np.max(np.abs(got - want[sel])))
+        assert err <= tol * scale, f"{name} {nm}: {err:.3e} > {tol}*{scale:.3e}"
+        empty = [i for i in sel if md["tokens_per_expert"][picks[i][1]] == 0]
+        assert all(float(r.g[nm][picks[i][1]].abs().max()) == 0.0 for i in empty)
