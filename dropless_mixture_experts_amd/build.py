@@ -26,6 +26,9 @@ HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in VGPRs: with the default heuristic the
+    # register allocator shuffles them through AGPRs on every K step
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I" + INCLUDE,
 ]
 

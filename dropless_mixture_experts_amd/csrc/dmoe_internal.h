@@ -62,4 +62,22 @@ hipError_t launch_gemm_wgrad_up(const Shape& s, const void* x_perm,
                                 const MetaPtrs& m, void* dw1, void* dw3,
                                 hipStream_t stream);
 
+// gemm_bf16.hip: the bf16 engine behind the launch_gemm_* entry points.
+hipError_t launch_bf16_up(const Shape& s, const void* x_perm, const void* w1, const void* w3,
+                          const MetaPtrs& m, void* h1, void* h3, void* act,
+                          hipStream_t stream);
+hipError_t launch_bf16_down(const Shape& s, const void* act, const void* w2,
+                            const MetaPtrs& m, void* y_perm, hipStream_t stream);
+hipError_t launch_bf16_down_dgrad(const Shape& s, const void* dy_perm, const void* w2,
+                                  const void* h1, const void* h3, const MetaPtrs& m,
+                                  void* dh1, void* dh3, hipStream_t stream);
+hipError_t launch_bf16_up_dgrad(const Shape& s, const void* dh1, const void* dh3,
+                                const void* w1, const void* w3, const MetaPtrs& m,
+                                void* dx_perm, hipStream_t stream);
+hipError_t launch_bf16_wgrad_down(const Shape& s, const void* act, const void* dy_perm,
+                                  const MetaPtrs& m, void* dw2, hipStream_t stream);
+hipError_t launch_bf16_wgrad_up(const Shape& s, const void* x_perm, const void* dh1,
+                                const void* dh3, const MetaPtrs& m, void* dw1, void* dw3,
+                                hipStream_t stream);
+
 }  // namespace dmoe

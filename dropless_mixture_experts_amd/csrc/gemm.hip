@@ -495,28 +495,20 @@ hipError_t launch_gemm_up(const Shape& s, const void* x_perm, const void* w1,
                           const void* w3, const MetaPtrs& m, void* h1, void* h3,
                           void* act, hipStream_t stream) {
   const dim3 grid(cdiv(s.F, 128), (unsigned)s.max_tiles);
-  if (s.bf16)
-    hipLaunchKernelGGL(gemm_up_kernel<bf16>, grid, dim3(kGemmThreads), 0, stream,
-                       cp<bf16>(x_perm), cp<bf16>(w1), cp<bf16>(w3), s.H, s.F,
-                       m.tile_expert, mp<bf16>(h1), mp<bf16>(h3), mp<bf16>(act));
-  else
-    hipLaunchKernelGGL(gemm_up_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
-                       cp<float>(x_perm), cp<float>(w1), cp<float>(w3), s.H, s.F,
-                       m.tile_expert, mp<float>(h1), mp<float>(h3), mp<float>(act));
+  if (s.bf16) return launch_bf16_up(s, x_perm, w1, w3, m, h1, h3, act, stream);
+  hipLaunchKernelGGL(gemm_up_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
+                     cp<float>(x_perm), cp<float>(w1), cp<float>(w3), s.H, s.F,
+                     m.tile_expert, mp<float>(h1), mp<float>(h3), mp<float>(act));
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_down(const Shape& s, const void* act, const void* w2,
                             const MetaPtrs& m, void* y_perm, hipStream_t stream) {
   const dim3 grid(cdiv(s.H, kTileA), (unsigned)s.max_tiles);
-  if (s.bf16)
-    hipLaunchKernelGGL(gemm_down_kernel<bf16>, grid, dim3(kGemmThreads), 0, stream,
-                       cp<bf16>(act), cp<bf16>(w2), s.H, s.F, m.tile_expert,
-                       mp<bf16>(y_perm));
-  else
-    hipLaunchKernelGGL(gemm_down_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
-                       cp<float>(act), cp<float>(w2), s.H, s.F, m.tile_expert,
-                       mp<float>(y_perm));
+  if (s.bf16) return launch_bf16_down(s, act, w2, m, y_perm, stream);
+  hipLaunchKernelGGL(gemm_down_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
+                     cp<float>(act), cp<float>(w2), s.H, s.F, m.tile_expert,
+                     mp<float>(y_perm));
   return hipGetLastError();
 }
 
@@ -525,14 +517,10 @@ hipError_t launch_gemm_down_dgrad(const Shape& s, const void* dy_perm,
                                   const MetaPtrs& m, void* dh1, void* dh3,
                                   hipStream_t stream) {
   const dim3 grid(cdiv(s.F, kTileA), (unsigned)s.max_tiles);
-  if (s.bf16)
-    hipLaunchKernelGGL(gemm_down_dgrad_kernel<bf16>, grid, dim3(kGemmThreads), 0, stream,
-                       cp<bf16>(dy_perm), cp<bf16>(w2), cp<bf16>(h1), cp<bf16>(h3),
-                       s.H, s.F, m.tile_expert, mp<bf16>(dh1), mp<bf16>(dh3));
-  else
-    hipLaunchKernelGGL(gemm_down_dgrad_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
-                       cp<float>(dy_perm), cp<float>(w2), cp<float>(h1), cp<float>(h3),
-                       s.H, s.F, m.tile_expert, mp<float>(dh1), mp<float>(dh3));
+  if (s.bf16) return launch_bf16_down_dgrad(s, dy_perm, w2, h1, h3, m, dh1, dh3, stream);
+  hipLaunchKernelGGL(gemm_down_dgrad_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
+                     cp<float>(dy_perm), cp<float>(w2), cp<float>(h1), cp<float>(h3),
+                     s.H, s.F, m.tile_expert, mp<float>(dh1), mp<float>(dh3));
   return hipGetLastError();
 }
 
@@ -540,14 +528,10 @@ hipError_t launch_gemm_up_dgrad(const Shape& s, const void* dh1, const void* dh3
                                 const void* w1, const void* w3, const MetaPtrs& m,
                                 void* dx_perm, hipStream_t stream) {
   const dim3 grid(cdiv(s.H, kTileA), (unsigned)s.max_tiles);
-  if (s.bf16)
-    hipLaunchKernelGGL(gemm_up_dgrad_kernel<bf16>, grid, dim3(kGemmThreads), 0, stream,
-                       cp<bf16>(dh1), cp<bf16>(dh3), cp<bf16>(w1), cp<bf16>(w3), s.H,
-                       s.F, m.tile_expert, mp<bf16>(dx_perm));
-  else
-    hipLaunchKernelGGL(gemm_up_dgrad_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
-                       cp<float>(dh1), cp<float>(dh3), cp<float>(w1), cp<float>(w3), s.H,
-                       s.F, m.tile_expert, mp<float>(dx_perm));
+  if (s.bf16) return launch_bf16_up_dgrad(s, dh1, dh3, w1, w3, m, dx_perm, stream);
+  hipLaunchKernelGGL(gemm_up_dgrad_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
+                     cp<float>(dh1), cp<float>(dh3), cp<float>(w1), cp<float>(w3), s.H,
+                     s.F, m.tile_expert, mp<float>(dx_perm));
   return hipGetLastError();
 }
 
@@ -555,14 +539,10 @@ hipError_t launch_gemm_wgrad_down(const Shape& s, const void* act,
                                   const void* dy_perm, const MetaPtrs& m,
                                   void* dw2, hipStream_t stream) {
   const dim3 grid(cdiv(s.H, kTileA), cdiv(s.F, 128), (unsigned)s.E);
-  if (s.bf16)
-    hipLaunchKernelGGL(gemm_wgrad_down_kernel<bf16>, grid, dim3(kGemmThreads), 0, stream,
-                       cp<bf16>(act), cp<bf16>(dy_perm), s.H, s.F, m.tokens_per_expert,
-                       m.padded_bins, mp<bf16>(dw2));
-  else
-    hipLaunchKernelGGL(gemm_wgrad_down_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
-                       cp<float>(act), cp<float>(dy_perm), s.H, s.F, m.tokens_per_expert,
-                       m.padded_bins, mp<float>(dw2));
+  if (s.bf16) return launch_bf16_wgrad_down(s, act, dy_perm, m, dw2, stream);
+  hipLaunchKernelGGL(gemm_wgrad_down_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
+                     cp<float>(act), cp<float>(dy_perm), s.H, s.F, m.tokens_per_expert,
+                     m.padded_bins, mp<float>(dw2));
   return hipGetLastError();
 }
 
@@ -571,14 +551,10 @@ hipError_t launch_gemm_wgrad_up(const Shape& s, const void* x_perm,
                                 const MetaPtrs& m, void* dw1, void* dw3,
                                 hipStream_t stream) {
   const dim3 grid(cdiv(s.F, 128), cdiv(s.H, 128), (unsigned)s.E);
-  if (s.bf16)
-    hipLaunchKernelGGL(gemm_wgrad_up_kernel<bf16>, grid, dim3(kGemmThreads), 0, stream,
-                       cp<bf16>(x_perm), cp<bf16>(dh1), cp<bf16>(dh3), s.H, s.F,
-                       m.tokens_per_expert, m.padded_bins, mp<bf16>(dw1), mp<bf16>(dw3));
-  else
-    hipLaunchKernelGGL(gemm_wgrad_up_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
-                       cp<float>(x_perm), cp<float>(dh1), cp<float>(dh3), s.H, s.F,
-                       m.tokens_per_expert, m.padded_bins, mp<float>(dw1), mp<float>(dw3));
+  if (s.bf16) return launch_bf16_wgrad_up(s, x_perm, dh1, dh3, m, dw1, dw3, stream);
+  hipLaunchKernelGGL(gemm_wgrad_up_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
+                     cp<float>(x_perm), cp<float>(dh1), cp<float>(dh3), s.H, s.F,
+                     m.tokens_per_expert, m.padded_bins, mp<float>(dw1), mp<float>(dw3));
   return hipGetLastError();
 }
 
