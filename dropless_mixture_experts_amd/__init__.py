@@ -65,7 +65,8 @@ class _Dims(ctypes.Structure):
 class _Meta(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "tokens_per_expert", "bins", "padded_bins", "indices", "bin_ids",
-        "row_of_entry", "tile_expert", "num_padded_rows", "status")]
+        "row_of_entry", "tile_expert", "num_padded_rows", "status",
+        "pair_first", "num_pairs")]
 
 
 class _Saved(ctypes.Structure):
@@ -156,6 +157,8 @@ class Meta:
     tile_expert: torch.Tensor
     num_padded_rows: torch.Tensor
     status: torch.Tensor
+    pair_first: torch.Tensor
+    num_pairs: torch.Tensor
 
     def _c(self) -> _Meta:
         return _Meta(*[_ptr(getattr(self, f.name), torch.int32, f.name)
@@ -242,7 +245,8 @@ def _check_meta(dims: Dims, meta: Meta):
     for name, size in (("tokens_per_expert", dims.E), ("bins", dims.E),
                        ("padded_bins", dims.E), ("indices", n), ("bin_ids", n),
                        ("row_of_entry", n), ("tile_expert", dmoe_max_tiles(dims)),
-                       ("num_padded_rows", 1), ("status", 1)):
+                       ("num_padded_rows", 1), ("status", 1),
+                       ("pair_first", dmoe_max_tiles(dims)), ("num_pairs", 1)):
         _need(getattr(meta, name), name, size)
 
 
@@ -375,7 +379,8 @@ def allocate_meta(dims: Dims, device):
     i32 = dict(dtype=torch.int32, device=device)
     meta = Meta(torch.empty(E, **i32), torch.empty(E, **i32), torch.empty(E, **i32),
                 torch.empty(n, **i32), torch.empty(n, **i32), torch.empty(n, **i32),
-                torch.empty(nt, **i32), torch.empty(1, **i32), torch.empty(1, **i32))
+                torch.empty(nt, **i32), torch.empty(1, **i32), torch.empty(1, **i32),
+                torch.empty(nt, **i32), torch.empty(1, **i32))
     ws = torch.empty(dmoe_workspace_bytes(dims), dtype=torch.uint8, device=device)
     return meta, ws
 

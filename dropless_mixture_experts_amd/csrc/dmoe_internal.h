@@ -13,6 +13,7 @@ struct MetaPtrs {
   int32_t *tokens_per_expert, *bins, *padded_bins;
   int32_t *indices, *bin_ids, *row_of_entry;
   int32_t *tile_expert, *num_padded_rows, *status;
+  int32_t *pair_first, *num_pairs;
 };
 
 struct Shape {

@@ -15,7 +15,8 @@
 //               (LDS counters) and an invalid-id flag.
 //   meta_scan   one workgroup: per-expert totals, bins / padded_bins / P,
 //               each chunk's starting sorted position per expert, the
-//               block -> expert table, the status word.
+//               block -> expert table, the pairs of row blocks that the
+//               matrix products process together, the status word.
 //   meta_place  one wave per chunk: stable rank of every entry among the
 //               chunk's entries of the same expert (64-lane ballots on the
 //               bits of the id + mbcnt), then writes indices, bin_ids and
@@ -67,12 +68,15 @@ meta_scan_kernel(int32_t* __restrict__ hist, const int32_t* __restrict__ err,
                  int32_t* __restrict__ bins, int32_t* __restrict__ padded_bins,
                  int32_t* __restrict__ tile_expert,
                  int32_t* __restrict__ num_padded_rows,
-                 int32_t* __restrict__ status) {
+                 int32_t* __restrict__ status,
+                 int32_t* __restrict__ pair_first,
+                 int32_t* __restrict__ num_pairs) {
   __shared__ int32_t seg_tot[kScanThreads];
   __shared__ int32_t count_s[kMaxExperts];
   __shared__ int32_t start_s[kMaxExperts];
   __shared__ int32_t pend_s[kMaxExperts];
-  __shared__ int32_t P_s, bad_s;
+  __shared__ int32_t pair_s[kMaxExperts];   // first group of each expert
+  __shared__ int32_t P_s, S_s, bad_s;
   const int tid = threadIdx.x;
   const int S = kScanThreads / Ecap;
   const int e = tid % Ecap, seg = tid / Ecap;
@@ -97,31 +101,38 @@ meta_scan_kernel(int32_t* __restrict__ hist, const int32_t* __restrict__ err,
 
   // Inclusive scans over experts of the counts and the rounded-up counts:
   // wave 0, four consecutive experts per lane, then a 64-lane shuffle scan.
+  // The same scan also numbers the groups of (at most) two row blocks of one
+  // expert that the matrix products work on: ceil(blocks / 2) per expert.
   if (tid < kWave) {
-    int c[4], pc[4], cs = 0, ps = 0;
+    int c[4], pc[4], gp[4], cs = 0, ps = 0, gs = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ee = tid * 4 + i;
       c[i] = ee < E ? count_s[ee] : 0;
       pc[i] = round_up_block(c[i]);
+      gp[i] = (pc[i] / kBlock + 1) / 2;
       cs += c[i];
       ps += pc[i];
+      gs += gp[i];
     }
-    int ci = cs, pi = ps;
+    int ci = cs, pi = ps, gi = gs;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
       const int cu = __shfl_up(ci, off, kWave);
       const int pu = __shfl_up(pi, off, kWave);
-      if (tid >= off) { ci += cu; pi += pu; }
+      const int gu = __shfl_up(gi, off, kWave);
+      if (tid >= off) { ci += cu; pi += pu; gi += gu; }
     }
-    int crun = ci - cs, prun = pi - ps;    // exclusive starts of this lane
+    int crun = ci - cs, prun = pi - ps, grun = gi - gs;   // exclusive starts
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ee = tid * 4 + i;
       if (ee < E) {
         start_s[ee] = crun;
+        pair_s[ee] = grun;
         crun += c[i];
         prun += pc[i];
+        grun += gp[i];
         pend_s[ee] = prun;
         tokens_per_expert[ee] = c[i];
         bins[ee] = crun;
@@ -130,7 +141,9 @@ meta_scan_kernel(int32_t* __restrict__ hist, const int32_t* __restrict__ err,
     }
     if (tid == kWave - 1) {
       P_s = pi;
+      S_s = gi;
       *num_padded_rows = pi;
+      *num_pairs = gi;
     }
   }
   __syncthreads();
@@ -161,6 +174,15 @@ meta_scan_kernel(int32_t* __restrict__ hist, const int32_t* __restrict__ err,
     }
     tile_expert[r] = owner;
   }
+  // Groups of expert e start at block (pend - pc) / 128 and step by two.
+  if (tid < E) {
+    const int pc = round_up_block(count_s[tid]);
+    const int t0 = (pend_s[tid] - pc) / kBlock;
+    const int ng = (pc / kBlock + 1) / 2;
+    const int g0 = pair_s[tid];
+    for (int q = 0; q < ng; ++q) pair_first[g0 + q] = t0 + 2 * q;
+  }
+  for (int r = S_s + tid; r < max_tiles; r += kScanThreads) pair_first[r] = -1;
   if (tid == 0) *status = bad_s ? kErrExpertId : 0;
 }
 
@@ -247,7 +269,7 @@ hipError_t launch_metadata(int64_t n, int E, int64_t max_tiles,
   hipLaunchKernelGGL(meta_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream,
                      hist, err, nchunks, E, Ecap, (int)max_tiles,
                      m.tokens_per_expert, m.bins, m.padded_bins, m.tile_expert,
-                     m.num_padded_rows, m.status);
+                     m.num_padded_rows, m.status, m.pair_first, m.num_pairs);
   if (ev) hipEventRecord(ev[2], stream);
   hipLaunchKernelGGL(meta_place_kernel, dim3(blocks), dim3(kMetaWaves * kWave), 0,
                      stream, ids, n, chunk, nchunks, E, nbits, hist,

@@ -94,13 +94,22 @@ typedef struct {
  *                         (s - bins[e-1]) + padded_bins[e-1], both starts 0 at e=0
  *   tile_expert[max_tiles] expert owning 128-row block r; -1 for r >= P/128
  *   num_padded_rows[1]    P = padded_bins[E-1]
- *   status[1]             0, or DMOE_ERR_EXPERT_ID                        */
+ *   status[1]             0, or DMOE_ERR_EXPERT_ID
+ *   pair_first[max_tiles] the row blocks grouped for the matrix products:
+ *                         group s starts at block pair_first[s] and also
+ *                         takes the next block when that block belongs to
+ *                         the same expert (each expert's blocks are paired
+ *                         in order; an odd last block stays single); -1
+ *                         past the last group
+ *   num_pairs[1]          number of groups                                 */
 typedef struct {
   int32_t *tokens_per_expert, *bins, *padded_bins;
   int32_t *indices, *bin_ids, *row_of_entry;
   int32_t *tile_expert;
   int32_t *num_padded_rows;
   int32_t *status;
+  int32_t *pair_first;
+  int32_t *num_pairs;
 } dmoe_meta;
 
 /* Activations kept from forward for backward, each [P_max, H] or [P_max, F]

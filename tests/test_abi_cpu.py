@@ -64,19 +64,19 @@ def test_bad_dims_rejected(lib, kw, code):
     d = _dims(**kw)
     assert lib.dmoe_max_tiles(ctypes.byref(d)) == code
     assert lib.dmoe_workspace_bytes(ctypes.byref(d)) == code
-    meta = dm._Meta(*([ctypes.c_void_p(0x1000)] * 9))
+    meta = dm._Meta(*([ctypes.c_void_p(0x1000)] * 11))
     assert lib.dmoe_metadata(ctypes.byref(d), ctypes.c_void_p(0x1000),
                              ctypes.byref(meta), ctypes.c_void_p(0x1000), None) == code
 
 
 def test_null_pointers_rejected_before_launch(lib):
     d = _dims()
-    meta = dm._Meta(*([ctypes.c_void_p(0x1000)] * 9))
+    meta = dm._Meta(*([ctypes.c_void_p(0x1000)] * 11))
     assert lib.dmoe_metadata(ctypes.byref(d), None, ctypes.byref(meta),
                              ctypes.c_void_p(0x1000), None) == -1
     assert lib.dmoe_metadata(ctypes.byref(d), ctypes.c_void_p(0x1000),
                              ctypes.byref(meta), None, None) == -1
-    bad = dm._Meta(*([ctypes.c_void_p(0x1000)] * 8 + [None]))
+    bad = dm._Meta(*([ctypes.c_void_p(0x1000)] * 10 + [None]))
     assert lib.dmoe_metadata(ctypes.byref(d), ctypes.c_void_p(0x1000),
                              ctypes.byref(bad), ctypes.c_void_p(0x1000), None) == -1
     saved = dm._Saved(*([ctypes.c_void_p(0x1000)] * 4 + [None]))

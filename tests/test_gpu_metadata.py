@@ -35,7 +35,25 @@ def _run_meta(ids_np, E, dtype=dm.DMOE_BF16, H=128, F=128):
     out = {k: getattr(meta, k).cpu().numpy().astype(np.int64) for k in KEYS}
     out["P"] = int(meta.num_padded_rows.item())
     out["status"] = int(meta.status.item())
+    out["pair_first"] = meta.pair_first.cpu().numpy().astype(np.int64)
+    out["num_pairs"] = int(meta.num_pairs.item())
     return out, dm.dmoe_max_tiles(D)
+
+
+def _check_pairs(got):
+    """The row-block groups: each expert's blocks in order, two at a time
+    (an odd last block alone), every block exactly once, -1 afterwards."""
+    te = got["tile_expert"]
+    nb = got["P"] // 128
+    expect = []
+    r = 0
+    while r < nb:
+        expect.append(r)
+        r += 2 if r + 1 < nb and te[r + 1] == te[r] else 1
+    S = got["num_pairs"]
+    assert S == len(expect)
+    np.testing.assert_array_equal(got["pair_first"][:S], expect)
+    assert np.all(got["pair_first"][S:] == -1)
 
 
 def _compare(ids_np, E):
@@ -45,6 +63,7 @@ def _compare(ids_np, E):
     for key in KEYS:
         np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
     assert got["P"] == ref["P"]
+    _check_pairs(got)
     return got
 
 
