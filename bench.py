@@ -62,6 +62,31 @@ def kernel_work(cfg, P):
     return w
 
 
+def committed_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter summaries under
+    profiles/ (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None
+    if there is none for this kernel and workload or the kernel's source
+    changed since the counters were taken."""
+    import glob
+    import hashlib
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*traffic*.json"))):
+        try:
+            with open(path) as fh:
+                d = json.load(fh)
+        except (OSError, ValueError):
+            continue
+        if d.get("bench_name") != kernel or d.get("workload") != workload:
+            continue
+        src = os.path.join(ROOT, d.get("source", ""))
+        if not os.path.isfile(src):
+            return None
+        with open(src, "rb") as fh:
+            if hashlib.sha256(fh.read()).hexdigest() != d.get("source_sha256"):
+                return None
+        return float(d["traffic_bytes_per_launch"])
+    return None
+
+
 def cpu_baseline(inp, budget_s=30.0):
     """Time the fp64 CPU oracle (metadata + forward + backward) on the host."""
     import numpy as np
@@ -96,6 +121,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--kernels", action="store_true",
                     help="also print the per-kernel table on stderr")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="after timing, run a plain device copy of this many MiB "
+                         "three times (reference for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
@@ -202,6 +230,7 @@ def main():
                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
     roof["algorithmic_per_launch"] = fl if fl else by
+    roof["traffic"] = committed_traffic(dom, cfg.name)
 
     out = {
         "metric": METRIC,
@@ -229,6 +258,14 @@ def main():
     if args.kernels:
         for n in names:
             print(f"{n:22s} {table[n]}", file=sys.stderr)
+    if args.calibrate_copy_mb:
+        nbytes = args.calibrate_copy_mb << 20
+        src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calibration_copy_bytes"] = nbytes
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(inp)
     else:

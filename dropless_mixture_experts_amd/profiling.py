@@ -1,0 +1,128 @@
+"""Summaries of rocprofv3 output for the dMoE kernels.
+
+    python -m dropless_mixture_experts_amd.profiling stats DIR
+        Per-kernel call count, total and average duration from the
+        kernel-trace CSV under DIR (rocprofv3 --kernel-trace --stats
+        --output-format csv).
+
+    python -m dropless_mixture_experts_amd.profiling traffic \\
+        --fetch DIR_F --write DIR_W --kernel REGEX --name BENCH_NAME \\
+        --workload NAME \\
+        --copy-bytes N [--copy-kernel REGEX] [--source FILE] --out JSON
+        HBM traffic per launch of the kernels matching REGEX from two
+        counter runs (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch).
+        Each counter is scaled by what it reads for a plain copy kernel of
+        N bytes in the same run (bytes read = bytes written = N), so the
+        factor corrects whatever unit or sampling the counter has.  The
+        sha256 of --source is stored so that a later change of the kernel
+        makes the figure stale.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+
+
+def _rows(directory: str, pattern: str):
+    files = glob.glob(os.path.join(directory, "**", pattern), recursive=True)
+    out = []
+    for f in sorted(files):
+        with open(f) as fh:
+            out.extend(csv.DictReader(fh))
+    return out
+
+
+def kernel_stats(directory: str):
+    """{kernel name: (calls, total_ns, avg_ns)} from a kernel-trace CSV."""
+    rows = _rows(directory, "*kernel_trace.csv")
+    acc = {}
+    for r in rows:
+        name = r.get("Kernel_Name") or r.get("KernelName")
+        dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        acc.setdefault(name, []).append(dur)
+    return {k: (len(v), sum(v), sum(v) / len(v)) for k, v in acc.items()}
+
+
+def _counter(directory: str, counter: str, kernel_re: str):
+    vals = []
+    for r in _rows(directory, "*counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        if re.search(kernel_re, r["Kernel_Name"]):
+            vals.append(float(r["Counter_Value"]))
+    return vals
+
+
+def traffic(args) -> dict:
+    fetch = _counter(args.fetch, "FETCH_SIZE", args.kernel)
+    write = _counter(args.write, "WRITE_SIZE", args.kernel)
+    cf = _counter(args.fetch, "FETCH_SIZE", args.copy_kernel)
+    cw = _counter(args.write, "WRITE_SIZE", args.copy_kernel)
+    if not (fetch and write and cf and cw):
+        raise SystemExit("missing counter rows: kernel or copy kernel not found")
+    # the copy of N bytes: median dispatch, counters in KiB
+    f_factor = args.copy_bytes / (statistics.median(cf) * 1024.0)
+    w_factor = args.copy_bytes / (statistics.median(cw) * 1024.0)
+    fetch_b = statistics.median(fetch) * 1024.0 * f_factor
+    write_b = statistics.median(write) * 1024.0 * w_factor
+    out = {
+        "bench_name": args.name,
+        "kernel_regex": args.kernel,
+        "workload": args.workload,
+        "fetch_kib_per_dispatch": statistics.median(fetch),
+        "write_kib_per_dispatch": statistics.median(write),
+        "copy_bytes": args.copy_bytes,
+        "copy_fetch_kib": statistics.median(cf),
+        "copy_write_kib": statistics.median(cw),
+        "fetch_factor": f_factor,
+        "write_factor": w_factor,
+        "traffic_bytes_per_launch": fetch_b + write_b,
+        "fetch_bytes_per_launch": fetch_b,
+        "write_bytes_per_launch": write_b,
+    }
+    if args.source:
+        with open(args.source, "rb") as fh:
+            out["source"] = os.path.relpath(args.source)
+            out["source_sha256"] = hashlib.sha256(fh.read()).hexdigest()
+    return out
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--name", required=True, help="kernel name in bench.py's table")
+    t.add_argument("--copy-kernel", default="elementwise|copy")
+    t.add_argument("--copy-bytes", type=float, required=True)
+    t.add_argument("--source")
+    t.add_argument("--out")
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        st = kernel_stats(a.dir)
+        print(f"{'kernel':72s} {'calls':>6s} {'total_us':>11s} {'avg_us':>10s}")
+        for k, (n, tot, avg) in sorted(st.items(), key=lambda kv: -kv[1][1]):
+            print(f"{k[:72]:72s} {n:6d} {tot / 1e3:11.1f} {avg / 1e3:10.2f}")
+    else:
+        res = traffic(a)
+        text = json.dumps(res, indent=1)
+        if a.out:
+            with open(a.out, "w") as fh:
+                fh.write(text + "\n")
+        print(text)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
