@@ -46,16 +46,18 @@ constexpr int kStage = 2 * kReg;              // 64 KB
 constexpr int kStages = 2;
 constexpr int kLds = kStages * kStage;        // 128 KB
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// Buffer resource: base, no stride, the largest record count, 32-bit data
+// format (every access is in bounds by construction, so the range only has
+// to cover them).
+typedef uint32_t rsrc_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(3))) bf16x4* lds_bf16x4_t;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p) {
-  // raw buffer, no stride; every access is in bounds by construction, so
-  // the range only has to cover them: take the largest positive size.
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, 0x7fffffff, 0x00020000);
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return rsrc_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, 0x7fffffffu, 0x00020000u};
 }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0): at most N vector-memory operations of this
@@ -109,15 +111,35 @@ struct Dma {
   }
 };
 
-__device__ __forceinline__ void dma16(rsrc_t r, char* lds_dst, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_dst, 16, voff, soff, 0, 0);
+// 16 bytes per lane from r + voff + soff into LDS at lds_addr + 16 * lane.
+// Written as asm so that the compiler does not see an LDS write it cannot
+// place: it would then make every transposed LDS read wait for all DMA in
+// flight, the prefetch of later steps included.  Completion is awaited
+// explicitly (wait_vm + barrier) before a stage is read.  The asm has no
+// register outputs.  The nops cover the SGPR-written-by-VALU and M0-write
+// hazards of an LDS DMA.
+__device__ __forceinline__ uint32_t uniform(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+__device__ __forceinline__ void dma16(const rsrc_t& rv, uint32_t lds_addr, uint32_t voff,
+                                      uint32_t soff) {
+  const rsrc_t r{uniform(rv[0]), uniform(rv[1]), uniform(rv[2]), uniform(rv[3])};
+  asm volatile(
+      "s_nop 4\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds"
+      :
+      : "v"(voff), "s"(r), "s"(uniform(soff)), "{m0}"(uniform(lds_addr))
+      : "memory");
+}
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(lds_ptr_t)const_cast<char*>(p);
 }
 
-// One operand, one K step into `reg` (32 KB = 32 blocks of 1 KB).  Wave w
-// fills blocks 4w..4w+3, all in half w / 4.
+// One operand, one K step into the LDS region at address `reg` (32 KB = 32
+// blocks of 1 KB).  Wave w fills blocks 4w..4w+3, all in half w / 4.
 template <bool TRANS>
 __device__ __forceinline__ void issue(const Op& op, const Dma<TRANS>& d, int ks, int w,
-                                      char* reg) {
+                                      uint32_t reg) {
   const rsrc_t r = w < 4 ? op.r0 : op.r1;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -190,12 +212,12 @@ __device__ __forceinline__ void mma(Acc& acc, const Frags& f) {
   }
 }
 
-// DMA of K step ks into its stage.
+// DMA of K step ks into its stage (lds: LDS address of the stages).
 template <bool ATR, bool BTR>
 __device__ __forceinline__ void start_step(const Op& A, const Op& B, const Dma<ATR>& da,
                                            const Dma<BTR>& db, int ks, int w, bool load_a,
-                                           bool load_b, char* lds) {
-  char* st = lds + (ks % kStages) * kStage;
+                                           bool load_b, uint32_t lds) {
+  const uint32_t st = lds + (ks % kStages) * kStage;
   if (load_a) issue<ATR>(A, da, ks, w, st);
   if (load_b) issue<BTR>(B, db, ks, w, st + kReg);
 }
@@ -220,9 +242,10 @@ __device__ __forceinline__ void mainloop(Acc& acc, const Op& A, const Op& B, int
   Dma<BTR> db;
   da.init(A.ld, lane);
   db.init(B.ld, lane);
-  start_step<ATR, BTR>(A, B, da, db, 0, w, load_a, load_b, lds);
+  const uint32_t lbase = uniform(lds_addr(lds));
+  start_step<ATR, BTR>(A, B, da, db, 0, w, load_a, load_b, lbase);
   if (nk > 1) {
-    start_step<ATR, BTR>(A, B, da, db, 1, w, load_a, load_b, lds);
+    start_step<ATR, BTR>(A, B, da, db, 1, w, load_a, load_b, lbase);
     // wait for step 0: step 1 (0, 4 or 8 instructions) may stay in flight
     if (load_a && load_b) wait_vm<8>(); else if (load_a || load_b) wait_vm<4>(); else wait_vm<0>();
   } else {
@@ -241,7 +264,7 @@ __device__ __forceinline__ void mainloop(Acc& acc, const Op& A, const Op& B, int
       } else if (ks + 1 < nk) {
         wait_vm<0>();                       // step ks+1 landed (nothing later in flight)
         barrier();
-        if (ks + 2 < nk) start_step<ATR, BTR>(A, B, da, db, ks + 2, w, load_a, load_b, lds);
+        if (ks + 2 < nk) start_step<ATR, BTR>(A, B, da, db, ks + 2, w, load_a, load_b, lbase);
         if (work)
           load_frags<ATR, BTR, FA>(f[0], lds + ((ks + 1) % kStages) * kStage, 0, wm, wn, lane);
       }
