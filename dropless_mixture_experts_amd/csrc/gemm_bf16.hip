@@ -314,8 +314,7 @@ __device__ __forceinline__ void store4(bf16* p, const f32x4& v) {
                      ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<bf16>(v[3])) << 16);
   *reinterpret_cast<u32x2*>(p) = u32x2{a, b};
 }
-__device__ __forceinline__ f32x4 load4(const bf16* p) {
-  const u32x2 u = *reinterpret_cast<const u32x2*>(p);
+__device__ __forceinline__ f32x4 unpack4(const u32x2& u) {
   return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
                __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
 }
@@ -489,19 +488,48 @@ __device__ __forceinline__ void down_dgrad_body(const bf16* dy_perm, const bf16*
   zero(acc);
   mainloop<false, false, FA, FB>(acc, A, B, (int)(H / kKStep), lds);
   const int64_t base = t.mt * kBlock * F + fb;
-  for_quads<FA, FB>(acc, lane, [&](int, int arow, int brow, const f32x4& da) {
-    const int64_t o = base + (int64_t)brow * F + arow;
-    const f32x4 g1 = load4(h1 + o), g3 = load4(h3 + o);
-    f32x4 d1, d3;
+  const int w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
+  if (!FB && wn >= 2) return;
+  // h1/h3 of half of this lane's outputs are loaded before any of them is
+  // stored, so the loads overlap (dh1/dh3 may alias h1/h3, which keeps the
+  // compiler from hoisting a load above an earlier store; each element is
+  // read by the lane that overwrites it).
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float s = 1.0f / (1.0f + __expf(-g1[r]));
-      d3[r] = da[r] * g1[r] * s;
-      d1[r] = da[r] * g3[r] * s * (1.0f + g1[r] * (1.0f - s));
-    }
-    store4(dh1 + o, d1);
-    store4(dh3 + o, d3);
-  });
+  for (int i0 = 0; i0 < 4; i0 += 2) {
+    if (!FA && i0 >= 2) break;
+    u32x2 g1[2][2][4], g3[2][2][4];
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t o = base + (int64_t)(b_row(j, wn) + (lane & 31)) * F +
+                            a_row(i0 + ii, wm) + 8 * g + 4 * (lane >> 5);
+          g1[ii][j][g] = *reinterpret_cast<const u32x2*>(h1 + o);
+          g3[ii][j][g] = *reinterpret_cast<const u32x2*>(h3 + o);
+        }
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t o = base + (int64_t)(b_row(j, wn) + (lane & 31)) * F +
+                            a_row(i0 + ii, wm) + 8 * g + 4 * (lane >> 5);
+          const f32x4 da = quad(acc[i0 + ii][j], g);
+          const f32x4 x1 = unpack4(g1[ii][j][g]), x3 = unpack4(g3[ii][j][g]);
+          f32x4 d1, d3;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float s = 1.0f / (1.0f + __expf(-x1[r]));
+            d3[r] = da[r] * x1[r] * s;
+            d1[r] = da[r] * x3[r] * s * (1.0f + x1[r] * (1.0f - s));
+          }
+          store4(dh1 + o, d1);
+          store4(dh3 + o, d3);
+        }
+  }
 }
 
 __global__ void __launch_bounds__(kThreads)
