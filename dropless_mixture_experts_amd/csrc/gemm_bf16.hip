@@ -6,14 +6,21 @@
 // engine of gemm.hip; this file is the bf16 fast path.
 //
 // Engine
-//   * 512 threads = 8 waves (2 x 4).  A block computes a 256 x 256 tile:
-//     256 "A rows" along the output's contiguous dimension (weights side)
-//     x 256 "B rows" (two 128-row blocks of the same expert, or the m
+//   * 512 threads = 8 waves (2 x 4).  A block computes 256 x 256 output
+//     tiles: 256 "A rows" along the output's contiguous dimension (weights
+//     side) x 256 "B rows" (two 128-row blocks of the same expert, or the m
 //     dimension of a weight gradient).  Each wave owns 128 x 64 as 4 x 2
 //     v_mfma_f32_32x32x16_bf16 tiles (128 fp32 accumulators); two waves
 //     share each SIMD.  The 256 x 256 tile halves the bytes each CU pulls
-//     per FLOP compared with 256 x 128, which is what bounds these
-//     products: the number of memory requests a CU can keep in flight.
+//     per FLOP compared with 256 x 128, which is what bounds these products.
+//   * Persistent: one block per CU walks its share of the tiles.  The first
+//     two K steps of the next tile are fetched while the current tile
+//     finishes and stores its outputs, so neither the start of a block nor
+//     the latency of its first loads nor the epilogue idles the matrix cores
+//     between tiles.  Tiles are dealt per XCD (block b runs on XCD b % 8, and
+//     each XCD has its own L2): each XCD takes one contiguous range of the
+//     tile order and its blocks walk it side by side, so concurrent tiles
+//     share operands in one L2.
 //   * K step 64.  Two LDS stages of 64 KB (32 KB A + 32 KB B) are filled by
 //     buffer_load ... lds (16 bytes per lane straight into LDS, no
 //     registers).  Each wave fills whole 1 KB LDS blocks; the global address
@@ -28,9 +35,14 @@
 //     each 16-lane group, lane i fetches 4 values of k-row i/4 at columns
 //     4(i%4).. and receives the 4 k-values of column i, which is exactly an
 //     MFMA operand fragment.
-//   * Either half of A or B may be absent (a dimension that is an odd
-//     multiple of 128, or an expert with an odd number of row blocks); the
-//     same code runs with that half compiled out.
+//   * A tile whose second half of A or B does not exist (a dimension that is
+//     an odd multiple of 128, or an expert with an odd number of row blocks)
+//     loads its first half twice, so every wave issues the same loads; the
+//     waves of a missing B half skip their MFMAs and no missing half is
+//     stored.
+#include <algorithm>
+#include <atomic>
+
 #include "dmoe_device.h"
 #include "dmoe_internal.h"
 
@@ -43,8 +55,9 @@ constexpr int kKStep = 64;                    // K per stage
 constexpr int kReg = 256 * kRowB;             // 32 KB per operand per stage
 constexpr int kHalf = 16384;                  // one 128-row (or -column) half
 constexpr int kStage = 2 * kReg;              // 64 KB
-constexpr int kStages = 2;
-constexpr int kLds = kStages * kStage;        // 128 KB
+constexpr int kStgWave = 4096;                // epilogue staging per wave
+constexpr int kLds = 2 * kStage + 8 * kStgWave;   // two stages + staging, 160 KB
+constexpr int kDmaPerStep = 8;                // DMA instructions per wave per K step
 
 // Buffer resource: base, no stride, the largest record count, 32-bit data
 // format (every access is in bounds by construction, so the range only has
@@ -55,9 +68,16 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(3))) bf16x4* lds_bf16x4_t;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ rsrc_t make_rsrc(const void* p) {
+__device__ __forceinline__ uint32_t uniform(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+__device__ __forceinline__ rsrc_t make_rsrc(const char* p) {
   const uint64_t a = reinterpret_cast<uint64_t>(p);
-  return rsrc_t{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, 0x7fffffffu, 0x00020000u};
+  return rsrc_t{uniform((uint32_t)a), uniform((uint32_t)(a >> 32) & 0xffffu), 0x7fffffffu,
+                0x00020000u};
+}
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return (uint32_t)(uintptr_t)(lds_ptr_t)const_cast<char*>(p);
 }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0): at most N vector-memory operations of this
@@ -67,6 +87,22 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+// wait_vm for a count known at run time (a multiple of 8 up to 40; any other
+// count waits for everything, which is never wrong).
+__device__ __forceinline__ void wait_vm_n(int n) {
+  switch (n) {
+    case 8: wait_vm<8>(); break;
+    case 16: wait_vm<16>(); break;
+    case 24: wait_vm<24>(); break;
+    case 32: wait_vm<32>(); break;
+    case 40: wait_vm<40>(); break;
+    default: wait_vm<0>(); break;
+  }
+}
+// s_waitcnt lgkmcnt(0) only.
+__device__ __forceinline__ void wait_lds() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
 }
 // Workgroup barrier without a memory fence: the fence of __syncthreads()
 // would wait for every LDS DMA in flight, including the ones for later steps.
@@ -82,13 +118,6 @@ __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1
 __device__ __forceinline__ int lds_off(int row, int chunk) {
   return row * kRowB + ((chunk ^ swz(row)) << 4);
 }
-
-// One operand.  Tile rows (direct) or columns (trans) [0,128) come from r0
-// and [128,256) from r1.  ld: bytes between consecutive source rows.
-struct Op {
-  rsrc_t r0, r1;
-  uint32_t ld;
-};
 
 // Per-lane source offset for the DMA of one operand.  A wave instruction
 // fills one 1 KB LDS block: 8 direct rows (lane l -> row l/8, physical chunk
@@ -111,48 +140,40 @@ struct Dma {
   }
 };
 
-// 16 bytes per lane from r + voff + soff into LDS at lds_addr + 16 * lane.
+// 16 bytes per lane from r + voff + soff into LDS at lds + 16 * lane.
 // Written as asm so that the compiler does not see an LDS write it cannot
 // place: it would then make every transposed LDS read wait for all DMA in
 // flight, the prefetch of later steps included.  Completion is awaited
 // explicitly (wait_vm + barrier) before a stage is read.  The asm has no
 // register outputs.  The nops cover the SGPR-written-by-VALU and M0-write
 // hazards of an LDS DMA.
-__device__ __forceinline__ uint32_t uniform(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
-}
-__device__ __forceinline__ void dma16(const rsrc_t& rv, uint32_t lds_addr, uint32_t voff,
+__device__ __forceinline__ void dma16(const rsrc_t& r, uint32_t lds, uint32_t voff,
                                       uint32_t soff) {
-  const rsrc_t r{uniform(rv[0]), uniform(rv[1]), uniform(rv[2]), uniform(rv[3])};
   asm volatile(
       "s_nop 4\n\t"
       "buffer_load_dwordx4 %0, %1, %2 offen lds"
       :
-      : "v"(voff), "s"(r), "s"(uniform(soff)), "{m0}"(uniform(lds_addr))
+      : "v"(voff), "s"(r), "s"(uniform(soff)), "{m0}"(uniform(lds))
       : "memory");
-}
-__device__ __forceinline__ uint32_t lds_addr(const char* p) {
-  return (uint32_t)(uintptr_t)(lds_ptr_t)const_cast<char*>(p);
 }
 
 // One operand, one K step into the LDS region at address `reg` (32 KB = 32
-// blocks of 1 KB).  Wave w fills blocks 4w..4w+3, all in half w / 4.
+// blocks of 1 KB).  Wave w fills blocks 4w..4w+3, all in half w / 4 (p0 or
+// p1: the byte address of that half's first row or column).  The base
+// address is advanced in 64 bits, so only offsets within one step are 32-bit.
 template <bool TRANS>
-__device__ __forceinline__ void issue(const Op& op, const Dma<TRANS>& d, int ks, int w,
-                                      uint32_t reg) {
-  const rsrc_t r = w < 4 ? op.r0 : op.r1;
+__device__ __forceinline__ void issue(const char* p0, const char* p1, uint32_t ld,
+                                      const Dma<TRANS>& d, int ks, int w, uint32_t reg) {
+  const char* p = w < 4 ? p0 : p1;
+  if (!TRANS)
+    p += (uint64_t)(32 * (w & 3)) * ld + (uint64_t)ks * kRowB;   // 32 rows, this k range
+  else
+    p += (uint64_t)(ks * kKStep + 16 * (w & 3)) * ld;            // 16 k-rows
+  const rsrc_t r = make_rsrc(p);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int bb = 4 * (w & 3) + i;            // block within the half
-    uint32_t soff, vo;
-    if (!TRANS) {
-      soff = (uint32_t)ks * kRowB + (uint32_t)(8 * bb) * op.ld;
-      vo = d.voff[i & 1];
-    } else {
-      soff = (uint32_t)(ks * kKStep + 4 * bb) * op.ld;
-      vo = d.voff[0];
-    }
-    dma16(r, reg + (4 * w + i) * 1024, vo, soff);
+    const uint32_t soff = (uint32_t)(TRANS ? 4 * i : 8 * i) * ld;
+    dma16(r, reg + (4 * w + i) * 1024, TRANS ? d.voff[0] : d.voff[i & 1], soff);
   }
 }
 
@@ -189,91 +210,21 @@ struct Frags {
   bf16x8 b[2];
 };
 
-template <bool ATR, bool BTR, bool FA>
+template <bool ATR, bool BTR>
 __device__ __forceinline__ void load_frags(Frags& f, const char* stage, int kf, int wm, int wn,
                                            int lane) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) f.b[j] = frag<BTR>(stage + kReg, b_row(j, wn), kf, lane);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (!FA && i >= 2) break;
-    f.a[i] = frag<ATR>(stage, a_row(i, wm), kf, lane);
-  }
+  for (int i = 0; i < 4; ++i) f.a[i] = frag<ATR>(stage, a_row(i, wm), kf, lane);
 }
 
-template <bool FA>
 __device__ __forceinline__ void mma(Acc& acc, const Frags& f) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (!FA && i >= 2) break;
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
-  }
-}
-
-// DMA of K step ks into its stage (lds: LDS address of the stages).
-template <bool ATR, bool BTR>
-__device__ __forceinline__ void start_step(const Op& A, const Op& B, const Dma<ATR>& da,
-                                           const Dma<BTR>& db, int ks, int w, bool load_a,
-                                           bool load_b, uint32_t lds) {
-  const uint32_t st = lds + (ks % kStages) * kStage;
-  if (load_a) issue<ATR>(A, da, ks, w, st);
-  if (load_b) issue<BTR>(B, db, ks, w, st + kReg);
-}
-
-// acc += A . B^T over nk K steps (FA / FB: second half of A / B present).
-//
-// Each K step is four 16-wide k-fragments.  While the MFMAs of one fragment
-// run, the LDS reads of the next are in flight.  Before the last fragment of
-// step ks: wait for the DMA of step ks+1, barrier, start the DMA of step
-// ks+2 into the stage of step ks (nobody reads it any more) and read the
-// first fragment of step ks+1.  Ends with a barrier, so the LDS stages can
-// be refilled right away (the up-projection dgrad runs two of these).
-template <bool ATR, bool BTR, bool FA, bool FB>
-__device__ __forceinline__ void mainloop(Acc& acc, const Op& A, const Op& B, int nk, char* lds) {
-  if (nk <= 0) return;
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = w >> 2, wn = w & 3;
-  const bool load_a = FA || w < 4, load_b = FB || w < 4;
-  const bool work = FB || wn < 2;           // this wave has B rows
-  Dma<ATR> da;
-  Dma<BTR> db;
-  da.init(A.ld, lane);
-  db.init(B.ld, lane);
-  const uint32_t lbase = uniform(lds_addr(lds));
-  start_step<ATR, BTR>(A, B, da, db, 0, w, load_a, load_b, lbase);
-  if (nk > 1) {
-    start_step<ATR, BTR>(A, B, da, db, 1, w, load_a, load_b, lbase);
-    // wait for step 0: step 1 (0, 4 or 8 instructions) may stay in flight
-    if (load_a && load_b) wait_vm<8>(); else if (load_a || load_b) wait_vm<4>(); else wait_vm<0>();
-  } else {
-    wait_vm<0>();
-  }
-  barrier();
-  Frags f[2];
-  if (work) load_frags<ATR, BTR, FA>(f[0], lds, 0, wm, wn, lane);
-  for (int ks = 0; ks < nk; ++ks) {
-    const char* cur = lds + (ks % kStages) * kStage;
-#pragma unroll
-    for (int kf = 0; kf < 4; ++kf) {
-      sched_fence();
-      if (kf < 3) {
-        if (work) load_frags<ATR, BTR, FA>(f[(kf + 1) & 1], cur, kf + 1, wm, wn, lane);
-      } else if (ks + 1 < nk) {
-        wait_vm<0>();                       // step ks+1 landed (nothing later in flight)
-        barrier();
-        if (ks + 2 < nk) start_step<ATR, BTR>(A, B, da, db, ks + 2, w, load_a, load_b, lbase);
-        if (work)
-          load_frags<ATR, BTR, FA>(f[0], lds + ((ks + 1) % kStages) * kStage, 0, wm, wn, lane);
-      }
-      if (work) mma<FA>(acc, f[kf & 1]);
-    }
-  }
-  sched_fence();
-  wait_vm<0>();
-  barrier();
 }
 
 __device__ __forceinline__ void zero(Acc& acc) {
@@ -290,51 +241,83 @@ __device__ __forceinline__ void zero(Acc& acc) {
 __device__ __forceinline__ f32x4 quad(const f32x16& v, int g) {
   return f32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
 }
-template <bool FA, bool FB, class Fn>
-__device__ __forceinline__ void for_quads(const Acc& acc, int lane, Fn&& fn) {
-  const int w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
-  if (!FB && wn >= 2) return;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (!FA && i >= 2) break;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int brow = b_row(j, wn) + (lane & 31);
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        fn(i, a_row(i, wm) + 8 * g + 4 * (lane >> 5), brow, quad(acc[i][j], g));
-    }
-  }
-}
-
-__device__ __forceinline__ void store4(bf16* p, const f32x4& v) {
-  const uint32_t a = __builtin_bit_cast(uint16_t, from_f32<bf16>(v[0])) |
-                     ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<bf16>(v[1])) << 16);
-  const uint32_t b = __builtin_bit_cast(uint16_t, from_f32<bf16>(v[2])) |
-                     ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<bf16>(v[3])) << 16);
-  *reinterpret_cast<u32x2*>(p) = u32x2{a, b};
-}
 __device__ __forceinline__ f32x4 unpack4(const u32x2& u) {
   return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
                __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
 }
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
-
-// ---- Block -> tile order --------------------------------------------------
-// Workgroups are dealt to the 8 XCDs round-robin (block b runs on XCD b % 8),
-// and each XCD has its own L2.  Each XCD is given one contiguous range of the
-// logical tile order, so the blocks that share operands share an L2.
-constexpr int kXcds = 8;
-constexpr int kGroupM = 4;
-
-// Logical index of block b among `total` tiles, or -1 if the block is spare.
-__device__ __forceinline__ int xcd_tile(int b, int total) {
-  const int per = (total + kXcds - 1) / kXcds;
-  const int l = b / kXcds;
-  if (l >= per) return -1;
-  const int L = (b % kXcds) * per + l;
-  return L < total ? L : -1;
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return __builtin_bit_cast(uint16_t, from_f32<bf16>(a)) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<bf16>(b)) << 16);
 }
+
+// ---- Epilogue stores through LDS ------------------------------------------------
+// A wave's outputs of one A half form a 64 (B rows) x 64 (A rows) block, A
+// rows contiguous in memory.  In accumulator layout a store instruction would
+// touch 32 rows with 16 bytes each; instead the wave writes 32 B rows at a
+// time to its own 4 KB of LDS and reads them back as whole rows, so each
+// store instruction writes 8 full 128-byte rows.  Row r sits at 128 r with
+// its 16-byte chunk c at c ^ ((r >> 1) & 7) (the 32 rows written by one
+// instruction spread over all banks but for a factor of two).
+__device__ __forceinline__ u32x2 pack4(const f32x4& v) {
+  return u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+}
+
+// Stores per stage_out call and wave.
+constexpr int kStoresPerBlock = 8;
+
+// out: element (B row 0, A row 0) of this wave's block; ldo: elements between
+// B rows.  val(ii, j, g): the 4 values (bf16, packed) of A block ii (0/1 in
+// the half), B block j, quad g, in accumulator layout.  st: the wave's
+// staging space.
+template <class Val>
+__device__ __forceinline__ int stage_out(char* st, bf16* out, int64_t ldo, int lane_in,
+                                         Val&& val) {
+  // The lane index through an opaque move: the addresses below depend on the
+  // lane only, and would otherwise be hoisted out of the tile loop and kept
+  // in registers across the whole K loop.
+  int lane;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(lane) : "v"(lane_in));
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    wait_lds();   // the reads of the previous rows are done
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int r = lane & 31;
+        const int col = ii * 32 + 8 * g + 4 * (lane >> 5);
+        char* p = st + r * 128 + (((col >> 3) ^ ((r >> 1) & 7)) << 4) + ((col >> 2) & 1) * 8;
+        *reinterpret_cast<u32x2*>(p) = val(ii, j, g);
+      }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int r = it * 8 + (lane >> 3), c = lane & 7;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(st + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+      *reinterpret_cast<u32x4*>(out + (int64_t)(j * 32 + r) * ldo + c * 8) = v;
+    }
+  }
+  return kStoresPerBlock;
+}
+// The common case: A half h of the accumulators, stored as they are.
+__device__ __forceinline__ int stage_half(char* st, const Acc& acc, int h, bf16* out,
+                                          int64_t ldo, int lane) {
+  return stage_out(st, out, ldo, lane,
+                   [&](int ii, int j, int g) { return pack4(quad(acc[2 * h + ii][j], g)); });
+}
+
+// ---- Tiles ------------------------------------------------------------------
+// One output tile: `steps` K steps in one or two segments of `nk` steps (the
+// up-projection dgrad sums two products).  u, v and e are read by the
+// kernel's own operand and epilogue code.
+struct Job {
+  int steps, nk;
+  int e;            // expert (weight gradients: expert | first padded row << 8)
+  bool fa, fb;      // second half of A / B present
+  int64_t u, v;     // tile coordinates
+};
+
+constexpr int kGroupM = 4;
 
 // Row-tiled products: (m, n) for logical index L over MT x NT tiles, in
 // groups of kGroupM row tiles walked column by column, so that concurrent
@@ -349,303 +332,500 @@ __device__ __forceinline__ void group_mn(int L, int MT, int NT, int& m, int& n) 
   n = r / gm;
 }
 
-// The (pair of) row blocks and the column tile of this block, from the live
-// metadata; false if the block is spare.  two: the pair has two blocks.
-struct RowTile {
-  int64_t mt;    // first 128-row block
-  int64_t nt;    // column tile
-  int e;         // expert
-  bool two;
+// The pair of row blocks (u = first 128-row block) and the column tile (v)
+// of logical row tile L, from the live metadata.
+struct RowTiles {
+  const int32_t *tile_expert, *pair_first;
+  int pairs, MT, NT;
+  __device__ __forceinline__ void init(const int32_t* te, const int32_t* num_padded_rows,
+                                       const int32_t* pf, const int32_t* num_pairs, int nt) {
+    tile_expert = te;
+    pair_first = pf;
+    pairs = *num_pairs;
+    MT = *num_padded_rows / kBlock;
+    NT = nt;
+  }
+  __device__ __forceinline__ int total() const { return pairs * NT; }
+  __device__ __forceinline__ void get(int L, Job& j) const {
+    int s, n;
+    group_mn(L, pairs, NT, s, n);
+    const int m = pair_first[s];
+    j.e = tile_expert[m];
+    j.fb = m + 1 < MT && tile_expert[m + 1] == j.e;
+    j.u = m;
+    j.v = n;
+  }
 };
-__device__ __forceinline__ bool row_tile(const int32_t* num_pairs, const int32_t* pair_first,
-                                         const int32_t* tile_expert,
-                                         const int32_t* num_padded_rows, int NT, RowTile& t) {
-  const int S = *num_pairs;
-  const int L = xcd_tile(blockIdx.x, S * NT);
-  if (L < 0) return false;
-  int s, n;
-  group_mn(L, S, NT, s, n);
-  const int m = pair_first[s];
-  const int MT = *num_padded_rows / kBlock;
-  t.mt = m;
-  t.nt = n;
-  t.e = tile_expert[m];
-  t.two = m + 1 < MT && tile_expert[m + 1] == t.e;
-  return true;
-}
 
 #define ROW_TILE_ARGS                                                                   \
   const int32_t *__restrict__ tile_expert, const int32_t *__restrict__ num_padded_rows, \
       const int32_t *__restrict__ pair_first, const int32_t *__restrict__ num_pairs
 
-// Runs CALL with FA and FB as compile-time constants.
-#define DISPATCH2(FA_, FB_, CALL)                                   \
-  do {                                                              \
-    if (FA_) {                                                      \
-      if (FB_) { constexpr bool FA = true, FB = true; CALL; }       \
-      else { constexpr bool FA = true, FB = false; CALL; }          \
-    } else {                                                        \
-      if (FB_) { constexpr bool FA = false, FB = true; CALL; }      \
-      else { constexpr bool FA = false, FB = false; CALL; }         \
-    }                                                               \
-  } while (0)
+// ---- The products, as operand + epilogue policies ----------------------------
 
 // h1 = x_perm w1[e], h3 = x_perm w3[e], act = silu(h1) * h3 for one pair of
 // row blocks and 128 ffn columns (w1 columns in A rows 0..127, the same w3
 // columns in A rows 128..255, so A blocks i and i+2 pair up).
-template <bool FB>
-__device__ __forceinline__ void up_body(const bf16* x_perm, const bf16* w1, const bf16* w3,
-                                        int64_t H, int64_t F, const RowTile& t, bf16* h1,
-                                        bf16* h3, bf16* act, char* lds) {
-  const int lane = threadIdx.x & 63;
-  const int64_t f0 = t.nt * 128;
-  const int64_t wofs = (int64_t)t.e * H * F + f0;
-  const bf16* xb = x_perm + t.mt * kBlock * H;
-  const Op A{make_rsrc(w1 + wofs), make_rsrc(w3 + wofs), (uint32_t)(F * 2)};
-  const Op B{make_rsrc(xb), make_rsrc(xb + kBlock * H), (uint32_t)(H * 2)};
-  Acc acc;
-  zero(acc);
-  mainloop<true, false, true, FB>(acc, A, B, (int)(H / kKStep), lds);
-  const int64_t base = t.mt * kBlock * F + f0;
-  const int w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
-  if (!FB && wn >= 2) return;
+struct Up {
+  // step 1 of the next tile is issued after the epilogue (which loads)
+  static constexpr bool kLateStep1 = false;
+  static constexpr bool ATR = true, BTR = false;
+  const bf16 *x_perm, *w1, *w3;
+  int64_t H, F;
+  bf16 *h1, *h3, *act;
+  RowTiles rt;
+  __device__ uint32_t lda() const { return (uint32_t)(F * 2); }
+  __device__ uint32_t ldb() const { return (uint32_t)(H * 2); }
+  __device__ int total() const { return rt.total(); }
+  __device__ void tile(int L, Job& j) const {
+    rt.get(L, j);
+    j.fa = true;
+    j.nk = j.steps = (int)(H / kKStep);
+  }
+  __device__ void operands(const Job& j, int, const char*& a0, const char*& a1, const char*& b0,
+                           const char*& b1) const {
+    const int64_t wofs = (int64_t)j.e * H * F + j.v * 128;
+    a0 = (const char*)(w1 + wofs);
+    a1 = (const char*)(w3 + wofs);
+    b0 = (const char*)(x_perm + j.u * kBlock * H);
+    b1 = j.fb ? b0 + kBlock * H * 2 : b0;
+  }
+  __device__ int epilogue(const Job& j, const Acc& acc, char* st) const {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
+    if (!j.fb && wn >= 2) return 0;
+    const int64_t o = j.u * kBlock * F + j.v * 128 + (int64_t)(wn * 64) * F + wm * 64;
+    stage_half(st, acc, 0, h1 + o, F, lane);
+    stage_half(st, acc, 1, h3 + o, F, lane);
+    return 2 * kStoresPerBlock + stage_out(st, act + o, F, lane, [&](int ii, int jj, int g) {
+      const f32x4 v1 = quad(acc[ii][jj], g), v3 = quad(acc[2 + ii][jj], g);
+      f32x4 a;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+      for (int r = 0; r < 4; ++r) a[r] = silu(v1[r]) * v3[r];
+      return pack4(a);
+    });
+  }
+};
+
+// y_perm = act w2[e] for one pair of row blocks and 256 (or 128) hidden columns.
+struct Down {
+  // step 1 of the next tile is issued after the epilogue (which loads)
+  static constexpr bool kLateStep1 = false;
+  static constexpr bool ATR = true, BTR = false;
+  const bf16 *act, *w2;
+  int64_t H, F;
+  bf16* y_perm;
+  RowTiles rt;
+  __device__ uint32_t lda() const { return (uint32_t)(H * 2); }
+  __device__ uint32_t ldb() const { return (uint32_t)(F * 2); }
+  __device__ int total() const { return rt.total(); }
+  __device__ void tile(int L, Job& j) const {
+    rt.get(L, j);
+    j.fa = j.v * 256 + 256 <= H;
+    j.nk = j.steps = (int)(F / kKStep);
+  }
+  __device__ void operands(const Job& j, int, const char*& a0, const char*& a1, const char*& b0,
+                           const char*& b1) const {
+    a0 = (const char*)(w2 + (int64_t)j.e * F * H + j.v * 256);
+    a1 = j.fa ? a0 + 128 * 2 : a0;
+    b0 = (const char*)(act + j.u * kBlock * F);
+    b1 = j.fb ? b0 + kBlock * F * 2 : b0;
+  }
+  __device__ int epilogue(const Job& j, const Acc& acc, char* st) const {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
+    if (!j.fb && wn >= 2) return 0;
+    bf16* out = y_perm + j.u * kBlock * H + j.v * 256 + (int64_t)(wn * 64) * H + wm * 64;
+    int n = stage_half(st, acc, 0, out, H, lane);
+    if (j.fa) n += stage_half(st, acc, 1, out + 128, H, lane);
+    return n;
+  }
+};
+
+// dA = dy_perm w2[e]^T, then the gate's backward:
+// dh3 = dA * silu(h1), dh1 = dA * h3 * s * (1 + h1 (1 - s)), s = sigmoid(h1).
+struct DownDgrad {
+  // step 1 of the next tile is issued after the epilogue (which loads)
+  static constexpr bool kLateStep1 = true;
+  static constexpr bool ATR = false, BTR = false;
+  const bf16 *dy_perm, *w2, *h1, *h3;
+  int64_t H, F;
+  bf16 *dh1, *dh3;
+  RowTiles rt;
+  __device__ uint32_t lda() const { return (uint32_t)(H * 2); }
+  __device__ uint32_t ldb() const { return (uint32_t)(H * 2); }
+  __device__ int total() const { return rt.total(); }
+  __device__ void tile(int L, Job& j) const {
+    rt.get(L, j);
+    j.fa = j.v * 256 + 256 <= F;
+    j.nk = j.steps = (int)(H / kKStep);
+  }
+  __device__ void operands(const Job& j, int, const char*& a0, const char*& a1, const char*& b0,
+                           const char*& b1) const {
+    a0 = (const char*)(w2 + (int64_t)j.e * F * H + j.v * 256 * H);
+    a1 = j.fa ? a0 + 128 * H * 2 : a0;
+    b0 = (const char*)(dy_perm + j.u * kBlock * H);
+    b1 = j.fb ? b0 + kBlock * H * 2 : b0;
+  }
+  __device__ int epilogue(const Job& j, const Acc& acc, char* st) const {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
+    if (!j.fb && wn >= 2) return 0;
+    const int64_t base = j.u * kBlock * F + j.v * 256;
+    const int64_t wo = base + (int64_t)(wn * 64) * F + wm * 64;
+    // h1/h3 of one A half of this lane's outputs are loaded before any of them
+    // is stored, so the loads overlap (dh1/dh3 may alias h1/h3, which keeps the
+    // compiler from hoisting a load above an earlier store; each element is
+    // read before the block that overwrites it is stored).
+    int n = 0;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t prow = b_row(j, wn) + (lane & 31);
+    for (int h = 0; h < 2; ++h) {
+      if (!j.fa && h == 1) break;
+      u32x2 g1[2][2][4], g3[2][2][4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t o = base + prow * F + a_row(i, wm) + 8 * g + 4 * (lane >> 5);
-        const f32x4 v1 = quad(acc[i][j], g), v3 = quad(acc[i + 2][j], g);
-        f32x4 a;
+      for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) a[r] = silu(v1[r]) * v3[r];
-        store4(h1 + o, v1);
-        store4(h3 + o, v3);
-        store4(act + o, a);
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int64_t o = base + (int64_t)(b_row(jj, wn) + (lane & 31)) * F +
+                              a_row(2 * h + ii, wm) + 8 * g + 4 * (lane >> 5);
+            g1[ii][jj][g] = *reinterpret_cast<const u32x2*>(h1 + o);
+            g3[ii][jj][g] = *reinterpret_cast<const u32x2*>(h3 + o);
+          }
+      // dh3 = dA * silu(h1), dh1 = dA * h3 * s * (1 + h1 (1 - s)), s = sigmoid(h1),
+      // rounded right away so that h1, h3 and this half's accumulators die
+      u32x2 d1[2][2][4], d3[2][2][4];
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 da = quad(acc[2 * h + ii][jj], g), x1 = unpack4(g1[ii][jj][g]),
+                        x3 = unpack4(g3[ii][jj][g]);
+            f32x4 v1, v3;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float sg = 1.0f / (1.0f + __expf(-x1[r]));
+              v3[r] = da[r] * x1[r] * sg;
+              v1[r] = da[r] * x3[r] * sg * (1.0f + x1[r] * (1.0f - sg));
+            }
+            d1[ii][jj][g] = pack4(v1);
+            d3[ii][jj][g] = pack4(v3);
+          }
+      n += stage_out(st, dh1 + wo + h * 128, F, lane,
+                     [&](int ii, int jj, int g) { return d1[ii][jj][g]; });
+      n += stage_out(st, dh3 + wo + h * 128, F, lane,
+                     [&](int ii, int jj, int g) { return d3[ii][jj][g]; });
+    }
+    return n;
+  }
+};
+
+// dx_perm = dh1 w1[e]^T + dh3 w3[e]^T: two K segments into one accumulator.
+struct UpDgrad {
+  // step 1 of the next tile is issued after the epilogue (which loads)
+  static constexpr bool kLateStep1 = false;
+  static constexpr bool ATR = false, BTR = false;
+  const bf16 *dh1, *dh3, *w1, *w3;
+  int64_t H, F;
+  bf16* dx_perm;
+  RowTiles rt;
+  __device__ uint32_t lda() const { return (uint32_t)(F * 2); }
+  __device__ uint32_t ldb() const { return (uint32_t)(F * 2); }
+  __device__ int total() const { return rt.total(); }
+  __device__ void tile(int L, Job& j) const {
+    rt.get(L, j);
+    j.fa = j.v * 256 + 256 <= H;
+    j.nk = (int)(F / kKStep);
+    j.steps = 2 * j.nk;
+  }
+  __device__ void operands(const Job& j, int seg, const char*& a0, const char*& a1,
+                           const char*& b0, const char*& b1) const {
+    const int64_t wofs = (int64_t)j.e * H * F + j.v * 256 * F;
+    a0 = (const char*)((seg ? w3 : w1) + wofs);
+    a1 = j.fa ? a0 + 128 * F * 2 : a0;
+    b0 = (const char*)((seg ? dh3 : dh1) + j.u * kBlock * F);
+    b1 = j.fb ? b0 + kBlock * F * 2 : b0;
+  }
+  __device__ int epilogue(const Job& j, const Acc& acc, char* st) const {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
+    if (!j.fb && wn >= 2) return 0;
+    bf16* out = dx_perm + j.u * kBlock * H + j.v * 256 + (int64_t)(wn * 64) * H + wm * 64;
+    int n = stage_half(st, acc, 0, out, H, lane);
+    if (j.fa) n += stage_half(st, acc, 1, out + 128, H, lane);
+    return n;
+  }
+};
+
+// dw2[e] = act[rows_e]^T dy_perm[rows_e] ([F,H]); zero for an empty expert.
+// A = 256 (or 128) hidden columns of dy_perm (u = h0), B = 256 (or 128) ffn
+// columns of act (v = f0), K = the expert's padded rows.
+struct WgradDown {
+  // step 1 of the next tile is issued after the epilogue (which loads)
+  static constexpr bool kLateStep1 = false;
+  static constexpr bool ATR = true, BTR = true;
+  const bf16 *act, *dy_perm;
+  int64_t H, F;
+  int E;
+  const int32_t *tpe, *padded_bins;
+  bf16* dw2;
+  __device__ uint32_t lda() const { return (uint32_t)(H * 2); }
+  __device__ uint32_t ldb() const { return (uint32_t)(F * 2); }
+  __device__ int nh() const { return (int)((H + 255) / 256); }
+  __device__ int nf() const { return (int)((F + 255) / 256); }
+  __device__ int total() const { return E * nh() * nf(); }
+  __device__ void tile(int L, Job& j) const {
+    // the tiles of one expert are consecutive: each XCD works on whole experts
+    const int NH = nh(), NF = nf();
+    const int e = L / (NH * NF);
+    const int t = L - e * (NH * NF);
+    j.u = (int64_t)(t % NH) * 256;
+    j.v = (int64_t)(t / NH) * 256;
+    j.fa = j.u + 256 <= H;
+    j.fb = j.v + 256 <= F;
+    const int n = round_up_block(tpe[e]);
+    j.nk = j.steps = n / kKStep;
+    j.e = e | ((padded_bins[e] - n) << 8);
+  }
+  __device__ void operands(const Job& j, int, const char*& a0, const char*& a1, const char*& b0,
+                           const char*& b1) const {
+    const int64_t start = j.e >> 8;
+    a0 = (const char*)(dy_perm + start * H + j.u);
+    a1 = j.fa ? a0 + 128 * 2 : a0;
+    b0 = (const char*)(act + start * F + j.v);
+    b1 = j.fb ? b0 + 128 * 2 : b0;
+  }
+  __device__ int epilogue(const Job& j, const Acc& acc, char* st) const {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
+    if (!j.fb && wn >= 2) return 0;
+    bf16* out = dw2 + (int64_t)(j.e & 255) * F * H + j.v * H + j.u + (int64_t)(wn * 64) * H +
+                wm * 64;
+    int n = stage_half(st, acc, 0, out, H, lane);
+    if (j.fa) n += stage_half(st, acc, 1, out + 128, H, lane);
+    return n;
+  }
+};
+
+// dw1[e] = x_perm[rows_e]^T dh1[rows_e], dw3[e] = x_perm[rows_e]^T dh3[rows_e]
+// ([H,F] each).  A = 128 ffn columns of dh1 (rows 0..127) and the same
+// columns of dh3 (rows 128..255) (u = f0), B = 256 (or 128) hidden columns
+// of x_perm (v = h0).
+struct WgradUp {
+  // step 1 of the next tile is issued after the epilogue (which loads)
+  static constexpr bool kLateStep1 = false;
+  static constexpr bool ATR = true, BTR = true;
+  const bf16 *x_perm, *dh1, *dh3;
+  int64_t H, F;
+  int E;
+  const int32_t *tpe, *padded_bins;
+  bf16 *dw1, *dw3;
+  __device__ uint32_t lda() const { return (uint32_t)(F * 2); }
+  __device__ uint32_t ldb() const { return (uint32_t)(H * 2); }
+  __device__ int nf() const { return (int)(F / 128); }
+  __device__ int nh() const { return (int)((H + 255) / 256); }
+  __device__ int total() const { return E * nf() * nh(); }
+  __device__ void tile(int L, Job& j) const {
+    const int NF = nf(), NH = nh();
+    const int e = L / (NF * NH);
+    const int t = L - e * (NF * NH);
+    j.u = (int64_t)(t % NF) * 128;
+    j.v = (int64_t)(t / NF) * 256;
+    j.fa = true;
+    j.fb = j.v + 256 <= H;
+    const int n = round_up_block(tpe[e]);
+    j.nk = j.steps = n / kKStep;
+    j.e = e | ((padded_bins[e] - n) << 8);
+  }
+  __device__ void operands(const Job& j, int, const char*& a0, const char*& a1, const char*& b0,
+                           const char*& b1) const {
+    const int64_t start = j.e >> 8;
+    a0 = (const char*)(dh1 + start * F + j.u);
+    a1 = (const char*)(dh3 + start * F + j.u);
+    b0 = (const char*)(x_perm + start * H + j.v);
+    b1 = j.fb ? b0 + 128 * 2 : b0;
+  }
+  __device__ int epilogue(const Job& j, const Acc& acc, char* st) const {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
+    if (!j.fb && wn >= 2) return 0;
+    // A rows 0..127 are dw1 columns, 128..255 the same dw3 columns
+    const int64_t o = (int64_t)(j.e & 255) * H * F + j.v * F + j.u + (int64_t)(wn * 64) * F +
+                      wm * 64;
+    return stage_half(st, acc, 0, dw1 + o, F, lane) + stage_half(st, acc, 1, dw3 + o, F, lane);
+  }
+};
+
+// ---- The persistent pipeline ---------------------------------------------------
+
+template <class K>
+struct Pipe {
+  const K& k;
+  char* lds;            // the two stages
+  uint32_t lbase;       // their LDS address
+  int g;                // K steps run so far by this block (selects the stage)
+  int w, wm, wn, lane;
+  Dma<K::ATR> da;
+  Dma<K::BTR> db;
+
+  __device__ __forceinline__ uint32_t stage_addr(int s) const { return lbase + (s & 1) * kStage; }
+  __device__ __forceinline__ const char* stage_ptr(int s) const { return lds + (s & 1) * kStage; }
+
+  // DMA of step s of tile j into the stage of this block's step gs.
+  __device__ __forceinline__ void issue_step(const Job& j, int s, int gs) const {
+    const int seg = s >= j.nk ? 1 : 0;
+    const int ks = s - seg * j.nk;
+    const char *a0, *a1, *b0, *b1;
+    k.operands(j, seg, a0, a1, b0, b1);
+    const uint32_t st = stage_addr(gs);
+    issue<K::ATR>(a0, a1, k.lda(), da, ks, w, st);
+    issue<K::BTR>(b0, b1, k.ldb(), db, ks, w, st + kReg);
+  }
+
+  // acc += the product of tile `cur`.  primed: its steps 0 and 1 are already
+  // in flight.  Each K step is four 16-wide k-fragments; while the MFMAs of
+  // one fragment run, the LDS reads of the next are in flight.  Before the
+  // last fragment of step s: wait for the DMA of step s+1, barrier, start the
+  // DMA of step s+2 into the stage of step s (nobody reads it any more) --
+  // past the end of the tile that is step 0 of the next tile -- and read the
+  // first fragment of step s+1.  Ends with a barrier and no LDS read in
+  // flight.  Returns whether step 0 of `nxt` was started.  When primed, the
+  // waits for steps 0 and 1 let w0 and w1 younger vector-memory operations
+  // (the DMA of step 1, the previous tile's stores) stay in flight.
+  __device__ __forceinline__ bool run(Acc& acc, const Job& cur, const Job& nxt, bool primed,
+                                      int w0, int w1) {
+    const int n = cur.steps;
+    if (n <= 0) return false;
+    const bool work = cur.fb || wn < 2;     // this wave has B rows
+    if (!primed) {
+      issue_step(cur, 0, g);
+      if (n > 1) issue_step(cur, 1, g + 1);
+      w0 = n > 1 ? kDmaPerStep : 0;
+      w1 = 0;
+    }
+    wait_vm_n(w0);                          // step 0 landed
+    barrier();
+    Frags f[2];
+    if (work) load_frags<K::ATR, K::BTR>(f[0], stage_ptr(g), 0, wm, wn, lane);
+    bool next_started = false;
+    for (int s = 0; s < n; ++s) {
+      const char* cst = stage_ptr(g + s);
+#pragma unroll
+      for (int kf = 0; kf < 4; ++kf) {
+        sched_fence();
+        if (kf < 3) {
+          if (work) load_frags<K::ATR, K::BTR>(f[(kf + 1) & 1], cst, kf + 1, wm, wn, lane);
+        } else if (s + 1 < n) {
+          // step s+1 landed (after step 0 only the previous tile's stores
+          // may still be younger)
+          if (s == 0) wait_vm_n(w1); else wait_vm<0>();
+          barrier();
+          if (s + 2 < n) {
+            issue_step(cur, s + 2, g + s + 2);
+          } else if (nxt.steps > 0) {       // s + 2 == n
+            issue_step(nxt, 0, g + s + 2);
+            next_started = true;
+          }
+          if (work) load_frags<K::ATR, K::BTR>(f[0], stage_ptr(g + s + 1), 0, wm, wn, lane);
+        }
+        if (work) mma(acc, f[kf & 1]);
       }
     }
+    sched_fence();
+    wait_lds();
+    barrier();
+    g += n;
+    return next_started;
+  }
+};
+
+// One block per CU.  XCD x = blockIdx % 8 owns the logical tiles
+// [x*per, (x+1)*per); its S blocks take them round-robin, so at any time they
+// work on S consecutive tiles.  Every branch that reaches a barrier is
+// uniform over the block.
+template <class K>
+__device__ __forceinline__ void persistent(const K& k) {
+  __shared__ __attribute__((aligned(16))) char lds[kLds];
+  const int total = k.total();
+  const int S = (int)(gridDim.x / 8);
+  const int x = (int)(blockIdx.x % 8), r = (int)(blockIdx.x / 8);
+  const int per = (total + 7) / 8;
+  const int lo = x * per, hi = min(total, lo + per);
+  int L = lo + r;
+  if (L >= hi) return;
+  Pipe<K> p{k, lds, uniform(lds_addr(lds)), 0};
+  p.lane = threadIdx.x & 63;
+  p.w = (int)uniform(threadIdx.x >> 6);
+  p.wm = p.w >> 2;
+  p.wn = p.w & 3;
+  p.da.init(k.lda(), p.lane);
+  p.db.init(k.ldb(), p.lane);
+  char* const stg = lds + 2 * kStage + p.w * kStgWave;
+  Job cur;
+  k.tile(L, cur);
+  bool primed = false;
+  int w0 = 0, w1 = 0;
+  for (;;) {
+    const int Ln = L + S;
+    Job nxt;
+    nxt.steps = 0;
+    if (Ln < hi) k.tile(Ln, nxt);
+    Acc acc;
+    zero(acc);
+    primed = p.run(acc, cur, nxt, primed, w0, w1);
+    // step 1 of the next tile goes into the stage the last K step used (all
+    // its reads are done); it is started before the stores unless the
+    // epilogue loads, so that the stores can drain while the next tile runs
+    const bool step1 = primed && nxt.steps > 1;
+    if (!K::kLateStep1 && step1) p.issue_step(nxt, 1, p.g + 1);
+    const int nst = k.epilogue(cur, acc, stg);
+    if (Ln >= hi) break;
+    if (K::kLateStep1 && step1) p.issue_step(nxt, 1, p.g + 1);
+    // in flight, oldest first: step 0, [step 1,] the stores [, step 1]
+    w0 = (step1 ? kDmaPerStep : 0) + nst;
+    w1 = K::kLateStep1 ? 0 : nst;
+    cur = nxt;
+    L = Ln;
+  }
 }
 
 __global__ void __launch_bounds__(kThreads)
 up_kernel(const bf16* __restrict__ x_perm, const bf16* __restrict__ w1,
           const bf16* __restrict__ w3, int64_t H, int64_t F, ROW_TILE_ARGS,
           bf16* __restrict__ h1, bf16* __restrict__ h3, bf16* __restrict__ act) {
-  __shared__ __attribute__((aligned(16))) char lds[kLds];
-  RowTile t;
-  if (!row_tile(num_pairs, pair_first, tile_expert, num_padded_rows, (int)(F / 128), t)) return;
-  if (t.two)
-    up_body<true>(x_perm, w1, w3, H, F, t, h1, h3, act, lds);
-  else
-    up_body<false>(x_perm, w1, w3, H, F, t, h1, h3, act, lds);
-}
-
-// y_perm = act w2[e] for one pair of row blocks and 256 (or 128) hidden columns.
-template <bool FA, bool FB>
-__device__ __forceinline__ void down_body(const bf16* act, const bf16* w2, int64_t H,
-                                          int64_t F, const RowTile& t, bf16* y_perm,
-                                          char* lds) {
-  const int lane = threadIdx.x & 63;
-  const int64_t h0 = t.nt * 256;
-  const bf16* wb = w2 + (int64_t)t.e * F * H + h0;
-  const bf16* ab = act + t.mt * kBlock * F;
-  const Op A{make_rsrc(wb), make_rsrc(wb + 128), (uint32_t)(H * 2)};
-  const Op B{make_rsrc(ab), make_rsrc(ab + kBlock * F), (uint32_t)(F * 2)};
-  Acc acc;
-  zero(acc);
-  mainloop<true, false, FA, FB>(acc, A, B, (int)(F / kKStep), lds);
-  bf16* out = y_perm + t.mt * kBlock * H + h0;
-  for_quads<FA, FB>(acc, lane, [&](int, int arow, int brow, const f32x4& v) {
-    store4(out + (int64_t)brow * H + arow, v);
-  });
+  Up k{x_perm, w1, w3, H, F, h1, h3, act};
+  k.rt.init(tile_expert, num_padded_rows, pair_first, num_pairs, (int)(F / 128));
+  persistent(k);
 }
 
 __global__ void __launch_bounds__(kThreads)
 down_kernel(const bf16* __restrict__ act, const bf16* __restrict__ w2, int64_t H,
             int64_t F, ROW_TILE_ARGS, bf16* __restrict__ y_perm) {
-  __shared__ __attribute__((aligned(16))) char lds[kLds];
-  RowTile t;
-  if (!row_tile(num_pairs, pair_first, tile_expert, num_padded_rows, (int)((H + 255) / 256), t))
-    return;
-  DISPATCH2(t.nt * 256 + 256 <= H, t.two, (down_body<FA, FB>(act, w2, H, F, t, y_perm, lds)));
-}
-
-// dA = dy_perm w2[e]^T, then the gate's backward:
-// dh3 = dA * silu(h1), dh1 = dA * h3 * s * (1 + h1 (1 - s)), s = sigmoid(h1).
-template <bool FA, bool FB>
-__device__ __forceinline__ void down_dgrad_body(const bf16* dy_perm, const bf16* w2,
-                                                const bf16* h1, const bf16* h3, int64_t H,
-                                                int64_t F, const RowTile& t, bf16* dh1,
-                                                bf16* dh3, char* lds) {
-  const int lane = threadIdx.x & 63;
-  const int64_t fb = t.nt * 256;
-  const bf16* wb = w2 + (int64_t)t.e * F * H + fb * H;
-  const bf16* db = dy_perm + t.mt * kBlock * H;
-  const Op A{make_rsrc(wb), make_rsrc(wb + 128 * H), (uint32_t)(H * 2)};
-  const Op B{make_rsrc(db), make_rsrc(db + kBlock * H), (uint32_t)(H * 2)};
-  Acc acc;
-  zero(acc);
-  mainloop<false, false, FA, FB>(acc, A, B, (int)(H / kKStep), lds);
-  const int64_t base = t.mt * kBlock * F + fb;
-  const int w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
-  if (!FB && wn >= 2) return;
-  // h1/h3 of half of this lane's outputs are loaded before any of them is
-  // stored, so the loads overlap (dh1/dh3 may alias h1/h3, which keeps the
-  // compiler from hoisting a load above an earlier store; each element is
-  // read by the lane that overwrites it).
-#pragma unroll
-  for (int i0 = 0; i0 < 4; i0 += 2) {
-    if (!FA && i0 >= 2) break;
-    u32x2 g1[2][2][4], g3[2][2][4];
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int64_t o = base + (int64_t)(b_row(j, wn) + (lane & 31)) * F +
-                            a_row(i0 + ii, wm) + 8 * g + 4 * (lane >> 5);
-          g1[ii][j][g] = *reinterpret_cast<const u32x2*>(h1 + o);
-          g3[ii][j][g] = *reinterpret_cast<const u32x2*>(h3 + o);
-        }
-#pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int64_t o = base + (int64_t)(b_row(j, wn) + (lane & 31)) * F +
-                            a_row(i0 + ii, wm) + 8 * g + 4 * (lane >> 5);
-          const f32x4 da = quad(acc[i0 + ii][j], g);
-          const f32x4 x1 = unpack4(g1[ii][j][g]), x3 = unpack4(g3[ii][j][g]);
-          f32x4 d1, d3;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float s = 1.0f / (1.0f + __expf(-x1[r]));
-            d3[r] = da[r] * x1[r] * s;
-            d1[r] = da[r] * x3[r] * s * (1.0f + x1[r] * (1.0f - s));
-          }
-          store4(dh1 + o, d1);
-          store4(dh3 + o, d3);
-        }
-  }
+  Down k{act, w2, H, F, y_perm};
+  k.rt.init(tile_expert, num_padded_rows, pair_first, num_pairs, (int)((H + 255) / 256));
+  persistent(k);
 }
 
 __global__ void __launch_bounds__(kThreads)
 down_dgrad_kernel(const bf16* __restrict__ dy_perm, const bf16* __restrict__ w2,
                   const bf16* h1, const bf16* h3, int64_t H, int64_t F, ROW_TILE_ARGS,
                   bf16* dh1, bf16* dh3) {
-  __shared__ __attribute__((aligned(16))) char lds[kLds];
-  RowTile t;
-  if (!row_tile(num_pairs, pair_first, tile_expert, num_padded_rows, (int)((F + 255) / 256), t))
-    return;
-  DISPATCH2(t.nt * 256 + 256 <= F, t.two,
-            (down_dgrad_body<FA, FB>(dy_perm, w2, h1, h3, H, F, t, dh1, dh3, lds)));
-}
-
-// dx_perm = dh1 w1[e]^T + dh3 w3[e]^T.
-template <bool FA, bool FB>
-__device__ __forceinline__ void up_dgrad_body(const bf16* dh1, const bf16* dh3,
-                                              const bf16* w1, const bf16* w3, int64_t H,
-                                              int64_t F, const RowTile& t, bf16* dx_perm,
-                                              char* lds) {
-  const int lane = threadIdx.x & 63;
-  const int64_t h0 = t.nt * 256;
-  const int64_t wofs = (int64_t)t.e * H * F + h0 * F;
-  const int nk = (int)(F / kKStep);
-  Acc acc;
-  zero(acc);
-  {
-    const bf16* db = dh1 + t.mt * kBlock * F;
-    const Op A{make_rsrc(w1 + wofs), make_rsrc(w1 + wofs + 128 * F), (uint32_t)(F * 2)};
-    const Op B{make_rsrc(db), make_rsrc(db + kBlock * F), (uint32_t)(F * 2)};
-    mainloop<false, false, FA, FB>(acc, A, B, nk, lds);
-  }
-  {
-    const bf16* db = dh3 + t.mt * kBlock * F;
-    const Op A{make_rsrc(w3 + wofs), make_rsrc(w3 + wofs + 128 * F), (uint32_t)(F * 2)};
-    const Op B{make_rsrc(db), make_rsrc(db + kBlock * F), (uint32_t)(F * 2)};
-    mainloop<false, false, FA, FB>(acc, A, B, nk, lds);
-  }
-  bf16* out = dx_perm + t.mt * kBlock * H + h0;
-  for_quads<FA, FB>(acc, lane, [&](int, int arow, int brow, const f32x4& v) {
-    store4(out + (int64_t)brow * H + arow, v);
-  });
+  DownDgrad k{dy_perm, w2, h1, h3, H, F, dh1, dh3};
+  k.rt.init(tile_expert, num_padded_rows, pair_first, num_pairs, (int)((F + 255) / 256));
+  persistent(k);
 }
 
 __global__ void __launch_bounds__(kThreads)
 up_dgrad_kernel(const bf16* __restrict__ dh1, const bf16* __restrict__ dh3,
                 const bf16* __restrict__ w1, const bf16* __restrict__ w3, int64_t H,
                 int64_t F, ROW_TILE_ARGS, bf16* dx_perm) {
-  __shared__ __attribute__((aligned(16))) char lds[kLds];
-  RowTile t;
-  if (!row_tile(num_pairs, pair_first, tile_expert, num_padded_rows, (int)((H + 255) / 256), t))
-    return;
-  DISPATCH2(t.nt * 256 + 256 <= H, t.two,
-            (up_dgrad_body<FA, FB>(dh1, dh3, w1, w3, H, F, t, dx_perm, lds)));
-}
-
-// dw2[e] = act[rows_e]^T dy_perm[rows_e] ([F,H]); zero for an empty expert.
-// A = 256 (or 128) hidden columns of dy_perm, B = 256 (or 128) ffn columns
-// of act, K = the expert's padded rows.
-template <bool FA, bool FB>
-__device__ __forceinline__ void wgrad_down_body(const bf16* act, const bf16* dy_perm,
-                                                int64_t H, int64_t F, int64_t start, int n,
-                                                int64_t h0, int64_t f0, int e, bf16* dw2,
-                                                char* lds) {
-  const int lane = threadIdx.x & 63;
-  const bf16* ab = dy_perm + start * H + h0;
-  const bf16* bb = act + start * F + f0;
-  const Op A{make_rsrc(ab), make_rsrc(ab + 128), (uint32_t)(H * 2)};
-  const Op B{make_rsrc(bb), make_rsrc(bb + 128), (uint32_t)(F * 2)};
-  Acc acc;
-  zero(acc);
-  mainloop<true, true, FA, FB>(acc, A, B, n / kKStep, lds);
-  bf16* out = dw2 + (int64_t)e * F * H + f0 * H + h0;
-  for_quads<FA, FB>(acc, lane, [&](int, int arow, int brow, const f32x4& v) {
-    store4(out + (int64_t)brow * H + arow, v);
-  });
+  UpDgrad k{dh1, dh3, w1, w3, H, F, dx_perm};
+  k.rt.init(tile_expert, num_padded_rows, pair_first, num_pairs, (int)((H + 255) / 256));
+  persistent(k);
 }
 
 __global__ void __launch_bounds__(kThreads)
 wgrad_down_kernel(const bf16* __restrict__ act, const bf16* __restrict__ dy_perm,
                   int64_t H, int64_t F, int E, const int32_t* __restrict__ tpe,
                   const int32_t* __restrict__ padded_bins, bf16* __restrict__ dw2) {
-  __shared__ __attribute__((aligned(16))) char lds[kLds];
-  // tiles of one expert are consecutive: each XCD works on whole experts
-  const int NH = (int)((H + 255) / 256), NF = (int)((F + 255) / 256);
-  const int L = xcd_tile(blockIdx.x, E * NH * NF);
-  if (L < 0) return;
-  const int e = L / (NH * NF);
-  const int t = L - e * (NH * NF);
-  const int64_t h0 = (int64_t)(t % NH) * 256, f0 = (int64_t)(t / NH) * 256;
-  const int n = round_up_block(tpe[e]);
-  const int64_t start = padded_bins[e] - n;
-  DISPATCH2(h0 + 256 <= H, f0 + 256 <= F,
-            (wgrad_down_body<FA, FB>(act, dy_perm, H, F, start, n, h0, f0, e, dw2, lds)));
-}
-
-// dw1[e] = x_perm[rows_e]^T dh1[rows_e], dw3[e] = x_perm[rows_e]^T dh3[rows_e]
-// ([H,F] each).  A = 128 ffn columns of dh1 (rows 0..127) and the same
-// columns of dh3 (rows 128..255), B = 256 (or 128) hidden columns of x_perm.
-template <bool FB>
-__device__ __forceinline__ void wgrad_up_body(const bf16* x_perm, const bf16* dh1,
-                                              const bf16* dh3, int64_t H, int64_t F,
-                                              int64_t start, int n, int64_t h0, int64_t f0,
-                                              int e, bf16* dw1, bf16* dw3, char* lds) {
-  const int lane = threadIdx.x & 63;
-  const bf16* xb = x_perm + start * H + h0;
-  const Op A{make_rsrc(dh1 + start * F + f0), make_rsrc(dh3 + start * F + f0), (uint32_t)(F * 2)};
-  const Op B{make_rsrc(xb), make_rsrc(xb + 128), (uint32_t)(H * 2)};
-  Acc acc;
-  zero(acc);
-  mainloop<true, true, true, FB>(acc, A, B, n / kKStep, lds);
-  const int64_t eo = (int64_t)e * H * F + h0 * F + f0;
-  for_quads<true, FB>(acc, lane, [&](int, int arow, int brow, const f32x4& v) {
-    // A rows 0..127 are dw1 columns, 128..255 the same dw3 columns
-    store4((arow < 128 ? dw1 : dw3) + eo + (int64_t)brow * F + (arow & 127), v);
-  });
+  persistent(WgradDown{act, dy_perm, H, F, E, tpe, padded_bins, dw2});
 }
 
 __global__ void __launch_bounds__(kThreads)
@@ -653,27 +833,34 @@ wgrad_up_kernel(const bf16* __restrict__ x_perm, const bf16* __restrict__ dh1,
                 const bf16* __restrict__ dh3, int64_t H, int64_t F, int E,
                 const int32_t* __restrict__ tpe, const int32_t* __restrict__ padded_bins,
                 bf16* __restrict__ dw1, bf16* __restrict__ dw3) {
-  __shared__ __attribute__((aligned(16))) char lds[kLds];
-  const int NF = (int)(F / 128), NH = (int)((H + 255) / 256);
-  const int L = xcd_tile(blockIdx.x, E * NF * NH);
-  if (L < 0) return;
-  const int e = L / (NF * NH);
-  const int t = L - e * (NF * NH);
-  const int64_t f0 = (int64_t)(t % NF) * 128, h0 = (int64_t)(t / NF) * 256;
-  const int n = round_up_block(tpe[e]);
-  const int64_t start = padded_bins[e] - n;
-  if (h0 + 256 <= H)
-    wgrad_up_body<true>(x_perm, dh1, dh3, H, F, start, n, h0, f0, e, dw1, dw3, lds);
-  else
-    wgrad_up_body<false>(x_perm, dh1, dh3, H, F, start, n, h0, f0, e, dw1, dw3, lds);
+  persistent(WgradUp{x_perm, dh1, dh3, H, F, E, tpe, padded_bins, dw1, dw3});
 }
 
 }  // namespace bfk
 
-static unsigned cdiv_u(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
+static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Enough blocks for every XCD to take ceil(total / 8) tiles.
-static dim3 xcd_grid(int64_t total) { return dim3(8u * cdiv_u(total, 8)); }
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// One block per CU (a multiple of 8: one share per XCD), fewer when there are
+// fewer tiles.
+static dim3 persistent_grid(int64_t max_total) {
+  const int64_t slots = std::max<int64_t>(1, device_cus() / 8);
+  const int64_t per = std::max<int64_t>(1, cdiv(max_total, 8));
+  return dim3((unsigned)(8 * std::min(per, slots)));
+}
 
 template <typename T> static const T* cb(const void* p) { return static_cast<const T*>(p); }
 template <typename T> static T* mb(void* p) { return static_cast<T*>(p); }
@@ -681,7 +868,7 @@ template <typename T> static T* mb(void* p) { return static_cast<T*>(p); }
 hipError_t launch_bf16_up(const Shape& s, const void* x_perm, const void* w1, const void* w3,
                           const MetaPtrs& m, void* h1, void* h3, void* act,
                           hipStream_t stream) {
-  hipLaunchKernelGGL(bfk::up_kernel, xcd_grid(cdiv_u(s.F, 128) * s.max_tiles),
+  hipLaunchKernelGGL(bfk::up_kernel, persistent_grid(cdiv(s.F, 128) * s.max_tiles),
                      dim3(bfk::kThreads), 0, stream, cb<bf16>(x_perm), cb<bf16>(w1),
                      cb<bf16>(w3), s.H, s.F, m.tile_expert, m.num_padded_rows, m.pair_first,
                      m.num_pairs, mb<bf16>(h1), mb<bf16>(h3), mb<bf16>(act));
@@ -690,7 +877,7 @@ hipError_t launch_bf16_up(const Shape& s, const void* x_perm, const void* w1, co
 
 hipError_t launch_bf16_down(const Shape& s, const void* act, const void* w2,
                             const MetaPtrs& m, void* y_perm, hipStream_t stream) {
-  hipLaunchKernelGGL(bfk::down_kernel, xcd_grid(cdiv_u(s.H, 256) * s.max_tiles),
+  hipLaunchKernelGGL(bfk::down_kernel, persistent_grid(cdiv(s.H, 256) * s.max_tiles),
                      dim3(bfk::kThreads), 0, stream, cb<bf16>(act), cb<bf16>(w2), s.H, s.F,
                      m.tile_expert, m.num_padded_rows, m.pair_first, m.num_pairs,
                      mb<bf16>(y_perm));
@@ -700,7 +887,7 @@ hipError_t launch_bf16_down(const Shape& s, const void* act, const void* w2,
 hipError_t launch_bf16_down_dgrad(const Shape& s, const void* dy_perm, const void* w2,
                                   const void* h1, const void* h3, const MetaPtrs& m,
                                   void* dh1, void* dh3, hipStream_t stream) {
-  hipLaunchKernelGGL(bfk::down_dgrad_kernel, xcd_grid(cdiv_u(s.F, 256) * s.max_tiles),
+  hipLaunchKernelGGL(bfk::down_dgrad_kernel, persistent_grid(cdiv(s.F, 256) * s.max_tiles),
                      dim3(bfk::kThreads), 0, stream, cb<bf16>(dy_perm), cb<bf16>(w2),
                      cb<bf16>(h1), cb<bf16>(h3), s.H, s.F, m.tile_expert, m.num_padded_rows,
                      m.pair_first, m.num_pairs, mb<bf16>(dh1), mb<bf16>(dh3));
@@ -710,7 +897,7 @@ hipError_t launch_bf16_down_dgrad(const Shape& s, const void* dy_perm, const voi
 hipError_t launch_bf16_up_dgrad(const Shape& s, const void* dh1, const void* dh3,
                                 const void* w1, const void* w3, const MetaPtrs& m,
                                 void* dx_perm, hipStream_t stream) {
-  hipLaunchKernelGGL(bfk::up_dgrad_kernel, xcd_grid(cdiv_u(s.H, 256) * s.max_tiles),
+  hipLaunchKernelGGL(bfk::up_dgrad_kernel, persistent_grid(cdiv(s.H, 256) * s.max_tiles),
                      dim3(bfk::kThreads), 0, stream, cb<bf16>(dh1), cb<bf16>(dh3),
                      cb<bf16>(w1), cb<bf16>(w3), s.H, s.F, m.tile_expert, m.num_padded_rows,
                      m.pair_first, m.num_pairs, mb<bf16>(dx_perm));
@@ -720,7 +907,7 @@ hipError_t launch_bf16_up_dgrad(const Shape& s, const void* dh1, const void* dh3
 hipError_t launch_bf16_wgrad_down(const Shape& s, const void* act, const void* dy_perm,
                                   const MetaPtrs& m, void* dw2, hipStream_t stream) {
   hipLaunchKernelGGL(bfk::wgrad_down_kernel,
-                     xcd_grid((int64_t)cdiv_u(s.H, 256) * cdiv_u(s.F, 256) * s.E),
+                     persistent_grid(cdiv(s.H, 256) * cdiv(s.F, 256) * s.E),
                      dim3(bfk::kThreads), 0, stream, cb<bf16>(act), cb<bf16>(dy_perm), s.H,
                      s.F, s.E, m.tokens_per_expert, m.padded_bins, mb<bf16>(dw2));
   return hipGetLastError();
@@ -730,7 +917,7 @@ hipError_t launch_bf16_wgrad_up(const Shape& s, const void* x_perm, const void* 
                                 const void* dh3, const MetaPtrs& m, void* dw1, void* dw3,
                                 hipStream_t stream) {
   hipLaunchKernelGGL(bfk::wgrad_up_kernel,
-                     xcd_grid((int64_t)cdiv_u(s.F, 128) * cdiv_u(s.H, 256) * s.E),
+                     persistent_grid(cdiv(s.F, 128) * cdiv(s.H, 256) * s.E),
                      dim3(bfk::kThreads), 0, stream, cb<bf16>(x_perm), cb<bf16>(dh1),
                      cb<bf16>(dh3), s.H, s.F, s.E, m.tokens_per_expert, m.padded_bins,
                      mb<bf16>(dw1), mb<bf16>(dw3));
