@@ -32,7 +32,7 @@ METRIC = "dMoE fwd+bwd tokens/s and useful TFLOP/s (% bf16 MFMA peak), E=64 k=8"
 META_KERNELS = ["meta_hist", "meta_scan", "meta_place"]
 FWD_KERNELS = ["padded_gather", "gemm_up_gate", "gemm_down", "padded_scatter"]
 BWD_KERNELS = ["scatter_backward", "gemm_down_dgrad_gate", "gemm_wgrad_down",
-               "gemm_up_dgrad", "gemm_wgrad_up", "gather_backward"]
+               "gemm_up_dgrad", "gather_backward", "gemm_wgrad_up"]
 
 
 def kernel_work(cfg, P):

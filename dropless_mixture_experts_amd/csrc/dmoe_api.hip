@@ -170,10 +170,12 @@ int dmoe_backward_timed(const dmoe_dims* dims, const void* dy, const float* weig
   DMOE_TRY(dmoe::launch_gemm_up_dgrad(s, scratch->dh1, scratch->dh3, w1, w3, m,
                                       scratch->dx_perm, stream));
   rec(4);
+  // the gather's backward right away, while dx_perm is still in the
+  // last-level cache
+  DMOE_TRY(dmoe::launch_padded_scatter(s, scratch->dx_perm, nullptr, m, dx, stream));
+  rec(5);
   DMOE_TRY(dmoe::launch_gemm_wgrad_up(s, saved->x_perm, scratch->dh1, scratch->dh3, m,
                                       dw1, dw3, stream));
-  rec(5);
-  DMOE_TRY(dmoe::launch_padded_scatter(s, scratch->dx_perm, nullptr, m, dx, stream));
   rec(6);
   return DMOE_OK;
 }

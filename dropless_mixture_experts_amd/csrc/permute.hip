@@ -9,68 +9,86 @@
 // weights.  §5: pad rows hold zeros and the scatter reads only real rows.
 //
 // These kernels move bytes and do almost no arithmetic, so they are bound by
-// HBM.  One wave owns one row; each lane moves 16 bytes per access, so a
-// 4 KB bf16 row (H = 2048) is four fully coalesced 1 KB wave transactions.
-// No atomics: each output row is written by exactly one wave, and the top-k
-// sum runs in fp32 in slot order with one final rounding.
+// HBM.  One wave owns one token: it reads the token's row once and reaches
+// its k padded rows through row_of_entry; extra waves zero the pad rows.
+// Each lane moves 16 bytes per access, so a 4 KB bf16 row (H = 2048) is four
+// fully coalesced 1 KB wave transactions.  No atomics: each output row is
+// written by exactly one wave, and the top-k sum runs in fp32 in slot order
+// with one final rounding.
 #include "dmoe_device.h"
 #include "dmoe_internal.h"
 
 namespace dmoe {
 
-constexpr int kRowsPerBlock = 4;   // one wave per row
+constexpr int kRowsPerBlock = 4;   // one wave per row (or token)
 constexpr int kUnroll = 4;         // 16-byte accesses in flight per lane
+constexpr int kPadWaves = kBlock - 1;   // an expert has at most 127 pad rows
 
-// Real row p of expert e holds sorted entry s = bins[e] - count[e] + offset;
-// pad rows get -1.
-__device__ __forceinline__ int source_entry(int64_t p, const int32_t* tile_expert,
-                                            const int32_t* tpe, const int32_t* bins,
-                                            const int32_t* padded_bins,
-                                            const int32_t* indices) {
-  const int e = tile_expert[p / kBlock];
-  const int cnt = tpe[e];
-  const int off = (int)(p - (padded_bins[e] - round_up_block(cnt)));
-  return off < cnt ? indices[bins[e] - cnt + off] : -1;
+// Wave index of this lane's wave, the same in every lane.
+__device__ __forceinline__ int64_t wave_index() {
+  return (int64_t)blockIdx.x * kRowsPerBlock +
+         __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
 }
 
+// Pad row i of expert e for the wave q = e * 127 + i after the token waves, or
+// -1 if expert e has at most i pad rows (MegaBlocks §2: rows
+// [start_e + c_e, start_e + round_up(c_e)) of expert e are padding).
+__device__ __forceinline__ int64_t pad_row(int64_t q, const int32_t* tpe,
+                                           const int32_t* padded_bins) {
+  const int e = (int)(q / kPadWaves), i = (int)(q - (int64_t)e * kPadWaves);
+  const int c = tpe[e], pc = round_up_block(c);
+  return i < pc - c ? (int64_t)padded_bins[e] - pc + c + i : -1;
+}
+
+__device__ __forceinline__ void zero_row(char* dst, int64_t vecs, int lane) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int64_t v = lane; v < vecs; v += kWave) st16(dst + v * 16, z);
+}
+
+// Waves [0, ntok): token t copies its row of x to the padded rows of its k
+// entries (the row is read once, written k times).  Waves [ntok, ntok + 127 E):
+// zero the pad rows.
 template <typename T>
 __global__ void __launch_bounds__(kRowsPerBlock * kWave)
-padded_gather_kernel(const T* __restrict__ x, int64_t H, int k,
-                     const int32_t* __restrict__ tile_expert,
+padded_gather_kernel(const T* __restrict__ x, int64_t ntok, int64_t H, int k, int E,
+                     const int32_t* __restrict__ row_of_entry,
                      const int32_t* __restrict__ tpe,
-                     const int32_t* __restrict__ bins,
-                     const int32_t* __restrict__ padded_bins,
-                     const int32_t* __restrict__ indices,
-                     const int32_t* __restrict__ num_padded_rows,
-                     T* __restrict__ x_perm) {
+                     const int32_t* __restrict__ padded_bins, T* __restrict__ x_perm) {
   const int lane = threadIdx.x % kWave;
-  const int64_t p = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
-  if (p >= *num_padded_rows) return;
-  const int a = source_entry(p, tile_expert, tpe, bins, padded_bins, indices);
+  const int64_t q = wave_index();
   const int64_t vecs = H * (int64_t)sizeof(T) / 16;
-  char* dst = reinterpret_cast<char*>(x_perm + p * H);
-  if (a >= 0) {
-    const char* src = reinterpret_cast<const char*>(x + (int64_t)(a / k) * H);
-    for (int64_t v0 = lane; v0 < vecs; v0 += kWave * kUnroll) {
-      u32x4 r[kUnroll];
+  const int64_t rowb = H * (int64_t)sizeof(T);
+  char* out = reinterpret_cast<char*>(x_perm);
+  if (q >= ntok) {
+    if (q - ntok >= (int64_t)E * kPadWaves) return;
+    const int64_t p = pad_row(q - ntok, tpe, padded_bins);
+    if (p >= 0) zero_row(out + p * rowb, vecs, lane);
+    return;
+  }
+  const char* src = reinterpret_cast<const char*>(x) + q * rowb;
+  const int32_t* rows = row_of_entry + q * k;
+  for (int64_t v0 = lane; v0 < vecs; v0 += kWave * kUnroll) {
+    u32x4 r[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int64_t v = v0 + u * kWave;
-        if (v < vecs) r[u] = ld16(src + v * 16);
-      }
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t v = v0 + u * kWave;
+      if (v < vecs) r[u] = ld16(src + v * 16);
+    }
+    for (int j = 0; j < k; ++j) {
+      const int row = rows[j];
+      if (row < 0) continue;     // an invalid expert id: no row
+      char* dst = out + (int64_t)row * rowb;
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int64_t v = v0 + u * kWave;
         if (v < vecs) st16(dst + v * 16, r[u]);
       }
     }
-  } else {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int64_t v = lane; v < vecs; v += kWave) st16(dst + v * 16, z);
   }
 }
 
 // out[t] = sum_j w[t,j] * src_perm[row_of_entry[t*k+j]]  (w = 1 if null).
+// Two 16-byte columns per lane and pass, so 16 row reads are in flight.
 template <typename T>
 __global__ void __launch_bounds__(kRowsPerBlock * kWave)
 padded_scatter_kernel(const T* __restrict__ src_perm,
@@ -79,7 +97,7 @@ padded_scatter_kernel(const T* __restrict__ src_perm,
                       int64_t H, int k, T* __restrict__ out) {
   using V = Vec16<T>;
   const int lane = threadIdx.x % kWave;
-  const int64_t t = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+  const int64_t t = wave_index();
   if (t >= ntok) return;
   const int64_t vecs = H * (int64_t)sizeof(T) / 16;
   const int64_t rowb = H * (int64_t)sizeof(T);
@@ -87,12 +105,14 @@ padded_scatter_kernel(const T* __restrict__ src_perm,
   const int32_t* rows = row_of_entry + t * k;
   const float* wts = weights ? weights + t * k : nullptr;
   char* dst = reinterpret_cast<char*>(out + t * H);
-  for (int64_t v = lane; v < vecs; v += kWave) {
-    float acc[V::N];
+  for (int64_t v0 = lane; v0 < vecs; v0 += 2 * kWave) {
+    const int64_t v1 = v0 + kWave;
+    const bool has1 = v1 < vecs;
+    float acc0[V::N], acc1[V::N];
 #pragma unroll
-    for (int i = 0; i < V::N; ++i) acc[i] = 0.f;
+    for (int i = 0; i < V::N; ++i) acc0[i] = acc1[i] = 0.f;
     for (int j0 = 0; j0 < k; j0 += 8) {
-      u32x4 d[8];
+      u32x4 d0[8], d1[8];
       float wj[8];
       bool live[8];
 #pragma unroll
@@ -101,52 +121,62 @@ padded_scatter_kernel(const T* __restrict__ src_perm,
         const int r = j < k ? rows[j] : -1;
         live[u] = r >= 0;          // -1: padding of the unrolled loop, or an invalid id
         wj[u] = wts && live[u] ? wts[j] : 1.f;
-        if (live[u]) d[u] = ld16(src + (int64_t)r * rowb + v * 16);
-        else d[u] = u32x4{0u, 0u, 0u, 0u};
+        const char* row = src + (int64_t)(live[u] ? r : 0) * rowb;
+        d0[u] = live[u] ? ld16(row + v0 * 16) : u32x4{0u, 0u, 0u, 0u};
+        d1[u] = live[u] && has1 ? ld16(row + v1 * 16) : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (live[u]) {
-          float f[V::N];
-          V::unpack(d[u], f);
+          float f0[V::N], f1[V::N];
+          V::unpack(d0[u], f0);
+          V::unpack(d1[u], f1);
 #pragma unroll
-          for (int i = 0; i < V::N; ++i) acc[i] = __builtin_fmaf(wj[u], f[i], acc[i]);
+          for (int i = 0; i < V::N; ++i) {
+            acc0[i] = __builtin_fmaf(wj[u], f0[i], acc0[i]);
+            acc1[i] = __builtin_fmaf(wj[u], f1[i], acc1[i]);
+          }
         }
       }
     }
-    st16(dst + v * 16, V::pack(acc));
+    st16(dst + v0 * 16, V::pack(acc0));
+    if (has1) st16(dst + v1 * 16, V::pack(acc1));
   }
 }
 
-// dy_perm[p] = w[a] * dy[a / k] (pad rows 0) and
-// d_weights[a] = <dy[a / k], y_perm[p]> for the entry a on real row p.
+// Waves [0, ntok * k): entry a = t*k + j on padded row p gets
+// dy_perm[p] = w[a] * dy[t] and d_weights[a] = <dy[t], y_perm[p]>.  The waves
+// run in entry order, so the k waves of a token run side by side and read
+// dy[t] from HBM once.  Waves [ntok * k, ntok * k + 127 E): zero the pad rows
+// of dy_perm.
 template <typename T>
 __global__ void __launch_bounds__(kRowsPerBlock * kWave)
 scatter_backward_kernel(const T* __restrict__ dy, const T* __restrict__ y_perm,
-                        const float* __restrict__ weights, int64_t H, int k,
-                        const int32_t* __restrict__ tile_expert,
+                        const float* __restrict__ weights, int64_t nent, int64_t H, int k,
+                        int E, const int32_t* __restrict__ row_of_entry,
                         const int32_t* __restrict__ tpe,
-                        const int32_t* __restrict__ bins,
                         const int32_t* __restrict__ padded_bins,
-                        const int32_t* __restrict__ indices,
-                        const int32_t* __restrict__ num_padded_rows,
                         T* __restrict__ dy_perm, float* __restrict__ d_weights) {
   using V = Vec16<T>;
   const int lane = threadIdx.x % kWave;
-  const int64_t p = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
-  if (p >= *num_padded_rows) return;
-  const int a = source_entry(p, tile_expert, tpe, bins, padded_bins, indices);
+  const int64_t a = wave_index();
   const int64_t vecs = H * (int64_t)sizeof(T) / 16;
-  char* dst = reinterpret_cast<char*>(dy_perm + p * H);
-  if (a < 0) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int64_t v = lane; v < vecs; v += kWave) st16(dst + v * 16, z);
+  const int64_t rowb = H * (int64_t)sizeof(T);
+  char* out = reinterpret_cast<char*>(dy_perm);
+  if (a >= nent) {
+    if (a - nent >= (int64_t)E * kPadWaves) return;
+    const int64_t p = pad_row(a - nent, tpe, padded_bins);
+    if (p >= 0) zero_row(out + p * rowb, vecs, lane);
     return;
   }
-  const char* g = reinterpret_cast<const char*>(dy + (int64_t)(a / k) * H);
-  const char* yp = reinterpret_cast<const char*>(y_perm + p * H);
+  const int row = row_of_entry[a];
+  if (row < 0) return;           // an invalid expert id: no row
+  const char* g = reinterpret_cast<const char*>(dy) + (a / k) * rowb;
+  const char* yp = reinterpret_cast<const char*>(y_perm) + (int64_t)row * rowb;
+  char* dst = out + (int64_t)row * rowb;
   const float wt = weights[a];
   float dot = 0.f;
+#pragma unroll 4
   for (int64_t v = lane; v < vecs; v += kWave) {
     float gf[V::N], yf[V::N], o[V::N];
     V::unpack(ld16(g + v * 16), gf);
@@ -166,19 +196,22 @@ static unsigned blocks_for(int64_t rows) {
   return (unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock);
 }
 
+// Waves for the tokens plus 127 per expert for the pad rows.
+static unsigned permute_blocks(const Shape& s) {
+  return blocks_for(s.T + (int64_t)s.E * kPadWaves);
+}
+
 hipError_t launch_padded_gather(const Shape& s, const void* x, const MetaPtrs& m,
                                 void* x_perm, hipStream_t stream) {
-  const dim3 grid(blocks_for(s.max_tiles * kBlock)), block(kRowsPerBlock * kWave);
+  const dim3 grid(permute_blocks(s)), block(kRowsPerBlock * kWave);
   if (s.bf16)
     hipLaunchKernelGGL(padded_gather_kernel<bf16>, grid, block, 0, stream,
-                       static_cast<const bf16*>(x), s.H, s.k, m.tile_expert,
-                       m.tokens_per_expert, m.bins, m.padded_bins, m.indices,
-                       m.num_padded_rows, static_cast<bf16*>(x_perm));
+                       static_cast<const bf16*>(x), s.T, s.H, s.k, s.E, m.row_of_entry,
+                       m.tokens_per_expert, m.padded_bins, static_cast<bf16*>(x_perm));
   else
     hipLaunchKernelGGL(padded_gather_kernel<float>, grid, block, 0, stream,
-                       static_cast<const float*>(x), s.H, s.k, m.tile_expert,
-                       m.tokens_per_expert, m.bins, m.padded_bins, m.indices,
-                       m.num_padded_rows, static_cast<float*>(x_perm));
+                       static_cast<const float*>(x), s.T, s.H, s.k, s.E, m.row_of_entry,
+                       m.tokens_per_expert, m.padded_bins, static_cast<float*>(x_perm));
   return hipGetLastError();
 }
 
@@ -201,19 +234,17 @@ hipError_t launch_scatter_backward(const Shape& s, const void* dy,
                                    const void* y_perm, const float* weights,
                                    const MetaPtrs& m, void* dy_perm,
                                    float* d_weights, hipStream_t stream) {
-  const dim3 grid(blocks_for(s.max_tiles * kBlock)), block(kRowsPerBlock * kWave);
+  const dim3 grid(blocks_for(s.T * s.k + (int64_t)s.E * kPadWaves)), block(kRowsPerBlock * kWave);
   if (s.bf16)
     hipLaunchKernelGGL(scatter_backward_kernel<bf16>, grid, block, 0, stream,
                        static_cast<const bf16*>(dy), static_cast<const bf16*>(y_perm),
-                       weights, s.H, s.k, m.tile_expert, m.tokens_per_expert,
-                       m.bins, m.padded_bins, m.indices, m.num_padded_rows,
-                       static_cast<bf16*>(dy_perm), d_weights);
+                       weights, s.T * s.k, s.H, s.k, s.E, m.row_of_entry, m.tokens_per_expert,
+                       m.padded_bins, static_cast<bf16*>(dy_perm), d_weights);
   else
     hipLaunchKernelGGL(scatter_backward_kernel<float>, grid, block, 0, stream,
                        static_cast<const float*>(dy), static_cast<const float*>(y_perm),
-                       weights, s.H, s.k, m.tile_expert, m.tokens_per_expert,
-                       m.bins, m.padded_bins, m.indices, m.num_padded_rows,
-                       static_cast<float*>(dy_perm), d_weights);
+                       weights, s.T * s.k, s.H, s.k, s.E, m.row_of_entry, m.tokens_per_expert,
+                       m.padded_bins, static_cast<float*>(dy_perm), d_weights);
   return hipGetLastError();
 }
 

@@ -191,8 +191,8 @@ int dmoe_padded_scatter(const dmoe_dims* dims, const void* src_perm,
  *   forward  (n = 4): padded_gather, up projection + SiLU gate, down
  *                     projection, padded_scatter.
  *   backward (n = 6): scatter backward (dy_perm, d_weights), down dgrad +
- *                     gate backward, dw2, up dgrad (dx_perm), dw1 + dw3,
- *                     gather backward (dx).
+ *                     gate backward, dw2, up dgrad (dx_perm), gather
+ *                     backward (dx), dw1 + dw3.
  * Results are identical to the untimed calls. */
 int dmoe_metadata_timed(const dmoe_dims* dims, const int32_t* top_experts,
                         const dmoe_meta* meta, void* ws, hipStream_t stream,
