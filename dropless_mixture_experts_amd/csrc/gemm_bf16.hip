@@ -317,7 +317,7 @@ struct Job {
   int64_t u, v;     // tile coordinates
 };
 
-constexpr int kGroupM = 4;
+constexpr int kGroupM = 8;
 
 // Row-tiled products: (m, n) for logical index L over MT x NT tiles, in
 // groups of kGroupM row tiles walked column by column, so that concurrent
@@ -346,6 +346,12 @@ struct RowTiles {
     NT = nt;
   }
   __device__ __forceinline__ int total() const { return pairs * NT; }
+  // every tile has the same K: equal shares
+  __device__ __forceinline__ void xcd_range(int x, int& lo, int& hi) const {
+    const int per = (total() + 7) / 8;
+    lo = min(total(), x * per);
+    hi = min(total(), lo + per);
+  }
   __device__ __forceinline__ void get(int L, Job& j) const {
     int s, n;
     group_mn(L, pairs, NT, s, n);
@@ -376,7 +382,7 @@ struct Up {
   RowTiles rt;
   __device__ uint32_t lda() const { return (uint32_t)(F * 2); }
   __device__ uint32_t ldb() const { return (uint32_t)(H * 2); }
-  __device__ int total() const { return rt.total(); }
+  __device__ void xcd_range(int x, int& lo, int& hi) const { rt.xcd_range(x, lo, hi); }
   __device__ void tile(int L, Job& j) const {
     rt.get(L, j);
     j.fa = true;
@@ -417,7 +423,7 @@ struct Down {
   RowTiles rt;
   __device__ uint32_t lda() const { return (uint32_t)(H * 2); }
   __device__ uint32_t ldb() const { return (uint32_t)(F * 2); }
-  __device__ int total() const { return rt.total(); }
+  __device__ void xcd_range(int x, int& lo, int& hi) const { rt.xcd_range(x, lo, hi); }
   __device__ void tile(int L, Job& j) const {
     rt.get(L, j);
     j.fa = j.v * 256 + 256 <= H;
@@ -452,7 +458,7 @@ struct DownDgrad {
   RowTiles rt;
   __device__ uint32_t lda() const { return (uint32_t)(H * 2); }
   __device__ uint32_t ldb() const { return (uint32_t)(H * 2); }
-  __device__ int total() const { return rt.total(); }
+  __device__ void xcd_range(int x, int& lo, int& hi) const { rt.xcd_range(x, lo, hi); }
   __device__ void tile(int L, Job& j) const {
     rt.get(L, j);
     j.fa = j.v * 256 + 256 <= F;
@@ -531,7 +537,7 @@ struct UpDgrad {
   RowTiles rt;
   __device__ uint32_t lda() const { return (uint32_t)(F * 2); }
   __device__ uint32_t ldb() const { return (uint32_t)(F * 2); }
-  __device__ int total() const { return rt.total(); }
+  __device__ void xcd_range(int x, int& lo, int& hi) const { rt.xcd_range(x, lo, hi); }
   __device__ void tile(int L, Job& j) const {
     rt.get(L, j);
     j.fa = j.v * 256 + 256 <= H;
@@ -556,6 +562,33 @@ struct UpDgrad {
   }
 };
 
+// Weight-gradient tiles have K = the expert's padded rows, so equal tile
+// counts are not equal work under skewed routing.  Expert e goes to the XCD
+// holding the middle of its padded rows, min(7, 8 (start_e + n_e / 2) / P),
+// which gives each XCD about P / 8 rows and keeps every expert within one
+// L2; XCD x gets the experts [first(x), first(x + 1)).  One wave evaluates
+// all experts (E <= 256) with four loads per lane and counts with ballots.
+__device__ __forceinline__ int first_expert_of_xcd(int x, int E, const int32_t* tpe,
+                                                   const int32_t* padded_bins) {
+  if (x <= 0) return 0;
+  if (x >= 8) return E;
+  const int lane = threadIdx.x & 63;
+  const int64_t P = padded_bins[E - 1];
+  int count = 0;
+#pragma unroll
+  for (int q = 0; q < kMaxExperts / kWave; ++q) {
+    const int e = q * kWave + lane;
+    bool before = false;
+    if (e < E && P > 0) {
+      const int64_t n = round_up_block(tpe[e]);
+      const int64_t start = padded_bins[e] - n;
+      before = min<int64_t>(7, 8 * (start + n / 2) / P) < x;
+    }
+    count += __builtin_popcountll(__ballot(before));
+  }
+  return count;
+}
+
 // dw2[e] = act[rows_e]^T dy_perm[rows_e] ([F,H]); zero for an empty expert.
 // A = 256 (or 128) hidden columns of dy_perm (u = h0), B = 256 (or 128) ffn
 // columns of act (v = f0), K = the expert's padded rows.
@@ -572,7 +605,10 @@ struct WgradDown {
   __device__ uint32_t ldb() const { return (uint32_t)(F * 2); }
   __device__ int nh() const { return (int)((H + 255) / 256); }
   __device__ int nf() const { return (int)((F + 255) / 256); }
-  __device__ int total() const { return E * nh() * nf(); }
+  __device__ void xcd_range(int x, int& lo, int& hi) const {
+    lo = first_expert_of_xcd(x, E, tpe, padded_bins) * nh() * nf();
+    hi = first_expert_of_xcd(x + 1, E, tpe, padded_bins) * nh() * nf();
+  }
   __device__ void tile(int L, Job& j) const {
     // the tiles of one expert are consecutive: each XCD works on whole experts
     const int NH = nh(), NF = nf();
@@ -622,7 +658,10 @@ struct WgradUp {
   __device__ uint32_t ldb() const { return (uint32_t)(H * 2); }
   __device__ int nf() const { return (int)(F / 128); }
   __device__ int nh() const { return (int)((H + 255) / 256); }
-  __device__ int total() const { return E * nf() * nh(); }
+  __device__ void xcd_range(int x, int& lo, int& hi) const {
+    lo = first_expert_of_xcd(x, E, tpe, padded_bins) * nf() * nh();
+    hi = first_expert_of_xcd(x + 1, E, tpe, padded_bins) * nf() * nh();
+  }
   __device__ void tile(int L, Job& j) const {
     const int NF = nf(), NH = nh();
     const int e = L / (NF * NH);
@@ -736,18 +775,19 @@ struct Pipe {
   }
 };
 
-// One block per CU.  XCD x = blockIdx % 8 owns the logical tiles
-// [x*per, (x+1)*per); its S blocks take them round-robin, so at any time they
-// work on S consecutive tiles.  Every branch that reaches a barrier is
+// One block per CU.  XCD x = blockIdx % 8 owns the logical tiles [lo, hi)
+// that the product assigns it; its S blocks take them round-robin, so at any
+// time they work on S consecutive tiles.  Every branch that reaches a barrier is
 // uniform over the block.
 template <class K>
 __device__ __forceinline__ void persistent(const K& k) {
   __shared__ __attribute__((aligned(16))) char lds[kLds];
-  const int total = k.total();
   const int S = (int)(gridDim.x / 8);
   const int x = (int)(blockIdx.x % 8), r = (int)(blockIdx.x / 8);
-  const int per = (total + 7) / 8;
-  const int lo = x * per, hi = min(total, lo + per);
+  int lo, hi;
+  k.xcd_range(x, lo, hi);
+  lo = (int)uniform((uint32_t)lo);
+  hi = (int)uniform((uint32_t)hi);
   int L = lo + r;
   if (L >= hi) return;
   Pipe<K> p{k, lds, uniform(lds_addr(lds)), 0};
