@@ -24,8 +24,8 @@ struct Shape {
 };
 
 // meta.hip
-int64_t meta_chunk(int64_t n);
-int meta_nchunks(int64_t n);
+int64_t meta_chunk(int64_t n, int E);
+int meta_nchunks(int64_t n, int E);
 int64_t meta_workspace_bytes(int64_t n, int E);
 hipError_t launch_metadata(int64_t n, int E, int64_t max_tiles,
                            const int32_t* ids, const MetaPtrs& m, void* ws,

@@ -22,6 +22,9 @@
 //               bits of the id + mbcnt), then writes indices, bin_ids and
 //               row_of_entry.  Ties keep ascending entry order, so the
 //               result is unique and bit-identical on every run.
+#include <algorithm>
+#include <cmath>
+
 #include "dmoe_device.h"
 #include "dmoe_internal.h"
 
@@ -236,25 +239,42 @@ meta_place_kernel(const int32_t* __restrict__ ids, int64_t n, int64_t chunk,
   }
 }
 
-int64_t meta_chunk(int64_t n) {
-  // >= 1024 entries per wave, and at most 4096 chunks.
-  int64_t c = (n + 4095) / 4096;
-  c = ((c + kWave - 1) / kWave) * kWave;
-  return c < 1024 ? 1024 : c;
+static int expert_cap(int E) {
+  int Ecap = 1;
+  while (Ecap < E) Ecap <<= 1;
+  return Ecap;
 }
 
-int meta_nchunks(int64_t n) { return (int)((n + meta_chunk(n) - 1) / meta_chunk(n)); }
+int64_t meta_chunk(int64_t n, int E) {
+  // A multiple of 64 entries per wave.  meta_hist and meta_place walk a chunk
+  // per wave (n / chunks entries, 64 at a time); each thread of meta_scan
+  // walks chunks / S chunks of one expert (S = 1024 / Ecap threads per
+  // expert).  About sqrt(n S / 16) chunks balances the two, counting a
+  // 64-entry step of the placement as 4 scan loads; at most 4096 chunks.
+  const double S = (double)(kScanThreads / expert_cap(E));
+  const int64_t target =
+      std::max<int64_t>(1, std::min<int64_t>(4096, (int64_t)std::sqrt((double)n * S / 16.0)));
+  int64_t c = (n + target - 1) / target;
+  c = ((c + kWave - 1) / kWave) * kWave;
+  c = std::max<int64_t>(c, kWave);
+  while ((n + c - 1) / c > 4096) c += kWave;
+  return c;
+}
+
+int meta_nchunks(int64_t n, int E) {
+  return (int)((n + meta_chunk(n, E) - 1) / meta_chunk(n, E));
+}
 
 int64_t meta_workspace_bytes(int64_t n, int E) {
-  const int64_t nc = meta_nchunks(n);
+  const int64_t nc = meta_nchunks(n, E);
   return ((nc * E + nc) * (int64_t)sizeof(int32_t) + 255) / 256 * 256;
 }
 
 hipError_t launch_metadata(int64_t n, int E, int64_t max_tiles,
                            const int32_t* ids, const MetaPtrs& m, void* ws,
                            hipStream_t stream, hipEvent_t* ev) {
-  const int64_t chunk = meta_chunk(n);
-  const int nchunks = meta_nchunks(n);
+  const int64_t chunk = meta_chunk(n, E);
+  const int nchunks = meta_nchunks(n, E);
   int32_t* hist = static_cast<int32_t*>(ws);
   int32_t* err = hist + (int64_t)nchunks * E;
   int Ecap = 1;
