@@ -263,42 +263,83 @@ __device__ __forceinline__ u32x2 pack4(const f32x4& v) {
   return u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
 }
 
-// Stores per stage_out call and wave.
-constexpr int kStoresPerBlock = 8;
+// Stores per wave of one stage_pass call and of one stage_out call.
+constexpr int kStoresPerPass = 4;
+constexpr int kStoresPerBlock = 2 * kStoresPerPass;
 
-// out: element (B row 0, A row 0) of this wave's block; ldo: elements between
-// B rows.  val(ii, j, g): the 4 values (bf16, packed) of A block ii (0/1 in
-// the half), B block j, quad g, in accumulator layout.  st: the wave's
-// staging space.
-template <class Val>
-__device__ __forceinline__ int stage_out(char* st, bf16* out, int64_t ldo, int lane_in,
-                                         Val&& val) {
-  // The lane index through an opaque move: the addresses below depend on the
-  // lane only, and would otherwise be hoisted out of the tile loop and kept
-  // in registers across the whole K loop.
+// The lane index through an opaque move: the addresses of the staging code
+// depend on the lane only, and would otherwise be hoisted out of the tile
+// loop and kept in registers across the whole K loop.
+__device__ __forceinline__ int opaque_lane(int lane_in) {
   int lane;
   asm volatile("v_mov_b32 %0, %1" : "=v"(lane) : "v"(lane_in));
+  return lane;
+}
+
+// Byte offset in a 32-row staging region of the 4 values (8 bytes) that lane
+// `lane` holds in accumulator layout for A block ii, quad g.
+__device__ __forceinline__ int acc_slot(int lane, int ii, int g) {
+  const int r = lane & 31;
+  const int col = ii * 32 + 8 * g + 4 * (lane >> 5);
+  return r * 128 + (((col >> 3) ^ ((r >> 1) & 7)) << 4) + ((col >> 2) & 1) * 8;
+}
+
+// B rows [32 j, 32 j + 32) of the wave's block.  out: element (B row 0, A row
+// 0) of the block; ldo: elements between B rows.  val(ii, g): the 4 values
+// (bf16, packed) of A block ii (0/1 in the half), B block j, quad g, in
+// accumulator layout.  st: the wave's staging space.
+template <class Val>
+__device__ __forceinline__ int stage_pass(char* st, bf16* out, int64_t ldo, int lane_in, int j,
+                                          Val&& val) {
+  const int lane = opaque_lane(lane_in);
+  wait_lds();   // the reads of the previous rows are done
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    wait_lds();   // the reads of the previous rows are done
+  for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-    for (int ii = 0; ii < 2; ++ii)
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<u32x2*>(st + acc_slot(lane, ii, g)) = val(ii, g);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int r = lane & 31;
-        const int col = ii * 32 + 8 * g + 4 * (lane >> 5);
-        char* p = st + r * 128 + (((col >> 3) ^ ((r >> 1) & 7)) << 4) + ((col >> 2) & 1) * 8;
-        *reinterpret_cast<u32x2*>(p) = val(ii, j, g);
-      }
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int r = it * 8 + (lane >> 3), c = lane & 7;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(st + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
-      *reinterpret_cast<u32x4*>(out + (int64_t)(j * 32 + r) * ldo + c * 8) = v;
-    }
+  for (int it = 0; it < 4; ++it) {
+    const int r = it * 8 + (lane >> 3), c = lane & 7;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(st + r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+    *reinterpret_cast<u32x4*>(out + (int64_t)(j * 32 + r) * ldo + c * 8) = v;
   }
+  return kStoresPerPass;
+}
+// The whole block: val(ii, j, g).
+template <class Val>
+__device__ __forceinline__ int stage_out(char* st, bf16* out, int64_t ldo, int lane, Val&& val) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    stage_pass(st, out, ldo, lane, j, [&](int ii, int g) { return val(ii, j, g); });
   return kStoresPerBlock;
 }
+
+// 32 rows x 64 elements (128 bytes each, `ld` bytes apart, from `src`) into a
+// 4 KB LDS region at `lds` by DMA, in the swizzled layout of the staging
+// space: LDS row r holds source row r with its chunk c at c ^ ((r >> 1) & 7).
+__device__ __forceinline__ void dma_rows(const char* src, uint32_t ld, uint32_t lds, int lane) {
+  const rsrc_t rs = make_rsrc(src);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = i * 8 + (lane >> 3), pc = lane & 7;
+    const int c = pc ^ ((r >> 1) & 7);
+    dma16(rs, lds + i * 1024, (uint32_t)r * ld + (uint32_t)c * 16u, 0);
+  }
+}
+
+// LDS space of one wave for its epilogue: `stg` is its own 4 KB; `a` and `b`
+// (LDS addresses `a_addr`, `b_addr`) are the 4 KB blocks its DMA fills in the
+// stage the last K step used -- free until step 1 of the next tile is
+// started, which happens after the epilogue only for products with
+// kLateStep1.
+struct Epi {
+  char* stg;
+  const char* a;
+  const char* b;
+  uint32_t a_addr, b_addr;
+};
+
 // The common case: A half h of the accumulators, stored as they are.
 __device__ __forceinline__ int stage_half(char* st, const Acc& acc, int h, bf16* out,
                                           int64_t ldo, int lane) {
@@ -373,8 +414,8 @@ struct RowTiles {
 // row blocks and 128 ffn columns (w1 columns in A rows 0..127, the same w3
 // columns in A rows 128..255, so A blocks i and i+2 pair up).
 struct Up {
-  // step 1 of the next tile is issued after the epilogue (which loads)
   static constexpr bool kLateStep1 = false;
+  static constexpr bool kUsesFreeStage = false;
   static constexpr bool ATR = true, BTR = false;
   const bf16 *x_perm, *w1, *w3;
   int64_t H, F;
@@ -396,13 +437,13 @@ struct Up {
     b0 = (const char*)(x_perm + j.u * kBlock * H);
     b1 = j.fb ? b0 + kBlock * H * 2 : b0;
   }
-  __device__ int epilogue(const Job& j, const Acc& acc, char* st) const {
+  __device__ int epilogue(const Job& j, const Acc& acc, const Epi& ep) const {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
     if (!j.fb && wn >= 2) return 0;
     const int64_t o = j.u * kBlock * F + j.v * 128 + (int64_t)(wn * 64) * F + wm * 64;
-    stage_half(st, acc, 0, h1 + o, F, lane);
-    stage_half(st, acc, 1, h3 + o, F, lane);
-    return 2 * kStoresPerBlock + stage_out(st, act + o, F, lane, [&](int ii, int jj, int g) {
+    stage_half(ep.stg, acc, 0, h1 + o, F, lane);
+    stage_half(ep.stg, acc, 1, h3 + o, F, lane);
+    return 2 * kStoresPerBlock + stage_out(ep.stg, act + o, F, lane, [&](int ii, int jj, int g) {
       const f32x4 v1 = quad(acc[ii][jj], g), v3 = quad(acc[2 + ii][jj], g);
       f32x4 a;
 #pragma unroll
@@ -414,8 +455,8 @@ struct Up {
 
 // y_perm = act w2[e] for one pair of row blocks and 256 (or 128) hidden columns.
 struct Down {
-  // step 1 of the next tile is issued after the epilogue (which loads)
   static constexpr bool kLateStep1 = false;
+  static constexpr bool kUsesFreeStage = false;
   static constexpr bool ATR = true, BTR = false;
   const bf16 *act, *w2;
   int64_t H, F;
@@ -436,12 +477,12 @@ struct Down {
     b0 = (const char*)(act + j.u * kBlock * F);
     b1 = j.fb ? b0 + kBlock * F * 2 : b0;
   }
-  __device__ int epilogue(const Job& j, const Acc& acc, char* st) const {
+  __device__ int epilogue(const Job& j, const Acc& acc, const Epi& ep) const {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
     if (!j.fb && wn >= 2) return 0;
     bf16* out = y_perm + j.u * kBlock * H + j.v * 256 + (int64_t)(wn * 64) * H + wm * 64;
-    int n = stage_half(st, acc, 0, out, H, lane);
-    if (j.fa) n += stage_half(st, acc, 1, out + 128, H, lane);
+    int n = stage_half(ep.stg, acc, 0, out, H, lane);
+    if (j.fa) n += stage_half(ep.stg, acc, 1, out + 128, H, lane);
     return n;
   }
 };
@@ -449,8 +490,10 @@ struct Down {
 // dA = dy_perm w2[e]^T, then the gate's backward:
 // dh3 = dA * silu(h1), dh1 = dA * h3 * s * (1 + h1 (1 - s)), s = sigmoid(h1).
 struct DownDgrad {
-  // step 1 of the next tile is issued after the epilogue (which loads)
+  // step 1 of the next tile is issued after the epilogue, which uses the
+  // free stage to bring in h1 and h3
   static constexpr bool kLateStep1 = true;
+  static constexpr bool kUsesFreeStage = true;
   static constexpr bool ATR = false, BTR = false;
   const bf16 *dy_perm, *w2, *h1, *h3;
   int64_t H, F;
@@ -471,56 +514,65 @@ struct DownDgrad {
     b0 = (const char*)(dy_perm + j.u * kBlock * H);
     b1 = j.fb ? b0 + kBlock * H * 2 : b0;
   }
-  __device__ int epilogue(const Job& j, const Acc& acc, char* st) const {
+  __device__ int epilogue(const Job& j, const Acc& acc, const Epi& ep) const {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
     if (!j.fb && wn >= 2) return 0;
     const int64_t base = j.u * kBlock * F + j.v * 256;
     const int64_t wo = base + (int64_t)(wn * 64) * F + wm * 64;
-    // h1/h3 of one A half of this lane's outputs are loaded before any of them
-    // is stored, so the loads overlap (dh1/dh3 may alias h1/h3, which keeps the
-    // compiler from hoisting a load above an earlier store; each element is
-    // read before the block that overwrites it is stored).
+    // h1 and h3 come in 32-row passes (two per A half) by DMA into the two
+    // free 4 KB blocks of this wave, in the staging layout, and are read back
+    // in accumulator layout; the DMA of the next pass is in flight while one
+    // is computed and stored.  dh1/dh3 may alias h1/h3: every element is read
+    // before the pass that overwrites it is stored, and passes are disjoint.
+    const int npass = j.fa ? 4 : 2;
+    const uint32_t ld = (uint32_t)(F * 2);
+    const auto src = [&](const bf16* t, int q) {
+      return reinterpret_cast<const char*>(t + wo + (q >> 1) * 128 + (int64_t)((q & 1) * 32) * F);
+    };
+    dma_rows(src(h1, 0), ld, ep.a_addr, lane);
+    dma_rows(src(h3, 0), ld, ep.b_addr, lane);
     int n = 0;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      if (!j.fa && h == 1) break;
-      u32x2 g1[2][2][4], g3[2][2][4];
+    for (int q = 0; q < 4; ++q) {
+      if (q >= npass) break;
+      const int h = q >> 1, jr = q & 1;
+      // pass q landed (younger: the stores of pass q - 1)
+      if (q == 0) wait_vm<0>(); else wait_vm<2 * kStoresPerPass>();
+      u32x2 g1[2][4], g3[2][4];
 #pragma unroll
       for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int64_t o = base + (int64_t)(b_row(jj, wn) + (lane & 31)) * F +
-                              a_row(2 * h + ii, wm) + 8 * g + 4 * (lane >> 5);
-            g1[ii][jj][g] = *reinterpret_cast<const u32x2*>(h1 + o);
-            g3[ii][jj][g] = *reinterpret_cast<const u32x2*>(h3 + o);
-          }
-      // dh3 = dA * silu(h1), dh1 = dA * h3 * s * (1 + h1 (1 - s)), s = sigmoid(h1),
-      // rounded right away so that h1, h3 and this half's accumulators die
-      u32x2 d1[2][2][4], d3[2][2][4];
+        for (int g = 0; g < 4; ++g) {
+          g1[ii][g] = *reinterpret_cast<const u32x2*>(ep.a + acc_slot(lane, ii, g));
+          g3[ii][g] = *reinterpret_cast<const u32x2*>(ep.b + acc_slot(lane, ii, g));
+        }
+      wait_lds();
+      if (q + 1 < npass) {
+        dma_rows(src(h1, q + 1), ld, ep.a_addr, lane);
+        dma_rows(src(h3, q + 1), ld, ep.b_addr, lane);
+      }
+      // dh3 = dA * silu(h1), dh1 = dA * h3 * s * (1 + h1 (1 - s)), s = sigmoid(h1)
+      u32x2 d1[2][4], d3[2][4];
 #pragma unroll
       for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 da = quad(acc[2 * h + ii][jr], g), x1 = unpack4(g1[ii][g]),
+                      x3 = unpack4(g3[ii][g]);
+          f32x4 v1, v3;
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 da = quad(acc[2 * h + ii][jj], g), x1 = unpack4(g1[ii][jj][g]),
-                        x3 = unpack4(g3[ii][jj][g]);
-            f32x4 v1, v3;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float sg = 1.0f / (1.0f + __expf(-x1[r]));
-              v3[r] = da[r] * x1[r] * sg;
-              v1[r] = da[r] * x3[r] * sg * (1.0f + x1[r] * (1.0f - sg));
-            }
-            d1[ii][jj][g] = pack4(v1);
-            d3[ii][jj][g] = pack4(v3);
+          for (int r = 0; r < 4; ++r) {
+            const float sg = 1.0f / (1.0f + __expf(-x1[r]));
+            v3[r] = da[r] * x1[r] * sg;
+            v1[r] = da[r] * x3[r] * sg * (1.0f + x1[r] * (1.0f - sg));
           }
-      n += stage_out(st, dh1 + wo + h * 128, F, lane,
-                     [&](int ii, int jj, int g) { return d1[ii][jj][g]; });
-      n += stage_out(st, dh3 + wo + h * 128, F, lane,
-                     [&](int ii, int jj, int g) { return d3[ii][jj][g]; });
+          d1[ii][g] = pack4(v1);
+          d3[ii][g] = pack4(v3);
+        }
+      n += stage_pass(ep.stg, dh1 + wo + h * 128, F, lane, jr,
+                      [&](int ii, int g) { return d1[ii][g]; });
+      n += stage_pass(ep.stg, dh3 + wo + h * 128, F, lane, jr,
+                      [&](int ii, int g) { return d3[ii][g]; });
     }
     return n;
   }
@@ -528,8 +580,8 @@ struct DownDgrad {
 
 // dx_perm = dh1 w1[e]^T + dh3 w3[e]^T: two K segments into one accumulator.
 struct UpDgrad {
-  // step 1 of the next tile is issued after the epilogue (which loads)
   static constexpr bool kLateStep1 = false;
+  static constexpr bool kUsesFreeStage = false;
   static constexpr bool ATR = false, BTR = false;
   const bf16 *dh1, *dh3, *w1, *w3;
   int64_t H, F;
@@ -552,12 +604,12 @@ struct UpDgrad {
     b0 = (const char*)((seg ? dh3 : dh1) + j.u * kBlock * F);
     b1 = j.fb ? b0 + kBlock * F * 2 : b0;
   }
-  __device__ int epilogue(const Job& j, const Acc& acc, char* st) const {
+  __device__ int epilogue(const Job& j, const Acc& acc, const Epi& ep) const {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
     if (!j.fb && wn >= 2) return 0;
     bf16* out = dx_perm + j.u * kBlock * H + j.v * 256 + (int64_t)(wn * 64) * H + wm * 64;
-    int n = stage_half(st, acc, 0, out, H, lane);
-    if (j.fa) n += stage_half(st, acc, 1, out + 128, H, lane);
+    int n = stage_half(ep.stg, acc, 0, out, H, lane);
+    if (j.fa) n += stage_half(ep.stg, acc, 1, out + 128, H, lane);
     return n;
   }
 };
@@ -593,8 +645,8 @@ __device__ __forceinline__ int first_expert_of_xcd(int x, int E, const int32_t* 
 // A = 256 (or 128) hidden columns of dy_perm (u = h0), B = 256 (or 128) ffn
 // columns of act (v = f0), K = the expert's padded rows.
 struct WgradDown {
-  // step 1 of the next tile is issued after the epilogue (which loads)
   static constexpr bool kLateStep1 = false;
+  static constexpr bool kUsesFreeStage = false;
   static constexpr bool ATR = true, BTR = true;
   const bf16 *act, *dy_perm;
   int64_t H, F;
@@ -630,13 +682,13 @@ struct WgradDown {
     b0 = (const char*)(act + start * F + j.v);
     b1 = j.fb ? b0 + 128 * 2 : b0;
   }
-  __device__ int epilogue(const Job& j, const Acc& acc, char* st) const {
+  __device__ int epilogue(const Job& j, const Acc& acc, const Epi& ep) const {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
     if (!j.fb && wn >= 2) return 0;
     bf16* out = dw2 + (int64_t)(j.e & 255) * F * H + j.v * H + j.u + (int64_t)(wn * 64) * H +
                 wm * 64;
-    int n = stage_half(st, acc, 0, out, H, lane);
-    if (j.fa) n += stage_half(st, acc, 1, out + 128, H, lane);
+    int n = stage_half(ep.stg, acc, 0, out, H, lane);
+    if (j.fa) n += stage_half(ep.stg, acc, 1, out + 128, H, lane);
     return n;
   }
 };
@@ -646,8 +698,8 @@ struct WgradDown {
 // columns of dh3 (rows 128..255) (u = f0), B = 256 (or 128) hidden columns
 // of x_perm (v = h0).
 struct WgradUp {
-  // step 1 of the next tile is issued after the epilogue (which loads)
   static constexpr bool kLateStep1 = false;
+  static constexpr bool kUsesFreeStage = false;
   static constexpr bool ATR = true, BTR = true;
   const bf16 *x_perm, *dh1, *dh3;
   int64_t H, F;
@@ -682,13 +734,13 @@ struct WgradUp {
     b0 = (const char*)(x_perm + start * H + j.v);
     b1 = j.fb ? b0 + 128 * 2 : b0;
   }
-  __device__ int epilogue(const Job& j, const Acc& acc, char* st) const {
+  __device__ int epilogue(const Job& j, const Acc& acc, const Epi& ep) const {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
     if (!j.fb && wn >= 2) return 0;
     // A rows 0..127 are dw1 columns, 128..255 the same dw3 columns
     const int64_t o = (int64_t)(j.e & 255) * H * F + j.v * F + j.u + (int64_t)(wn * 64) * F +
                       wm * 64;
-    return stage_half(st, acc, 0, dw1 + o, F, lane) + stage_half(st, acc, 1, dw3 + o, F, lane);
+    return stage_half(ep.stg, acc, 0, dw1 + o, F, lane) + stage_half(ep.stg, acc, 1, dw3 + o, F, lane);
   }
 };
 
@@ -798,6 +850,7 @@ __device__ __forceinline__ void persistent(const K& k) {
   p.da.init(k.lda(), p.lane);
   p.db.init(k.ldb(), p.lane);
   char* const stg = lds + 2 * kStage + p.w * kStgWave;
+  static_assert(K::kLateStep1 || !K::kUsesFreeStage, "the free stage is refilled before the epilogue");
   Job cur;
   k.tile(L, cur);
   bool primed = false;
@@ -815,9 +868,14 @@ __device__ __forceinline__ void persistent(const K& k) {
     // epilogue loads, so that the stores can drain while the next tile runs
     const bool step1 = primed && nxt.steps > 1;
     if (!K::kLateStep1 && step1) p.issue_step(nxt, 1, p.g + 1);
-    const int nst = k.epilogue(cur, acc, stg);
+    const int fs = ((p.g + 1) & 1) * kStage + 4 * p.w * 1024;   // free stage, this wave's blocks
+    const int nst = k.epilogue(cur, acc, Epi{stg, lds + fs, lds + fs + kReg, p.lbase + fs,
+                                             p.lbase + fs + kReg});
     if (Ln >= hi) break;
-    if (K::kLateStep1 && step1) p.issue_step(nxt, 1, p.g + 1);
+    if (K::kLateStep1 && step1) {
+      wait_lds();   // this wave's reads of its free-stage blocks are done
+      p.issue_step(nxt, 1, p.g + 1);
+    }
     // in flight, oldest first: step 0, [step 1,] the stores [, step 1]
     w0 = (step1 ? kDmaPerStep : 0) + nst;
     w1 = K::kLateStep1 ? 0 : nst;
