@@ -7,3 +7,4 @@ check it.
 """
 from .dmoe import *  # noqa: F401,F403
 from .dmoe import __all__  # noqa: F401
+from . import router  # noqa: F401  (the router in front of the layer)
