@@ -112,6 +112,39 @@ def cpu_baseline(inp, budget_s=30.0):
                        f"host os.cpu_count()={os.cpu_count()}")}
 
 
+def router_time(dm, cfg, dev, stream, steps):
+    """Mean microseconds of the router's forward (top-k, softmax, z-loss) and
+    backward on this workload's seeded logits.  Reported beside the layer's
+    step, not part of it: the layer takes ids and weights as inputs."""
+    import torch
+    from workloads import make_logits
+    logits, d_weights = make_logits(cfg)
+    l = torch.from_numpy(logits).to(dev)
+    g = torch.from_numpy(d_weights).to(dev)
+    D = dm.Dims(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, dm.DMOE_F32)
+    ids = torch.empty(cfg.T, cfg.k, dtype=torch.int32, device=dev)
+    w = torch.empty(cfg.T, cfg.k, dtype=torch.float32, device=dev)
+    z = torch.empty(cfg.T, dtype=torch.float32, device=dev)
+    zl = torch.empty(1, dtype=torch.float32, device=dev)
+    dl = torch.empty(cfg.T, cfg.E, dtype=torch.float32, device=dev)
+
+    def once():
+        dm.dmoe_router_forward(D, l, ids, w, zloss_coef=0.001, z=z, zloss=zl, stream=stream)
+        dm.dmoe_router_backward(D, l, ids, w, g, dl, zloss_coef=0.001, stream=stream)
+
+    for _ in range(3):
+        once()
+    with torch.cuda.stream(stream):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            once()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return round(e0.elapsed_time(e1) * 1e3 / steps, 1)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -255,6 +288,7 @@ def main():
         "roofline": roof,
         "kernels": table,
     }
+    out["router_us"] = router_time(dm, cfg, dev, stream, K)
     if args.kernels:
         for n in names:
             print(f"{n:22s} {table[n]}", file=sys.stderr)

@@ -34,6 +34,7 @@ __all__ = [
     "Meta", "Saved", "GradScratch", "library_path", "load_library",
     "dmoe_max_tiles", "dmoe_workspace_bytes", "dmoe_metadata", "dmoe_forward",
     "dmoe_backward", "dmoe_padded_gather", "dmoe_padded_scatter",
+    "dmoe_router_forward", "dmoe_router_backward",
     "dmoe_status_string", "allocate", "allocate_meta", "DMoELayer",
     "dmoe_autograd",
 ]
@@ -123,6 +124,10 @@ def load_library() -> ctypes.CDLL:
                                         P(_Saved), P(_Scratch), vp, vp, vp, vp,
                                         vp, vp, vp]
     lib.dmoe_backward_timed.restype = ctypes.c_int
+    lib.dmoe_router_forward.argtypes = [P(_Dims), vp, ctypes.c_float, vp, vp, vp, vp, vp]
+    lib.dmoe_router_forward.restype = ctypes.c_int
+    lib.dmoe_router_backward.argtypes = [P(_Dims), vp, vp, vp, vp, ctypes.c_float, vp, vp]
+    lib.dmoe_router_backward.restype = ctypes.c_int
     lib.dmoe_status_string.argtypes = [ctypes.c_int]
     lib.dmoe_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -357,6 +362,45 @@ def dmoe_padded_scatter(dims: Dims, src_perm, weights, meta: Meta, out,
         ctypes.byref(dims._c()), _ptr(src_perm, dt, "src_perm"),
         _ptr(weights, torch.float32, "weights"), ctypes.byref(meta._c()),
         _ptr(out, dt, "out"), _stream(out, stream)), "dmoe_padded_scatter")
+
+
+def dmoe_router_forward(dims: Dims, logits, top_experts, weights, zloss_coef: float = 0.0,
+                        z=None, zloss=None, stream=None) -> None:
+    """Top-k + softmax over the chosen logits (+ z-loss); see include/dmoe.h.
+
+    logits [T,E] fp32; writes top_experts [T,k] int32 and weights [T,k] fp32,
+    and with zloss_coef != 0 also z [T] and zloss [1] (fp32)."""
+    lib = load_library()
+    _need(logits, "logits", dims.T * dims.E)
+    _need(top_experts, "top_experts", dims.T * dims.k)
+    _need(weights, "weights", dims.T * dims.k)
+    if zloss_coef != 0.0:
+        if z is None or zloss is None:
+            raise ValueError("zloss_coef != 0 needs z and zloss")
+        _need(z, "z", dims.T)
+        _need(zloss, "zloss", 1)
+    _check(lib.dmoe_router_forward(
+        ctypes.byref(dims._c()), _ptr(logits, torch.float32, "logits"),
+        ctypes.c_float(zloss_coef), _ptr(top_experts, torch.int32, "top_experts"),
+        _ptr(weights, torch.float32, "weights"), _ptr(z, torch.float32, "z"),
+        _ptr(zloss, torch.float32, "zloss"), _stream(logits, stream)),
+        "dmoe_router_forward")
+
+
+def dmoe_router_backward(dims: Dims, logits, top_experts, weights, d_weights, d_logits,
+                         zloss_coef: float = 0.0, stream=None) -> None:
+    """d_logits [T,E] fp32 from d_weights [T,k] (+ the z-loss's); see include/dmoe.h."""
+    lib = load_library()
+    _need(logits, "logits", dims.T * dims.E)
+    _need(d_logits, "d_logits", dims.T * dims.E)
+    for t, n in ((top_experts, "top_experts"), (weights, "weights"), (d_weights, "d_weights")):
+        _need(t, n, dims.T * dims.k)
+    _check(lib.dmoe_router_backward(
+        ctypes.byref(dims._c()), _ptr(logits, torch.float32, "logits"),
+        _ptr(top_experts, torch.int32, "top_experts"), _ptr(weights, torch.float32, "weights"),
+        _ptr(d_weights, torch.float32, "d_weights"), ctypes.c_float(zloss_coef),
+        _ptr(d_logits, torch.float32, "d_logits"), _stream(logits, stream)),
+        "dmoe_router_backward")
 
 
 # --------------------------------------------------------------------------

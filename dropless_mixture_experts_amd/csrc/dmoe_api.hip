@@ -211,6 +211,31 @@ int dmoe_padded_scatter(const dmoe_dims* dims, const void* src_perm,
   return DMOE_OK;
 }
 
+int dmoe_router_forward(const dmoe_dims* dims, const float* logits, float zloss_coef,
+                        int32_t* top_experts, float* weights, float* z, float* zloss,
+                        hipStream_t stream) {
+  const int rc = check_dims(dims);
+  if (rc != DMOE_OK) return rc;
+  if (!logits || !top_experts || !weights) return DMOE_ERR_ARG;
+  if (zloss_coef != 0.0f && (!z || !zloss)) return DMOE_ERR_ARG;
+  DMOE_TRY(dmoe::launch_router_forward(shape_of(dims), logits, zloss_coef, top_experts,
+                                       weights, zloss_coef != 0.0f ? z : nullptr, zloss,
+                                       stream));
+  return DMOE_OK;
+}
+
+int dmoe_router_backward(const dmoe_dims* dims, const float* logits,
+                         const int32_t* top_experts, const float* weights,
+                         const float* d_weights, float zloss_coef, float* d_logits,
+                         hipStream_t stream) {
+  const int rc = check_dims(dims);
+  if (rc != DMOE_OK) return rc;
+  if (!logits || !top_experts || !weights || !d_weights || !d_logits) return DMOE_ERR_ARG;
+  DMOE_TRY(dmoe::launch_router_backward(shape_of(dims), logits, top_experts, weights,
+                                        d_weights, zloss_coef, d_logits, stream));
+  return DMOE_OK;
+}
+
 const char* dmoe_status_string(int status) {
   switch (status) {
     case DMOE_OK: return "ok";

@@ -42,6 +42,14 @@ hipError_t launch_scatter_backward(const Shape& s, const void* dy,
                                    const MetaPtrs& m, void* dy_perm,
                                    float* d_weights, hipStream_t stream);
 
+// router.hip
+hipError_t launch_router_forward(const Shape& s, const float* logits, float coef,
+                                 int32_t* ids, float* weights, float* z, float* loss,
+                                 hipStream_t stream);
+hipError_t launch_router_backward(const Shape& s, const float* logits, const int32_t* ids,
+                                  const float* weights, const float* d_weights, float coef,
+                                  float* d_logits, hipStream_t stream);
+
 // gemm.hip
 hipError_t launch_gemm_up(const Shape& s, const void* x_perm, const void* w1,
                           const void* w3, const MetaPtrs& m, void* h1, void* h3,

@@ -183,6 +183,36 @@ int dmoe_padded_scatter(const dmoe_dims* dims, const void* src_perm,
                         const float* weights, const dmoe_meta* meta, void* out,
                         hipStream_t stream);
 
+/* The router in front of the layer (Fast-LLM issue "[feat] Support sparse
+ * copy for a large number of experts": each token goes to k of E experts,
+ * with an expert z-loss coefficient; "yikangshen/megablocks" README: the
+ * router z-loss of ST-MoE).
+ *   logits [T,E] fp32, finite (results are unspecified for NaN or inf).
+ *   top_experts [T,k] int32: the k largest logits of each token in
+ *     descending order, equal logits to the lower expert id (unique).
+ *   weights [T,k] fp32: the softmax over the k chosen logits.
+ *   zloss_coef: the z-loss weight; 0 skips it, and z and zloss may be NULL.
+ *   z [T] fp32: (log sum_e exp logits[t,e])^2 per token.
+ *   zloss [1] fp32: zloss_coef * mean_t z[t], summed in a fixed order.
+ * Only dims->T, E and k are used (H, F and dtype are checked as for the
+ * layer).  Returns a negative dmoe_status on bad arguments; nothing is
+ * enqueued then. */
+int dmoe_router_forward(const dmoe_dims* dims, const float* logits, float zloss_coef,
+                        int32_t* top_experts, float* weights, float* z, float* zloss,
+                        hipStream_t stream);
+
+/* Backward of dmoe_router_forward for upstream d_weights [T,k] fp32 (and
+ * unit weight on zloss): the selection carries no gradient, so
+ *   d_logits[t, top_experts[t,j]] = w_j (d_weights[t,j] - sum_i w_i d_weights[t,i])
+ * and 0 at the other experts, plus zloss_coef * 2 / T * lse_t *
+ * softmax(logits[t])_e at every expert when zloss_coef != 0.
+ * logits, top_experts and weights as produced by the forward; d_logits [T,E]
+ * fp32 is overwritten.  Ids outside [0, E) are ignored. */
+int dmoe_router_backward(const dmoe_dims* dims, const float* logits,
+                         const int32_t* top_experts, const float* weights,
+                         const float* d_weights, float zloss_coef, float* d_logits,
+                         hipStream_t stream);
+
 /* The same three calls with per-kernel timing.  `events` is NULL or an array
  * of n+1 caller-created hipEvent_t; event i is recorded on `stream` just
  * before kernel i and event n after the last kernel, so the elapsed time

@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("dmoe_metadata", "dmoe_forward", "dmoe_backward", "dmoe_max_tiles",
               "dmoe_workspace_bytes", "dmoe_padded_gather", "dmoe_padded_scatter",
-              "dmoe_status_string"):
+              "dmoe_status_string", "dmoe_router_forward", "dmoe_router_backward"):
         assert n in names
 
 
@@ -94,6 +94,29 @@ def test_null_pointers_rejected_before_launch(lib):
                                    None, None) == -1
     assert lib.dmoe_forward(None, p, p, p, p, p, ctypes.byref(meta),
                             ctypes.byref(saved), p, None) == -1
+
+
+def test_router_checks_before_launch(lib):
+    p = ctypes.c_void_p(0x1000)
+    d = _dims()
+    c0, c1 = ctypes.c_float(0.0), ctypes.c_float(0.001)
+    fwd, bwd = lib.dmoe_router_forward, lib.dmoe_router_backward
+    assert fwd(ctypes.byref(d), None, c0, p, p, None, None, None) == -1
+    assert fwd(ctypes.byref(d), p, c0, None, p, None, None, None) == -1
+    assert fwd(ctypes.byref(d), p, c0, p, None, None, None, None) == -1
+    # a z-loss needs both z and the scalar
+    assert fwd(ctypes.byref(d), p, c1, p, p, None, p, None) == -1
+    assert fwd(ctypes.byref(d), p, c1, p, p, p, None, None) == -1
+    assert fwd(None, p, c0, p, p, None, None, None) == -1
+    for i in range(5):
+        args = [p] * 5
+        args[i] = None
+        assert bwd(ctypes.byref(d), args[0], args[1], args[2], args[3], c0, args[4],
+                   None) == -1
+    for kw, code in ((dict(k=9, E=8), -1), (dict(E=257, k=2), -3), (dict(T=0), -1)):
+        bad = _dims(**kw)
+        assert fwd(ctypes.byref(bad), p, c0, p, p, None, None, None) == code
+        assert bwd(ctypes.byref(bad), p, p, p, p, c0, p, None) == code
 
 
 def test_status_strings(lib):

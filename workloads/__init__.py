@@ -19,6 +19,10 @@ Recipe (one numpy stream per tensor, spawned from ``SeedSequence(1000+id)``):
   and its weights are the softmax of its N(0,1) logits at the drawn ids.
   ``zero_ranks`` removes the least popular experts from the draw, which
   forces empty experts.
+* Router inputs (``make_logits``): the same fp32 N(0,1) logits the Gaussian
+  routing draws from, and upstream gradients ``d_weights ~ N(0,1)[T,k]``.
+  ``ties=True`` rounds the logits to multiples of 0.5 in [-2, 2], so that
+  most tokens have equal logits among their top k.
 * bf16 configs round every floating tensor except the routing weights to
   bf16 on the host (round to nearest even) before either side sees it;
   values are kept as fp32 arrays that hold bf16-representable numbers.
@@ -32,7 +36,7 @@ import numpy as np
 
 __all__ = [
     "Config", "CONFIGS", "Inputs", "make_inputs", "round_to_bf16",
-    "bf16_bits", "bf16_bits_to_f32", "shrink",
+    "bf16_bits", "bf16_bits_to_f32", "shrink", "make_logits",
 ]
 
 
@@ -173,3 +177,18 @@ def make_inputs(cfg: Config, seed: Optional[int] = None,
         w1 = w3 = w2 = None
     dy = _normal(rdy, (T, H), 1.0, cfg.dtype) if with_dy else None
     return Inputs(cfg, x, ids, w, w1, w3, w2, dy)
+
+
+def make_logits(cfg: Config, seed: Optional[int] = None, ties: bool = False):
+    """(logits [T,E] fp32, d_weights [T,k] fp32) for the router.
+
+    The logits are the very values the Gaussian routing of ``make_inputs``
+    draws for the same config and seed."""
+    sid = cfg.seed_id if seed is None else seed
+    rl, rg = (np.random.default_rng(s)
+              for s in np.random.SeedSequence(1000 + sid).spawn(8)[0::7])
+    logits = rl.standard_normal((cfg.T, cfg.E), dtype=np.float32)
+    if ties:
+        logits = np.clip(np.round(logits * 2.0) / 2.0, -2.0, 2.0).astype(np.float32)
+    d_weights = rg.standard_normal((cfg.T, cfg.k), dtype=np.float32)
+    return logits, d_weights
