@@ -31,8 +31,8 @@ METRIC = "dMoE fwd+bwd tokens/s and useful TFLOP/s (% bf16 MFMA peak), E=64 k=8"
 
 META_KERNELS = ["meta_hist", "meta_scan", "meta_place"]
 FWD_KERNELS = ["padded_gather", "gemm_up_gate", "gemm_down", "padded_scatter"]
-BWD_KERNELS = ["scatter_backward", "gemm_down_dgrad_gate", "gemm_wgrad_down",
-               "gemm_up_dgrad", "gather_backward", "gemm_wgrad_up"]
+BWD_KERNELS = ["scatter_backward", "gemm_down_dgrad_wgrad_down", "gemm_up_dgrad",
+               "gather_backward", "gemm_wgrad_up"]
 
 
 def kernel_work(cfg, P):
@@ -54,8 +54,9 @@ def kernel_work(cfg, P):
     w["gemm_down"] = (2 * P * F * H, (P * F + Ea * F * H + P * H) * s)
     w["padded_scatter"] = (0, (N * H + T * H) * s + 4 * N)
     w["scatter_backward"] = (0, (T * H + N * H + P * H) * s + 8 * N)
-    w["gemm_down_dgrad_gate"] = (2 * P * H * F, (P * H + Ea * F * H + 4 * P * F) * s)
-    w["gemm_wgrad_down"] = (2 * P * F * H, (P * F + P * H + Ea * F * H) * s)
+    # down dgrad + gate backward and dw2, one launch: dy_perm is read once
+    w["gemm_down_dgrad_wgrad_down"] = (
+        4 * P * H * F, (P * H + 2 * Ea * F * H + 5 * P * F) * s)
     w["gemm_up_dgrad"] = (4 * P * H * F, (2 * P * F + 2 * Ea * H * F + P * H) * s)
     w["gemm_wgrad_up"] = (4 * P * H * F, (P * H + 2 * P * F + 2 * Ea * H * F) * s)
     w["gather_backward"] = (0, (N * H + T * H) * s)
@@ -213,7 +214,7 @@ def main():
     assert int(layer.buf.meta.status.item()) == 0
 
     K = args.steps
-    evs = [(EventArray(4), EventArray(5), EventArray(7)) for _ in range(K)]
+    evs = [(EventArray(4), EventArray(5), EventArray(6)) for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):

@@ -311,7 +311,7 @@ def dmoe_backward(dims: Dims, dy, weights, w1, w3, w2, meta: Meta, saved: Saved,
                   scratch: GradScratch, dx, dw1, dw3, dw2, d_weights,
                   stream=None, events=None) -> None:
     """Backward of the layer; see include/dmoe.h.  `events`: optional
-    EventArray of 7 events for per-kernel timing (dmoe_backward_timed)."""
+    EventArray of 6 events for per-kernel timing (dmoe_backward_timed)."""
     lib = load_library()
     dt = dims.torch_dtype
     T, H, F, E, k = dims.T, dims.H, dims.F, dims.E, dims.k
@@ -333,7 +333,7 @@ def dmoe_backward(dims: Dims, dy, weights, w1, w3, w2, meta: Meta, saved: Saved,
         ctypes.byref(saved._c(dt)), ctypes.byref(scratch._c(dt)),
         _ptr(dx, dt, "dx"), _ptr(dw1, dt, "dw1"), _ptr(dw3, dt, "dw3"),
         _ptr(dw2, dt, "dw2"), _ptr(d_weights, torch.float32, "d_weights"),
-        _stream(dy, stream), _ev(events, 6)), "dmoe_backward")
+        _stream(dy, stream), _ev(events, 5)), "dmoe_backward")
 
 
 def dmoe_padded_gather(dims: Dims, x, meta: Meta, x_perm, stream=None) -> None:

@@ -162,21 +162,20 @@ int dmoe_backward_timed(const dmoe_dims* dims, const void* dy, const float* weig
   DMOE_TRY(dmoe::launch_scatter_backward(s, dy, saved->y_perm, weights, m,
                                          scratch->dy_perm, d_weights, stream));
   rec(1);
-  DMOE_TRY(dmoe::launch_gemm_down_dgrad(s, scratch->dy_perm, w2, saved->h1, saved->h3,
-                                        m, scratch->dh1, scratch->dh3, stream));
+  DMOE_TRY(dmoe::launch_gemm_down_dgrad_wgrad_down(s, scratch->dy_perm, w2, saved->h1,
+                                                   saved->h3, saved->act, m, scratch->dh1,
+                                                   scratch->dh3, dw2, stream));
   rec(2);
-  DMOE_TRY(dmoe::launch_gemm_wgrad_down(s, saved->act, scratch->dy_perm, m, dw2, stream));
-  rec(3);
   DMOE_TRY(dmoe::launch_gemm_up_dgrad(s, scratch->dh1, scratch->dh3, w1, w3, m,
                                       scratch->dx_perm, stream));
-  rec(4);
+  rec(3);
   // the gather's backward right away, while dx_perm is still in the
   // last-level cache
   DMOE_TRY(dmoe::launch_padded_scatter(s, scratch->dx_perm, nullptr, m, dx, stream));
-  rec(5);
+  rec(4);
   DMOE_TRY(dmoe::launch_gemm_wgrad_up(s, saved->x_perm, scratch->dh1, scratch->dh3, m,
                                       dw1, dw3, stream));
-  rec(6);
+  rec(5);
   return DMOE_OK;
 }
 

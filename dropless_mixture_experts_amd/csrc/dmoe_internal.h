@@ -66,6 +66,11 @@ hipError_t launch_gemm_up_dgrad(const Shape& s, const void* dh1, const void* dh3
 hipError_t launch_gemm_wgrad_down(const Shape& s, const void* act,
                                   const void* dy_perm, const MetaPtrs& m,
                                   void* dw2, hipStream_t stream);
+// down dgrad + gate backward and dw2; one launch for bf16
+hipError_t launch_gemm_down_dgrad_wgrad_down(const Shape& s, const void* dy_perm,
+                                             const void* w2, const void* h1, const void* h3,
+                                             const void* act, const MetaPtrs& m, void* dh1,
+                                             void* dh3, void* dw2, hipStream_t stream);
 hipError_t launch_gemm_wgrad_up(const Shape& s, const void* x_perm,
                                 const void* dh1, const void* dh3,
                                 const MetaPtrs& m, void* dw1, void* dw3,
@@ -85,6 +90,10 @@ hipError_t launch_bf16_up_dgrad(const Shape& s, const void* dh1, const void* dh3
                                 void* dx_perm, hipStream_t stream);
 hipError_t launch_bf16_wgrad_down(const Shape& s, const void* act, const void* dy_perm,
                                   const MetaPtrs& m, void* dw2, hipStream_t stream);
+hipError_t launch_bf16_down_dgrad_wgrad_down(const Shape& s, const void* dy_perm,
+                                             const void* w2, const void* h1, const void* h3,
+                                             const void* act, const MetaPtrs& m, void* dh1,
+                                             void* dh3, void* dw2, hipStream_t stream);
 hipError_t launch_bf16_wgrad_up(const Shape& s, const void* x_perm, const void* dh1,
                                 const void* dh3, const MetaPtrs& m, void* dw1, void* dw3,
                                 hipStream_t stream);

@@ -546,6 +546,18 @@ hipError_t launch_gemm_wgrad_down(const Shape& s, const void* act,
   return hipGetLastError();
 }
 
+hipError_t launch_gemm_down_dgrad_wgrad_down(const Shape& s, const void* dy_perm,
+                                             const void* w2, const void* h1, const void* h3,
+                                             const void* act, const MetaPtrs& m, void* dh1,
+                                             void* dh3, void* dw2, hipStream_t stream) {
+  if (s.bf16)
+    return launch_bf16_down_dgrad_wgrad_down(s, dy_perm, w2, h1, h3, act, m, dh1, dh3, dw2,
+                                             stream);
+  const hipError_t err = launch_gemm_down_dgrad(s, dy_perm, w2, h1, h3, m, dh1, dh3, stream);
+  if (err != hipSuccess) return err;
+  return launch_gemm_wgrad_down(s, act, dy_perm, m, dw2, stream);
+}
+
 hipError_t launch_gemm_wgrad_up(const Shape& s, const void* x_perm,
                                 const void* dh1, const void* dh3,
                                 const MetaPtrs& m, void* dw1, void* dw3,

@@ -353,6 +353,7 @@ __device__ __forceinline__ int stage_half(char* st, const Acc& acc, int h, bf16*
 // kernel's own operand and epilogue code.
 struct Job {
   int steps, nk;
+  int kind;         // which product of a merged launch (0 or 1)
   int e;            // expert (weight gradients: expert | first padded row << 8)
   bool fa, fb;      // second half of A / B present
   int64_t u, v;     // tile coordinates
@@ -501,6 +502,8 @@ struct DownDgrad {
   RowTiles rt;
   __device__ uint32_t lda() const { return (uint32_t)(H * 2); }
   __device__ uint32_t ldb() const { return (uint32_t)(H * 2); }
+  static constexpr int kEpiSteps = 4;   // h1, h3 in and dh1, dh3 out: ~4 K steps of traffic
+  __device__ int tile_steps() const { return (int)(H / kKStep); }
   __device__ void xcd_range(int x, int& lo, int& hi) const { rt.xcd_range(x, lo, hi); }
   __device__ void tile(int L, Job& j) const {
     rt.get(L, j);
@@ -589,6 +592,8 @@ struct UpDgrad {
   RowTiles rt;
   __device__ uint32_t lda() const { return (uint32_t)(F * 2); }
   __device__ uint32_t ldb() const { return (uint32_t)(F * 2); }
+  static constexpr int kEpiSteps = 2;
+  __device__ int tile_steps() const { return (int)(2 * F / kKStep); }
   __device__ void xcd_range(int x, int& lo, int& hi) const { rt.xcd_range(x, lo, hi); }
   __device__ void tile(int L, Job& j) const {
     rt.get(L, j);
@@ -657,6 +662,9 @@ struct WgradDown {
   __device__ uint32_t ldb() const { return (uint32_t)(F * 2); }
   __device__ int nh() const { return (int)((H + 255) / 256); }
   __device__ int nf() const { return (int)((F + 255) / 256); }
+  static constexpr int kEpiSteps = 2;
+  __device__ int tiles_per_expert() const { return nh() * nf(); }
+  __device__ int expert_steps(int e) const { return round_up_block(tpe[e]) / kKStep; }
   __device__ void xcd_range(int x, int& lo, int& hi) const {
     lo = first_expert_of_xcd(x, E, tpe, padded_bins) * nh() * nf();
     hi = first_expert_of_xcd(x + 1, E, tpe, padded_bins) * nh() * nf();
@@ -710,6 +718,9 @@ struct WgradUp {
   __device__ uint32_t ldb() const { return (uint32_t)(H * 2); }
   __device__ int nf() const { return (int)(F / 128); }
   __device__ int nh() const { return (int)((H + 255) / 256); }
+  static constexpr int kEpiSteps = 2;
+  __device__ int tiles_per_expert() const { return nf() * nh(); }
+  __device__ int expert_steps(int e) const { return round_up_block(tpe[e]) / kKStep; }
   __device__ void xcd_range(int x, int& lo, int& hi) const {
     lo = first_expert_of_xcd(x, E, tpe, padded_bins) * nf() * nh();
     hi = first_expert_of_xcd(x + 1, E, tpe, padded_bins) * nf() * nh();
@@ -777,11 +788,13 @@ struct Pipe {
   // DMA of step s+2 into the stage of step s (nobody reads it any more) --
   // past the end of the tile that is step 0 of the next tile -- and read the
   // first fragment of step s+1.  Ends with a barrier and no LDS read in
-  // flight.  Returns whether step 0 of `nxt` was started.  When primed, the
-  // waits for steps 0 and 1 let w0 and w1 younger vector-memory operations
-  // (the DMA of step 1, the previous tile's stores) stay in flight.
+  // flight.  Returns whether step 0 of `nxt` was started (by next(gs), which
+  // may belong to another product).  When primed, the waits for steps 0 and 1
+  // let w0 and w1 younger vector-memory operations (the DMA of step 1, the
+  // previous tile's stores) stay in flight.
+  template <class Next>
   __device__ __forceinline__ bool run(Acc& acc, const Job& cur, const Job& nxt, bool primed,
-                                      int w0, int w1) {
+                                      int w0, int w1, Next&& next) {
     const int n = cur.steps;
     if (n <= 0) return false;
     const bool work = cur.fb || wn < 2;     // this wave has B rows
@@ -811,7 +824,7 @@ struct Pipe {
           if (s + 2 < n) {
             issue_step(cur, s + 2, g + s + 2);
           } else if (nxt.steps > 0) {       // s + 2 == n
-            issue_step(nxt, 0, g + s + 2);
+            next(g + s + 2);
             next_started = true;
           }
           if (work) load_frags<K::ATR, K::BTR>(f[0], stage_ptr(g + s + 1), 0, wm, wn, lane);
@@ -862,7 +875,7 @@ __device__ __forceinline__ void persistent(const K& k) {
     if (Ln < hi) k.tile(Ln, nxt);
     Acc acc;
     zero(acc);
-    primed = p.run(acc, cur, nxt, primed, w0, w1);
+    primed = p.run(acc, cur, nxt, primed, w0, w1, [&](int gs) { p.issue_step(nxt, 0, gs); });
     // step 1 of the next tile goes into the stage the last K step used (all
     // its reads are done); it is started before the stores unless the
     // epilogue loads, so that the stores can drain while the next tile runs
@@ -881,6 +894,156 @@ __device__ __forceinline__ void persistent(const K& k) {
     w1 = K::kLateStep1 ? 0 : nst;
     cur = nxt;
     L = Ln;
+  }
+}
+
+
+// Two independent products in one persistent launch, so that the short
+// weight-gradient tiles of K2 fill the last round of K1's row tiles instead
+// of leaving CUs idle between two launches.  K1 has row tiles of equal cost
+// (tile_steps() K steps plus an epilogue); K2 has whole experts per XCD
+// (tiles_per_expert() tiles of expert_steps(e) K steps).  Within XCD x the
+// S blocks first take K1's tiles round-robin; with n1 = a S + m, blocks
+// 0..m-1 get one tile more, so the other S - m are free one K1 tile earlier
+// and take the first K2 tiles, about (S - m) K1 tiles' worth, round-robin
+// among themselves (phase A).  Then all S blocks take the remaining K2
+// tiles round-robin (phase B), so concurrent blocks still work on
+// consecutive tiles; phase B deals in order of the blocks' load so far
+// (light blocks with one phase-A tile fewer, then the m heavy blocks, then
+// the other light blocks), so that its last partial round goes to the
+// least loaded.  Every wave computes the same schedule from the live
+// metadata; blocks do not communicate.
+template <class K1, class K2>
+struct DualSched {
+  int lo1, lo2, r, S, m, nA;
+  int rho;          // this block's place in the phase-B order
+  int c1, cA, cB;   // this block's tiles of K1, of phase A, of phase B
+
+  // K2 tiles from `lo` (an expert boundary) whose cost midpoint lies within
+  // `budget` K steps.
+  __device__ static int prefix_tiles(const K2& k2, int lo, int hi, int budget) {
+    const int tpe = k2.tiles_per_expert();
+    int cum = 0, n = 0;
+    for (int e = lo / tpe; e * tpe < hi; ++e) {
+      const int c = k2.expert_steps(e) + K2::kEpiSteps;
+      if (2 * (cum + tpe * c) - c <= 2 * budget) {
+        cum += tpe * c;
+        n += tpe;
+        continue;
+      }
+      const int rem2 = 2 * (budget - cum) - c;
+      n += rem2 >= 0 ? min(tpe, rem2 / (2 * c) + 1) : 0;
+      break;
+    }
+    return n;
+  }
+
+  __device__ void init(const K1& k1, const K2& k2, int x, int r_, int S_) {
+    r = r_;
+    S = S_;
+    int hi1, hi2;
+    k1.xcd_range(x, lo1, hi1);
+    k2.xcd_range(x, lo2, hi2);
+    lo1 = (int)uniform((uint32_t)lo1);
+    lo2 = (int)uniform((uint32_t)lo2);
+    const int n1 = (int)uniform((uint32_t)(hi1 - lo1));
+    const int n2 = (int)uniform((uint32_t)(hi2 - lo2));
+    m = n1 % S;
+    c1 = n1 / S + (r < m ? 1 : 0);
+    nA = 0;
+    if (m > 0)
+      nA = (int)uniform((uint32_t)prefix_tiles(k2, lo2, lo2 + n2,
+                                               (S - m) * (k1.tile_steps() + K1::kEpiSteps)));
+    cA = (r >= m && nA > r - m) ? (nA - (r - m) + (S - m) - 1) / (S - m) : 0;
+    const int rem = nA % (S - m);   // light blocks r - m < rem have one more phase-A tile
+    if (r >= m) rho = r - m >= rem ? r - m - rem : S - rem + (r - m);
+    else rho = S - m - rem + r;
+    const int nB = n2 - nA;
+    cB = nB > rho ? (nB - rho + S - 1) / S : 0;
+  }
+  __device__ int count() const { return c1 + cA + cB; }
+  // this block's i-th tile (each branch fills its own Job, so that all of
+  // them stay in registers)
+  __device__ Job job(const K1& k1, const K2& k2, int i) const {
+    if (i < c1) {
+      Job a;
+      k1.tile(lo1 + r + i * S, a);
+      a.kind = 0;
+      return a;
+    }
+    i -= c1;
+    Job b;
+    k2.tile(i < cA ? lo2 + (r - m) + i * (S - m) : lo2 + nA + rho + (i - cA) * S, b);
+    b.kind = 1;
+    return b;
+  }
+};
+
+template <class K1, class K2>
+__device__ __forceinline__ void persistent_dual(const K1& k1, const K2& k2) {
+  __shared__ __attribute__((aligned(16))) char lds[kLds];
+  static_assert(K1::kLateStep1 || !K1::kUsesFreeStage, "the free stage is refilled before the epilogue");
+  static_assert(K2::kLateStep1 || !K2::kUsesFreeStage, "the free stage is refilled before the epilogue");
+  const int S = (int)(gridDim.x / 8);
+  const int x = (int)(blockIdx.x % 8), r = (int)(blockIdx.x / 8);
+  DualSched<K1, K2> sc;
+  sc.init(k1, k2, x, r, S);
+  const int total = sc.count();
+  if (total <= 0) return;
+  const uint32_t lbase = uniform(lds_addr(lds));
+  const int lane = threadIdx.x & 63, w = (int)uniform(threadIdx.x >> 6);
+  Pipe<K1> p1{k1, lds, lbase, 0};
+  Pipe<K2> p2{k2, lds, lbase, 0};
+  p1.lane = p2.lane = lane;
+  p1.w = p2.w = w;
+  p1.wm = p2.wm = w >> 2;
+  p1.wn = p2.wn = w & 3;
+  p1.da.init(k1.lda(), lane);
+  p1.db.init(k1.ldb(), lane);
+  p2.da.init(k2.lda(), lane);
+  p2.db.init(k2.ldb(), lane);
+  char* const stg = lds + 2 * kStage + w * kStgWave;
+  const auto issue = [&](const Job& j, int s, int gs) {
+    if (j.kind == 0) p1.issue_step(j, s, gs);
+    else p2.issue_step(j, s, gs);
+  };
+  int g = 0;   // K steps run so far (selects the stage)
+  Job cur = sc.job(k1, k2, 0);
+  bool primed = false;
+  int w0 = 0, w1 = 0;
+  for (int i = 0;; ++i) {
+    Job nxt;
+    nxt.steps = 0;
+    nxt.kind = 0;
+    if (i + 1 < total) nxt = sc.job(k1, k2, i + 1);
+    Acc acc;
+    zero(acc);
+    const auto next = [&](int gs) { issue(nxt, 0, gs); };
+    if (cur.kind == 0) {
+      p1.g = g;
+      primed = p1.run(acc, cur, nxt, primed, w0, w1, next);
+      g = p1.g;
+    } else {
+      p2.g = g;
+      primed = p2.run(acc, cur, nxt, primed, w0, w1, next);
+      g = p2.g;
+    }
+    // as in persistent(): step 1 of the next tile before the stores, unless
+    // this tile's epilogue uses the free stage
+    const bool late = cur.kind == 0 ? K1::kLateStep1 : K2::kLateStep1;
+    const bool step1 = primed && nxt.steps > 1;
+    if (!late && step1) issue(nxt, 1, g + 1);
+    const int fs = ((g + 1) & 1) * kStage + 4 * w * 1024;
+    const Epi ep{stg, lds + fs, lds + fs + kReg, lbase + fs, lbase + fs + kReg};
+    const int nst = cur.kind == 0 ? k1.epilogue(cur, acc, ep) : k2.epilogue(cur, acc, ep);
+    if (i + 1 >= total) break;
+    if (late && step1) {
+      wait_lds();
+      issue(nxt, 1, g + 1);
+    }
+    w0 = (step1 ? kDmaPerStep : 0) + nst;
+    w1 = late ? 0 : nst;
+    cur = nxt;
   }
 }
 
@@ -924,6 +1087,20 @@ wgrad_down_kernel(const bf16* __restrict__ act, const bf16* __restrict__ dy_perm
                   int64_t H, int64_t F, int E, const int32_t* __restrict__ tpe,
                   const int32_t* __restrict__ padded_bins, bf16* __restrict__ dw2) {
   persistent(WgradDown{act, dy_perm, H, F, E, tpe, padded_bins, dw2});
+}
+
+// down dgrad + gate backward (dh1, dh3) and dw2 in one launch: both read
+// dy_perm, neither reads what the other writes.
+__global__ void __launch_bounds__(kThreads)
+down_dgrad_wgrad_down_kernel(const bf16* __restrict__ dy_perm, const bf16* __restrict__ w2,
+                             const bf16* h1, const bf16* h3, const bf16* __restrict__ act,
+                             int64_t H, int64_t F, int E, ROW_TILE_ARGS,
+                             const int32_t* __restrict__ tpe,
+                             const int32_t* __restrict__ padded_bins, bf16* dh1, bf16* dh3,
+                             bf16* __restrict__ dw2) {
+  DownDgrad k1{dy_perm, w2, h1, h3, H, F, dh1, dh3};
+  k1.rt.init(tile_expert, num_padded_rows, pair_first, num_pairs, (int)((F + 255) / 256));
+  persistent_dual(k1, WgradDown{act, dy_perm, H, F, E, tpe, padded_bins, dw2});
 }
 
 __global__ void __launch_bounds__(kThreads)
@@ -1008,6 +1185,21 @@ hipError_t launch_bf16_wgrad_down(const Shape& s, const void* act, const void* d
                      persistent_grid(cdiv(s.H, 256) * cdiv(s.F, 256) * s.E),
                      dim3(bfk::kThreads), 0, stream, cb<bf16>(act), cb<bf16>(dy_perm), s.H,
                      s.F, s.E, m.tokens_per_expert, m.padded_bins, mb<bf16>(dw2));
+  return hipGetLastError();
+}
+
+hipError_t launch_bf16_down_dgrad_wgrad_down(const Shape& s, const void* dy_perm,
+                                             const void* w2, const void* h1, const void* h3,
+                                             const void* act, const MetaPtrs& m, void* dh1,
+                                             void* dh3, void* dw2, hipStream_t stream) {
+  const int64_t t1 = cdiv(s.F, 256) * s.max_tiles;
+  const int64_t t2 = cdiv(s.H, 256) * cdiv(s.F, 256) * s.E;
+  hipLaunchKernelGGL(bfk::down_dgrad_wgrad_down_kernel, persistent_grid(t1 + t2),
+                     dim3(bfk::kThreads), 0, stream, cb<bf16>(dy_perm), cb<bf16>(w2),
+                     cb<bf16>(h1), cb<bf16>(h3), cb<bf16>(act), s.H, s.F, s.E,
+                     m.tile_expert, m.num_padded_rows, m.pair_first, m.num_pairs,
+                     m.tokens_per_expert, m.padded_bins, mb<bf16>(dh1), mb<bf16>(dh3),
+                     mb<bf16>(dw2));
   return hipGetLastError();
 }
 

@@ -220,9 +220,10 @@ int dmoe_router_backward(const dmoe_dims* dims, const float* logits,
  *   metadata (n = 3): histogram, scan, placement.
  *   forward  (n = 4): padded_gather, up projection + SiLU gate, down
  *                     projection, padded_scatter.
- *   backward (n = 6): scatter backward (dy_perm, d_weights), down dgrad +
- *                     gate backward, dw2, up dgrad (dx_perm), gather
- *                     backward (dx), dw1 + dw3.
+ *   backward (n = 5): scatter backward (dy_perm, d_weights), down dgrad +
+ *                     gate backward together with dw2 (one launch for
+ *                     bf16), up dgrad (dx_perm), gather backward (dx),
+ *                     dw1 + dw3.
  * Results are identical to the untimed calls. */
 int dmoe_metadata_timed(const dmoe_dims* dims, const int32_t* top_experts,
                         const dmoe_meta* meta, void* ws, hipStream_t stream,
