@@ -166,15 +166,15 @@ int dmoe_backward_timed(const dmoe_dims* dims, const void* dy, const float* weig
                                                    saved->h3, saved->act, m, scratch->dh1,
                                                    scratch->dh3, dw2, stream));
   rec(2);
-  DMOE_TRY(dmoe::launch_gemm_up_dgrad(s, scratch->dh1, scratch->dh3, w1, w3, m,
-                                      scratch->dx_perm, stream));
+  DMOE_TRY(dmoe::launch_gemm_up_dgrad(s, scratch->dh1, scratch->dh3, w1, w3, saved->x_perm,
+                                      m, scratch->dx_perm, dw1, dw3, stream));
   rec(3);
   // the gather's backward right away, while dx_perm is still in the
   // last-level cache
   DMOE_TRY(dmoe::launch_padded_scatter(s, scratch->dx_perm, nullptr, m, dx, stream));
   rec(4);
-  DMOE_TRY(dmoe::launch_gemm_wgrad_up(s, saved->x_perm, scratch->dh1, scratch->dh3, m,
-                                      dw1, dw3, stream));
+  DMOE_TRY(dmoe::launch_gemm_wgrad_up(s, scratch->dh1, scratch->dh3, w1, w3, saved->x_perm,
+                                      m, scratch->dx_perm, dw1, dw3, stream));
   rec(5);
   return DMOE_OK;
 }

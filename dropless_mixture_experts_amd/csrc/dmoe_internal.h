@@ -50,52 +50,47 @@ hipError_t launch_router_backward(const Shape& s, const float* logits, const int
                                   const float* weights, const float* d_weights, float coef,
                                   float* d_logits, hipStream_t stream);
 
-// gemm.hip
+// gemm.hip: the products of the layer.  bf16 runs on the engine in
+// gemm_bf16.hip; fp32 on the tiled kernels of gemm.hip.
 hipError_t launch_gemm_up(const Shape& s, const void* x_perm, const void* w1,
                           const void* w3, const MetaPtrs& m, void* h1, void* h3,
                           void* act, hipStream_t stream);
 hipError_t launch_gemm_down(const Shape& s, const void* act, const void* w2,
                             const MetaPtrs& m, void* y_perm, hipStream_t stream);
-hipError_t launch_gemm_down_dgrad(const Shape& s, const void* dy_perm,
-                                  const void* w2, const void* h1, const void* h3,
-                                  const MetaPtrs& m, void* dh1, void* dh3,
-                                  hipStream_t stream);
-hipError_t launch_gemm_up_dgrad(const Shape& s, const void* dh1, const void* dh3,
-                                const void* w1, const void* w3, const MetaPtrs& m,
-                                void* dx_perm, hipStream_t stream);
-hipError_t launch_gemm_wgrad_down(const Shape& s, const void* act,
-                                  const void* dy_perm, const MetaPtrs& m,
-                                  void* dw2, hipStream_t stream);
-// down dgrad + gate backward and dw2; one launch for bf16
+// down dgrad + gate backward (dh1, dh3) and dw2; one launch for bf16
 hipError_t launch_gemm_down_dgrad_wgrad_down(const Shape& s, const void* dy_perm,
                                              const void* w2, const void* h1, const void* h3,
                                              const void* act, const MetaPtrs& m, void* dh1,
                                              void* dh3, void* dw2, hipStream_t stream);
-hipError_t launch_gemm_wgrad_up(const Shape& s, const void* x_perm,
-                                const void* dh1, const void* dh3,
-                                const MetaPtrs& m, void* dw1, void* dw3,
+// up dgrad (dx_perm) and dw1/dw3 as two calls, with the gather's backward
+// between them: for bf16 the first also computes the dw1/dw3 tiles that
+// fill its last round, the second the others.  Both take every operand.
+hipError_t launch_gemm_up_dgrad(const Shape& s, const void* dh1, const void* dh3,
+                                const void* w1, const void* w3, const void* x_perm,
+                                const MetaPtrs& m, void* dx_perm, void* dw1, void* dw3,
+                                hipStream_t stream);
+hipError_t launch_gemm_wgrad_up(const Shape& s, const void* dh1, const void* dh3,
+                                const void* w1, const void* w3, const void* x_perm,
+                                const MetaPtrs& m, void* dx_perm, void* dw1, void* dw3,
                                 hipStream_t stream);
 
-// gemm_bf16.hip: the bf16 engine behind the launch_gemm_* entry points.
+// gemm_bf16.hip
 hipError_t launch_bf16_up(const Shape& s, const void* x_perm, const void* w1, const void* w3,
                           const MetaPtrs& m, void* h1, void* h3, void* act,
                           hipStream_t stream);
 hipError_t launch_bf16_down(const Shape& s, const void* act, const void* w2,
                             const MetaPtrs& m, void* y_perm, hipStream_t stream);
-hipError_t launch_bf16_down_dgrad(const Shape& s, const void* dy_perm, const void* w2,
-                                  const void* h1, const void* h3, const MetaPtrs& m,
-                                  void* dh1, void* dh3, hipStream_t stream);
-hipError_t launch_bf16_up_dgrad(const Shape& s, const void* dh1, const void* dh3,
-                                const void* w1, const void* w3, const MetaPtrs& m,
-                                void* dx_perm, hipStream_t stream);
-hipError_t launch_bf16_wgrad_down(const Shape& s, const void* act, const void* dy_perm,
-                                  const MetaPtrs& m, void* dw2, hipStream_t stream);
 hipError_t launch_bf16_down_dgrad_wgrad_down(const Shape& s, const void* dy_perm,
                                              const void* w2, const void* h1, const void* h3,
                                              const void* act, const MetaPtrs& m, void* dh1,
                                              void* dh3, void* dw2, hipStream_t stream);
-hipError_t launch_bf16_wgrad_up(const Shape& s, const void* x_perm, const void* dh1,
-                                const void* dh3, const MetaPtrs& m, void* dw1, void* dw3,
+hipError_t launch_bf16_up_dgrad(const Shape& s, const void* dh1, const void* dh3,
+                                const void* w1, const void* w3, const void* x_perm,
+                                const MetaPtrs& m, void* dx_perm, void* dw1, void* dw3,
+                                hipStream_t stream);
+hipError_t launch_bf16_wgrad_up(const Shape& s, const void* dh1, const void* dh3,
+                                const void* w1, const void* w3, const void* x_perm,
+                                const MetaPtrs& m, void* dx_perm, void* dw1, void* dw3,
                                 hipStream_t stream);
 
 }  // namespace dmoe

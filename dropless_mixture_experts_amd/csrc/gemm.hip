@@ -512,34 +512,19 @@ hipError_t launch_gemm_down(const Shape& s, const void* act, const void* w2,
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_down_dgrad(const Shape& s, const void* dy_perm,
-                                  const void* w2, const void* h1, const void* h3,
-                                  const MetaPtrs& m, void* dh1, void* dh3,
-                                  hipStream_t stream) {
+static hipError_t f32_down_dgrad(const Shape& s, const void* dy_perm, const void* w2,
+                                 const void* h1, const void* h3, const MetaPtrs& m, void* dh1,
+                                 void* dh3, hipStream_t stream) {
   const dim3 grid(cdiv(s.F, kTileA), (unsigned)s.max_tiles);
-  if (s.bf16) return launch_bf16_down_dgrad(s, dy_perm, w2, h1, h3, m, dh1, dh3, stream);
   hipLaunchKernelGGL(gemm_down_dgrad_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
                      cp<float>(dy_perm), cp<float>(w2), cp<float>(h1), cp<float>(h3),
                      s.H, s.F, m.tile_expert, mp<float>(dh1), mp<float>(dh3));
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_up_dgrad(const Shape& s, const void* dh1, const void* dh3,
-                                const void* w1, const void* w3, const MetaPtrs& m,
-                                void* dx_perm, hipStream_t stream) {
-  const dim3 grid(cdiv(s.H, kTileA), (unsigned)s.max_tiles);
-  if (s.bf16) return launch_bf16_up_dgrad(s, dh1, dh3, w1, w3, m, dx_perm, stream);
-  hipLaunchKernelGGL(gemm_up_dgrad_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
-                     cp<float>(dh1), cp<float>(dh3), cp<float>(w1), cp<float>(w3), s.H,
-                     s.F, m.tile_expert, mp<float>(dx_perm));
-  return hipGetLastError();
-}
-
-hipError_t launch_gemm_wgrad_down(const Shape& s, const void* act,
-                                  const void* dy_perm, const MetaPtrs& m,
-                                  void* dw2, hipStream_t stream) {
+static hipError_t f32_wgrad_down(const Shape& s, const void* act, const void* dy_perm,
+                                 const MetaPtrs& m, void* dw2, hipStream_t stream) {
   const dim3 grid(cdiv(s.H, kTileA), cdiv(s.F, 128), (unsigned)s.E);
-  if (s.bf16) return launch_bf16_wgrad_down(s, act, dy_perm, m, dw2, stream);
   hipLaunchKernelGGL(gemm_wgrad_down_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
                      cp<float>(act), cp<float>(dy_perm), s.H, s.F, m.tokens_per_expert,
                      m.padded_bins, mp<float>(dw2));
@@ -553,17 +538,31 @@ hipError_t launch_gemm_down_dgrad_wgrad_down(const Shape& s, const void* dy_perm
   if (s.bf16)
     return launch_bf16_down_dgrad_wgrad_down(s, dy_perm, w2, h1, h3, act, m, dh1, dh3, dw2,
                                              stream);
-  const hipError_t err = launch_gemm_down_dgrad(s, dy_perm, w2, h1, h3, m, dh1, dh3, stream);
+  const hipError_t err = f32_down_dgrad(s, dy_perm, w2, h1, h3, m, dh1, dh3, stream);
   if (err != hipSuccess) return err;
-  return launch_gemm_wgrad_down(s, act, dy_perm, m, dw2, stream);
+  return f32_wgrad_down(s, act, dy_perm, m, dw2, stream);
 }
 
-hipError_t launch_gemm_wgrad_up(const Shape& s, const void* x_perm,
-                                const void* dh1, const void* dh3,
-                                const MetaPtrs& m, void* dw1, void* dw3,
+hipError_t launch_gemm_up_dgrad(const Shape& s, const void* dh1, const void* dh3,
+                                const void* w1, const void* w3, const void* x_perm,
+                                const MetaPtrs& m, void* dx_perm, void* dw1, void* dw3,
                                 hipStream_t stream) {
+  if (s.bf16)
+    return launch_bf16_up_dgrad(s, dh1, dh3, w1, w3, x_perm, m, dx_perm, dw1, dw3, stream);
+  const dim3 grid(cdiv(s.H, kTileA), (unsigned)s.max_tiles);
+  hipLaunchKernelGGL(gemm_up_dgrad_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
+                     cp<float>(dh1), cp<float>(dh3), cp<float>(w1), cp<float>(w3), s.H,
+                     s.F, m.tile_expert, mp<float>(dx_perm));
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_wgrad_up(const Shape& s, const void* dh1, const void* dh3,
+                                const void* w1, const void* w3, const void* x_perm,
+                                const MetaPtrs& m, void* dx_perm, void* dw1, void* dw3,
+                                hipStream_t stream) {
+  if (s.bf16)
+    return launch_bf16_wgrad_up(s, dh1, dh3, w1, w3, x_perm, m, dx_perm, dw1, dw3, stream);
   const dim3 grid(cdiv(s.F, 128), cdiv(s.H, 128), (unsigned)s.E);
-  if (s.bf16) return launch_bf16_wgrad_up(s, x_perm, dh1, dh3, m, dw1, dw3, stream);
   hipLaunchKernelGGL(gemm_wgrad_up_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
                      cp<float>(x_perm), cp<float>(dh1), cp<float>(dh3), s.H, s.F,
                      m.tokens_per_expert, m.padded_bins, mp<float>(dw1), mp<float>(dw3));

@@ -42,6 +42,7 @@
 //     stored.
 #include <algorithm>
 #include <atomic>
+#include <cmath>
 
 #include "dmoe_device.h"
 #include "dmoe_internal.h"
@@ -905,40 +906,45 @@ __device__ __forceinline__ void persistent(const K& k) {
 // (tiles_per_expert() tiles of expert_steps(e) K steps).  Within XCD x the
 // S blocks first take K1's tiles round-robin; with n1 = a S + m, blocks
 // 0..m-1 get one tile more, so the other S - m are free one K1 tile earlier
-// and take the first K2 tiles, about (S - m) K1 tiles' worth, round-robin
-// among themselves (phase A).  Then all S blocks take the remaining K2
+// and take the first K2 tiles round-robin among themselves (phase A), as
+// many as keep each of them within one K1 tile of extra work.  Then all S blocks take the remaining K2
 // tiles round-robin (phase B), so concurrent blocks still work on
 // consecutive tiles; phase B deals in order of the blocks' load so far
 // (light blocks with one phase-A tile fewer, then the m heavy blocks, then
 // the other light blocks), so that its last partial round goes to the
 // least loaded.  Every wave computes the same schedule from the live
 // metadata; blocks do not communicate.
-template <class K1, class K2>
+//
+// kTailFill runs K1 and phase A only, and a later launch with kRest (same
+// grid) runs phase B: other work can then sit between the two, here the
+// gather's backward, which reads K1's output while it is still in the
+// last-level cache.
+enum DualMode { kAll, kTailFill, kRest };
+
+template <class K1, class K2, DualMode M = kAll>
 struct DualSched {
   int lo1, lo2, r, S, m, nA;
   int rho;          // this block's place in the phase-B order
   int c1, cA, cB;   // this block's tiles of K1, of phase A, of phase B
 
-  // K2 tiles from `lo` (an expert boundary) whose cost midpoint lies within
-  // `budget` K steps.
-  __device__ static int prefix_tiles(const K2& k2, int lo, int hi, int budget) {
+  // The longest prefix of K2's tiles from `lo` (an expert boundary) that,
+  // dealt round-robin over `nb` blocks, gives no block more than `gap` K
+  // steps: ceil(n / nb) tiles of at most the largest cost among them.
+  __device__ static int prefix_tiles(const K2& k2, int lo, int hi, int nb, int gap) {
     const int tpe = k2.tiles_per_expert();
-    int cum = 0, n = 0;
+    int n = 0, cmax = 1;
     for (int e = lo / tpe; e * tpe < hi; ++e) {
-      const int c = k2.expert_steps(e) + K2::kEpiSteps;
-      if (2 * (cum + tpe * c) - c <= 2 * budget) {
-        cum += tpe * c;
-        n += tpe;
-        continue;
-      }
-      const int rem2 = 2 * (budget - cum) - c;
-      n += rem2 >= 0 ? min(tpe, rem2 / (2 * c) + 1) : 0;
-      break;
+      cmax = max(cmax, k2.expert_steps(e) + K2::kEpiSteps);
+      const int cap = (gap / cmax) * nb;   // tiles allowed at this cost
+      if (cap <= n) break;
+      if (cap < n + tpe) return cap;
+      n += tpe;
     }
     return n;
   }
 
-  __device__ void init(const K1& k1, const K2& k2, int x, int r_, int S_) {
+  // filled: whether a kTailFill launch ran phase A (kRest only)
+  __device__ void init(const K1& k1, const K2& k2, int x, int r_, int S_, bool filled = true) {
     r = r_;
     S = S_;
     int hi1, hi2;
@@ -951,21 +957,27 @@ struct DualSched {
     m = n1 % S;
     c1 = n1 / S + (r < m ? 1 : 0);
     nA = 0;
-    if (m > 0)
-      nA = (int)uniform((uint32_t)prefix_tiles(k2, lo2, lo2 + n2,
-                                               (S - m) * (k1.tile_steps() + K1::kEpiSteps)));
+    if (m > 0 && filled)
+      nA = (int)uniform((uint32_t)prefix_tiles(k2, lo2, lo2 + n2, S - m,
+                                               k1.tile_steps() + K1::kEpiSteps));
     cA = (r >= m && nA > r - m) ? (nA - (r - m) + (S - m) - 1) / (S - m) : 0;
     const int rem = nA % (S - m);   // light blocks r - m < rem have one more phase-A tile
     if (r >= m) rho = r - m >= rem ? r - m - rem : S - rem + (r - m);
     else rho = S - m - rem + r;
     const int nB = n2 - nA;
     cB = nB > rho ? (nB - rho + S - 1) / S : 0;
+    if (M == kTailFill) cB = 0;
+    if (M == kRest) {               // a fresh launch: plain round-robin
+      c1 = cA = 0;
+      rho = r;
+      cB = nB > r ? (nB - r + S - 1) / S : 0;
+    }
   }
   __device__ int count() const { return c1 + cA + cB; }
   // this block's i-th tile (each branch fills its own Job, so that all of
   // them stay in registers)
   __device__ Job job(const K1& k1, const K2& k2, int i) const {
-    if (i < c1) {
+    if (M != kRest && i < c1) {
       Job a;
       k1.tile(lo1 + r + i * S, a);
       a.kind = 0;
@@ -979,15 +991,15 @@ struct DualSched {
   }
 };
 
-template <class K1, class K2>
-__device__ __forceinline__ void persistent_dual(const K1& k1, const K2& k2) {
+template <DualMode M = kAll, class K1, class K2>
+__device__ __forceinline__ void persistent_dual(const K1& k1, const K2& k2, bool filled = true) {
   __shared__ __attribute__((aligned(16))) char lds[kLds];
   static_assert(K1::kLateStep1 || !K1::kUsesFreeStage, "the free stage is refilled before the epilogue");
   static_assert(K2::kLateStep1 || !K2::kUsesFreeStage, "the free stage is refilled before the epilogue");
   const int S = (int)(gridDim.x / 8);
   const int x = (int)(blockIdx.x % 8), r = (int)(blockIdx.x / 8);
-  DualSched<K1, K2> sc;
-  sc.init(k1, k2, x, r, S);
+  DualSched<K1, K2, M> sc;
+  sc.init(k1, k2, x, r, S, filled);
   const int total = sc.count();
   if (total <= 0) return;
   const uint32_t lbase = uniform(lds_addr(lds));
@@ -1003,8 +1015,10 @@ __device__ __forceinline__ void persistent_dual(const K1& k1, const K2& k2) {
   p2.da.init(k2.lda(), lane);
   p2.db.init(k2.ldb(), lane);
   char* const stg = lds + 2 * kStage + w * kStgWave;
+  // kRest runs K2 tiles only: the K1 paths are not compiled in
+  constexpr bool kOnly2 = M == kRest;
   const auto issue = [&](const Job& j, int s, int gs) {
-    if (j.kind == 0) p1.issue_step(j, s, gs);
+    if (!kOnly2 && j.kind == 0) p1.issue_step(j, s, gs);
     else p2.issue_step(j, s, gs);
   };
   int g = 0;   // K steps run so far (selects the stage)
@@ -1019,7 +1033,7 @@ __device__ __forceinline__ void persistent_dual(const K1& k1, const K2& k2) {
     Acc acc;
     zero(acc);
     const auto next = [&](int gs) { issue(nxt, 0, gs); };
-    if (cur.kind == 0) {
+    if (!kOnly2 && cur.kind == 0) {
       p1.g = g;
       primed = p1.run(acc, cur, nxt, primed, w0, w1, next);
       g = p1.g;
@@ -1030,12 +1044,13 @@ __device__ __forceinline__ void persistent_dual(const K1& k1, const K2& k2) {
     }
     // as in persistent(): step 1 of the next tile before the stores, unless
     // this tile's epilogue uses the free stage
-    const bool late = cur.kind == 0 ? K1::kLateStep1 : K2::kLateStep1;
+    const bool late = (!kOnly2 && cur.kind == 0) ? K1::kLateStep1 : K2::kLateStep1;
     const bool step1 = primed && nxt.steps > 1;
     if (!late && step1) issue(nxt, 1, g + 1);
     const int fs = ((g + 1) & 1) * kStage + 4 * w * 1024;
     const Epi ep{stg, lds + fs, lds + fs + kReg, lbase + fs, lbase + fs + kReg};
-    const int nst = cur.kind == 0 ? k1.epilogue(cur, acc, ep) : k2.epilogue(cur, acc, ep);
+    const int nst =
+        (!kOnly2 && cur.kind == 0) ? k1.epilogue(cur, acc, ep) : k2.epilogue(cur, acc, ep);
     if (i + 1 >= total) break;
     if (late && step1) {
       wait_lds();
@@ -1065,15 +1080,6 @@ down_kernel(const bf16* __restrict__ act, const bf16* __restrict__ w2, int64_t H
 }
 
 __global__ void __launch_bounds__(kThreads)
-down_dgrad_kernel(const bf16* __restrict__ dy_perm, const bf16* __restrict__ w2,
-                  const bf16* h1, const bf16* h3, int64_t H, int64_t F, ROW_TILE_ARGS,
-                  bf16* dh1, bf16* dh3) {
-  DownDgrad k{dy_perm, w2, h1, h3, H, F, dh1, dh3};
-  k.rt.init(tile_expert, num_padded_rows, pair_first, num_pairs, (int)((F + 255) / 256));
-  persistent(k);
-}
-
-__global__ void __launch_bounds__(kThreads)
 up_dgrad_kernel(const bf16* __restrict__ dh1, const bf16* __restrict__ dh3,
                 const bf16* __restrict__ w1, const bf16* __restrict__ w3, int64_t H,
                 int64_t F, ROW_TILE_ARGS, bf16* dx_perm) {
@@ -1082,11 +1088,19 @@ up_dgrad_kernel(const bf16* __restrict__ dh1, const bf16* __restrict__ dh3,
   persistent(k);
 }
 
+// dx_perm = dh1 w1^T + dh3 w3^T, with the first dw1/dw3 tiles filling its
+// last round (kTailFill); wgrad_up_kernel (kRest, same grid, filled = 1)
+// does the rest.
 __global__ void __launch_bounds__(kThreads)
-wgrad_down_kernel(const bf16* __restrict__ act, const bf16* __restrict__ dy_perm,
-                  int64_t H, int64_t F, int E, const int32_t* __restrict__ tpe,
-                  const int32_t* __restrict__ padded_bins, bf16* __restrict__ dw2) {
-  persistent(WgradDown{act, dy_perm, H, F, E, tpe, padded_bins, dw2});
+up_dgrad_fill_kernel(const bf16* __restrict__ dh1, const bf16* __restrict__ dh3,
+                     const bf16* __restrict__ w1, const bf16* __restrict__ w3,
+                     const bf16* __restrict__ x_perm, int64_t H, int64_t F, int E,
+                     ROW_TILE_ARGS, const int32_t* __restrict__ tpe,
+                     const int32_t* __restrict__ padded_bins, bf16* dx_perm,
+                     bf16* __restrict__ dw1, bf16* __restrict__ dw3) {
+  UpDgrad k1{dh1, dh3, w1, w3, H, F, dx_perm};
+  k1.rt.init(tile_expert, num_padded_rows, pair_first, num_pairs, (int)((H + 255) / 256));
+  persistent_dual<kTailFill>(k1, WgradUp{x_perm, dh1, dh3, H, F, E, tpe, padded_bins, dw1, dw3});
 }
 
 // down dgrad + gate backward (dh1, dh3) and dw2 in one launch: both read
@@ -1104,11 +1118,15 @@ down_dgrad_wgrad_down_kernel(const bf16* __restrict__ dy_perm, const bf16* __res
 }
 
 __global__ void __launch_bounds__(kThreads)
-wgrad_up_kernel(const bf16* __restrict__ x_perm, const bf16* __restrict__ dh1,
-                const bf16* __restrict__ dh3, int64_t H, int64_t F, int E,
+wgrad_up_kernel(const bf16* __restrict__ dh1, const bf16* __restrict__ dh3,
+                const bf16* __restrict__ w1, const bf16* __restrict__ w3,
+                const bf16* __restrict__ x_perm, int64_t H, int64_t F, int E, ROW_TILE_ARGS,
                 const int32_t* __restrict__ tpe, const int32_t* __restrict__ padded_bins,
-                bf16* __restrict__ dw1, bf16* __restrict__ dw3) {
-  persistent(WgradUp{x_perm, dh1, dh3, H, F, E, tpe, padded_bins, dw1, dw3});
+                int filled, bf16* dx_perm, bf16* __restrict__ dw1, bf16* __restrict__ dw3) {
+  UpDgrad k1{dh1, dh3, w1, w3, H, F, dx_perm};
+  k1.rt.init(tile_expert, num_padded_rows, pair_first, num_pairs, (int)((H + 255) / 256));
+  persistent_dual<kRest>(k1, WgradUp{x_perm, dh1, dh3, H, F, E, tpe, padded_bins, dw1, dw3},
+                         filled != 0);
 }
 
 }  // namespace bfk
@@ -1159,32 +1177,39 @@ hipError_t launch_bf16_down(const Shape& s, const void* act, const void* w2,
   return hipGetLastError();
 }
 
-hipError_t launch_bf16_down_dgrad(const Shape& s, const void* dy_perm, const void* w2,
-                                  const void* h1, const void* h3, const MetaPtrs& m,
-                                  void* dh1, void* dh3, hipStream_t stream) {
-  hipLaunchKernelGGL(bfk::down_dgrad_kernel, persistent_grid(cdiv(s.F, 256) * s.max_tiles),
-                     dim3(bfk::kThreads), 0, stream, cb<bf16>(dy_perm), cb<bf16>(w2),
-                     cb<bf16>(h1), cb<bf16>(h3), s.H, s.F, m.tile_expert, m.num_padded_rows,
-                     m.pair_first, m.num_pairs, mb<bf16>(dh1), mb<bf16>(dh3));
-  return hipGetLastError();
+// The up-projection dgrad and dw1/dw3 are two launches on one grid, with the
+// gather's backward between them.  When the dgrad's last round of row tiles
+// is expected to be less than 90% full, the first launch also takes the
+// dw1/dw3 tiles that fill it (see DualSched).  The estimate assumes balanced
+// routing: each expert has T k / E rows, so about T k / (256 E) + 1/2 pairs
+// of row blocks.  It depends on the shape only, so both launches agree.
+static dim3 up_dgrad_grid(const Shape& s) {
+  return persistent_grid(cdiv(s.H, 256) * s.max_tiles + cdiv(s.F, 128) * cdiv(s.H, 256) * s.E);
+}
+
+static bool up_dgrad_fills_tail(const Shape& s) {
+  const double rows = (double)s.T * s.k / s.E;
+  const double tiles = s.E * (rows / 256.0 + 0.5) * (double)cdiv(s.H, 256);
+  const double rounds = tiles / (double)up_dgrad_grid(s).x;
+  return rounds / std::ceil(rounds) < 0.9;
 }
 
 hipError_t launch_bf16_up_dgrad(const Shape& s, const void* dh1, const void* dh3,
-                                const void* w1, const void* w3, const MetaPtrs& m,
-                                void* dx_perm, hipStream_t stream) {
-  hipLaunchKernelGGL(bfk::up_dgrad_kernel, persistent_grid(cdiv(s.H, 256) * s.max_tiles),
-                     dim3(bfk::kThreads), 0, stream, cb<bf16>(dh1), cb<bf16>(dh3),
-                     cb<bf16>(w1), cb<bf16>(w3), s.H, s.F, m.tile_expert, m.num_padded_rows,
-                     m.pair_first, m.num_pairs, mb<bf16>(dx_perm));
-  return hipGetLastError();
-}
-
-hipError_t launch_bf16_wgrad_down(const Shape& s, const void* act, const void* dy_perm,
-                                  const MetaPtrs& m, void* dw2, hipStream_t stream) {
-  hipLaunchKernelGGL(bfk::wgrad_down_kernel,
-                     persistent_grid(cdiv(s.H, 256) * cdiv(s.F, 256) * s.E),
-                     dim3(bfk::kThreads), 0, stream, cb<bf16>(act), cb<bf16>(dy_perm), s.H,
-                     s.F, s.E, m.tokens_per_expert, m.padded_bins, mb<bf16>(dw2));
+                                const void* w1, const void* w3, const void* x_perm,
+                                const MetaPtrs& m, void* dx_perm, void* dw1, void* dw3,
+                                hipStream_t stream) {
+  if (up_dgrad_fills_tail(s)) {
+    hipLaunchKernelGGL(bfk::up_dgrad_fill_kernel, up_dgrad_grid(s), dim3(bfk::kThreads), 0,
+                       stream, cb<bf16>(dh1), cb<bf16>(dh3), cb<bf16>(w1), cb<bf16>(w3),
+                       cb<bf16>(x_perm), s.H, s.F, s.E, m.tile_expert, m.num_padded_rows,
+                       m.pair_first, m.num_pairs, m.tokens_per_expert, m.padded_bins,
+                       mb<bf16>(dx_perm), mb<bf16>(dw1), mb<bf16>(dw3));
+  } else {
+    hipLaunchKernelGGL(bfk::up_dgrad_kernel, persistent_grid(cdiv(s.H, 256) * s.max_tiles),
+                       dim3(bfk::kThreads), 0, stream, cb<bf16>(dh1), cb<bf16>(dh3),
+                       cb<bf16>(w1), cb<bf16>(w3), s.H, s.F, m.tile_expert,
+                       m.num_padded_rows, m.pair_first, m.num_pairs, mb<bf16>(dx_perm));
+  }
   return hipGetLastError();
 }
 
@@ -1203,14 +1228,16 @@ hipError_t launch_bf16_down_dgrad_wgrad_down(const Shape& s, const void* dy_perm
   return hipGetLastError();
 }
 
-hipError_t launch_bf16_wgrad_up(const Shape& s, const void* x_perm, const void* dh1,
-                                const void* dh3, const MetaPtrs& m, void* dw1, void* dw3,
+hipError_t launch_bf16_wgrad_up(const Shape& s, const void* dh1, const void* dh3,
+                                const void* w1, const void* w3, const void* x_perm,
+                                const MetaPtrs& m, void* dx_perm, void* dw1, void* dw3,
                                 hipStream_t stream) {
-  hipLaunchKernelGGL(bfk::wgrad_up_kernel,
-                     persistent_grid(cdiv(s.F, 128) * cdiv(s.H, 256) * s.E),
-                     dim3(bfk::kThreads), 0, stream, cb<bf16>(x_perm), cb<bf16>(dh1),
-                     cb<bf16>(dh3), s.H, s.F, s.E, m.tokens_per_expert, m.padded_bins,
-                     mb<bf16>(dw1), mb<bf16>(dw3));
+  hipLaunchKernelGGL(bfk::wgrad_up_kernel, up_dgrad_grid(s), dim3(bfk::kThreads), 0, stream,
+                     cb<bf16>(dh1), cb<bf16>(dh3), cb<bf16>(w1), cb<bf16>(w3),
+                     cb<bf16>(x_perm), s.H, s.F, s.E, m.tile_expert, m.num_padded_rows,
+                     m.pair_first, m.num_pairs, m.tokens_per_expert, m.padded_bins,
+                     up_dgrad_fills_tail(s) ? 1 : 0, mb<bf16>(dx_perm), mb<bf16>(dw1),
+                     mb<bf16>(dw3));
   return hipGetLastError();
 }
 
