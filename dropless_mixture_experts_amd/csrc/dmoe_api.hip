@@ -64,8 +64,8 @@ MetaPtrs meta_ptrs(const dmoe_meta* m) {
 struct Recorder {
   hipEvent_t* events;
   hipStream_t stream;
-  void operator()(int i) const {
-    if (events) (void)hipEventRecord(events[i], stream);
+  hipError_t operator()(int i) const {
+    return events ? hipEventRecord(events[i], stream) : hipSuccess;
   }
 };
 
@@ -119,16 +119,16 @@ int dmoe_forward_timed(const dmoe_dims* dims, const void* x, const float* weight
   const Shape s = shape_of(dims);
   const MetaPtrs m = meta_ptrs(meta);
   Recorder rec{ev, stream};
-  rec(0);
+  DMOE_TRY(rec(0));
   DMOE_TRY(dmoe::launch_padded_gather(s, x, m, saved->x_perm, stream));
-  rec(1);
+  DMOE_TRY(rec(1));
   DMOE_TRY(dmoe::launch_gemm_up(s, saved->x_perm, w1, w3, m, saved->h1, saved->h3,
                                 saved->act, stream));
-  rec(2);
+  DMOE_TRY(rec(2));
   DMOE_TRY(dmoe::launch_gemm_down(s, saved->act, w2, m, saved->y_perm, stream));
-  rec(3);
+  DMOE_TRY(rec(3));
   DMOE_TRY(dmoe::launch_padded_scatter(s, saved->y_perm, weights, m, y, stream));
-  rec(4);
+  DMOE_TRY(rec(4));
   return DMOE_OK;
 }
 
@@ -158,24 +158,24 @@ int dmoe_backward_timed(const dmoe_dims* dims, const void* dy, const float* weig
   Recorder rec{ev, stream};
   // Order matters for the permitted aliases: dy_perm is last read by the
   // down-projection weight gradient, before dx_perm is written.
-  rec(0);
+  DMOE_TRY(rec(0));
   DMOE_TRY(dmoe::launch_scatter_backward(s, dy, saved->y_perm, weights, m,
                                          scratch->dy_perm, d_weights, stream));
-  rec(1);
+  DMOE_TRY(rec(1));
   DMOE_TRY(dmoe::launch_gemm_down_dgrad_wgrad_down(s, scratch->dy_perm, w2, saved->h1,
                                                    saved->h3, saved->act, m, scratch->dh1,
                                                    scratch->dh3, dw2, stream));
-  rec(2);
+  DMOE_TRY(rec(2));
   DMOE_TRY(dmoe::launch_gemm_up_dgrad(s, scratch->dh1, scratch->dh3, w1, w3, saved->x_perm,
                                       m, scratch->dx_perm, dw1, dw3, stream));
-  rec(3);
+  DMOE_TRY(rec(3));
   // the gather's backward right away, while dx_perm is still in the
   // last-level cache
   DMOE_TRY(dmoe::launch_padded_scatter(s, scratch->dx_perm, nullptr, m, dx, stream));
-  rec(4);
+  DMOE_TRY(rec(4));
   DMOE_TRY(dmoe::launch_gemm_wgrad_up(s, scratch->dh1, scratch->dh3, w1, w3, saved->x_perm,
                                       m, scratch->dx_perm, dw1, dw3, stream));
-  rec(5);
+  DMOE_TRY(rec(5));
   return DMOE_OK;
 }
 
