@@ -124,6 +124,10 @@ def load_library() -> ctypes.CDLL:
                                         P(_Saved), P(_Scratch), vp, vp, vp, vp,
                                         vp, vp, vp]
     lib.dmoe_backward_timed.restype = ctypes.c_int
+    lib.dmoe_backward_recompute.argtypes = lib.dmoe_backward.argtypes
+    lib.dmoe_backward_recompute.restype = ctypes.c_int
+    lib.dmoe_backward_recompute_timed.argtypes = lib.dmoe_backward_timed.argtypes
+    lib.dmoe_backward_recompute_timed.restype = ctypes.c_int
     lib.dmoe_router_forward.argtypes = [P(_Dims), vp, ctypes.c_float, vp, vp, vp, vp, vp]
     lib.dmoe_router_forward.restype = ctypes.c_int
     lib.dmoe_router_backward.argtypes = [P(_Dims), vp, vp, vp, vp, ctypes.c_float, vp, vp]
@@ -309,9 +313,11 @@ def dmoe_forward(dims: Dims, x, weights, w1, w3, w2, meta: Meta, saved: Saved,
 
 def dmoe_backward(dims: Dims, dy, weights, w1, w3, w2, meta: Meta, saved: Saved,
                   scratch: GradScratch, dx, dw1, dw3, dw2, d_weights,
-                  stream=None, events=None) -> None:
+                  stream=None, events=None, recompute: bool = False) -> None:
     """Backward of the layer; see include/dmoe.h.  `events`: optional
-    EventArray of 6 events for per-kernel timing (dmoe_backward_timed)."""
+    EventArray of 6 events (7 with recompute) for per-kernel timing.
+    recompute: saved.act is scratch on entry and is rebuilt from h1 and h3
+    (dmoe_backward_recompute)."""
     lib = load_library()
     dt = dims.torch_dtype
     T, H, F, E, k = dims.T, dims.H, dims.F, dims.E, dims.k
@@ -326,14 +332,15 @@ def dmoe_backward(dims: Dims, dy, weights, w1, w3, w2, meta: Meta, saved: Saved,
                     (scratch.dx_perm, "dx_perm", pm * H)):
         _need(t, n, s)
     _check_meta(dims, meta)
-    _check(lib.dmoe_backward_timed(
+    fn = lib.dmoe_backward_recompute_timed if recompute else lib.dmoe_backward_timed
+    _check(fn(
         ctypes.byref(dims._c()), _ptr(dy, dt, "dy"),
         _ptr(weights, torch.float32, "weights"), _ptr(w1, dt, "w1"),
         _ptr(w3, dt, "w3"), _ptr(w2, dt, "w2"), ctypes.byref(meta._c()),
         ctypes.byref(saved._c(dt)), ctypes.byref(scratch._c(dt)),
         _ptr(dx, dt, "dx"), _ptr(dw1, dt, "dw1"), _ptr(dw3, dt, "dw3"),
         _ptr(dw2, dt, "dw2"), _ptr(d_weights, torch.float32, "d_weights"),
-        _stream(dy, stream), _ev(events, 5)), "dmoe_backward")
+        _stream(dy, stream), _ev(events, 6 if recompute else 5)), "dmoe_backward")
 
 
 def dmoe_padded_gather(dims: Dims, x, meta: Meta, x_perm, stream=None) -> None:
@@ -477,7 +484,7 @@ class DMoELayer:
         return y
 
     def backward(self, dy, weights, w1, w3, w2, grads=None, stream=None,
-                 events=None):
+                 events=None, recompute=False):
         d = self.dims
         if grads is None:
             fl = dict(dtype=d.torch_dtype, device=self.device)
@@ -489,7 +496,7 @@ class DMoELayer:
                                                device=self.device))
         dmoe_backward(d, dy, weights, w1, w3, w2, self.buf.meta, self.buf.saved,
                       self.buf.scratch, grads["dx"], grads["dw1"], grads["dw3"],
-                      grads["dw2"], grads["d_weights"], stream, events)
+                      grads["dw2"], grads["d_weights"], stream, events, recompute)
         return grads
 
 

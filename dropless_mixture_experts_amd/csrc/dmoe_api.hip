@@ -139,12 +139,17 @@ int dmoe_forward(const dmoe_dims* dims, const void* x, const float* weights,
   return dmoe_forward_timed(dims, x, weights, w1, w3, w2, meta, saved, y, stream, nullptr);
 }
 
-int dmoe_backward_timed(const dmoe_dims* dims, const void* dy, const float* weights,
-                        const void* w1, const void* w3, const void* w2,
-                        const dmoe_meta* meta, const dmoe_saved* saved,
-                        const dmoe_grad_scratch* scratch, void* dx, void* dw1,
-                        void* dw3, void* dw2, float* d_weights, hipStream_t stream,
-                        hipEvent_t* ev) {
+}  // extern "C"
+
+namespace {
+
+// The backward of the layer; with `recompute`, act is rebuilt from h1 and h3
+// first (event 0 then brackets that kernel and the others shift by one).
+int backward_impl(const dmoe_dims* dims, const void* dy, const float* weights, const void* w1,
+                  const void* w3, const void* w2, const dmoe_meta* meta,
+                  const dmoe_saved* saved, const dmoe_grad_scratch* scratch, void* dx,
+                  void* dw1, void* dw3, void* dw2, float* d_weights, hipStream_t stream,
+                  hipEvent_t* ev, bool recompute) {
   int rc = check_gemm_dims(dims);
   if (rc != DMOE_OK) return rc;
   if ((rc = check_meta(meta)) != DMOE_OK) return rc;
@@ -156,27 +161,47 @@ int dmoe_backward_timed(const dmoe_dims* dims, const void* dy, const float* weig
   const Shape s = shape_of(dims);
   const MetaPtrs m = meta_ptrs(meta);
   Recorder rec{ev, stream};
+  int i = 0;
+  if (recompute) {
+    // before the down dgrad, which may overwrite h1 and h3 (dh1, dh3 alias)
+    DMOE_TRY(rec(i++));
+    DMOE_TRY(dmoe::launch_recompute_act(s, saved->h1, saved->h3, m, saved->act, stream));
+  }
   // Order matters for the permitted aliases: dy_perm is last read by the
   // down-projection weight gradient, before dx_perm is written.
-  DMOE_TRY(rec(0));
+  DMOE_TRY(rec(i++));
   DMOE_TRY(dmoe::launch_scatter_backward(s, dy, saved->y_perm, weights, m,
                                          scratch->dy_perm, d_weights, stream));
-  DMOE_TRY(rec(1));
+  DMOE_TRY(rec(i++));
   DMOE_TRY(dmoe::launch_gemm_down_dgrad_wgrad_down(s, scratch->dy_perm, w2, saved->h1,
                                                    saved->h3, saved->act, m, scratch->dh1,
                                                    scratch->dh3, dw2, stream));
-  DMOE_TRY(rec(2));
+  DMOE_TRY(rec(i++));
   DMOE_TRY(dmoe::launch_gemm_up_dgrad(s, scratch->dh1, scratch->dh3, w1, w3, saved->x_perm,
                                       m, scratch->dx_perm, dw1, dw3, stream));
-  DMOE_TRY(rec(3));
+  DMOE_TRY(rec(i++));
   // the gather's backward right away, while dx_perm is still in the
   // last-level cache
   DMOE_TRY(dmoe::launch_padded_scatter(s, scratch->dx_perm, nullptr, m, dx, stream));
-  DMOE_TRY(rec(4));
+  DMOE_TRY(rec(i++));
   DMOE_TRY(dmoe::launch_gemm_wgrad_up(s, scratch->dh1, scratch->dh3, w1, w3, saved->x_perm,
                                       m, scratch->dx_perm, dw1, dw3, stream));
-  DMOE_TRY(rec(5));
+  DMOE_TRY(rec(i++));
   return DMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dmoe_backward_timed(const dmoe_dims* dims, const void* dy, const float* weights,
+                        const void* w1, const void* w3, const void* w2,
+                        const dmoe_meta* meta, const dmoe_saved* saved,
+                        const dmoe_grad_scratch* scratch, void* dx, void* dw1,
+                        void* dw3, void* dw2, float* d_weights, hipStream_t stream,
+                        hipEvent_t* ev) {
+  return backward_impl(dims, dy, weights, w1, w3, w2, meta, saved, scratch, dx, dw1, dw3, dw2,
+                       d_weights, stream, ev, false);
 }
 
 int dmoe_backward(const dmoe_dims* dims, const void* dy, const float* weights,
@@ -184,8 +209,27 @@ int dmoe_backward(const dmoe_dims* dims, const void* dy, const float* weights,
                   const dmoe_meta* meta, const dmoe_saved* saved,
                   const dmoe_grad_scratch* scratch, void* dx, void* dw1,
                   void* dw3, void* dw2, float* d_weights, hipStream_t stream) {
-  return dmoe_backward_timed(dims, dy, weights, w1, w3, w2, meta, saved, scratch, dx,
-                             dw1, dw3, dw2, d_weights, stream, nullptr);
+  return backward_impl(dims, dy, weights, w1, w3, w2, meta, saved, scratch, dx, dw1, dw3, dw2,
+                       d_weights, stream, nullptr, false);
+}
+
+int dmoe_backward_recompute_timed(const dmoe_dims* dims, const void* dy, const float* weights,
+                                  const void* w1, const void* w3, const void* w2,
+                                  const dmoe_meta* meta, const dmoe_saved* saved,
+                                  const dmoe_grad_scratch* scratch, void* dx, void* dw1,
+                                  void* dw3, void* dw2, float* d_weights, hipStream_t stream,
+                                  hipEvent_t* ev) {
+  return backward_impl(dims, dy, weights, w1, w3, w2, meta, saved, scratch, dx, dw1, dw3, dw2,
+                       d_weights, stream, ev, true);
+}
+
+int dmoe_backward_recompute(const dmoe_dims* dims, const void* dy, const float* weights,
+                            const void* w1, const void* w3, const void* w2,
+                            const dmoe_meta* meta, const dmoe_saved* saved,
+                            const dmoe_grad_scratch* scratch, void* dx, void* dw1,
+                            void* dw3, void* dw2, float* d_weights, hipStream_t stream) {
+  return backward_impl(dims, dy, weights, w1, w3, w2, meta, saved, scratch, dx, dw1, dw3, dw2,
+                       d_weights, stream, nullptr, true);
 }
 
 int dmoe_padded_gather(const dmoe_dims* dims, const void* x, const dmoe_meta* meta,

@@ -78,6 +78,13 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// The gated SiLU of the expert FFN, silu(h1) * h3 with silu(z) = z / (1 +
+// exp(-z)), on the stored (layer-dtype) values of h1 and h3.  The forward
+// epilogue and the activation recompute both call this one definition, so
+// a recomputed activation is bit-identical to the forward's.
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float gated_silu(float h1, float h3) { return silu(h1) * h3; }
+
 __device__ __forceinline__ int round_up_block(int c) {
   return ((c + kBlock - 1) / kBlock) * kBlock;
 }

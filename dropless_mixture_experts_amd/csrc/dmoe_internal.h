@@ -42,6 +42,10 @@ hipError_t launch_scatter_backward(const Shape& s, const void* dy,
                                    const MetaPtrs& m, void* dy_perm,
                                    float* d_weights, hipStream_t stream);
 
+// activation.hip: act = silu(h1) * h3 over rows [0, P) (backward recompute)
+hipError_t launch_recompute_act(const Shape& s, const void* h1, const void* h3,
+                                const MetaPtrs& m, void* act, hipStream_t stream);
+
 // router.hip
 hipError_t launch_router_forward(const Shape& s, const float* logits, float coef,
                                  int32_t* ids, float* weights, float* z, float* loss,

@@ -256,7 +256,6 @@ template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
                __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 #define GEMM_PROLOGUE                                        \
   __shared__ __attribute__((aligned(16))) char lds[2 * kLdsStage]; \
@@ -294,7 +293,7 @@ gemm_up_kernel(const T* __restrict__ x_perm, const T* __restrict__ w1,
       const f32x4 v1 = acc[i][j], v3 = acc[i + 4][j];
       f32x4 a;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) a[r] = silu(v1[r]) * v3[r];
+      for (int r = 0; r < 4; ++r) a[r] = gated_silu(v1[r], v3[r]);
       store4(h1 + p * F + f, v1);
       store4(h3 + p * F + f, v3);
       store4(act + p * F + f, a);

@@ -246,7 +246,6 @@ __device__ __forceinline__ f32x4 unpack4(const u32x2& u) {
   return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
                __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
 }
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return __builtin_bit_cast(uint16_t, from_f32<bf16>(a)) |
          ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<bf16>(b)) << 16);
@@ -445,11 +444,13 @@ struct Up {
     const int64_t o = j.u * kBlock * F + j.v * 128 + (int64_t)(wn * 64) * F + wm * 64;
     stage_half(ep.stg, acc, 0, h1 + o, F, lane);
     stage_half(ep.stg, acc, 1, h3 + o, F, lane);
+    // act from the stored (bf16-rounded) h1 and h3
     return 2 * kStoresPerBlock + stage_out(ep.stg, act + o, F, lane, [&](int ii, int jj, int g) {
-      const f32x4 v1 = quad(acc[ii][jj], g), v3 = quad(acc[2 + ii][jj], g);
+      const f32x4 v1 = unpack4(pack4(quad(acc[ii][jj], g)));
+      const f32x4 v3 = unpack4(pack4(quad(acc[2 + ii][jj], g)));
       f32x4 a;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) a[r] = silu(v1[r]) * v3[r];
+      for (int r = 0; r < 4; ++r) a[r] = gated_silu(v1[r], v3[r]);
       return pack4(a);
     });
   }

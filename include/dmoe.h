@@ -169,6 +169,20 @@ int dmoe_backward(const dmoe_dims* dims, const void* dy, const float* weights,
                   const dmoe_grad_scratch* scratch, void* dx, void* dw1,
                   void* dw3, void* dw2, float* d_weights, hipStream_t stream);
 
+/* dmoe_backward for callers that did not keep the activation: the
+ * memory-optimized MLP of the MegaBlocks chapter (§4.4) recomputes the
+ * activation in the backward instead of storing it.  saved->act is scratch
+ * on entry (its contents are ignored, so its memory may serve other work
+ * between forward and backward); the call first rebuilds act = silu(h1) *
+ * h3 from saved->h1 and saved->h3, bit-identical to the forward's, and
+ * leaves it there.  Every other buffer and every result are as for
+ * dmoe_backward, bit for bit. */
+int dmoe_backward_recompute(const dmoe_dims* dims, const void* dy, const float* weights,
+                            const void* w1, const void* w3, const void* w2,
+                            const dmoe_meta* meta, const dmoe_saved* saved,
+                            const dmoe_grad_scratch* scratch, void* dx, void* dw1,
+                            void* dw3, void* dw2, float* d_weights, hipStream_t stream);
+
 /* padded_gather alone (MegaBlocks §4.2, gather direction): for every real
  * padded row p of entry a, x_perm[p] = x[a / k]; pad rows below P are zero.
  * x [T,H], x_perm [P_max,H] of dtype; *meta from dmoe_metadata. */
@@ -222,8 +236,10 @@ int dmoe_router_backward(const dmoe_dims* dims, const float* logits,
  *                     projection, padded_scatter.
  *   backward (n = 5): scatter backward (dy_perm, d_weights), down dgrad +
  *                     gate backward together with dw2 (one launch for
- *                     bf16), up dgrad (dx_perm), gather backward (dx),
- *                     dw1 + dw3.
+ *                     bf16), up dgrad (dx_perm; for bf16 possibly with the
+ *                     first dw1/dw3 tiles), gather backward (dx), dw1 + dw3.
+ *   backward_recompute (n = 6): the activation recompute, then the five
+ *                     kernels of the backward.
  * Results are identical to the untimed calls. */
 int dmoe_metadata_timed(const dmoe_dims* dims, const int32_t* top_experts,
                         const dmoe_meta* meta, void* ws, hipStream_t stream,
@@ -238,6 +254,12 @@ int dmoe_backward_timed(const dmoe_dims* dims, const void* dy, const float* weig
                         const dmoe_grad_scratch* scratch, void* dx, void* dw1,
                         void* dw3, void* dw2, float* d_weights, hipStream_t stream,
                         hipEvent_t* events);
+int dmoe_backward_recompute_timed(const dmoe_dims* dims, const void* dy, const float* weights,
+                                  const void* w1, const void* w3, const void* w2,
+                                  const dmoe_meta* meta, const dmoe_saved* saved,
+                                  const dmoe_grad_scratch* scratch, void* dx, void* dw1,
+                                  void* dw3, void* dw2, float* d_weights, hipStream_t stream,
+                                  hipEvent_t* events);
 
 /* Static text for a dmoe_status value. */
 const char* dmoe_status_string(int status);

@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("dmoe_metadata", "dmoe_forward", "dmoe_backward", "dmoe_max_tiles",
               "dmoe_workspace_bytes", "dmoe_padded_gather", "dmoe_padded_scatter",
-              "dmoe_status_string", "dmoe_router_forward", "dmoe_router_backward"):
+              "dmoe_status_string", "dmoe_router_forward", "dmoe_router_backward",
+              "dmoe_backward_recompute", "dmoe_backward_recompute_timed"):
         assert n in names
 
 
@@ -88,6 +89,14 @@ def test_null_pointers_rejected_before_launch(lib):
     assert lib.dmoe_backward(ctypes.byref(d), p, p, p, p, p, ctypes.byref(meta),
                              ctypes.byref(saved), ctypes.byref(scratch), p, p, p,
                              p, p, None) == -1
+    for fn in (lib.dmoe_backward_recompute, lib.dmoe_backward):
+        assert fn(ctypes.byref(d), p, p, p, p, p, ctypes.byref(meta), ctypes.byref(saved),
+                  ctypes.byref(scratch), p, p, p, p, p, None) == -1
+    bad_saved = dm._Saved(*([p] * 4 + [None]))
+    good_scratch = dm._Scratch(p, p, p, p)
+    assert lib.dmoe_backward_recompute(ctypes.byref(d), p, p, p, p, p, ctypes.byref(meta),
+                                       ctypes.byref(bad_saved), ctypes.byref(good_scratch),
+                                       p, p, p, p, p, None) == -1
     assert lib.dmoe_padded_gather(ctypes.byref(d), None, ctypes.byref(meta), p,
                                   None) == -1
     assert lib.dmoe_padded_scatter(ctypes.byref(d), p, None, ctypes.byref(meta),

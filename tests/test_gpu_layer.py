@@ -11,7 +11,7 @@ import torch
 import oracle
 from workloads import CONFIGS, make_inputs, shrink
 
-from gpu_helpers import TOL, Run, assert_close, down
+from gpu_helpers import TOL, Run, assert_close, down, torch_dtype, up
 
 pytestmark = pytest.mark.gpu
 
@@ -85,6 +85,32 @@ def test_lean_buffers_match_and_runs_are_bitwise_identical():
     assert torch.equal(a.y, c.y)
     for key in OUTS:
         assert torch.equal(a.g[key], c.g[key]), key
+
+
+@pytest.mark.parametrize("name,dims,lean", [
+    ("zipf_e64_empty", dict(T=600, H=256, F=256), False),
+    ("zipf_e64_empty", dict(T=600, H=256, F=256), True),
+    ("coarse_e8", dict(T=1024, H=512, F=1024), True),
+    ("tiny_f32", {}, False),
+], ids=["zipf_empty", "zipf_empty_lean", "coarse_lean", "tiny_f32"])
+def test_backward_recompute_is_bitwise_identical(name, dims, lean):
+    """dmoe_backward_recompute with saved.act overwritten by NaN after the
+    forward gives the plain backward's results bit for bit, and rebuilds act
+    as the forward wrote it."""
+    cfg = shrink(CONFIGS[name], **dims) if dims else CONFIGS[name]
+    inp = make_inputs(cfg)
+    print(f"recompute {cfg.name} lean={lean}", flush=True)
+    a = Run(inp, lean=lean)
+    b = Run(inp, lean=lean, backward=False)
+    P = b.P
+    act_fwd = b.saved.act[:P].clone()
+    b.saved.act.fill_(float("nan"))
+    dy = up(inp.dy, torch_dtype(cfg), b.dev)
+    g = b.layer.backward(dy, b.w, b.w1, b.w3, b.w2, recompute=True)
+    torch.cuda.synchronize()
+    assert torch.equal(b.saved.act[:P], act_fwd)
+    for key in OUTS:
+        assert torch.equal(g[key], a.g[key]), key
 
 
 def _picks(inp, md, rng, n=24):
