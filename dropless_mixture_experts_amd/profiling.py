@@ -16,6 +16,16 @@
         factor corrects whatever unit or sampling the counter has.  The
         sha256 of --source is stored so that a later change of the kernel
         makes the figure stale.
+
+    python -m dropless_mixture_experts_amd.profiling counters \
+        --kernel NAME=REGEX [--kernel ...] DIR [DIR ...]
+        Medians over dispatches of every counter found in the counter CSVs
+        under the DIRs (one rocprofv3 --pmc pass each), per kernel, and the
+        derived figures: mfma = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE
+        * 128) (GRBM_GUI_ACTIVE is summed over 8 XCDs of 128 SIMDs each),
+        l2hit = TCC_HIT / (TCC_HIT + TCC_MISS), ta = TA_TA_BUSY /
+        (GRBM_GUI_ACTIVE * 32) and tcp = TCP_PENDING_STALL_CYCLES /
+        (GRBM_GUI_ACTIVE * 32) (32 CUs per XCD).
 """
 from __future__ import annotations
 
@@ -58,6 +68,35 @@ def _counter(directory: str, counter: str, kernel_re: str):
         if re.search(kernel_re, r["Kernel_Name"]):
             vals.append(float(r["Counter_Value"]))
     return vals
+
+
+def counter_medians(dirs, kernels):
+    """{name: {counter: median over dispatches}} for (name, regex) pairs."""
+    rows = [r for d in dirs for r in _rows(d, "*counter_collection.csv")]
+    out = {}
+    for name, rx in kernels:
+        per = {}
+        for r in rows:
+            if re.search(rx, r["Kernel_Name"]):
+                per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        out[name] = {c: statistics.median(v) for c, v in per.items()}
+    return out
+
+
+def derived(c: dict) -> dict:
+    def ratio(num, den, scale=1.0):
+        if num in c and den in c and c[den] > 0:
+            return c[num] / (c[den] * scale)
+        return None
+    hit, miss = c.get("TCC_HIT_sum"), c.get("TCC_MISS_sum")
+    return {
+        "mfma": ratio("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", 128.0),
+        "l2hit": hit / (hit + miss) if hit is not None and miss is not None and hit + miss > 0
+        else None,
+        "ta": ratio("TA_TA_BUSY_sum", "GRBM_GUI_ACTIVE", 32.0),
+        "tcp": ratio("TCP_PENDING_STALL_CYCLES_sum", "GRBM_GUI_ACTIVE", 32.0),
+        "lds_bankcf": c.get("SQ_LDS_BANK_CONFLICT"),
+    }
 
 
 def traffic(args) -> dict:
@@ -109,7 +148,24 @@ def main(argv=None):
     t.add_argument("--copy-bytes", type=float, required=True)
     t.add_argument("--source")
     t.add_argument("--out")
+    c = sub.add_parser("counters")
+    c.add_argument("--kernel", action="append", required=True, help="NAME=REGEX")
+    c.add_argument("dirs", nargs="+")
     a = ap.parse_args(argv)
+    if a.cmd == "counters":
+        kernels = [tuple(k.split("=", 1)) for k in a.kernel]
+        med = counter_medians(a.dirs, kernels)
+        cols = ("mfma", "l2hit", "ta", "tcp", "lds_bankcf")
+        print(f"{'kernel':28s} " + " ".join(f"{c:>10s}" for c in cols))
+        for name, _ in kernels:
+            d = derived(med[name])
+            cells = []
+            for col in cols:
+                v = d[col]
+                cells.append(f"{'-':>10s}" if v is None else
+                             (f"{v:10.0f}" if col == "lds_bankcf" else f"{v:10.3f}"))
+            print(f"{name:28s} " + " ".join(cells))
+        return 0
     if a.cmd == "stats":
         st = kernel_stats(a.dir)
         print(f"{'kernel':72s} {'calls':>6s} {'total_us':>11s} {'avg_us':>10s}")
