@@ -25,6 +25,9 @@
 //     buffer_load ... lds (16 bytes per lane straight into LDS, no
 //     registers).  Each wave fills whole 1 KB LDS blocks; the global address
 //     of every lane is chosen so that the LDS image comes out swizzled.
+//   * Ping-pong: the two waves of a SIMD run half a phase apart, one issuing
+//     the MFMAs of two k-fragments while the other reads its next two from
+//     LDS, swapping at a barrier (Pipe::run).
 //   * An operand whose source has K contiguous ("direct") is kept as
 //     [row][64 k] (128-byte rows); its 16-byte chunk c of row r sits at chunk
 //     c ^ ((r & 7) ^ ((r >> 3) & 1)) and is read with ds_read_b128.
@@ -360,6 +363,12 @@ struct Job {
 };
 
 constexpr int kGroupM = 8;
+
+// k-fragments per phase of the main loop: two (16 MFMAs per wave) measured
+// faster than one; four would need four fragment sets, more VGPRs than two
+// waves per SIMD leave.
+constexpr int kPhaseFrags = 2;
+static_assert(kPhaseFrags == 1 || kPhaseFrags == 2, "one or two fragments per phase");
 
 // Row-tiled products: (m, n) for logical index L over MT x NT tiles, in
 // groups of kGroupM row tiles walked column by column, so that concurrent
@@ -784,22 +793,27 @@ struct Pipe {
   }
 
   // acc += the product of tile `cur`.  primed: its steps 0 and 1 are already
-  // in flight.  Each K step is four 16-wide k-fragments; while the MFMAs of
-  // one fragment run, the LDS reads of the next are in flight.  Before the
-  // last fragment of step s: wait for the DMA of step s+1, barrier, start the
-  // DMA of step s+2 into the stage of step s (nobody reads it any more) --
-  // past the end of the tile that is step 0 of the next tile -- and read the
-  // first fragment of step s+1.  Ends with a barrier and no LDS read in
-  // flight.  Returns whether step 0 of `nxt` was started (by next(gs), which
-  // may belong to another product).  When primed, the waits for steps 0 and 1
-  // let w0 and w1 younger vector-memory operations (the DMA of step 1, the
-  // previous tile's stores) stay in flight.
+  // in flight; otherwise they are started here.  The two waves of each SIMD
+  // (wm = 0 and wm = 1 share one) run half a phase apart: while one issues
+  // the MFMAs of two k-fragments, the other reads its next two fragments
+  // from LDS, and they swap at a barrier, so the matrix core and the LDS
+  // are each kept busy by one wave at a time.  With chunk c = 2s + h (k-
+  // fragments 2h, 2h + 1 of step s), group 0 computes c in phase 2c and
+  // reads c + 1 in phase 2c + 1; group 1 reads c in phase 2c and computes it
+  // in phase 2c + 1.  Stage s is last read in phase 4s + 2; at its end every
+  // wave waits for its DMA of step s + 1, and after that barrier each wave
+  // starts its DMA of step s + 2 -- past the end of the tile, step 0 of
+  // `nxt`, by next(gs), which may belong to another product -- in its next
+  // read phase.  Every wave runs the same barriers: one before phase 0 and
+  // one after each phase.  Returns whether step 0 of `nxt` was started.
+  // When primed, the waits for steps 0 and 1 let w0 and w1 younger vector-
+  // memory operations (the DMA of step 1, the previous tile's stores) stay
+  // in flight.
   template <class Next>
   __device__ __forceinline__ bool run(Acc& acc, const Job& cur, const Job& nxt, bool primed,
-                                      int w0, int w1, Next&& next) {
+                                         int w0, int w1, Next&& next) {
     const int n = cur.steps;
     if (n <= 0) return false;
-    const bool work = cur.fb || wn < 2;     // this wave has B rows
     if (!primed) {
       issue_step(cur, 0, g);
       if (n > 1) issue_step(cur, 1, g + 1);
@@ -808,37 +822,78 @@ struct Pipe {
     }
     wait_vm_n(w0);                          // step 0 landed
     barrier();
+    // one straight-line loop per group; s_barrier counts arrivals, not
+    // program locations, so the two loops meet at their matching barriers
+    if (wm == 0) group_loop<true>(acc, cur, nxt, w1, next);
+    else group_loop<false>(acc, cur, nxt, w1, next);
+    g += n;
+    return n >= 2 && nxt.steps > 0;   // step 0 of nxt went out with step n
+  }
+
+  // The loop of one group (G0: wm == 0), kPhaseFrags k-fragments per phase.
+  template <bool G0, class Next>
+  __device__ __forceinline__ void group_loop(Acc& acc, const Job& cur, const Job& nxt, int w1,
+                                             Next&& next) {
+    constexpr int PF = kPhaseFrags;          // fragments per phase
+    constexpr int NP = 4 / PF;               // phases of each kind per step
+    const int n = cur.steps;
+    const bool work = cur.fb || wn < 2;
+    // the DMA of step t >= 2 (or of the next tile's step 0 when t == n)
+    const auto dma = [&](int t) {
+      if (t < n) issue_step(cur, t, g + t);
+      else if (t == n && nxt.steps > 0) next(g + t);
+    };
     Frags f[2];
-    if (work) load_frags<K::ATR, K::BTR>(f[0], stage_ptr(g), 0, wm, wn, lane);
-    bool next_started = false;
+    const auto load = [&](const char* st, int q) {   // fragments of chunk q of a step
+      if (work)
+#pragma unroll
+        for (int i = 0; i < PF; ++i)
+          load_frags<K::ATR, K::BTR>(f[(q * PF + i) & 1], st, q * PF + i, wm, wn, lane);
+    };
+    const auto compute = [&](int q) {
+      if (work) {
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int i = 0; i < PF; ++i) mma(acc, f[(q * PF + i) & 1]);
+        __builtin_amdgcn_s_setprio(0);
+      }
+    };
+    if (G0) load(stage_ptr(g), 0);
     for (int s = 0; s < n; ++s) {
       const char* cst = stage_ptr(g + s);
 #pragma unroll
-      for (int kf = 0; kf < 4; ++kf) {
+      for (int q = 0; q < NP; ++q) {
+        // group 0 computes chunk q, group 1 reads it
         sched_fence();
-        if (kf < 3) {
-          if (work) load_frags<K::ATR, K::BTR>(f[(kf + 1) & 1], cst, kf + 1, wm, wn, lane);
-        } else if (s + 1 < n) {
-          // step s+1 landed (after step 0 only the previous tile's stores
-          // may still be younger)
-          if (s == 0) wait_vm_n(w1); else wait_vm<0>();
-          barrier();
-          if (s + 2 < n) {
-            issue_step(cur, s + 2, g + s + 2);
-          } else if (nxt.steps > 0) {       // s + 2 == n
-            next(g + s + 2);
-            next_started = true;
-          }
-          if (work) load_frags<K::ATR, K::BTR>(f[0], stage_ptr(g + s + 1), 0, wm, wn, lane);
+        if (G0) {
+          compute(q);
+        } else {
+          if (q == 0 && s > 0) dma(s + 1);
+          load(cst, q);
+          wait_lds();
         }
-        if (work) mma(acc, f[kf & 1]);
+        sched_fence();
+        if (q == NP - 1 && s + 1 < n) {     // the last read of step s: step s + 1 landed
+          if (s == 0) wait_vm_n(w1); else wait_vm<0>();
+        }
+        barrier();
+        // group 0 reads the next chunk, group 1 computes chunk q
+        sched_fence();
+        if (G0) {
+          if (q < NP - 1) {
+            load(cst, q + 1);
+          } else if (s + 1 < n) {
+            dma(s + 2);
+            load(stage_ptr(g + s + 1), 0);
+          }
+          wait_lds();
+        } else {
+          compute(q);
+        }
+        sched_fence();
+        barrier();
       }
     }
-    sched_fence();
-    wait_lds();
-    barrier();
-    g += n;
-    return next_started;
   }
 };
 
