@@ -368,6 +368,7 @@ constexpr int kGroupM = 8;
 // faster than one; four would need four fragment sets, more VGPRs than two
 // waves per SIMD leave.
 constexpr int kPhaseFrags = 2;
+
 static_assert(kPhaseFrags == 1 || kPhaseFrags == 2, "one or two fragments per phase");
 
 // Row-tiled products: (m, n) for logical index L over MT x NT tiles, in
@@ -792,45 +793,22 @@ struct Pipe {
     issue<K::BTR>(b0, b1, k.ldb(), db, ks, w, st + kReg);
   }
 
-  // acc += the product of tile `cur`.  primed: its steps 0 and 1 are already
-  // in flight; otherwise they are started here.  The two waves of each SIMD
+  // The K loop of one tile for one group of waves (G0: wm == 0), after the
+  // barrier that follows the landing of step 0.  The two waves of each SIMD
   // (wm = 0 and wm = 1 share one) run half a phase apart: while one issues
   // the MFMAs of two k-fragments, the other reads its next two fragments
-  // from LDS, and they swap at a barrier, so the matrix core and the LDS
-  // are each kept busy by one wave at a time.  With chunk c = 2s + h (k-
+  // from LDS, and they swap at a barrier, so the matrix core and the LDS are
+  // each kept busy by one wave at a time.  With chunk c = 2s + h (k-
   // fragments 2h, 2h + 1 of step s), group 0 computes c in phase 2c and
   // reads c + 1 in phase 2c + 1; group 1 reads c in phase 2c and computes it
   // in phase 2c + 1.  Stage s is last read in phase 4s + 2; at its end every
-  // wave waits for its DMA of step s + 1, and after that barrier each wave
-  // starts its DMA of step s + 2 -- past the end of the tile, step 0 of
-  // `nxt`, by next(gs), which may belong to another product -- in its next
-  // read phase.  Every wave runs the same barriers: one before phase 0 and
-  // one after each phase.  Returns whether step 0 of `nxt` was started.
-  // When primed, the waits for steps 0 and 1 let w0 and w1 younger vector-
-  // memory operations (the DMA of step 1, the previous tile's stores) stay
-  // in flight.
-  template <class Next>
-  __device__ __forceinline__ bool run(Acc& acc, const Job& cur, const Job& nxt, bool primed,
-                                         int w0, int w1, Next&& next) {
-    const int n = cur.steps;
-    if (n <= 0) return false;
-    if (!primed) {
-      issue_step(cur, 0, g);
-      if (n > 1) issue_step(cur, 1, g + 1);
-      w0 = n > 1 ? kDmaPerStep : 0;
-      w1 = 0;
-    }
-    wait_vm_n(w0);                          // step 0 landed
-    barrier();
-    // one straight-line loop per group; s_barrier counts arrivals, not
-    // program locations, so the two loops meet at their matching barriers
-    if (wm == 0) group_loop<true>(acc, cur, nxt, w1, next);
-    else group_loop<false>(acc, cur, nxt, w1, next);
-    g += n;
-    return n >= 2 && nxt.steps > 0;   // step 0 of nxt went out with step n
-  }
-
-  // The loop of one group (G0: wm == 0), kPhaseFrags k-fragments per phase.
+  // wave waits for its DMA of step s + 1 (for s = 0 letting w1 younger
+  // operations stay in flight), and after that barrier each wave starts its
+  // DMA of step s + 2 -- past the end of the tile, step 0 of `nxt`, by
+  // next(gs), which may belong to another product -- in its next read
+  // phase.  Both groups run the same barriers: one after every phase but
+  // the last, so group 0 goes on to its stores while group 1 runs the last
+  // phase's MFMAs.  Group 0 reads chunk 0 first (its phase 0 computes it).
   template <bool G0, class Next>
   __device__ __forceinline__ void group_loop(Acc& acc, const Job& cur, const Job& nxt, int w1,
                                              Next&& next) {
@@ -891,11 +869,110 @@ struct Pipe {
           compute(q);
         }
         sched_fence();
-        barrier();
+        if (s + 1 < n || q + 1 < NP) barrier();
       }
     }
   }
 };
+
+// The products of one launch as the engine sees them: K1 alone (kTwo =
+// false), or K1 and K2 chosen per tile by Job::kind.
+template <class K1, class K2, bool kTwo>
+struct Ops {
+  const K1& k1;
+  const K2& k2;
+  Pipe<K1>& p1;
+  Pipe<K2>& p2;
+  __device__ __forceinline__ bool first(const Job& j) const { return !kTwo || j.kind == 0; }
+  __device__ __forceinline__ void issue(const Job& j, int s, int gs) const {
+    if (first(j)) p1.issue_step(j, s, gs);
+    else p2.issue_step(j, s, gs);
+  }
+  // whether the tile's epilogue reads through its free-stage blocks, so that
+  // step 1 of the next tile (which lands there) must wait for it
+  __device__ __forceinline__ bool late(const Job& j) const {
+    return first(j) ? K1::kLateStep1 : K2::kLateStep1;
+  }
+  __device__ __forceinline__ int epilogue(const Job& j, const Acc& acc, const Epi& ep) const {
+    return first(j) ? k1.epilogue(j, acc, ep) : k2.epilogue(j, acc, ep);
+  }
+  template <bool G0, class Next>
+  __device__ __forceinline__ void loop(Acc& acc, const Job& j, const Job& nxt, int g, int w1,
+                                       Next&& next) {
+    if (first(j)) {
+      p1.g = g;
+      p1.template group_loop<G0>(acc, j, nxt, w1, next);
+    } else {
+      p2.g = g;
+      p2.template group_loop<G0>(acc, j, nxt, w1, next);
+    }
+  }
+};
+
+// This block's `total` tiles (tile_of(i)).  Steps 0 and 1 of the next tile
+// are fetched while the current one finishes and stores, so neither a
+// block's start nor the epilogue leaves the next tile's loads unissued.
+// Group 0 (wm == 0) stores a tile while group 1 runs the MFMAs of its last
+// phase.  Tiles without K steps (empty experts) run no barrier and store
+// zeros.  Every barrier is reached by all waves: one after the landing of
+// step 0 and 4 n - 1 in the K loop of each tile with n > 0 steps.  (Keeping
+// group 1's accumulators until the next tile's first phase, to store them
+// under group 0's MFMAs, measured 11% slower: the stores take several
+// phases, so group 0 waits for them at the next barrier.)
+template <class O, class TileOf>
+__device__ __forceinline__ void engine(O& o, int total, TileOf&& tile_of, char* lds,
+                                       uint32_t lbase, char* stg, int w) {
+  const auto epi_at = [&](int g) {   // this wave's blocks of the free stage after step g - 1
+    const int fs = ((g + 1) & 1) * kStage + 4 * w * 1024;
+    return Epi{stg, lds + fs, lds + fs + kReg, lbase + fs, lbase + fs + kReg};
+  };
+  int g = 0;                 // K steps run so far (selects the stage)
+  Job cur = tile_of(0);
+  bool primed = false;       // steps 0 and (if it has one) 1 of cur are in flight
+  int w0 = 0, w1 = 0;        // younger vm operations allowed at the waits for steps 0, 1
+  for (int i = 0;; ++i) {
+    Job nxt;
+    nxt.steps = 0;
+    nxt.kind = 0;
+    if (i + 1 < total) nxt = tile_of(i + 1);
+    const int n = cur.steps;
+    Acc acc;
+    zero(acc);
+    bool started = false;
+    if (n > 0) {
+      if (!primed) {
+        o.issue(cur, 0, g);
+        if (n > 1) o.issue(cur, 1, g + 1);
+        w0 = n > 1 ? kDmaPerStep : 0;
+        w1 = 0;
+      }
+      wait_vm_n(w0);                       // step 0 landed
+      barrier();
+      const auto next = [&](int gs) { o.issue(nxt, 0, gs); };
+      if (w < 4) o.template loop<true>(acc, cur, nxt, g, w1, next);
+      else o.template loop<false>(acc, cur, nxt, g, w1, next);
+      g += n;
+      started = n >= 2 && nxt.steps > 0;
+    }
+    primed = started;
+    // step 1 of the next tile goes into the stage the last K step used (all
+    // its reads are done); before the stores unless the epilogue reads
+    // through that stage, so that the stores drain while the next tile runs
+    const bool step1 = primed && nxt.steps > 1;
+    const bool lt = o.late(cur);
+    if (!lt && step1) o.issue(nxt, 1, g + 1);
+    const int nst = o.epilogue(cur, acc, epi_at(g));
+    if (i + 1 >= total) break;
+    if (lt && step1) {
+      wait_lds();                          // this wave's free-stage reads are done
+      o.issue(nxt, 1, g + 1);
+    }
+    // in flight, oldest first: step 0, [step 1,] the stores [, step 1]
+    w0 = (step1 ? kDmaPerStep : 0) + nst;
+    w1 = lt ? 0 : nst;
+    cur = nxt;
+  }
+}
 
 // One block per CU.  XCD x = blockIdx % 8 owns the logical tiles [lo, hi)
 // that the product assigns it; its S blocks take them round-robin, so at any
@@ -904,15 +981,17 @@ struct Pipe {
 template <class K>
 __device__ __forceinline__ void persistent(const K& k) {
   __shared__ __attribute__((aligned(16))) char lds[kLds];
+  static_assert(K::kLateStep1 || !K::kUsesFreeStage, "the free stage is refilled before the epilogue");
   const int S = (int)(gridDim.x / 8);
   const int x = (int)(blockIdx.x % 8), r = (int)(blockIdx.x / 8);
   int lo, hi;
   k.xcd_range(x, lo, hi);
   lo = (int)uniform((uint32_t)lo);
   hi = (int)uniform((uint32_t)hi);
-  int L = lo + r;
-  if (L >= hi) return;
-  Pipe<K> p{k, lds, uniform(lds_addr(lds)), 0};
+  const int total = hi - lo > r ? (hi - lo - r + S - 1) / S : 0;
+  if (total <= 0) return;
+  const uint32_t lbase = uniform(lds_addr(lds));
+  Pipe<K> p{k, lds, lbase, 0};
   p.lane = threadIdx.x & 63;
   p.w = (int)uniform(threadIdx.x >> 6);
   p.wm = p.w >> 2;
@@ -920,38 +999,14 @@ __device__ __forceinline__ void persistent(const K& k) {
   p.da.init(k.lda(), p.lane);
   p.db.init(k.ldb(), p.lane);
   char* const stg = lds + 2 * kStage + p.w * kStgWave;
-  static_assert(K::kLateStep1 || !K::kUsesFreeStage, "the free stage is refilled before the epilogue");
-  Job cur;
-  k.tile(L, cur);
-  bool primed = false;
-  int w0 = 0, w1 = 0;
-  for (;;) {
-    const int Ln = L + S;
-    Job nxt;
-    nxt.steps = 0;
-    if (Ln < hi) k.tile(Ln, nxt);
-    Acc acc;
-    zero(acc);
-    primed = p.run(acc, cur, nxt, primed, w0, w1, [&](int gs) { p.issue_step(nxt, 0, gs); });
-    // step 1 of the next tile goes into the stage the last K step used (all
-    // its reads are done); it is started before the stores unless the
-    // epilogue loads, so that the stores can drain while the next tile runs
-    const bool step1 = primed && nxt.steps > 1;
-    if (!K::kLateStep1 && step1) p.issue_step(nxt, 1, p.g + 1);
-    const int fs = ((p.g + 1) & 1) * kStage + 4 * p.w * 1024;   // free stage, this wave's blocks
-    const int nst = k.epilogue(cur, acc, Epi{stg, lds + fs, lds + fs + kReg, p.lbase + fs,
-                                             p.lbase + fs + kReg});
-    if (Ln >= hi) break;
-    if (K::kLateStep1 && step1) {
-      wait_lds();   // this wave's reads of its free-stage blocks are done
-      p.issue_step(nxt, 1, p.g + 1);
-    }
-    // in flight, oldest first: step 0, [step 1,] the stores [, step 1]
-    w0 = (step1 ? kDmaPerStep : 0) + nst;
-    w1 = K::kLateStep1 ? 0 : nst;
-    cur = nxt;
-    L = Ln;
-  }
+  Ops<K, K, false> o{k, k, p, p};
+  const auto tile_of = [&](int i) {
+    Job j;
+    k.tile(lo + r + i * S, j);
+    j.kind = 0;
+    return j;
+  };
+  engine(o, total, tile_of, lds, lbase, stg, p.w);
 }
 
 
@@ -1071,50 +1126,13 @@ __device__ __forceinline__ void persistent_dual(const K1& k1, const K2& k2, bool
   p2.da.init(k2.lda(), lane);
   p2.db.init(k2.ldb(), lane);
   char* const stg = lds + 2 * kStage + w * kStgWave;
-  // kRest runs K2 tiles only: the K1 paths are not compiled in
-  constexpr bool kOnly2 = M == kRest;
-  const auto issue = [&](const Job& j, int s, int gs) {
-    if (!kOnly2 && j.kind == 0) p1.issue_step(j, s, gs);
-    else p2.issue_step(j, s, gs);
-  };
-  int g = 0;   // K steps run so far (selects the stage)
-  Job cur = sc.job(k1, k2, 0);
-  bool primed = false;
-  int w0 = 0, w1 = 0;
-  for (int i = 0;; ++i) {
-    Job nxt;
-    nxt.steps = 0;
-    nxt.kind = 0;
-    if (i + 1 < total) nxt = sc.job(k1, k2, i + 1);
-    Acc acc;
-    zero(acc);
-    const auto next = [&](int gs) { issue(nxt, 0, gs); };
-    if (!kOnly2 && cur.kind == 0) {
-      p1.g = g;
-      primed = p1.run(acc, cur, nxt, primed, w0, w1, next);
-      g = p1.g;
-    } else {
-      p2.g = g;
-      primed = p2.run(acc, cur, nxt, primed, w0, w1, next);
-      g = p2.g;
-    }
-    // as in persistent(): step 1 of the next tile before the stores, unless
-    // this tile's epilogue uses the free stage
-    const bool late = (!kOnly2 && cur.kind == 0) ? K1::kLateStep1 : K2::kLateStep1;
-    const bool step1 = primed && nxt.steps > 1;
-    if (!late && step1) issue(nxt, 1, g + 1);
-    const int fs = ((g + 1) & 1) * kStage + 4 * w * 1024;
-    const Epi ep{stg, lds + fs, lds + fs + kReg, lbase + fs, lbase + fs + kReg};
-    const int nst =
-        (!kOnly2 && cur.kind == 0) ? k1.epilogue(cur, acc, ep) : k2.epilogue(cur, acc, ep);
-    if (i + 1 >= total) break;
-    if (late && step1) {
-      wait_lds();
-      issue(nxt, 1, g + 1);
-    }
-    w0 = (step1 ? kDmaPerStep : 0) + nst;
-    w1 = late ? 0 : nst;
-    cur = nxt;
+  const auto tile_of = [&](int i) { return sc.job(k1, k2, i); };
+  if constexpr (M == kRest) {   // K2 tiles only
+    Ops<K2, K2, false> o{k2, k2, p2, p2};
+    engine(o, total, tile_of, lds, lbase, stg, w);
+  } else {
+    Ops<K1, K2, true> o{k1, k2, p1, p2};
+    engine(o, total, tile_of, lds, lbase, stg, w);
   }
 }
 
