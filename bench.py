@@ -253,17 +253,28 @@ def main():
     gs_bytes = sum(work[n][1] for n in gs)
     dom = max(names, key=lambda n: per[n])
     fl, by = work[dom]
-    if fl:
-        achieved = fl / (per[dom] * 1e-3) / 1e12
+    # the binding roof at the kernel's arithmetic intensity (algorithmic FLOP
+    # per unique byte): the matrix cores above the ridge, HBM below it
+    ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    intensity = fl / by if fl else 0.0
+    t_dom = per[dom] * 1e-3
+    if fl and intensity >= ridge:
+        achieved = fl / t_dom / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": None}
     else:
-        achieved = by / (per[dom] * 1e-3) / 1e9
+        achieved = by / t_dom / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
-    roof["algorithmic_per_launch"] = fl if fl else by
+    roof["intensity_flop_per_byte"] = round(intensity, 1)
+    roof["ridge_flop_per_byte"] = round(ridge, 1)
+    if fl:
+        roof["tflops"] = round(fl / t_dom / 1e12, 1)
+        roof["tflops_frac_of_mfma_peak"] = round(fl / t_dom / 1e12 / peak, 4)
+    roof["algorithmic_bytes_per_launch"] = by
+    roof["algorithmic_flop_per_launch"] = fl
     roof["traffic"] = committed_traffic(dom, cfg.name)
 
     out = {
