@@ -31,6 +31,9 @@ SMALL = [
     shrink(CONFIGS["fine_e64"], T=128, H=256, F=384, E=1, k=1),    # exactly one tile
     shrink(CONFIGS["sparse_e256"], T=16, H=128, F=128),            # most experts empty
     shrink(CONFIGS["tiny_f32"], T=129, H=384, F=384, E=3, k=1),    # fp32, 2 tiles + tail
+    # 256 expected up-dgrad row tiles (one whole round of 256 CUs): the plain
+    # up-dgrad launch, not the one that fills its last round with dw1/dw3 tiles
+    shrink(CONFIGS["fine_e64"], T=3584, H=2048, F=128, E=8, k=2),
 ]
 
 
