@@ -113,6 +113,41 @@ def cpu_baseline(inp, budget_s=30.0):
                        f"host os.cpu_count()={os.cpu_count()}")}
 
 
+def gpu_sclk_mhz():
+    """The shader clock the driver reports as current (sysfs pp_dpm_sclk, the
+    level marked '*'), or None where it is not readable."""
+    import glob
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            for line in open(f):
+                if "*" in line:
+                    return int(line.split(":")[1].strip().lower().split("mhz")[0])
+        except (OSError, ValueError, IndexError):
+            continue
+    return None
+
+
+def cold_steps(step, stream, n, flush_mb=512):
+    """Median milliseconds of n steps, each started after a flush_mb write
+    that evicts the last-level cache (256 MB), so that every input and weight
+    comes from HBM.  The flush sits between the two events, not inside them."""
+    import statistics
+    import torch
+    scratch = torch.empty(flush_mb << 18, dtype=torch.float32, device=stream.device)
+    times = []
+    for _ in range(n):
+        scratch.fill_(1.0)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del scratch
+    return statistics.median(times)
+
+
 def router_time(dm, cfg, dev, stream, steps):
     """Mean microseconds of the router's forward (top-k, softmax, z-loss) and
     backward on this workload's seeded logits.  Reported beside the layer's
@@ -219,6 +254,13 @@ def main():
     t0 = time.perf_counter()
     for i in range(K):
         step(evs[i])
+    sclk = []                      # sampled every ~1 ms while the queued steps run
+    while not stream.query() and len(sclk) < 1000:
+        c = gpu_sclk_mhz()
+        if c is None:
+            break
+        sclk.append(c)
+        time.sleep(0.001)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -273,6 +315,12 @@ def main():
     if fl:
         roof["tflops"] = round(fl / t_dom / 1e12, 1)
         roof["tflops_frac_of_mfma_peak"] = round(fl / t_dom / 1e12 / peak, 4)
+    if fl and sclk:
+        # the published peak assumes the 2.4 GHz top clock; the matrix cores
+        # scale with the clock the chip holds under this load
+        at_clk = peak * (sorted(sclk)[len(sclk) // 2] / 2400.0)
+        roof["mfma_peak_at_median_sclk"] = round(at_clk, 1)
+        roof["tflops_frac_at_median_sclk"] = round(fl / t_dom / 1e12 / at_clk, 4)
     roof["algorithmic_bytes_per_launch"] = by
     roof["algorithmic_flop_per_launch"] = fl
     roof["traffic"] = committed_traffic(dom, cfg.name)
@@ -297,10 +345,17 @@ def main():
         "gemm_executed_frac_peak": round(executed_flop / (gemm_ms * 1e-3) / 1e12 / peak, 4),
         "gather_scatter_frac_hbm": round(gs_bytes / (gs_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "metadata_us": round(1e3 * sum(per[n] for n in META_KERNELS), 1),
+        "sclk_mhz_during_timing": ({"samples": len(sclk), "min": min(sclk),
+                                    "median": sorted(sclk)[len(sclk) // 2],
+                                    "max": max(sclk)} if sclk else None),
         "roofline": roof,
         "kernels": table,
     }
     out["router_us"] = router_time(dm, cfg, dev, stream, K)
+    cold = cold_steps(step, stream, min(K, 10))
+    out["cold_cache"] = {"ms_per_step_median": round(cold, 4),
+                         "tokens_s": round(cfg.T / (cold * 1e-3), 1),
+                         "note": "last-level cache flushed by a 512 MB write before each step"}
     if args.kernels:
         for n in names:
             print(f"{n:22s} {table[n]}", file=sys.stderr)

@@ -72,7 +72,7 @@ padded_gather_kernel(const T* __restrict__ x, int64_t ntok, int64_t H, int k, in
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t v = v0 + u * kWave;
-      if (v < vecs) r[u] = ld16(src + v * 16);
+      if (v < vecs) r[u] = ld16_nt(src + v * 16);
     }
     for (int j = 0; j < k; ++j) {
       const int row = rows[j];
@@ -122,8 +122,8 @@ padded_scatter_kernel(const T* __restrict__ src_perm,
         live[u] = r >= 0;          // -1: padding of the unrolled loop, or an invalid id
         wj[u] = wts && live[u] ? wts[j] : 1.f;
         const char* row = src + (int64_t)(live[u] ? r : 0) * rowb;
-        d0[u] = live[u] ? ld16(row + v0 * 16) : u32x4{0u, 0u, 0u, 0u};
-        d1[u] = live[u] && has1 ? ld16(row + v1 * 16) : u32x4{0u, 0u, 0u, 0u};
+        d0[u] = live[u] ? ld16_nt(row + v0 * 16) : u32x4{0u, 0u, 0u, 0u};
+        d1[u] = live[u] && has1 ? ld16_nt(row + v1 * 16) : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
@@ -180,7 +180,7 @@ scatter_backward_kernel(const T* __restrict__ dy, const T* __restrict__ y_perm,
   for (int64_t v = lane; v < vecs; v += kWave) {
     float gf[V::N], yf[V::N], o[V::N];
     V::unpack(ld16(g + v * 16), gf);
-    V::unpack(ld16(yp + v * 16), yf);
+    V::unpack(ld16_nt(yp + v * 16), yf);
 #pragma unroll
     for (int i = 0; i < V::N; ++i) {
       o[i] = wt * gf[i];
