@@ -88,7 +88,9 @@ padded_gather_kernel(const T* __restrict__ x, int64_t ntok, int64_t H, int k, in
 }
 
 // out[t] = sum_j w[t,j] * src_perm[row_of_entry[t*k+j]]  (w = 1 if null).
-// Two 16-byte columns per lane and pass, so 16 row reads are in flight.
+// Four 16-byte columns per lane and pass (a whole 4 KB bf16 row per wave) and
+// rows in groups of four, so 16 loads are in flight and each row is read in
+// one pass rather than in halves.
 template <typename T>
 __global__ void __launch_bounds__(kRowsPerBlock * kWave)
 padded_scatter_kernel(const T* __restrict__ src_perm,
@@ -105,42 +107,46 @@ padded_scatter_kernel(const T* __restrict__ src_perm,
   const int32_t* rows = row_of_entry + t * k;
   const float* wts = weights ? weights + t * k : nullptr;
   char* dst = reinterpret_cast<char*>(out + t * H);
-  for (int64_t v0 = lane; v0 < vecs; v0 += 2 * kWave) {
-    const int64_t v1 = v0 + kWave;
-    const bool has1 = v1 < vecs;
-    float acc0[V::N], acc1[V::N];
+  for (int64_t v0 = lane; v0 < vecs; v0 += 4 * kWave) {
+    bool has[4];
+    float acc[4][V::N];
 #pragma unroll
-    for (int i = 0; i < V::N; ++i) acc0[i] = acc1[i] = 0.f;
-    for (int j0 = 0; j0 < k; j0 += 8) {
-      u32x4 d0[8], d1[8];
-      float wj[8];
-      bool live[8];
+    for (int c = 0; c < 4; ++c) {
+      has[c] = v0 + c * kWave < vecs;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int i = 0; i < V::N; ++i) acc[c][i] = 0.f;
+    }
+    for (int j0 = 0; j0 < k; j0 += 4) {
+      u32x4 d[4][4];
+      float wj[4];
+      bool live[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
         const int j = j0 + u;
         const int r = j < k ? rows[j] : -1;
-        live[u] = r >= 0;          // -1: padding of the unrolled loop, or an invalid id
+        live[u] = r >= 0;
         wj[u] = wts && live[u] ? wts[j] : 1.f;
         const char* row = src + (int64_t)(live[u] ? r : 0) * rowb;
-        d0[u] = live[u] ? ld16_nt(row + v0 * 16) : u32x4{0u, 0u, 0u, 0u};
-        d1[u] = live[u] && has1 ? ld16_nt(row + v1 * 16) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          d[u][c] = live[u] && has[c] ? ld16_nt(row + (v0 + c * kWave) * 16) : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 4; ++u) {
         if (live[u]) {
-          float f0[V::N], f1[V::N];
-          V::unpack(d0[u], f0);
-          V::unpack(d1[u], f1);
 #pragma unroll
-          for (int i = 0; i < V::N; ++i) {
-            acc0[i] = __builtin_fmaf(wj[u], f0[i], acc0[i]);
-            acc1[i] = __builtin_fmaf(wj[u], f1[i], acc1[i]);
+          for (int c = 0; c < 4; ++c) {
+            float f[V::N];
+            V::unpack(d[u][c], f);
+#pragma unroll
+            for (int i = 0; i < V::N; ++i) acc[c][i] = __builtin_fmaf(wj[u], f[i], acc[c][i]);
           }
         }
       }
     }
-    st16(dst + v0 * 16, V::pack(acc0));
-    if (has1) st16(dst + v1 * 16, V::pack(acc1));
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (has[c]) st16(dst + (v0 + c * kWave) * 16, V::pack(acc[c]));
   }
 }
 
