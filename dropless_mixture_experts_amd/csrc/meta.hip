@@ -32,6 +32,7 @@ namespace dmoe {
 
 constexpr int kMetaWaves = 4;  // waves (chunks) per workgroup
 constexpr int kScanThreads = 1024;
+constexpr int kScanBatch = 8;   // chunk counts a scan thread loads at once
 
 __global__ void __launch_bounds__(kMetaWaves * kWave)
 meta_hist_kernel(const int32_t* __restrict__ ids, int64_t n, int64_t chunk,
@@ -87,9 +88,18 @@ meta_scan_kernel(int32_t* __restrict__ hist, const int32_t* __restrict__ err,
   const int c0 = min(nchunks, seg * seg_len);
   const int c1 = min(nchunks, c0 + seg_len);
 
+  // Batches of kScanBatch independent loads, so a thread waits for memory
+  // once per batch rather than once per chunk.
   int sum = 0;
   if (e < E)
-    for (int c = c0; c < c1; ++c) sum += hist[(int64_t)c * E + e];
+    for (int cb = c0; cb < c1; cb += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i)
+        v[i] = cb + i < c1 ? hist[(int64_t)(cb + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) sum += v[i];
+    }
   seg_tot[tid] = sum;
   if (tid == 0) bad_s = 0;
   __syncthreads();
@@ -155,11 +165,17 @@ meta_scan_kernel(int32_t* __restrict__ hist, const int32_t* __restrict__ err,
   if (e < E) {
     int run = start_s[e];
     for (int s = 0; s < seg; ++s) run += seg_tot[s * Ecap + e];
-    for (int c = c0; c < c1; ++c) {
-      const int64_t i = (int64_t)c * E + e;
-      const int v = hist[i];
-      hist[i] = run;
-      run += v;
+    for (int cb = c0; cb < c1; cb += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i)
+        v[i] = cb + i < c1 ? hist[(int64_t)(cb + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i)
+        if (cb + i < c1) {
+          hist[(int64_t)(cb + i) * E + e] = run;
+          run += v[i];
+        }
     }
   }
   // 128-row block r -> its expert: the first e with padded_bins[e] > 128 r.
