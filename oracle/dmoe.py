@@ -52,7 +52,7 @@ BLOCK = 128
 
 __all__ = [
     "BLOCK", "round_up", "max_tiles", "metadata", "metadata_counting_sort",
-    "padded_gather", "padded_scatter", "silu", "sigmoid", "forward_loop",
+    "padded_gather", "row_token", "padded_scatter", "silu", "sigmoid", "forward_loop",
     "backward_loop", "forward_padded", "backward_padded", "sampled_rows",
     "sampled_dw",
 ]
@@ -184,6 +184,21 @@ def padded_gather(x, md, k: int) -> np.ndarray:
     out = np.zeros((md["P"], x.shape[1]), dtype=np.float64)
     a = np.arange(md["row_of_entry"].size)
     out[md["row_of_entry"]] = x[a // k]
+    return out
+
+
+def row_token(md, k: int) -> np.ndarray:
+    """The token each padded row holds, -1 for a pad row.
+
+    [MB] §4.2: the gather copies token ``a // k`` (R3) onto padded row
+    ``row_of_entry[a]``; [MB] §2: the rows of an expert's padded range past
+    its count receive no entry.  This is the same index rule read from the
+    row side: the table a kernel needs to fetch a padded row's token row
+    straight from x.  Length P.
+    """
+    out = np.full(md["P"], -1, dtype=np.int64)
+    a = np.arange(md["row_of_entry"].size)
+    out[md["row_of_entry"]] = a // k
     return out
 
 

@@ -149,3 +149,30 @@ def test_scatter_reads_only_real_rows():
     yp2 = yp.copy()
     yp2[~real] = 1e30
     np.testing.assert_array_equal(oracle.padded_scatter(yp2, md, w, T, k), y1)
+
+
+@pytest.mark.parametrize("T,k,E,seed", [
+    (1, 1, 1, 0), (3, 2, 5, 1), (77, 3, 6, 2), (200, 8, 16, 3), (129, 1, 2, 4)])
+def test_row_token_agrees_with_the_gather_and_padding(T, k, E, seed):
+    """row_token read against the separately pinned gather and §2's padding:
+    a real row holds the token the gather copies there, every token appears
+    k times, and the -1 rows are exactly each expert's tail past its count."""
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, E, (T, k)).astype(np.int32)
+    md = oracle.metadata(ids, E)
+    rt = oracle.row_token(md, k)
+    assert rt.shape == (md["P"],)
+    # rows of x that are all distinct and non-zero: x[t] = t + 1
+    x = np.repeat(np.arange(1, T + 1, dtype=np.float32)[:, None], 3, axis=1)
+    xp = oracle.padded_gather(x, md, k)
+    real = rt >= 0
+    np.testing.assert_array_equal(xp[real, 0], rt[real] + 1)
+    assert np.all(xp[~real] == 0.0)
+    assert np.array_equal(np.bincount(rt[real], minlength=T), np.full(T, k))
+    c = md["tokens_per_expert"]
+    pc = np.diff(np.concatenate([[0], md["padded_bins"]]))
+    pad = np.zeros(md["P"], dtype=bool)
+    for e in range(E):
+        pad[md["padded_bins"][e] - pc[e] + c[e]:md["padded_bins"][e]] = True
+    np.testing.assert_array_equal(~real, pad)
+    assert (~real).sum() == md["P"] - T * k
