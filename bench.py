@@ -35,12 +35,14 @@ BWD_KERNELS = ["scatter_backward", "gemm_down_dgrad_wgrad_down", "gemm_up_dgrad"
                "gather_backward", "gemm_wgrad_up"]
 
 
-def kernel_work(cfg, P):
+def kernel_work(cfg, P, fused=False):
     """Algorithmic FLOPs and bytes of each kernel for P padded rows.
 
     Bytes are unique reads plus writes; weights are counted once per kernel
     for the experts that have rows.  GEMM FLOPs are the executed (padded)
-    multiply-adds x2."""
+    multiply-adds x2.  fused: the gather fused into the up projection's
+    operand loads, so that product reads the T token rows of x instead of
+    the P rows of x_perm (the gather then runs in the backward)."""
     s = 4 if cfg.dtype == "f32" else 2
     T, H, F, E, k = cfg.T, cfg.H, cfg.F, cfg.E, cfg.k
     N = T * k
@@ -50,7 +52,8 @@ def kernel_work(cfg, P):
     w["meta_scan"] = (0, 16 * E)
     w["meta_place"] = (0, 4 * N + 12 * N)
     w["padded_gather"] = (0, (T * H + P * H) * s)
-    w["gemm_up_gate"] = (4 * P * H * F, (P * H + 2 * Ea * H * F + 3 * P * F) * s)
+    X = T * H if fused else P * H     # rows the up projection reads
+    w["gemm_up_gate"] = (4 * P * H * F, (X + 2 * Ea * H * F + 3 * P * F) * s)
     w["gemm_down"] = (2 * P * F * H, (P * F + Ea * F * H + P * H) * s)
     w["padded_scatter"] = (0, (N * H + T * H) * s + 4 * N)
     w["scatter_backward"] = (0, (T * H + N * H + P * H) * s + 8 * N)
@@ -190,6 +193,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--kernels", action="store_true",
                     help="also print the per-kernel table on stderr")
+    ap.add_argument("--fused-gather", action="store_true",
+                    help="time the path with the gather fused into the up "
+                         "projection's operand loads (the backward gathers x_perm)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB "
                          "three times (reference for hardware byte counters)")
@@ -227,7 +233,12 @@ def main():
     w1, w3, w2 = up(inp.w1), up(inp.w3), up(inp.w2)
     D = dm.Dims(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k,
                 dm.DMOE_F32 if cfg.dtype == "f32" else dm.DMOE_BF16)
-    layer = dm.DMoELayer(D, dev)
+    fused = args.fused_gather and cfg.dtype == "bf16"
+    layer = dm.DMoELayer(D, dev, fused_gather=fused)
+    fwd_kernels = [n for n in FWD_KERNELS if not (fused and n == "padded_gather")]
+    bwd_kernels = list(BWD_KERNELS)
+    if fused:   # the backward gathers x_perm right before the up dgrad
+        bwd_kernels.insert(bwd_kernels.index("gemm_up_dgrad"), "padded_gather")
     y = torch.empty(cfg.T, cfg.H, dtype=dt, device=dev)
     grads = dict(dx=torch.empty(cfg.T, cfg.H, dtype=dt, device=dev),
                  dw1=torch.empty_like(w1), dw3=torch.empty_like(w3),
@@ -249,7 +260,8 @@ def main():
     assert int(layer.buf.meta.status.item()) == 0
 
     K = args.steps
-    evs = [(EventArray(4), EventArray(5), EventArray(6)) for _ in range(K)]
+    evs = [(EventArray(4), EventArray(len(fwd_kernels) + 1), EventArray(len(bwd_kernels) + 1))
+           for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -264,10 +276,10 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    names = META_KERNELS + FWD_KERNELS + BWD_KERNELS
+    names = META_KERNELS + fwd_kernels + bwd_kernels
     per = {n: 0.0 for n in names}
     for ev in evs:
-        for arr, ks in zip(ev, (META_KERNELS, FWD_KERNELS, BWD_KERNELS)):
+        for arr, ks in zip(ev, (META_KERNELS, fwd_kernels, bwd_kernels)):
             for j, n in enumerate(ks):
                 per[n] += arr.elapsed_ms(j, j + 1) / K
     for ev in evs:
@@ -280,7 +292,7 @@ def main():
     executed_flop = 18.0 * P * cfg.H * cfg.F
     peak = PEAK_F32_TFLOPS if cfg.dtype == "f32" else PEAK_BF16_TFLOPS
     useful_tf = useful_flop / (ms * 1e-3) / 1e12
-    work = kernel_work(cfg, P)
+    work = kernel_work(cfg, P, fused)
     table = {}
     for n in names:
         fl, by = work[n]
@@ -290,7 +302,8 @@ def main():
                     "gbs": round(by / t / 1e9, 1) if t > 0 else None}
     gemms = [n for n in names if n.startswith("gemm")]
     gemm_ms = sum(per[n] for n in gemms)
-    gs = ["padded_gather", "padded_scatter", "scatter_backward", "gather_backward"]
+    gs = [n for n in ("padded_gather", "padded_scatter", "scatter_backward",
+                      "gather_backward") if n in names]
     gs_ms = sum(per[n] for n in gs)
     gs_bytes = sum(work[n][1] for n in gs)
     dom = max(names, key=lambda n: per[n])
@@ -339,7 +352,9 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic (seeded; Gaussian router logits, top-k + softmax)",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "F": cfg.F,
-                   "E": cfg.E, "k": cfg.k, "routing": cfg.routing, "P": P},
+                   "E": cfg.E, "k": cfg.k, "routing": cfg.routing, "P": P,
+                   "gather": ("fused into the up projection's loads; gathered in the "
+                              "backward" if fused else "padded copy in the forward")},
         "useful_tflops": round(useful_tf, 1),
         "useful_frac_peak": round(useful_tf / peak, 4),
         "gemm_executed_frac_peak": round(executed_flop / (gemm_ms * 1e-3) / 1e12 / peak, 4),

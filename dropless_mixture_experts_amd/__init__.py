@@ -67,7 +67,7 @@ class _Meta(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "tokens_per_expert", "bins", "padded_bins", "indices", "bin_ids",
         "row_of_entry", "tile_expert", "num_padded_rows", "status",
-        "pair_first", "num_pairs")]
+        "pair_first", "num_pairs", "row_token")]
 
 
 class _Saved(ctypes.Structure):
@@ -128,6 +128,15 @@ def load_library() -> ctypes.CDLL:
     lib.dmoe_backward_recompute.restype = ctypes.c_int
     lib.dmoe_backward_recompute_timed.argtypes = lib.dmoe_backward_timed.argtypes
     lib.dmoe_backward_recompute_timed.restype = ctypes.c_int
+    lib.dmoe_forward_fused_gather.argtypes = lib.dmoe_forward.argtypes
+    lib.dmoe_forward_fused_gather.restype = ctypes.c_int
+    lib.dmoe_forward_fused_gather_timed.argtypes = lib.dmoe_forward_timed.argtypes
+    lib.dmoe_forward_fused_gather_timed.restype = ctypes.c_int
+    lib.dmoe_backward_fused_gather.argtypes = [P(_Dims), vp] + lib.dmoe_backward.argtypes[1:]
+    lib.dmoe_backward_fused_gather.restype = ctypes.c_int
+    lib.dmoe_backward_fused_gather_timed.argtypes = ([P(_Dims), vp]
+                                                     + lib.dmoe_backward_timed.argtypes[1:])
+    lib.dmoe_backward_fused_gather_timed.restype = ctypes.c_int
     lib.dmoe_router_forward.argtypes = [P(_Dims), vp, ctypes.c_float, vp, vp, vp, vp, vp]
     lib.dmoe_router_forward.restype = ctypes.c_int
     lib.dmoe_router_backward.argtypes = [P(_Dims), vp, vp, vp, vp, ctypes.c_float, vp, vp]
@@ -168,6 +177,7 @@ class Meta:
     status: torch.Tensor
     pair_first: torch.Tensor
     num_pairs: torch.Tensor
+    row_token: torch.Tensor
 
     def _c(self) -> _Meta:
         return _Meta(*[_ptr(getattr(self, f.name), torch.int32, f.name)
@@ -176,7 +186,7 @@ class Meta:
 
 @dataclasses.dataclass
 class Saved:
-    x_perm: torch.Tensor
+    x_perm: Optional[torch.Tensor]      # may be None for the fused-gather forward
     h1: torch.Tensor
     h3: torch.Tensor
     act: torch.Tensor
@@ -255,7 +265,8 @@ def _check_meta(dims: Dims, meta: Meta):
                        ("padded_bins", dims.E), ("indices", n), ("bin_ids", n),
                        ("row_of_entry", n), ("tile_expert", dmoe_max_tiles(dims)),
                        ("num_padded_rows", 1), ("status", 1),
-                       ("pair_first", dmoe_max_tiles(dims)), ("num_pairs", 1)):
+                       ("pair_first", dmoe_max_tiles(dims)), ("num_pairs", 1),
+                       ("row_token", 128 * dmoe_max_tiles(dims))):
         _need(getattr(meta, name), name, size)
 
 
@@ -288,36 +299,46 @@ def _pmax(dims: Dims) -> int:
 
 
 def dmoe_forward(dims: Dims, x, weights, w1, w3, w2, meta: Meta, saved: Saved,
-                 y, stream=None, events=None) -> None:
+                 y, stream=None, events=None, fused_gather: bool = False) -> None:
     """Forward of the layer; see include/dmoe.h.  `events`: optional
-    EventArray of 5 events for per-kernel timing (dmoe_forward_timed)."""
+    EventArray of 5 events (4 with fused_gather) for per-kernel timing.
+    fused_gather: the up projection reads token rows of x directly
+    (dmoe_forward_fused_gather); saved.x_perm may be None."""
     lib = load_library()
     dt = dims.torch_dtype
     T, H, F, E, k = dims.T, dims.H, dims.F, dims.E, dims.k
     pm = _pmax(dims)
-    for t, n, s in ((x, "x", T * H), (weights, "weights", T * k),
-                    (w1, "w1", E * H * F), (w3, "w3", E * H * F),
-                    (w2, "w2", E * F * H), (y, "y", T * H),
-                    (saved.x_perm, "x_perm", pm * H), (saved.h1, "h1", pm * F),
-                    (saved.h3, "h3", pm * F), (saved.act, "act", pm * F),
-                    (saved.y_perm, "y_perm", pm * H)):
+    need = [(x, "x", T * H), (weights, "weights", T * k),
+            (w1, "w1", E * H * F), (w3, "w3", E * H * F),
+            (w2, "w2", E * F * H), (y, "y", T * H), (saved.h1, "h1", pm * F),
+            (saved.h3, "h3", pm * F), (saved.act, "act", pm * F),
+            (saved.y_perm, "y_perm", pm * H)]
+    if not fused_gather:
+        need.append((saved.x_perm, "x_perm", pm * H))
+    for t, n, s in need:
         _need(t, n, s)
     _check_meta(dims, meta)
-    _check(lib.dmoe_forward_timed(
+    fn = lib.dmoe_forward_fused_gather_timed if fused_gather else lib.dmoe_forward_timed
+    _check(fn(
         ctypes.byref(dims._c()), _ptr(x, dt, "x"),
         _ptr(weights, torch.float32, "weights"), _ptr(w1, dt, "w1"),
         _ptr(w3, dt, "w3"), _ptr(w2, dt, "w2"), ctypes.byref(meta._c()),
         ctypes.byref(saved._c(dt)), _ptr(y, dt, "y"), _stream(x, stream),
-        _ev(events, 4)), "dmoe_forward")
+        _ev(events, 3 if fused_gather else 4)), "dmoe_forward")
 
 
 def dmoe_backward(dims: Dims, dy, weights, w1, w3, w2, meta: Meta, saved: Saved,
                   scratch: GradScratch, dx, dw1, dw3, dw2, d_weights,
-                  stream=None, events=None, recompute: bool = False) -> None:
+                  stream=None, events=None, recompute: bool = False,
+                  x=None) -> None:
     """Backward of the layer; see include/dmoe.h.  `events`: optional
-    EventArray of 6 events (7 with recompute) for per-kernel timing.
+    EventArray of 6 events (7 with recompute or x) for per-kernel timing.
     recompute: saved.act is scratch on entry and is rebuilt from h1 and h3
-    (dmoe_backward_recompute)."""
+    (dmoe_backward_recompute).  x: the forward's input, after the
+    fused-gather forward (dmoe_backward_fused_gather): saved.x_perm is then
+    scratch on entry and is gathered from x first."""
+    if x is not None and recompute:
+        raise ValueError("the fused gather has no recompute variant")
     lib = load_library()
     dt = dims.torch_dtype
     T, H, F, E, k = dims.T, dims.H, dims.F, dims.E, dims.k
@@ -327,12 +348,19 @@ def dmoe_backward(dims: Dims, dy, weights, w1, w3, w2, meta: Meta, saved: Saved,
                     (w2, "w2", E * F * H), (dx, "dx", T * H),
                     (dw1, "dw1", E * H * F), (dw3, "dw3", E * H * F),
                     (dw2, "dw2", E * F * H), (d_weights, "d_weights", T * k),
+                    (saved.x_perm, "x_perm", pm * H),
                     (scratch.dy_perm, "dy_perm", pm * H),
                     (scratch.dh1, "dh1", pm * F), (scratch.dh3, "dh3", pm * F),
                     (scratch.dx_perm, "dx_perm", pm * H)):
         _need(t, n, s)
     _check_meta(dims, meta)
-    fn = lib.dmoe_backward_recompute_timed if recompute else lib.dmoe_backward_timed
+    if x is not None:
+        _need(x, "x", T * H)
+        fn = lambda *a: lib.dmoe_backward_fused_gather_timed(a[0], _ptr(x, dt, "x"), *a[1:])
+    elif recompute:
+        fn = lib.dmoe_backward_recompute_timed
+    else:
+        fn = lib.dmoe_backward_timed
     _check(fn(
         ctypes.byref(dims._c()), _ptr(dy, dt, "dy"),
         _ptr(weights, torch.float32, "weights"), _ptr(w1, dt, "w1"),
@@ -340,7 +368,8 @@ def dmoe_backward(dims: Dims, dy, weights, w1, w3, w2, meta: Meta, saved: Saved,
         ctypes.byref(saved._c(dt)), ctypes.byref(scratch._c(dt)),
         _ptr(dx, dt, "dx"), _ptr(dw1, dt, "dw1"), _ptr(dw3, dt, "dw3"),
         _ptr(dw2, dt, "dw2"), _ptr(d_weights, torch.float32, "d_weights"),
-        _stream(dy, stream), _ev(events, 6 if recompute else 5)), "dmoe_backward")
+        _stream(dy, stream), _ev(events, 6 if recompute or x is not None else 5)),
+        "dmoe_backward")
 
 
 def dmoe_padded_gather(dims: Dims, x, meta: Meta, x_perm, stream=None) -> None:
@@ -431,7 +460,8 @@ def allocate_meta(dims: Dims, device):
     meta = Meta(torch.empty(E, **i32), torch.empty(E, **i32), torch.empty(E, **i32),
                 torch.empty(n, **i32), torch.empty(n, **i32), torch.empty(n, **i32),
                 torch.empty(nt, **i32), torch.empty(1, **i32), torch.empty(1, **i32),
-                torch.empty(nt, **i32), torch.empty(1, **i32))
+                torch.empty(nt, **i32), torch.empty(1, **i32),
+                torch.empty(128 * nt, **i32))
     ws = torch.empty(dmoe_workspace_bytes(dims), dtype=torch.uint8, device=device)
     return meta, ws
 
@@ -461,12 +491,19 @@ def allocate(dims: Dims, device, with_backward: bool = True,
 
 
 class DMoELayer:
-    """Runs metadata + forward + backward on preallocated buffers."""
+    """Runs metadata + forward + backward on preallocated buffers.
 
-    def __init__(self, dims: Dims, device="cuda", lean: bool = False):
+    fused_gather=True (bf16): the forward's up projection reads token rows
+    of x directly and writes no x_perm; the backward gathers x_perm from x
+    first, so the x given to forward must be unchanged until backward."""
+
+    def __init__(self, dims: Dims, device="cuda", lean: bool = False,
+                 fused_gather: bool = False):
         self.dims = dims
+        self.fused_gather = fused_gather
         self.buf = allocate(dims, device, True, lean)
         self.device = torch.device(device)
+        self._x = None
 
     def metadata(self, top_experts, stream=None, events=None):
         dmoe_metadata(self.dims, top_experts, self.buf.meta, self.buf.ws, stream,
@@ -480,7 +517,8 @@ class DMoELayer:
             y = torch.empty(self.dims.T, self.dims.H, dtype=self.dims.torch_dtype,
                             device=self.device)
         dmoe_forward(self.dims, x, weights, w1, w3, w2, self.buf.meta,
-                     self.buf.saved, y, stream, events)
+                     self.buf.saved, y, stream, events, self.fused_gather)
+        self._x = x if self.fused_gather else None
         return y
 
     def backward(self, dy, weights, w1, w3, w2, grads=None, stream=None,
@@ -494,9 +532,12 @@ class DMoELayer:
                          dw2=torch.empty(d.E, d.F, d.H, **fl),
                          d_weights=torch.empty(d.T, d.k, dtype=torch.float32,
                                                device=self.device))
+        if self.fused_gather and self._x is None:
+            raise RuntimeError("fused_gather: backward needs a forward first")
         dmoe_backward(d, dy, weights, w1, w3, w2, self.buf.meta, self.buf.saved,
                       self.buf.scratch, grads["dx"], grads["dw1"], grads["dw3"],
-                      grads["dw2"], grads["d_weights"], stream, events, recompute)
+                      grads["dw2"], grads["d_weights"], stream, events, recompute,
+                      self._x)
         return grads
 
 

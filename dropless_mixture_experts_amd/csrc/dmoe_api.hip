@@ -49,7 +49,7 @@ Shape shape_of(const dmoe_dims* d) {
 int check_meta(const dmoe_meta* m) {
   if (!m || !m->tokens_per_expert || !m->bins || !m->padded_bins || !m->indices ||
       !m->bin_ids || !m->row_of_entry || !m->tile_expert || !m->num_padded_rows ||
-      !m->status || !m->pair_first || !m->num_pairs)
+      !m->status || !m->pair_first || !m->num_pairs || !m->row_token)
     return DMOE_ERR_ARG;
   return DMOE_OK;
 }
@@ -57,7 +57,7 @@ int check_meta(const dmoe_meta* m) {
 MetaPtrs meta_ptrs(const dmoe_meta* m) {
   return MetaPtrs{m->tokens_per_expert, m->bins, m->padded_bins, m->indices,
                   m->bin_ids, m->row_of_entry, m->tile_expert, m->num_padded_rows,
-                  m->status, m->pair_first, m->num_pairs};
+                  m->status, m->pair_first, m->num_pairs, m->row_token};
 }
 
 // Records events[i] on the stream when timing is requested.
@@ -96,7 +96,7 @@ int dmoe_metadata_timed(const dmoe_dims* dims, const int32_t* top_experts,
   if (rc != DMOE_OK) return rc;
   if ((rc = check_meta(meta)) != DMOE_OK) return rc;
   if (!top_experts || !ws) return DMOE_ERR_ARG;
-  DMOE_TRY(dmoe::launch_metadata(dims->T * (int64_t)dims->k, dims->E, max_tiles_of(dims),
+  DMOE_TRY(dmoe::launch_metadata(dims->T * (int64_t)dims->k, dims->E, dims->k, max_tiles_of(dims),
                                  top_experts, meta_ptrs(meta), ws, stream, events));
   return DMOE_OK;
 }
@@ -106,30 +106,74 @@ int dmoe_metadata(const dmoe_dims* dims, const int32_t* top_experts,
   return dmoe_metadata_timed(dims, top_experts, meta, ws, stream, nullptr);
 }
 
-int dmoe_forward_timed(const dmoe_dims* dims, const void* x, const float* weights,
-                       const void* w1, const void* w3, const void* w2,
-                       const dmoe_meta* meta, const dmoe_saved* saved, void* y,
-                       hipStream_t stream, hipEvent_t* ev) {
+}  // extern "C"
+
+namespace {
+
+// The gather fused into the operand loads: bf16 only, and x must stay below
+// 2 GB (the records of the buffer resource its rows are read through).
+int check_fused(const dmoe_dims* d) {
+  if (d->dtype != DMOE_BF16) return DMOE_ERR_UNSUPPORTED;
+  if (d->T * d->H * 2 >= (int64_t(1) << 31)) return DMOE_ERR_UNSUPPORTED;
+  return DMOE_OK;
+}
+
+// The forward; with `fused`, no padded_gather: the up projection reads each
+// padded row's token row of x directly and saved->x_perm is not used (event
+// 0 then brackets the up projection).
+int forward_impl(const dmoe_dims* dims, const void* x, const float* weights, const void* w1,
+                 const void* w3, const void* w2, const dmoe_meta* meta,
+                 const dmoe_saved* saved, void* y, hipStream_t stream, hipEvent_t* ev,
+                 bool fused) {
   int rc = check_gemm_dims(dims);
   if (rc != DMOE_OK) return rc;
+  if (fused && (rc = check_fused(dims)) != DMOE_OK) return rc;
   if ((rc = check_meta(meta)) != DMOE_OK) return rc;
-  if (!x || !weights || !w1 || !w3 || !w2 || !saved || !y || !saved->x_perm ||
+  if (!x || !weights || !w1 || !w3 || !w2 || !saved || !y || (!fused && !saved->x_perm) ||
       !saved->h1 || !saved->h3 || !saved->act || !saved->y_perm)
     return DMOE_ERR_ARG;
   const Shape s = shape_of(dims);
   const MetaPtrs m = meta_ptrs(meta);
   Recorder rec{ev, stream};
-  DMOE_TRY(rec(0));
-  DMOE_TRY(dmoe::launch_padded_gather(s, x, m, saved->x_perm, stream));
-  DMOE_TRY(rec(1));
-  DMOE_TRY(dmoe::launch_gemm_up(s, saved->x_perm, w1, w3, m, saved->h1, saved->h3,
-                                saved->act, stream));
-  DMOE_TRY(rec(2));
+  int i = 0;
+  if (!fused) {
+    DMOE_TRY(rec(i++));
+    DMOE_TRY(dmoe::launch_padded_gather(s, x, m, saved->x_perm, stream));
+  }
+  DMOE_TRY(rec(i++));
+  DMOE_TRY(dmoe::launch_gemm_up(s, fused ? nullptr : saved->x_perm, fused ? x : nullptr, w1, w3,
+                                m, saved->h1, saved->h3, saved->act, stream));
+  DMOE_TRY(rec(i++));
   DMOE_TRY(dmoe::launch_gemm_down(s, saved->act, w2, m, saved->y_perm, stream));
-  DMOE_TRY(rec(3));
+  DMOE_TRY(rec(i++));
   DMOE_TRY(dmoe::launch_padded_scatter(s, saved->y_perm, weights, m, y, stream));
-  DMOE_TRY(rec(4));
+  DMOE_TRY(rec(i++));
   return DMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dmoe_forward_timed(const dmoe_dims* dims, const void* x, const float* weights,
+                       const void* w1, const void* w3, const void* w2,
+                       const dmoe_meta* meta, const dmoe_saved* saved, void* y,
+                       hipStream_t stream, hipEvent_t* ev) {
+  return forward_impl(dims, x, weights, w1, w3, w2, meta, saved, y, stream, ev, false);
+}
+
+int dmoe_forward_fused_gather_timed(const dmoe_dims* dims, const void* x, const float* weights,
+                                    const void* w1, const void* w3, const void* w2,
+                                    const dmoe_meta* meta, const dmoe_saved* saved, void* y,
+                                    hipStream_t stream, hipEvent_t* ev) {
+  return forward_impl(dims, x, weights, w1, w3, w2, meta, saved, y, stream, ev, true);
+}
+
+int dmoe_forward_fused_gather(const dmoe_dims* dims, const void* x, const float* weights,
+                              const void* w1, const void* w3, const void* w2,
+                              const dmoe_meta* meta, const dmoe_saved* saved, void* y,
+                              hipStream_t stream) {
+  return forward_impl(dims, x, weights, w1, w3, w2, meta, saved, y, stream, nullptr, true);
 }
 
 int dmoe_forward(const dmoe_dims* dims, const void* x, const float* weights,
@@ -144,14 +188,17 @@ int dmoe_forward(const dmoe_dims* dims, const void* x, const float* weights,
 namespace {
 
 // The backward of the layer; with `recompute`, act is rebuilt from h1 and h3
-// first (event 0 then brackets that kernel and the others shift by one).
-int backward_impl(const dmoe_dims* dims, const void* dy, const float* weights, const void* w1,
-                  const void* w3, const void* w2, const dmoe_meta* meta,
+// first, and with a non-null x (after the fused-gather forward) x_perm is
+// gathered from x before the up dgrad.  Each such kernel has an event of its
+// own in launch order.
+int backward_impl(const dmoe_dims* dims, const void* x, const void* dy, const float* weights,
+                  const void* w1, const void* w3, const void* w2, const dmoe_meta* meta,
                   const dmoe_saved* saved, const dmoe_grad_scratch* scratch, void* dx,
                   void* dw1, void* dw3, void* dw2, float* d_weights, hipStream_t stream,
                   hipEvent_t* ev, bool recompute) {
   int rc = check_gemm_dims(dims);
   if (rc != DMOE_OK) return rc;
+  if (x && (rc = check_fused(dims)) != DMOE_OK) return rc;
   if ((rc = check_meta(meta)) != DMOE_OK) return rc;
   if (!dy || !weights || !w1 || !w3 || !w2 || !saved || !scratch || !dx || !dw1 ||
       !dw3 || !dw2 || !d_weights || !saved->x_perm || !saved->h1 || !saved->h3 ||
@@ -177,15 +224,21 @@ int backward_impl(const dmoe_dims* dims, const void* dy, const float* weights, c
                                                    saved->h3, saved->act, m, scratch->dh1,
                                                    scratch->dh3, dw2, stream));
   DMOE_TRY(rec(i++));
-  DMOE_TRY(dmoe::launch_gemm_up_dgrad(s, scratch->dh1, scratch->dh3, w1, w3, saved->x_perm,
-                                      m, scratch->dx_perm, dw1, dw3, stream));
+  if (x) {
+    // the forward did not keep x_perm: gather it for the products that read
+    // it (dw1/dw3, some of them in the up dgrad's launch)
+    DMOE_TRY(dmoe::launch_padded_gather(s, x, m, saved->x_perm, stream));
+    DMOE_TRY(rec(i++));
+  }
+  DMOE_TRY(dmoe::launch_gemm_up_dgrad(s, scratch->dh1, scratch->dh3, w1, w3, saved->x_perm, m,
+                                      scratch->dx_perm, dw1, dw3, stream));
   DMOE_TRY(rec(i++));
   // the gather's backward right away, while dx_perm is still in the
   // last-level cache
   DMOE_TRY(dmoe::launch_padded_scatter(s, scratch->dx_perm, nullptr, m, dx, stream));
   DMOE_TRY(rec(i++));
-  DMOE_TRY(dmoe::launch_gemm_wgrad_up(s, scratch->dh1, scratch->dh3, w1, w3, saved->x_perm,
-                                      m, scratch->dx_perm, dw1, dw3, stream));
+  DMOE_TRY(dmoe::launch_gemm_wgrad_up(s, scratch->dh1, scratch->dh3, w1, w3, saved->x_perm, m,
+                                      scratch->dx_perm, dw1, dw3, stream));
   DMOE_TRY(rec(i++));
   return DMOE_OK;
 }
@@ -200,8 +253,8 @@ int dmoe_backward_timed(const dmoe_dims* dims, const void* dy, const float* weig
                         const dmoe_grad_scratch* scratch, void* dx, void* dw1,
                         void* dw3, void* dw2, float* d_weights, hipStream_t stream,
                         hipEvent_t* ev) {
-  return backward_impl(dims, dy, weights, w1, w3, w2, meta, saved, scratch, dx, dw1, dw3, dw2,
-                       d_weights, stream, ev, false);
+  return backward_impl(dims, nullptr, dy, weights, w1, w3, w2, meta, saved, scratch, dx, dw1,
+                       dw3, dw2, d_weights, stream, ev, false);
 }
 
 int dmoe_backward(const dmoe_dims* dims, const void* dy, const float* weights,
@@ -209,8 +262,8 @@ int dmoe_backward(const dmoe_dims* dims, const void* dy, const float* weights,
                   const dmoe_meta* meta, const dmoe_saved* saved,
                   const dmoe_grad_scratch* scratch, void* dx, void* dw1,
                   void* dw3, void* dw2, float* d_weights, hipStream_t stream) {
-  return backward_impl(dims, dy, weights, w1, w3, w2, meta, saved, scratch, dx, dw1, dw3, dw2,
-                       d_weights, stream, nullptr, false);
+  return backward_impl(dims, nullptr, dy, weights, w1, w3, w2, meta, saved, scratch, dx, dw1,
+                       dw3, dw2, d_weights, stream, nullptr, false);
 }
 
 int dmoe_backward_recompute_timed(const dmoe_dims* dims, const void* dy, const float* weights,
@@ -219,8 +272,8 @@ int dmoe_backward_recompute_timed(const dmoe_dims* dims, const void* dy, const f
                                   const dmoe_grad_scratch* scratch, void* dx, void* dw1,
                                   void* dw3, void* dw2, float* d_weights, hipStream_t stream,
                                   hipEvent_t* ev) {
-  return backward_impl(dims, dy, weights, w1, w3, w2, meta, saved, scratch, dx, dw1, dw3, dw2,
-                       d_weights, stream, ev, true);
+  return backward_impl(dims, nullptr, dy, weights, w1, w3, w2, meta, saved, scratch, dx, dw1,
+                       dw3, dw2, d_weights, stream, ev, true);
 }
 
 int dmoe_backward_recompute(const dmoe_dims* dims, const void* dy, const float* weights,
@@ -228,8 +281,28 @@ int dmoe_backward_recompute(const dmoe_dims* dims, const void* dy, const float* 
                             const dmoe_meta* meta, const dmoe_saved* saved,
                             const dmoe_grad_scratch* scratch, void* dx, void* dw1,
                             void* dw3, void* dw2, float* d_weights, hipStream_t stream) {
-  return backward_impl(dims, dy, weights, w1, w3, w2, meta, saved, scratch, dx, dw1, dw3, dw2,
-                       d_weights, stream, nullptr, true);
+  return backward_impl(dims, nullptr, dy, weights, w1, w3, w2, meta, saved, scratch, dx, dw1,
+                       dw3, dw2, d_weights, stream, nullptr, true);
+}
+
+int dmoe_backward_fused_gather_timed(const dmoe_dims* dims, const void* x, const void* dy,
+                                     const float* weights, const void* w1, const void* w3,
+                                     const void* w2, const dmoe_meta* meta,
+                                     const dmoe_saved* saved, const dmoe_grad_scratch* scratch,
+                                     void* dx, void* dw1, void* dw3, void* dw2, float* d_weights,
+                                     hipStream_t stream, hipEvent_t* ev) {
+  if (!x) return DMOE_ERR_ARG;
+  return backward_impl(dims, x, dy, weights, w1, w3, w2, meta, saved, scratch, dx, dw1, dw3, dw2,
+                       d_weights, stream, ev, false);
+}
+
+int dmoe_backward_fused_gather(const dmoe_dims* dims, const void* x, const void* dy,
+                               const float* weights, const void* w1, const void* w3,
+                               const void* w2, const dmoe_meta* meta, const dmoe_saved* saved,
+                               const dmoe_grad_scratch* scratch, void* dx, void* dw1, void* dw3,
+                               void* dw2, float* d_weights, hipStream_t stream) {
+  return dmoe_backward_fused_gather_timed(dims, x, dy, weights, w1, w3, w2, meta, saved, scratch,
+                                          dx, dw1, dw3, dw2, d_weights, stream, nullptr);
 }
 
 int dmoe_padded_gather(const dmoe_dims* dims, const void* x, const dmoe_meta* meta,

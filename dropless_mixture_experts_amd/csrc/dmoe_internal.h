@@ -14,6 +14,7 @@ struct MetaPtrs {
   int32_t *indices, *bin_ids, *row_of_entry;
   int32_t *tile_expert, *num_padded_rows, *status;
   int32_t *pair_first, *num_pairs;
+  int32_t *row_token;
 };
 
 struct Shape {
@@ -27,7 +28,7 @@ struct Shape {
 int64_t meta_chunk(int64_t n, int E);
 int meta_nchunks(int64_t n, int E);
 int64_t meta_workspace_bytes(int64_t n, int E);
-hipError_t launch_metadata(int64_t n, int E, int64_t max_tiles,
+hipError_t launch_metadata(int64_t n, int E, int k, int64_t max_tiles,
                            const int32_t* ids, const MetaPtrs& m, void* ws,
                            hipStream_t stream, hipEvent_t* ev);
 
@@ -55,8 +56,10 @@ hipError_t launch_router_backward(const Shape& s, const float* logits, const int
                                   float* d_logits, hipStream_t stream);
 
 // gemm.hip: the products of the layer.  bf16 runs on the engine in
-// gemm_bf16.hip; fp32 on the tiled kernels of gemm.hip.
-hipError_t launch_gemm_up(const Shape& s, const void* x_perm, const void* w1,
+// gemm_bf16.hip; fp32 on the tiled kernels of gemm.hip.  In the up
+// projection, a non-null x (bf16 only) makes it read each padded row's token
+// row of x through m.row_token (zeros for a pad row) instead of x_perm.
+hipError_t launch_gemm_up(const Shape& s, const void* x_perm, const void* x, const void* w1,
                           const void* w3, const MetaPtrs& m, void* h1, void* h3,
                           void* act, hipStream_t stream);
 hipError_t launch_gemm_down(const Shape& s, const void* act, const void* w2,
@@ -79,8 +82,8 @@ hipError_t launch_gemm_wgrad_up(const Shape& s, const void* dh1, const void* dh3
                                 hipStream_t stream);
 
 // gemm_bf16.hip
-hipError_t launch_bf16_up(const Shape& s, const void* x_perm, const void* w1, const void* w3,
-                          const MetaPtrs& m, void* h1, void* h3, void* act,
+hipError_t launch_bf16_up(const Shape& s, const void* x_perm, const void* x, const void* w1,
+                          const void* w3, const MetaPtrs& m, void* h1, void* h3, void* act,
                           hipStream_t stream);
 hipError_t launch_bf16_down(const Shape& s, const void* act, const void* w2,
                             const MetaPtrs& m, void* y_perm, hipStream_t stream);

@@ -490,11 +490,12 @@ static unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b);
 template <typename T> static const T* cp(const void* p) { return static_cast<const T*>(p); }
 template <typename T> static T* mp(void* p) { return static_cast<T*>(p); }
 
-hipError_t launch_gemm_up(const Shape& s, const void* x_perm, const void* w1,
+hipError_t launch_gemm_up(const Shape& s, const void* x_perm, const void* x, const void* w1,
                           const void* w3, const MetaPtrs& m, void* h1, void* h3,
                           void* act, hipStream_t stream) {
   const dim3 grid(cdiv(s.F, 128), (unsigned)s.max_tiles);
-  if (s.bf16) return launch_bf16_up(s, x_perm, w1, w3, m, h1, h3, act, stream);
+  if (s.bf16) return launch_bf16_up(s, x_perm, x, w1, w3, m, h1, h3, act, stream);
+  if (x) return hipErrorNotSupported;   // rows from x: bf16 engine only
   hipLaunchKernelGGL(gemm_up_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
                      cp<float>(x_perm), cp<float>(w1), cp<float>(w3), s.H, s.F,
                      m.tile_expert, mp<float>(h1), mp<float>(h3), mp<float>(act));

@@ -80,6 +80,16 @@ __device__ __forceinline__ rsrc_t make_rsrc(const char* p) {
   return rsrc_t{uniform((uint32_t)a), uniform((uint32_t)(a >> 32) & 0xffffu), 0x7fffffffu,
                 0x00020000u};
 }
+// The same with `bytes` records: a lane whose offset is at or past `bytes`
+// reads zeros (the buffer range check), which is how a pad row's token
+// row reads as zeros when rows come straight from x.
+__device__ __forceinline__ rsrc_t make_rsrc_n(const char* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return rsrc_t{uniform((uint32_t)a), uniform((uint32_t)(a >> 32) & 0xffffu), uniform(bytes),
+                0x00020000u};
+}
+// Offset given to a pad row: past the records of any x of under 2 GB.
+constexpr uint32_t kNoRow = 0x80000000u;
 __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return (uint32_t)(uintptr_t)(lds_ptr_t)const_cast<char*>(p);
 }
@@ -92,17 +102,22 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
 }
-// wait_vm for a count known at run time (a multiple of 8 up to 40; any other
-// count waits for everything, which is never wrong).
-__device__ __forceinline__ void wait_vm_n(int n) {
-  switch (n) {
-    case 8: wait_vm<8>(); break;
-    case 16: wait_vm<16>(); break;
-    case 24: wait_vm<24>(); break;
-    case 32: wait_vm<32>(); break;
-    case 40: wait_vm<40>(); break;
-    default: wait_vm<0>(); break;
+// wait_vm for a count known at run time (wave-uniform), by a binary search
+// over the immediates LO..HI; a count outside it waits for everything, which
+// is never wrong.
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vm_range(int n) {
+  if constexpr (LO == HI) {
+    wait_vm<LO>();
+  } else {
+    constexpr int MID = (LO + HI) / 2;
+    if (n <= MID) wait_vm_range<LO, MID>(n);
+    else wait_vm_range<MID + 1, HI>(n);
   }
+}
+__device__ __forceinline__ void wait_vm_n(int n) {
+  if (n <= 0 || n > 63) wait_vm<0>();
+  else wait_vm_range<1, 63>(n);
 }
 // s_waitcnt lgkmcnt(0) only.
 __device__ __forceinline__ void wait_lds() {
@@ -421,17 +436,37 @@ struct RowTiles {
 
 // ---- The products, as operand + epilogue policies ----------------------------
 
+// Where a product's B operand comes from: its own array (kXNone), or token
+// rows of x fetched straight into the tile, the gather fused into the operand
+// loads (kXDirect, B rows are padded rows with K along the row): padded row p
+// is row row_token[p] of x, zeros for a pad row (row_token < 0).
+enum XMode { kXNone, kXDirect };
+
+struct XRows {
+  const bf16* x;              // [T, H]
+  const int32_t* row_token;   // [P]
+  uint32_t bytes;             // T * H * 2, below 2 GB
+};
+
 // h1 = x_perm w1[e], h3 = x_perm w3[e], act = silu(h1) * h3 for one pair of
 // row blocks and 128 ffn columns (w1 columns in A rows 0..127, the same w3
-// columns in A rows 128..255, so A blocks i and i+2 pair up).
-struct Up {
+// columns in A rows 128..255, so A blocks i and i+2 pair up).  X: the rows of
+// x_perm come straight from x (xr).
+template <bool X>
+struct UpT {
   static constexpr bool kLateStep1 = false;
   static constexpr bool kUsesFreeStage = false;
   static constexpr bool ATR = true, BTR = false;
+  static constexpr XMode kXB = X ? kXDirect : kXNone;
   const bf16 *x_perm, *w1, *w3;
   int64_t H, F;
   bf16 *h1, *h3, *act;
   RowTiles rt;
+  XRows xr;
+  // first padded row of the 32 B rows that wave w loads
+  __device__ int64_t x_rows(const Job& j, int w) const {
+    return j.u * kBlock + (w < 4 ? 0 : (j.fb ? kBlock : 0)) + 32 * (w & 3);
+  }
   __device__ uint32_t lda() const { return (uint32_t)(F * 2); }
   __device__ uint32_t ldb() const { return (uint32_t)(H * 2); }
   __device__ void xcd_range(int x, int& lo, int& hi) const { rt.xcd_range(x, lo, hi); }
@@ -466,11 +501,14 @@ struct Up {
   }
 };
 
+using Up = UpT<false>;
+
 // y_perm = act w2[e] for one pair of row blocks and 256 (or 128) hidden columns.
 struct Down {
   static constexpr bool kLateStep1 = false;
   static constexpr bool kUsesFreeStage = false;
   static constexpr bool ATR = true, BTR = false;
+  static constexpr XMode kXB = kXNone;
   const bf16 *act, *w2;
   int64_t H, F;
   bf16* y_perm;
@@ -508,6 +546,7 @@ struct DownDgrad {
   static constexpr bool kLateStep1 = true;
   static constexpr bool kUsesFreeStage = true;
   static constexpr bool ATR = false, BTR = false;
+  static constexpr XMode kXB = kXNone;
   const bf16 *dy_perm, *w2, *h1, *h3;
   int64_t H, F;
   bf16 *dh1, *dh3;
@@ -598,6 +637,7 @@ struct UpDgrad {
   static constexpr bool kLateStep1 = false;
   static constexpr bool kUsesFreeStage = false;
   static constexpr bool ATR = false, BTR = false;
+  static constexpr XMode kXB = kXNone;
   const bf16 *dh1, *dh3, *w1, *w3;
   int64_t H, F;
   bf16* dx_perm;
@@ -665,6 +705,7 @@ struct WgradDown {
   static constexpr bool kLateStep1 = false;
   static constexpr bool kUsesFreeStage = false;
   static constexpr bool ATR = true, BTR = true;
+  static constexpr XMode kXB = kXNone;
   const bf16 *act, *dy_perm;
   int64_t H, F;
   int E;
@@ -721,6 +762,7 @@ struct WgradUp {
   static constexpr bool kLateStep1 = false;
   static constexpr bool kUsesFreeStage = false;
   static constexpr bool ATR = true, BTR = true;
+  static constexpr XMode kXB = kXNone;
   const bf16 *x_perm, *dh1, *dh3;
   int64_t H, F;
   int E;
@@ -778,19 +820,64 @@ struct Pipe {
   int w, wm, wn, lane;
   Dma<K::ATR> da;
   Dma<K::BTR> db;
+  // B rows straight from x (K::kXB == kXDirect): na holds the padded-row ->
+  // token lookup of the next tile's 32 rows of this wave (one vector load,
+  // issued a tile ahead by lookup()); boff, this tile's row offsets, worked
+  // out from it at step 0.  The lookup is read only after an explicit wait
+  // that covers it: the compiler cannot see the DMA, so a wait of its own
+  // there would be for all vector memory in flight, the DMA included.
+  uint32_t na = 0;
+  uint32_t boff[4] = {0u, 0u, 0u, 0u};
 
   __device__ __forceinline__ uint32_t stage_addr(int s) const { return lbase + (s & 1) * kStage; }
+
+  // Issues tile j's first lookups; returns the vector-memory operations
+  // issued (they are younger than everything in flight).
+  __device__ __forceinline__ int lookup(const Job& j) {
+    if constexpr (K::kXB == kXDirect) {
+      na = (uint32_t)k.xr.row_token[k.x_rows(j, w) + (lane & 31)];
+      return 1;
+    } else {
+      return 0;
+    }
+  }
   __device__ __forceinline__ const char* stage_ptr(int s) const { return lds + (s & 1) * kStage; }
 
   // DMA of step s of tile j into the stage of this block's step gs.
-  __device__ __forceinline__ void issue_step(const Job& j, int s, int gs) const {
+  __device__ __forceinline__ void issue_step(const Job& j, int s, int gs) {
     const int seg = s >= j.nk ? 1 : 0;
     const int ks = s - seg * j.nk;
     const char *a0, *a1, *b0, *b1;
     k.operands(j, seg, a0, a1, b0, b1);
     const uint32_t st = stage_addr(gs);
+    // B rows straight from x: the lanes fill the same LDS image as issue<>,
+    // each from its row's token row of x (a pad row's offset is past the
+    // records of x).  The offsets are worked out before any DMA of this
+    // step goes out (see na).
+    uint32_t off[4];
+    if constexpr (K::kXB == kXDirect) {
+      // instruction i, lane l: B row 8i + l/8 of the wave's 32, physical
+      // chunk l%8 (the direct swizzle of a block of parity i%2)
+      const uint32_t ld = k.ldb();
+      if (s == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = __builtin_amdgcn_ds_bpermute((8 * i + (lane >> 3)) << 2, (int)na);
+          const uint32_t c = (uint32_t)((lane & 7) ^ (lane >> 3) ^ (i & 1)) << 4;
+          boff[i] = (tok >= 0 ? (uint32_t)tok * ld : kNoRow) + c;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) off[i] = boff[i] + (uint32_t)ks * kRowB;
+    }
     issue<K::ATR>(a0, a1, k.lda(), da, ks, w, st);
-    issue<K::BTR>(b0, b1, k.ldb(), db, ks, w, st + kReg);
+    if constexpr (K::kXB == kXNone) {
+      issue<K::BTR>(b0, b1, k.ldb(), db, ks, w, st + kReg);
+    } else {
+      const rsrc_t r = make_rsrc_n(reinterpret_cast<const char*>(k.xr.x), k.xr.bytes);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma16(r, st + kReg + (4 * w + i) * 1024, off[i], 0u);
+    }
   }
 
   // The K loop of one tile for one group of waves (G0: wm == 0), after the
@@ -888,6 +975,9 @@ struct Ops {
     if (first(j)) p1.issue_step(j, s, gs);
     else p2.issue_step(j, s, gs);
   }
+  __device__ __forceinline__ int lookup(const Job& j) const {
+    return first(j) ? p1.lookup(j) : p2.lookup(j);
+  }
   // whether the tile's epilogue reads through its free-stage blocks, so that
   // step 1 of the next tile (which lands there) must wait for it
   __device__ __forceinline__ bool late(const Job& j) const {
@@ -941,6 +1031,7 @@ __device__ __forceinline__ void engine(O& o, int total, TileOf&& tile_of, char* 
     bool started = false;
     if (n > 0) {
       if (!primed) {
+        o.lookup(cur);
         o.issue(cur, 0, g);
         if (n > 1) o.issue(cur, 1, g + 1);
         w0 = n > 1 ? kDmaPerStep : 0;
@@ -948,9 +1039,11 @@ __device__ __forceinline__ void engine(O& o, int total, TileOf&& tile_of, char* 
       }
       wait_vm_n(w0);                       // step 0 landed
       barrier();
+      // the next tile's B-row lookups (x rows), younger than all in flight
+      const int lk = nxt.steps > 0 ? o.lookup(nxt) : 0;
       const auto next = [&](int gs) { o.issue(nxt, 0, gs); };
-      if (w < 4) o.template loop<true>(acc, cur, nxt, g, w1, next);
-      else o.template loop<false>(acc, cur, nxt, g, w1, next);
+      if (w < 4) o.template loop<true>(acc, cur, nxt, g, w1 + lk, next);
+      else o.template loop<false>(acc, cur, nxt, g, w1 + lk, next);
       g += n;
       started = n >= 2 && nxt.steps > 0;
     }
@@ -1136,12 +1229,16 @@ __device__ __forceinline__ void persistent_dual(const K1& k1, const K2& k2, bool
   }
 }
 
+// X: x_perm is x itself ([T, H]) and B rows come through row_token.
+template <bool X>
 __global__ void __launch_bounds__(kThreads)
 up_kernel(const bf16* __restrict__ x_perm, const bf16* __restrict__ w1,
           const bf16* __restrict__ w3, int64_t H, int64_t F, ROW_TILE_ARGS,
+          const int32_t* __restrict__ row_token, uint32_t x_bytes,
           bf16* __restrict__ h1, bf16* __restrict__ h3, bf16* __restrict__ act) {
-  Up k{x_perm, w1, w3, H, F, h1, h3, act};
+  UpT<X> k{x_perm, w1, w3, H, F, h1, h3, act};
   k.rt.init(tile_expert, num_padded_rows, pair_first, num_pairs, (int)(F / 128));
+  k.xr = XRows{x_perm, row_token, x_bytes};
   persistent(k);
 }
 
@@ -1232,13 +1329,24 @@ static dim3 persistent_grid(int64_t max_total) {
 template <typename T> static const T* cb(const void* p) { return static_cast<const T*>(p); }
 template <typename T> static T* mb(void* p) { return static_cast<T*>(p); }
 
-hipError_t launch_bf16_up(const Shape& s, const void* x_perm, const void* w1, const void* w3,
-                          const MetaPtrs& m, void* h1, void* h3, void* act,
+// Bytes of x [T, H] bf16, the records of its buffer resource (the callers
+// check that it stays below 2 GB).
+static uint32_t x_bytes(const Shape& s) { return (uint32_t)(s.T * s.H * 2); }
+
+hipError_t launch_bf16_up(const Shape& s, const void* x_perm, const void* x, const void* w1,
+                          const void* w3, const MetaPtrs& m, void* h1, void* h3, void* act,
                           hipStream_t stream) {
-  hipLaunchKernelGGL(bfk::up_kernel, persistent_grid(cdiv(s.F, 128) * s.max_tiles),
-                     dim3(bfk::kThreads), 0, stream, cb<bf16>(x_perm), cb<bf16>(w1),
-                     cb<bf16>(w3), s.H, s.F, m.tile_expert, m.num_padded_rows, m.pair_first,
-                     m.num_pairs, mb<bf16>(h1), mb<bf16>(h3), mb<bf16>(act));
+  const dim3 grid = persistent_grid(cdiv(s.F, 128) * s.max_tiles);
+  if (x)
+    hipLaunchKernelGGL(bfk::up_kernel<true>, grid, dim3(bfk::kThreads), 0, stream, cb<bf16>(x),
+                       cb<bf16>(w1), cb<bf16>(w3), s.H, s.F, m.tile_expert, m.num_padded_rows,
+                       m.pair_first, m.num_pairs, m.row_token, x_bytes(s), mb<bf16>(h1),
+                       mb<bf16>(h3), mb<bf16>(act));
+  else
+    hipLaunchKernelGGL(bfk::up_kernel<false>, grid, dim3(bfk::kThreads), 0, stream,
+                       cb<bf16>(x_perm), cb<bf16>(w1), cb<bf16>(w3), s.H, s.F, m.tile_expert,
+                       m.num_padded_rows, m.pair_first, m.num_pairs, m.row_token, 0u,
+                       mb<bf16>(h1), mb<bf16>(h3), mb<bf16>(act));
   return hipGetLastError();
 }
 

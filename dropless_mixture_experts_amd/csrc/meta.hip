@@ -19,9 +19,11 @@
 //               matrix products process together, the status word.
 //   meta_place  one wave per chunk: stable rank of every entry among the
 //               chunk's entries of the same expert (64-lane ballots on the
-//               bits of the id + mbcnt), then writes indices, bin_ids and
-//               row_of_entry.  Ties keep ascending entry order, so the
-//               result is unique and bit-identical on every run.
+//               bits of the id + mbcnt), then writes indices, bin_ids,
+//               row_of_entry and the token of the entry's padded row
+//               (row_token; meta_scan marks the pad rows -1).  Ties keep
+//               ascending entry order, so the result is unique and
+//               bit-identical on every run.
 #include <algorithm>
 #include <cmath>
 
@@ -74,7 +76,8 @@ meta_scan_kernel(int32_t* __restrict__ hist, const int32_t* __restrict__ err,
                  int32_t* __restrict__ num_padded_rows,
                  int32_t* __restrict__ status,
                  int32_t* __restrict__ pair_first,
-                 int32_t* __restrict__ num_pairs) {
+                 int32_t* __restrict__ num_pairs,
+                 int32_t* __restrict__ row_token) {
   __shared__ int32_t seg_tot[kScanThreads];
   __shared__ int32_t count_s[kMaxExperts];
   __shared__ int32_t start_s[kMaxExperts];
@@ -202,18 +205,25 @@ meta_scan_kernel(int32_t* __restrict__ hist, const int32_t* __restrict__ err,
     for (int q = 0; q < ng; ++q) pair_first[g0 + q] = t0 + 2 * q;
   }
   for (int r = S_s + tid; r < max_tiles; r += kScanThreads) pair_first[r] = -1;
+  // Pad rows hold no token: rows [pend - pc + c, pend) of each expert (at
+  // most 127 per expert, MegaBlocks §2).
+  for (int q = tid; q < E * (kBlock - 1); q += kScanThreads) {
+    const int ee = q / (kBlock - 1), i = q - ee * (kBlock - 1);
+    const int c = count_s[ee], pc = round_up_block(c);
+    if (i < pc - c) row_token[pend_s[ee] - pc + c + i] = -1;
+  }
   if (tid == 0) *status = bad_s ? kErrExpertId : 0;
 }
 
 __global__ void __launch_bounds__(kMetaWaves * kWave)
 meta_place_kernel(const int32_t* __restrict__ ids, int64_t n, int64_t chunk,
-                  int nchunks, int E, int nbits,
+                  int nchunks, int E, int k, int nbits,
                   const int32_t* __restrict__ chunk_start,
                   const int32_t* __restrict__ tokens_per_expert,
                   const int32_t* __restrict__ bins,
                   const int32_t* __restrict__ padded_bins,
                   int32_t* __restrict__ indices, int32_t* __restrict__ bin_ids,
-                  int32_t* __restrict__ row_of_entry) {
+                  int32_t* __restrict__ row_of_entry, int32_t* __restrict__ row_token) {
   __shared__ int32_t run[kMetaWaves][kMaxExperts];
   __shared__ int32_t shift_s[kMaxExperts];   // padded start - sorted start
   const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -248,6 +258,7 @@ meta_place_kernel(const int32_t* __restrict__ ids, int64_t n, int64_t chunk,
       indices[pos] = (int32_t)a;
       bin_ids[pos] = e;
       row_of_entry[a] = pos + shift_s[e];
+      row_token[pos + shift_s[e]] = (int32_t)(a / k);
       if ((same & lt) == 0ull) run[w][e] = pos + __popcll(same);  // group leader
     } else if (in) {
       row_of_entry[a] = -1;
@@ -286,7 +297,7 @@ int64_t meta_workspace_bytes(int64_t n, int E) {
   return ((nc * E + nc) * (int64_t)sizeof(int32_t) + 255) / 256 * 256;
 }
 
-hipError_t launch_metadata(int64_t n, int E, int64_t max_tiles,
+hipError_t launch_metadata(int64_t n, int E, int k, int64_t max_tiles,
                            const int32_t* ids, const MetaPtrs& m, void* ws,
                            hipStream_t stream, hipEvent_t* ev) {
   const int64_t chunk = meta_chunk(n, E);
@@ -306,12 +317,12 @@ hipError_t launch_metadata(int64_t n, int E, int64_t max_tiles,
   hipLaunchKernelGGL(meta_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream,
                      hist, err, nchunks, E, Ecap, (int)max_tiles,
                      m.tokens_per_expert, m.bins, m.padded_bins, m.tile_expert,
-                     m.num_padded_rows, m.status, m.pair_first, m.num_pairs);
+                     m.num_padded_rows, m.status, m.pair_first, m.num_pairs, m.row_token);
   if (ev && (rc = hipEventRecord(ev[2], stream)) != hipSuccess) return rc;
   hipLaunchKernelGGL(meta_place_kernel, dim3(blocks), dim3(kMetaWaves * kWave), 0,
-                     stream, ids, n, chunk, nchunks, E, nbits, hist,
+                     stream, ids, n, chunk, nchunks, E, k, nbits, hist,
                      m.tokens_per_expert, m.bins, m.padded_bins, m.indices,
-                     m.bin_ids, m.row_of_entry);
+                     m.bin_ids, m.row_of_entry, m.row_token);
   if (ev && (rc = hipEventRecord(ev[3], stream)) != hipSuccess) return rc;
   return hipGetLastError();
 }

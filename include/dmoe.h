@@ -101,7 +101,11 @@ typedef struct {
  *                         the same expert (each expert's blocks are paired
  *                         in order; an odd last block stays single); -1
  *                         past the last group
- *   num_pairs[1]          number of groups                                 */
+ *   num_pairs[1]          number of groups
+ *   row_token[max_tiles*128] the token whose row padded row p holds: a / k
+ *                         for the entry a placed there (the §4.2 index rule
+ *                         read from the row side), -1 for a pad row below P;
+ *                         rows from P on are left untouched                */
 typedef struct {
   int32_t *tokens_per_expert, *bins, *padded_bins;
   int32_t *indices, *bin_ids, *row_of_entry;
@@ -110,6 +114,7 @@ typedef struct {
   int32_t *status;
   int32_t *pair_first;
   int32_t *num_pairs;
+  int32_t *row_token;
 } dmoe_meta;
 
 /* Activations kept from forward for backward, each [P_max, H] or [P_max, F]
@@ -183,6 +188,33 @@ int dmoe_backward_recompute(const dmoe_dims* dims, const void* dy, const float* 
                             const dmoe_grad_scratch* scratch, void* dx, void* dw1,
                             void* dw3, void* dw2, float* d_weights, hipStream_t stream);
 
+/* The forward with the gather fused into the up projection's operand loads
+ * (bf16 only), and its backward.  Fine-grained experts are bound by memory
+ * IO, and overlapping that IO with the products is how the pages' own
+ * design answers it ("SonicMoE: Accelerating MoE with IO and Tile-aware
+ * Optimizations", abstract).  Here the up projection fetches padded row p
+ * as token row meta.row_token[p] of x (zeros for a pad row) straight into
+ * its tiles, so the forward writes no x_perm: the padded copy of
+ * MegaBlocks §4.2 is never made in the forward and need not be kept until
+ * the backward.  dmoe_backward_fused_gather takes the forward's x and
+ * gathers x_perm into saved->x_perm, which is scratch on entry (its memory
+ * may serve other work between forward and backward), before the products
+ * that read it.  Every result and every other saved or scratch
+ * buffer is bit-identical to dmoe_forward / dmoe_backward on the same
+ * inputs.
+ *   dmoe_forward_fused_gather: saved->x_perm may be NULL (it is not used).
+ * DMOE_ERR_UNSUPPORTED for fp32 or when T*H*2 >= 2^31 (x is read through a
+ * buffer resource of T*H*2 bytes). */
+int dmoe_forward_fused_gather(const dmoe_dims* dims, const void* x, const float* weights,
+                              const void* w1, const void* w3, const void* w2,
+                              const dmoe_meta* meta, const dmoe_saved* saved, void* y,
+                              hipStream_t stream);
+int dmoe_backward_fused_gather(const dmoe_dims* dims, const void* x, const void* dy,
+                               const float* weights, const void* w1, const void* w3,
+                               const void* w2, const dmoe_meta* meta, const dmoe_saved* saved,
+                               const dmoe_grad_scratch* scratch, void* dx, void* dw1, void* dw3,
+                               void* dw2, float* d_weights, hipStream_t stream);
+
 /* padded_gather alone (MegaBlocks §4.2, gather direction): for every real
  * padded row p of entry a, x_perm[p] = x[a / k]; pad rows below P are zero.
  * x [T,H], x_perm [P_max,H] of dtype; *meta from dmoe_metadata. */
@@ -227,7 +259,7 @@ int dmoe_router_backward(const dmoe_dims* dims, const float* logits,
                          const float* d_weights, float zloss_coef, float* d_logits,
                          hipStream_t stream);
 
-/* The same three calls with per-kernel timing.  `events` is NULL or an array
+/* The forward and backward calls with per-kernel timing.  `events` is NULL or an array
  * of n+1 caller-created hipEvent_t; event i is recorded on `stream` just
  * before kernel i and event n after the last kernel, so the elapsed time
  * between events i and i+1 is kernel i's duration on the stream.
@@ -240,6 +272,10 @@ int dmoe_router_backward(const dmoe_dims* dims, const float* logits,
  *                     first dw1/dw3 tiles), gather backward (dx), dw1 + dw3.
  *   backward_recompute (n = 6): the activation recompute, then the five
  *                     kernels of the backward.
+ *   forward_fused_gather (n = 3): the forward's kernels but padded_gather.
+ *   backward_fused_gather (n = 6): scatter backward, down dgrad + dw2,
+ *                     padded_gather (x_perm), up dgrad, gather backward,
+ *                     dw1 + dw3.
  * Results are identical to the untimed calls. */
 int dmoe_metadata_timed(const dmoe_dims* dims, const int32_t* top_experts,
                         const dmoe_meta* meta, void* ws, hipStream_t stream,
@@ -260,6 +296,17 @@ int dmoe_backward_recompute_timed(const dmoe_dims* dims, const void* dy, const f
                                   const dmoe_grad_scratch* scratch, void* dx, void* dw1,
                                   void* dw3, void* dw2, float* d_weights, hipStream_t stream,
                                   hipEvent_t* events);
+
+int dmoe_forward_fused_gather_timed(const dmoe_dims* dims, const void* x, const float* weights,
+                                    const void* w1, const void* w3, const void* w2,
+                                    const dmoe_meta* meta, const dmoe_saved* saved, void* y,
+                                    hipStream_t stream, hipEvent_t* events);
+int dmoe_backward_fused_gather_timed(const dmoe_dims* dims, const void* x, const void* dy,
+                                     const float* weights, const void* w1, const void* w3,
+                                     const void* w2, const dmoe_meta* meta,
+                                     const dmoe_saved* saved, const dmoe_grad_scratch* scratch,
+                                     void* dx, void* dw1, void* dw3, void* dw2, float* d_weights,
+                                     hipStream_t stream, hipEvent_t* events);
 
 /* Static text for a dmoe_status value. */
 const char* dmoe_status_string(int status);

@@ -47,7 +47,7 @@ def assert_close(got, ref, tol, name):
 class Run:
     """Uploads one workload and runs metadata + forward + backward."""
 
-    def __init__(self, inp, dev=None, lean=False, backward=True):
+    def __init__(self, inp, dev=None, lean=False, backward=True, fused_gather=False):
         self.inp = inp
         self.cfg = inp.cfg
         self.dev = dev or device()
@@ -60,7 +60,7 @@ class Run:
         self.w3 = up(inp.w3, dt, self.dev)
         self.w2 = up(inp.w2, dt, self.dev)
         self.dy = up(inp.dy, dt, self.dev) if backward else None
-        self.layer = dm.DMoELayer(self.D, self.dev, lean=lean)
+        self.layer = dm.DMoELayer(self.D, self.dev, lean=lean, fused_gather=fused_gather)
         self.y = self.layer.forward(self.x, self.ids, self.w, self.w1, self.w3, self.w2)
         self.g = (self.layer.backward(self.dy, self.w, self.w1, self.w3, self.w2)
                   if backward else None)

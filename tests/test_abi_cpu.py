@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
     for n in ("dmoe_metadata", "dmoe_forward", "dmoe_backward", "dmoe_max_tiles",
               "dmoe_workspace_bytes", "dmoe_padded_gather", "dmoe_padded_scatter",
               "dmoe_status_string", "dmoe_router_forward", "dmoe_router_backward",
-              "dmoe_backward_recompute", "dmoe_backward_recompute_timed"):
+              "dmoe_backward_recompute", "dmoe_backward_recompute_timed",
+              "dmoe_forward_fused_gather", "dmoe_backward_fused_gather"):
         assert n in names
 
 
@@ -65,19 +66,19 @@ def test_bad_dims_rejected(lib, kw, code):
     d = _dims(**kw)
     assert lib.dmoe_max_tiles(ctypes.byref(d)) == code
     assert lib.dmoe_workspace_bytes(ctypes.byref(d)) == code
-    meta = dm._Meta(*([ctypes.c_void_p(0x1000)] * 11))
+    meta = dm._Meta(*([ctypes.c_void_p(0x1000)] * 12))
     assert lib.dmoe_metadata(ctypes.byref(d), ctypes.c_void_p(0x1000),
                              ctypes.byref(meta), ctypes.c_void_p(0x1000), None) == code
 
 
 def test_null_pointers_rejected_before_launch(lib):
     d = _dims()
-    meta = dm._Meta(*([ctypes.c_void_p(0x1000)] * 11))
+    meta = dm._Meta(*([ctypes.c_void_p(0x1000)] * 12))
     assert lib.dmoe_metadata(ctypes.byref(d), None, ctypes.byref(meta),
                              ctypes.c_void_p(0x1000), None) == -1
     assert lib.dmoe_metadata(ctypes.byref(d), ctypes.c_void_p(0x1000),
                              ctypes.byref(meta), None, None) == -1
-    bad = dm._Meta(*([ctypes.c_void_p(0x1000)] * 10 + [None]))
+    bad = dm._Meta(*([ctypes.c_void_p(0x1000)] * 11 + [None]))
     assert lib.dmoe_metadata(ctypes.byref(d), ctypes.c_void_p(0x1000),
                              ctypes.byref(bad), ctypes.c_void_p(0x1000), None) == -1
     saved = dm._Saved(*([ctypes.c_void_p(0x1000)] * 4 + [None]))
@@ -103,6 +104,38 @@ def test_null_pointers_rejected_before_launch(lib):
                                    None, None) == -1
     assert lib.dmoe_forward(None, p, p, p, p, p, ctypes.byref(meta),
                             ctypes.byref(saved), p, None) == -1
+
+
+def test_fused_gather_checks_before_launch(lib):
+    """The fused gather is bf16 only, needs x below 2 GB and, in the
+    backward, the forward's x; a meta without row_token is rejected."""
+    p = ctypes.c_void_p(0x1000)
+    meta = dm._Meta(*([p] * 12))
+    saved = dm._Saved(None, p, p, p, p)          # no x_perm: allowed here
+    scratch = dm._Scratch(p, p, p, p)
+    f32 = _dims()
+    big = _dims(T=1 << 20, H=1024, E=8, k=1, dtype=dm.DMOE_BF16)   # T*H*2 = 2^31
+    for d in (f32, big):
+        assert lib.dmoe_forward_fused_gather(ctypes.byref(d), p, p, p, p, p, ctypes.byref(meta),
+                                             ctypes.byref(saved), p, None) == -3
+        assert lib.dmoe_backward_fused_gather(ctypes.byref(d), p, p, p, p, p, p,
+                                              ctypes.byref(meta), ctypes.byref(saved),
+                                              ctypes.byref(scratch), p, p, p, p, p,
+                                              None) == -3
+    bf = _dims(dtype=dm.DMOE_BF16)
+    assert lib.dmoe_backward_fused_gather(ctypes.byref(bf), None, p, p, p, p, p,
+                                          ctypes.byref(meta), ctypes.byref(saved),
+                                          ctypes.byref(scratch), p, p, p, p, p, None) == -1
+    no_rt = dm._Meta(*([p] * 11 + [None]))
+    assert lib.dmoe_forward_fused_gather(ctypes.byref(bf), p, p, p, p, p, ctypes.byref(no_rt),
+                                         ctypes.byref(saved), p, None) == -1
+    # the plain path needs x_perm, and so does the fused backward (it
+    # gathers into it)
+    assert lib.dmoe_forward(ctypes.byref(bf), p, p, p, p, p, ctypes.byref(meta),
+                            ctypes.byref(saved), p, None) == -1
+    assert lib.dmoe_backward_fused_gather(ctypes.byref(bf), p, p, p, p, p, p,
+                                          ctypes.byref(meta), ctypes.byref(saved),
+                                          ctypes.byref(scratch), p, p, p, p, p, None) == -1
 
 
 def test_router_checks_before_launch(lib):

@@ -28,6 +28,7 @@ def _run_meta(ids_np, E, dtype=dm.DMOE_BF16, H=128, F=128):
     for name in KEYS:
         getattr(meta, name).fill_(-12345)
     meta.status.fill_(777)
+    meta.row_token.fill_(-12345)
     ids = torch.from_numpy(np.ascontiguousarray(ids_np, dtype=np.int32)).to(dev)
     print(f"metadata T={T} k={k} E={E}", flush=True)
     dm.dmoe_metadata(D, ids, meta, ws)
@@ -37,6 +38,7 @@ def _run_meta(ids_np, E, dtype=dm.DMOE_BF16, H=128, F=128):
     out["status"] = int(meta.status.item())
     out["pair_first"] = meta.pair_first.cpu().numpy().astype(np.int64)
     out["num_pairs"] = int(meta.num_pairs.item())
+    out["row_token"] = meta.row_token.cpu().numpy().astype(np.int64)
     return out, dm.dmoe_max_tiles(D)
 
 
@@ -64,6 +66,10 @@ def _compare(ids_np, E):
         np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
     assert got["P"] == ref["P"]
     _check_pairs(got)
+    P = ref["P"]
+    np.testing.assert_array_equal(got["row_token"][:P], oracle.row_token(ref, ids_np.shape[1]),
+                                  err_msg="row_token")
+    assert np.all(got["row_token"][P:] == -12345)     # rows from P on untouched
     return got
 
 
