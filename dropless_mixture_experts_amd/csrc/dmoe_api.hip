@@ -60,12 +60,13 @@ MetaPtrs meta_ptrs(const dmoe_meta* m) {
                   m->status, m->pair_first, m->num_pairs, m->row_token};
 }
 
-// Records events[i] on the stream when timing is requested.
+// Records events[i] on the stream when timing is requested and the entry is
+// not NULL.
 struct Recorder {
   hipEvent_t* events;
   hipStream_t stream;
   hipError_t operator()(int i) const {
-    return events ? hipEventRecord(events[i], stream) : hipSuccess;
+    return events && events[i] ? hipEventRecord(events[i], stream) : hipSuccess;
   }
 };
 

@@ -310,20 +310,20 @@ hipError_t launch_metadata(int64_t n, int E, int k, int64_t max_tiles,
   while ((1 << nbits) < E) ++nbits;
   const int blocks = (nchunks + kMetaWaves - 1) / kMetaWaves;
   hipError_t rc = hipSuccess;
-  if (ev && (rc = hipEventRecord(ev[0], stream)) != hipSuccess) return rc;
+  if (ev && ev[0] && (rc = hipEventRecord(ev[0], stream)) != hipSuccess) return rc;
   hipLaunchKernelGGL(meta_hist_kernel, dim3(blocks), dim3(kMetaWaves * kWave), 0,
                      stream, ids, n, chunk, nchunks, E, hist, err);
-  if (ev && (rc = hipEventRecord(ev[1], stream)) != hipSuccess) return rc;
+  if (ev && ev[1] && (rc = hipEventRecord(ev[1], stream)) != hipSuccess) return rc;
   hipLaunchKernelGGL(meta_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream,
                      hist, err, nchunks, E, Ecap, (int)max_tiles,
                      m.tokens_per_expert, m.bins, m.padded_bins, m.tile_expert,
                      m.num_padded_rows, m.status, m.pair_first, m.num_pairs, m.row_token);
-  if (ev && (rc = hipEventRecord(ev[2], stream)) != hipSuccess) return rc;
+  if (ev && ev[2] && (rc = hipEventRecord(ev[2], stream)) != hipSuccess) return rc;
   hipLaunchKernelGGL(meta_place_kernel, dim3(blocks), dim3(kMetaWaves * kWave), 0,
                      stream, ids, n, chunk, nchunks, E, k, nbits, hist,
                      m.tokens_per_expert, m.bins, m.padded_bins, m.indices,
                      m.bin_ids, m.row_of_entry, m.row_token);
-  if (ev && (rc = hipEventRecord(ev[3], stream)) != hipSuccess) return rc;
+  if (ev && ev[3] && (rc = hipEventRecord(ev[3], stream)) != hipSuccess) return rc;
   return hipGetLastError();
 }
 

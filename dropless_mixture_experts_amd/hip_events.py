@@ -28,12 +28,17 @@ def _lib():
 
 
 class EventArray:
-    """n hipEvent_t handles, created on the current device."""
+    """n hipEvent_t handles, created on the current device.  only: if given,
+    the indices that get an event; the other entries are NULL, and the
+    library skips those records (so that timing one kernel costs two
+    records, not one per kernel)."""
 
-    def __init__(self, n: int):
+    def __init__(self, n: int, only=None):
         lib = _lib()
         self._arr = (ctypes.c_void_p * n)()
         for i in range(n):
+            if only is not None and i not in only:
+                continue
             h = ctypes.c_void_p()
             rc = lib.hipEventCreate(ctypes.byref(h))
             if rc != 0:

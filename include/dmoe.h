@@ -259,10 +259,13 @@ int dmoe_router_backward(const dmoe_dims* dims, const float* logits,
                          const float* d_weights, float zloss_coef, float* d_logits,
                          hipStream_t stream);
 
-/* The forward and backward calls with per-kernel timing.  `events` is NULL or an array
- * of n+1 caller-created hipEvent_t; event i is recorded on `stream` just
- * before kernel i and event n after the last kernel, so the elapsed time
- * between events i and i+1 is kernel i's duration on the stream.
+/* The metadata, forward and backward calls with per-kernel timing.  `events`
+ * is NULL or an array of n+1 hipEvent_t; event i is recorded on `stream`
+ * just before kernel i and event n after the last kernel, so the elapsed
+ * time between events i and i+1 is kernel i's duration on the stream.  An
+ * entry may be NULL: that record is skipped (each record puts a timestamp
+ * between two kernels, so timing one kernel with two records disturbs the
+ * sequence less than timing all of them).
  *   metadata (n = 3): histogram, scan, placement.
  *   forward  (n = 4): padded_gather, up projection + SiLU gate, down
  *                     projection, padded_scatter.
