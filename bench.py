@@ -378,6 +378,10 @@ def main():
         "gemm_executed_frac_peak": round(executed_flop / (gemm_ms * 1e-3) / 1e12 / peak, 4),
         "gather_scatter_frac_hbm": round(gs_bytes / (gs_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "metadata_us": round(1e3 * sum(per[n] for n in META_KERNELS), 1),
+        # latency-bound: a few MB in three small launches
+        "metadata_frac_hbm": round(sum(work[n][1] for n in META_KERNELS)
+                                   / (sum(per[n] for n in META_KERNELS) * 1e-3) / 1e9
+                                   / PEAK_HBM_GBS, 5),
         "sclk_mhz_during_timing": ({"samples": len(sclk), "min": min(sclk),
                                     "median": sorted(sclk)[len(sclk) // 2],
                                     "max": max(sclk)} if sclk else None),

@@ -1,9 +1,11 @@
 """Summaries of rocprofv3 output for the dMoE kernels.
 
-    python -m dropless_mixture_experts_amd.profiling stats DIR
+    python -m dropless_mixture_experts_amd.profiling stats DIR [--window S:N]
         Per-kernel call count, total and average duration from the
         kernel-trace CSV under DIR (rocprofv3 --kernel-trace --stats
-        --output-format csv).
+        --output-format csv).  --window S:N adds the average over each
+        kernel's calls S .. S+N-1 in launch order (e.g. a benchmark's timed
+        steps, without its warm-up and untimed passes).
 
     python -m dropless_mixture_experts_amd.profiling traffic \\
         --fetch DIR_F --write DIR_W --kernel REGEX --name BENCH_NAME \\
@@ -49,15 +51,20 @@ def _rows(directory: str, pattern: str):
     return out
 
 
-def kernel_stats(directory: str):
-    """{kernel name: (calls, total_ns, avg_ns)} from a kernel-trace CSV."""
+def kernel_durations(directory: str):
+    """{kernel name: [duration_ns, ...] in launch order} from a kernel-trace CSV."""
     rows = _rows(directory, "*kernel_trace.csv")
     acc = {}
     for r in rows:
         name = r.get("Kernel_Name") or r.get("KernelName")
-        dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
-        acc.setdefault(name, []).append(dur)
-    return {k: (len(v), sum(v), sum(v) / len(v)) for k, v in acc.items()}
+        start = int(r["Start_Timestamp"])
+        acc.setdefault(name, []).append((start, int(r["End_Timestamp"]) - start))
+    return {k: [d for _, d in sorted(v)] for k, v in acc.items()}
+
+
+def kernel_stats(directory: str):
+    """{kernel name: (calls, total_ns, avg_ns)} from a kernel-trace CSV."""
+    return {k: (len(v), sum(v), sum(v) / len(v)) for k, v in kernel_durations(directory).items()}
 
 
 def _counter(directory: str, counter: str, kernel_re: str):
@@ -138,6 +145,7 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("dir")
+    s.add_argument("--window", help="S:N, the average over calls S .. S+N-1 too")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -167,10 +175,16 @@ def main(argv=None):
             print(f"{name:28s} " + " ".join(cells))
         return 0
     if a.cmd == "stats":
-        st = kernel_stats(a.dir)
-        print(f"{'kernel':72s} {'calls':>6s} {'total_us':>11s} {'avg_us':>10s}")
-        for k, (n, tot, avg) in sorted(st.items(), key=lambda kv: -kv[1][1]):
-            print(f"{k[:72]:72s} {n:6d} {tot / 1e3:11.1f} {avg / 1e3:10.2f}")
+        durs = kernel_durations(a.dir)
+        win = tuple(int(v) for v in a.window.split(":")) if a.window else None
+        head = f"{'kernel':72s} {'calls':>6s} {'total_us':>11s} {'avg_us':>10s}"
+        print(head + (f" {'window_avg_us':>14s}" if win else ""))
+        for k, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+            line = f"{k[:72]:72s} {len(v):6d} {sum(v) / 1e3:11.1f} {sum(v) / len(v) / 1e3:10.2f}"
+            if win:
+                w = v[win[0]:win[0] + win[1]]
+                line += f" {sum(w) / len(w) / 1e3:14.2f}" if w else f" {'-':>14s}"
+            print(line)
     else:
         res = traffic(a)
         text = json.dumps(res, indent=1)
