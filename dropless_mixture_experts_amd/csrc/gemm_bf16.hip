@@ -372,7 +372,8 @@ __device__ __forceinline__ int stage_half(char* st, const Acc& acc, int h, bf16*
 struct Job {
   int steps, nk;
   int kind;         // which product of a merged launch (0 or 1)
-  int e;            // expert (weight gradients: expert | first padded row << 8)
+  int e;            // expert
+  int start;        // weight gradients: the expert's first padded row
   bool fa, fb;      // second half of A / B present
   int64_t u, v;     // tile coordinates
 };
@@ -733,11 +734,12 @@ struct WgradDown {
     j.fb = j.v + 256 <= F;
     const int n = round_up_block(tpe[e]);
     j.nk = j.steps = n / kKStep;
-    j.e = e | ((padded_bins[e] - n) << 8);
+    j.e = e;
+    j.start = padded_bins[e] - n;
   }
   __device__ void operands(const Job& j, int, const char*& a0, const char*& a1, const char*& b0,
                            const char*& b1) const {
-    const int64_t start = j.e >> 8;
+    const int64_t start = j.start;
     a0 = (const char*)(dy_perm + start * H + j.u);
     a1 = j.fa ? a0 + 128 * 2 : a0;
     b0 = (const char*)(act + start * F + j.v);
@@ -746,7 +748,7 @@ struct WgradDown {
   __device__ int epilogue(const Job& j, const Acc& acc, const Epi& ep) const {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
     if (!j.fb && wn >= 2) return 0;
-    bf16* out = dw2 + (int64_t)(j.e & 255) * F * H + j.v * H + j.u + (int64_t)(wn * 64) * H +
+    bf16* out = dw2 + (int64_t)j.e * F * H + j.v * H + j.u + (int64_t)(wn * 64) * H +
                 wm * 64;
     int n = stage_half(ep.stg, acc, 0, out, H, lane);
     if (j.fa) n += stage_half(ep.stg, acc, 1, out + 128, H, lane);
@@ -789,11 +791,12 @@ struct WgradUp {
     j.fb = j.v + 256 <= H;
     const int n = round_up_block(tpe[e]);
     j.nk = j.steps = n / kKStep;
-    j.e = e | ((padded_bins[e] - n) << 8);
+    j.e = e;
+    j.start = padded_bins[e] - n;
   }
   __device__ void operands(const Job& j, int, const char*& a0, const char*& a1, const char*& b0,
                            const char*& b1) const {
-    const int64_t start = j.e >> 8;
+    const int64_t start = j.start;
     a0 = (const char*)(dh1 + start * F + j.u);
     a1 = (const char*)(dh3 + start * F + j.u);
     b0 = (const char*)(x_perm + start * H + j.v);
@@ -803,7 +806,7 @@ struct WgradUp {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w >> 2, wn = w & 3;
     if (!j.fb && wn >= 2) return 0;
     // A rows 0..127 are dw1 columns, 128..255 the same dw3 columns
-    const int64_t o = (int64_t)(j.e & 255) * H * F + j.v * F + j.u + (int64_t)(wn * 64) * F +
+    const int64_t o = (int64_t)j.e * H * F + j.v * F + j.u + (int64_t)(wn * 64) * F +
                       wm * 64;
     return stage_half(ep.stg, acc, 0, dw1 + o, F, lane) + stage_half(ep.stg, acc, 1, dw3 + o, F, lane);
   }

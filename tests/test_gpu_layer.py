@@ -133,13 +133,26 @@ def _picks(inp, md, rng, n=24):
     return picks
 
 
+# Padded buffers of 4.4 GB each (P x H x 2 > 2^32 bytes): every offset past
+# 32 bits, at the largest row counts the tests reach.
+LARGE = shrink(CONFIGS["fine_e64"], T=32768, H=8192, F=128)
+
+
 @pytest.mark.parametrize("name", ["tiny_f32", "fine_e64", "zipf_e64",
-                                  "zipf_e64_empty", "coarse_e8", "sparse_e256"])
+                                  "zipf_e64_empty", "coarse_e8", "sparse_e256",
+                                  "large_over_4gb"])
 def test_full_size_sampled(name):
-    cfg = CONFIGS[name]
+    cfg = LARGE if name == "large_over_4gb" else CONFIGS[name]
     inp = make_inputs(cfg)
     print(f"full {name}", flush=True)
     r = Run(inp)
+    if name == "large_over_4gb":
+        assert r.P * cfg.H * 2 > (1 << 32)
+        f = Run(inp, fused_gather=True)
+        assert torch.equal(f.y, r.y)
+        for key in OUTS:
+            assert torch.equal(f.g[key], r.g[key]), key
+        del f
     tol = TOL[cfg.dtype]
     md = oracle.metadata(inp.top_experts, cfg.E, len(r.meta.tile_expert))
     got_md = r.meta_np()
