@@ -117,8 +117,8 @@ def cpu_baseline(inp, budget_s=30.0):
 
 
 def gpu_sclk_mhz():
-    """The shader clock the driver reports as current (sysfs pp_dpm_sclk, the
-    level marked '*'), or None where it is not readable."""
+    """The shader clock the amdgpu kernel driver reports as current (sysfs
+    pp_dpm_sclk, the level marked '*'), or None where it is not readable."""
     import glob
     for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
         try:
