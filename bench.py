@@ -113,7 +113,30 @@ def cpu_baseline(inp, budget_s=30.0):
             "kind": "oracle",
             "sample": (f"one full step (metadata + forward + backward, fp64 numpy, "
                        f"expert-batched) of the same {T}-token workload: {dt:.2f} s; "
-                       f"host os.cpu_count()={os.cpu_count()}")}
+                       f"host os.cpu_count()={os.cpu_count()}"),
+            "literal_loop": cpu_literal_loop(inp, threads)}
+
+
+def cpu_literal_loop(inp, threads, max_tokens=64, budget_s=20.0):
+    """The oracle's per-(token, slot) loop, forward and backward, over the
+    workload's first tokens, one token per call, until max_tokens or the time
+    budget is reached; tokens/s of that sample."""
+    import numpy as np
+    import oracle
+    n, dt = 0, 0.0
+    while n < min(max_tokens, inp.cfg.T) and dt < budget_s:
+        sl = slice(n, n + 1)
+        t0 = time.perf_counter()
+        y, _ = oracle.forward_loop(inp.x[sl], inp.top_experts[sl], inp.weights[sl],
+                                   inp.w1, inp.w3, inp.w2)
+        g = oracle.backward_loop(inp.x[sl], inp.top_experts[sl], inp.weights[sl],
+                                 inp.w1, inp.w3, inp.w2, inp.dy[sl])
+        dt += time.perf_counter() - t0
+        assert np.isfinite(y).all() and np.isfinite(g["dx"]).all()
+        n += 1
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads),
+            "sample": (f"per-token loop (fp64 numpy, forward + backward) over the first "
+                       f"{n} tokens of the workload, one token per call: {dt:.2f} s")}
 
 
 def gpu_sclk_mhz():
