@@ -387,30 +387,22 @@ constexpr int kPhaseFrags = 2;
 
 static_assert(kPhaseFrags == 1 || kPhaseFrags == 2, "one or two fragments per phase");
 
-// Row-tiled products: (m, n) for logical index L over MT x NT tiles, in
-// groups of kGroupM row tiles walked column by column, so that concurrent
-// blocks reuse both the token rows and the weight columns.
-__device__ __forceinline__ void group_mn(int L, int MT, int NT, int& m, int& n) {
-  const int per_group = kGroupM * NT;
-  const int g = L / per_group;
-  const int m0 = g * kGroupM;
-  const int gm = min(kGroupM, MT - m0);
-  const int r = L - g * per_group;
-  m = m0 + r % gm;
-  n = r / gm;
-}
-
 // The pair of row blocks (u = first 128-row block) and the column tile (v)
-// of logical row tile L, from the live metadata.
+// of logical row tile L, from the live metadata.  The pairs of each expert
+// (consecutive, from its first block) are split into ceil(p / kGroupM)
+// groups of near-equal size; a group of gm pairs from pair g0 owns logical
+// tiles [g0 NT, (g0 + gm) NT), walked column by column (pair g0 + r % gm,
+// column r / gm), so that concurrent blocks share one expert's weight
+// columns and its token rows.
 struct RowTiles {
-  const int32_t *tile_expert, *pair_first;
-  int pairs, MT, NT;
-  __device__ __forceinline__ void init(const int32_t* te, const int32_t* num_padded_rows,
-                                       const int32_t* pf, const int32_t* num_pairs, int nt) {
+  const int32_t *tile_expert, *pair_first, *padded_bins;
+  int pairs, NT;
+  __device__ __forceinline__ void init(const int32_t* te, const int32_t* pf,
+                                       const int32_t* num_pairs, const int32_t* pb, int nt) {
     tile_expert = te;
     pair_first = pf;
+    padded_bins = pb;
     pairs = *num_pairs;
-    MT = *num_padded_rows / kBlock;
     NT = nt;
   }
   __device__ __forceinline__ int total() const { return pairs * NT; }
@@ -421,19 +413,30 @@ struct RowTiles {
     hi = min(total(), lo + per);
   }
   __device__ __forceinline__ void get(int L, Job& j) const {
-    int s, n;
-    group_mn(L, pairs, NT, s, n);
-    const int m = pair_first[s];
-    j.e = tile_expert[m];
-    j.fb = m + 1 < MT && tile_expert[m + 1] == j.e;
+    const int q = L / NT;                 // a pair of L's group
+    const int mq = pair_first[q];
+    const int e = tile_expert[mq];
+    const int b0 = e > 0 ? padded_bins[e - 1] / kBlock : 0;   // the expert's blocks [b0, b1)
+    const int b1 = padded_bins[e] / kBlock;
+    const int pe = (b1 - b0 + 1) / 2;     // its pairs, the first one se
+    const int se = q - (mq - b0) / 2;
+    const int ng = (pe + kGroupM - 1) / kGroupM;
+    // group gi = [se + ceil(gi pe / ng), se + ceil((gi + 1) pe / ng)) holds q
+    const int gi = (q - se) * ng / pe;
+    const int g0 = se + (gi * pe + ng - 1) / ng;
+    const int gm = se + ((gi + 1) * pe + ng - 1) / ng - g0;
+    const int r = L - g0 * NT;
+    const int m = b0 + 2 * (g0 - se + r % gm);
+    j.e = e;
+    j.fb = m + 1 < b1;
     j.u = m;
-    j.v = n;
+    j.v = r / gm;
   }
 };
 
-#define ROW_TILE_ARGS                                                                   \
-  const int32_t *__restrict__ tile_expert, const int32_t *__restrict__ num_padded_rows, \
-      const int32_t *__restrict__ pair_first, const int32_t *__restrict__ num_pairs
+#define ROW_TILE_ARGS                                                              \
+  const int32_t *__restrict__ tile_expert, const int32_t *__restrict__ pair_first, \
+      const int32_t *__restrict__ num_pairs, const int32_t *__restrict__ padded_bins
 
 // ---- The products, as operand + epilogue policies ----------------------------
 
@@ -1240,7 +1243,7 @@ up_kernel(const bf16* __restrict__ x_perm, const bf16* __restrict__ w1,
           const int32_t* __restrict__ row_token, uint32_t x_bytes,
           bf16* __restrict__ h1, bf16* __restrict__ h3, bf16* __restrict__ act) {
   UpT<X> k{x_perm, w1, w3, H, F, h1, h3, act};
-  k.rt.init(tile_expert, num_padded_rows, pair_first, num_pairs, (int)(F / 128));
+  k.rt.init(tile_expert, pair_first, num_pairs, padded_bins, (int)(F / 128));
   k.xr = XRows{x_perm, row_token, x_bytes};
   persistent(k);
 }
@@ -1249,7 +1252,7 @@ __global__ void __launch_bounds__(kThreads)
 down_kernel(const bf16* __restrict__ act, const bf16* __restrict__ w2, int64_t H,
             int64_t F, ROW_TILE_ARGS, bf16* __restrict__ y_perm) {
   Down k{act, w2, H, F, y_perm};
-  k.rt.init(tile_expert, num_padded_rows, pair_first, num_pairs, (int)((H + 255) / 256));
+  k.rt.init(tile_expert, pair_first, num_pairs, padded_bins, (int)((H + 255) / 256));
   persistent(k);
 }
 
@@ -1258,7 +1261,7 @@ up_dgrad_kernel(const bf16* __restrict__ dh1, const bf16* __restrict__ dh3,
                 const bf16* __restrict__ w1, const bf16* __restrict__ w3, int64_t H,
                 int64_t F, ROW_TILE_ARGS, bf16* dx_perm) {
   UpDgrad k{dh1, dh3, w1, w3, H, F, dx_perm};
-  k.rt.init(tile_expert, num_padded_rows, pair_first, num_pairs, (int)((H + 255) / 256));
+  k.rt.init(tile_expert, pair_first, num_pairs, padded_bins, (int)((H + 255) / 256));
   persistent(k);
 }
 
@@ -1269,11 +1272,10 @@ __global__ void __launch_bounds__(kThreads)
 up_dgrad_fill_kernel(const bf16* __restrict__ dh1, const bf16* __restrict__ dh3,
                      const bf16* __restrict__ w1, const bf16* __restrict__ w3,
                      const bf16* __restrict__ x_perm, int64_t H, int64_t F, int E,
-                     ROW_TILE_ARGS, const int32_t* __restrict__ tpe,
-                     const int32_t* __restrict__ padded_bins, bf16* dx_perm,
+                     ROW_TILE_ARGS, const int32_t* __restrict__ tpe, bf16* dx_perm,
                      bf16* __restrict__ dw1, bf16* __restrict__ dw3) {
   UpDgrad k1{dh1, dh3, w1, w3, H, F, dx_perm};
-  k1.rt.init(tile_expert, num_padded_rows, pair_first, num_pairs, (int)((H + 255) / 256));
+  k1.rt.init(tile_expert, pair_first, num_pairs, padded_bins, (int)((H + 255) / 256));
   persistent_dual<kTailFill>(k1, WgradUp{x_perm, dh1, dh3, H, F, E, tpe, padded_bins, dw1, dw3});
 }
 
@@ -1283,11 +1285,10 @@ __global__ void __launch_bounds__(kThreads)
 down_dgrad_wgrad_down_kernel(const bf16* __restrict__ dy_perm, const bf16* __restrict__ w2,
                              const bf16* h1, const bf16* h3, const bf16* __restrict__ act,
                              int64_t H, int64_t F, int E, ROW_TILE_ARGS,
-                             const int32_t* __restrict__ tpe,
-                             const int32_t* __restrict__ padded_bins, bf16* dh1, bf16* dh3,
+                             const int32_t* __restrict__ tpe, bf16* dh1, bf16* dh3,
                              bf16* __restrict__ dw2) {
   DownDgrad k1{dy_perm, w2, h1, h3, H, F, dh1, dh3};
-  k1.rt.init(tile_expert, num_padded_rows, pair_first, num_pairs, (int)((F + 255) / 256));
+  k1.rt.init(tile_expert, pair_first, num_pairs, padded_bins, (int)((F + 255) / 256));
   persistent_dual(k1, WgradDown{act, dy_perm, H, F, E, tpe, padded_bins, dw2});
 }
 
@@ -1295,10 +1296,9 @@ __global__ void __launch_bounds__(kThreads)
 wgrad_up_kernel(const bf16* __restrict__ dh1, const bf16* __restrict__ dh3,
                 const bf16* __restrict__ w1, const bf16* __restrict__ w3,
                 const bf16* __restrict__ x_perm, int64_t H, int64_t F, int E, ROW_TILE_ARGS,
-                const int32_t* __restrict__ tpe, const int32_t* __restrict__ padded_bins,
-                int filled, bf16* dx_perm, bf16* __restrict__ dw1, bf16* __restrict__ dw3) {
+                const int32_t* __restrict__ tpe, int filled, bf16* dx_perm, bf16* __restrict__ dw1, bf16* __restrict__ dw3) {
   UpDgrad k1{dh1, dh3, w1, w3, H, F, dx_perm};
-  k1.rt.init(tile_expert, num_padded_rows, pair_first, num_pairs, (int)((H + 255) / 256));
+  k1.rt.init(tile_expert, pair_first, num_pairs, padded_bins, (int)((H + 255) / 256));
   persistent_dual<kRest>(k1, WgradUp{x_perm, dh1, dh3, H, F, E, tpe, padded_bins, dw1, dw3},
                          filled != 0);
 }
@@ -1342,13 +1342,13 @@ hipError_t launch_bf16_up(const Shape& s, const void* x_perm, const void* x, con
   const dim3 grid = persistent_grid(cdiv(s.F, 128) * s.max_tiles);
   if (x)
     hipLaunchKernelGGL(bfk::up_kernel<true>, grid, dim3(bfk::kThreads), 0, stream, cb<bf16>(x),
-                       cb<bf16>(w1), cb<bf16>(w3), s.H, s.F, m.tile_expert, m.num_padded_rows,
-                       m.pair_first, m.num_pairs, m.row_token, x_bytes(s), mb<bf16>(h1),
+                       cb<bf16>(w1), cb<bf16>(w3), s.H, s.F, m.tile_expert, m.pair_first,
+                       m.num_pairs, m.padded_bins, m.row_token, x_bytes(s), mb<bf16>(h1),
                        mb<bf16>(h3), mb<bf16>(act));
   else
     hipLaunchKernelGGL(bfk::up_kernel<false>, grid, dim3(bfk::kThreads), 0, stream,
                        cb<bf16>(x_perm), cb<bf16>(w1), cb<bf16>(w3), s.H, s.F, m.tile_expert,
-                       m.num_padded_rows, m.pair_first, m.num_pairs, m.row_token, 0u,
+                       m.pair_first, m.num_pairs, m.padded_bins, m.row_token, 0u,
                        mb<bf16>(h1), mb<bf16>(h3), mb<bf16>(act));
   return hipGetLastError();
 }
@@ -1357,7 +1357,7 @@ hipError_t launch_bf16_down(const Shape& s, const void* act, const void* w2,
                             const MetaPtrs& m, void* y_perm, hipStream_t stream) {
   hipLaunchKernelGGL(bfk::down_kernel, persistent_grid(cdiv(s.H, 256) * s.max_tiles),
                      dim3(bfk::kThreads), 0, stream, cb<bf16>(act), cb<bf16>(w2), s.H, s.F,
-                     m.tile_expert, m.num_padded_rows, m.pair_first, m.num_pairs,
+                     m.tile_expert, m.pair_first, m.num_pairs, m.padded_bins,
                      mb<bf16>(y_perm));
   return hipGetLastError();
 }
@@ -1386,14 +1386,14 @@ hipError_t launch_bf16_up_dgrad(const Shape& s, const void* dh1, const void* dh3
   if (up_dgrad_fills_tail(s)) {
     hipLaunchKernelGGL(bfk::up_dgrad_fill_kernel, up_dgrad_grid(s), dim3(bfk::kThreads), 0,
                        stream, cb<bf16>(dh1), cb<bf16>(dh3), cb<bf16>(w1), cb<bf16>(w3),
-                       cb<bf16>(x_perm), s.H, s.F, s.E, m.tile_expert, m.num_padded_rows,
-                       m.pair_first, m.num_pairs, m.tokens_per_expert, m.padded_bins,
+                       cb<bf16>(x_perm), s.H, s.F, s.E, m.tile_expert, m.pair_first,
+                       m.num_pairs, m.padded_bins, m.tokens_per_expert,
                        mb<bf16>(dx_perm), mb<bf16>(dw1), mb<bf16>(dw3));
   } else {
     hipLaunchKernelGGL(bfk::up_dgrad_kernel, persistent_grid(cdiv(s.H, 256) * s.max_tiles),
                        dim3(bfk::kThreads), 0, stream, cb<bf16>(dh1), cb<bf16>(dh3),
                        cb<bf16>(w1), cb<bf16>(w3), s.H, s.F, m.tile_expert,
-                       m.num_padded_rows, m.pair_first, m.num_pairs, mb<bf16>(dx_perm));
+                       m.pair_first, m.num_pairs, m.padded_bins, mb<bf16>(dx_perm));
   }
   return hipGetLastError();
 }
@@ -1407,8 +1407,8 @@ hipError_t launch_bf16_down_dgrad_wgrad_down(const Shape& s, const void* dy_perm
   hipLaunchKernelGGL(bfk::down_dgrad_wgrad_down_kernel, persistent_grid(t1 + t2),
                      dim3(bfk::kThreads), 0, stream, cb<bf16>(dy_perm), cb<bf16>(w2),
                      cb<bf16>(h1), cb<bf16>(h3), cb<bf16>(act), s.H, s.F, s.E,
-                     m.tile_expert, m.num_padded_rows, m.pair_first, m.num_pairs,
-                     m.tokens_per_expert, m.padded_bins, mb<bf16>(dh1), mb<bf16>(dh3),
+                     m.tile_expert, m.pair_first, m.num_pairs, m.padded_bins,
+                     m.tokens_per_expert, mb<bf16>(dh1), mb<bf16>(dh3),
                      mb<bf16>(dw2));
   return hipGetLastError();
 }
@@ -1419,8 +1419,8 @@ hipError_t launch_bf16_wgrad_up(const Shape& s, const void* dh1, const void* dh3
                                 hipStream_t stream) {
   hipLaunchKernelGGL(bfk::wgrad_up_kernel, up_dgrad_grid(s), dim3(bfk::kThreads), 0, stream,
                      cb<bf16>(dh1), cb<bf16>(dh3), cb<bf16>(w1), cb<bf16>(w3),
-                     cb<bf16>(x_perm), s.H, s.F, s.E, m.tile_expert, m.num_padded_rows,
-                     m.pair_first, m.num_pairs, m.tokens_per_expert, m.padded_bins,
+                     cb<bf16>(x_perm), s.H, s.F, s.E, m.tile_expert, m.pair_first,
+                     m.num_pairs, m.padded_bins, m.tokens_per_expert,
                      up_dgrad_fills_tail(s) ? 1 : 0, mb<bf16>(dx_perm), mb<bf16>(dw1),
                      mb<bf16>(dw3));
   return hipGetLastError();
