@@ -18,6 +18,7 @@ import argparse
 import json
 import os
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -311,19 +312,31 @@ def main():
         ev = [None, None, None]
         ev[dph] = EventArray(len(phases[dph]) + 1, only=(dj, dj + 1))
         evs.append(tuple(ev))
+    # The shader clock is sampled every ~1 ms by a thread of its own while the
+    # steps run: a sysfs read of it takes about a millisecond, so polling it
+    # in the wait for the last step would notice the end late.
+    sclk = []
+    stop = threading.Event()
+
+    def sample():
+        while not stop.is_set() and len(sclk) < 1000:
+            c = gpu_sclk_mhz()
+            if c is None:
+                break
+            sclk.append(c)
+            stop.wait(0.001)
+
+    sampler = threading.Thread(target=sample, daemon=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         step(evs[i])
-    sclk = []                      # sampled every ~1 ms while the queued steps run
-    while not stream.query() and len(sclk) < 1000:
-        c = gpu_sclk_mhz()
-        if c is None:
-            break
-        sclk.append(c)
-        time.sleep(0.001)
+        if i == 0:
+            sampler.start()        # while the first step runs
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    stop.set()
+    sampler.join()
     dom_ms = sum(ev[dph].elapsed_ms(dj, dj + 1) for ev in evs) / K
     for ev in evs:
         ev[dph].close()
