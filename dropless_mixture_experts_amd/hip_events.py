@@ -24,6 +24,7 @@ def _lib():
         _hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         _hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
                                              ctypes.c_void_p, ctypes.c_void_p]
+        _hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     return _hip
 
 
@@ -50,6 +51,12 @@ class EventArray:
 
     def pointer(self):
         return ctypes.cast(self._arr, ctypes.c_void_p)
+
+    def record(self, i: int, stream) -> None:
+        """Record event i on a torch stream (hipEventRecord)."""
+        rc = _lib().hipEventRecord(self._arr[i], ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
 
     def elapsed_ms(self, i: int, j: int) -> float:
         lib = _lib()
