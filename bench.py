@@ -69,6 +69,12 @@ def kernel_work(cfg, P, fused=False):
     return w
 
 
+def roof_time(flop, nbytes, peak_tflops):
+    """Seconds a kernel takes at its roofline: the larger of its FLOP at the
+    matrix-core peak and its algorithmic bytes at the HBM peak."""
+    return max((flop or 0.0) / (peak_tflops * 1e12), nbytes / (PEAK_HBM_GBS * 1e9))
+
+
 def committed_traffic(kernel, workload):
     """HBM bytes per launch from the committed counter summaries under
     profiles/ (FETCH_SIZE + WRITE_SIZE, calibrated on a plain copy), or None
@@ -378,9 +384,12 @@ def main():
         t = per[n] * 1e-3
         table[n] = {"ms": round(per[n], 4), "interval_ms": round(raw[n], 4),
                     "tflops": round(fl / t / 1e12, 1) if fl and t > 0 else None,
-                    "gbs": round(by / t / 1e9, 1) if t > 0 else None}
+                    "gbs": round(by / t / 1e9, 1) if t > 0 else None,
+                    "roofline_frac": (round(roof_time(fl, by, peak) / t, 4)
+                                      if t > 0 else None)}
     gemms = [n for n in names if n.startswith("gemm")]
     gemm_ms = sum(per[n] for n in gemms)
+    gemm_roof_s = sum(roof_time(*work[n], peak) for n in gemms)
     gs = [n for n in ("padded_gather", "padded_scatter", "scatter_backward",
                       "gather_backward") if n in names]
     gs_ms = sum(per[n] for n in gs)
@@ -438,6 +447,9 @@ def main():
         "useful_tflops": round(useful_tf, 1),
         "useful_frac_peak": round(useful_tf / peak, 4),
         "gemm_executed_frac_peak": round(executed_flop / (gemm_ms * 1e-3) / 1e12 / peak, 4),
+        # the GEMMs' time at their per-kernel roofline, max(FLOP / peak,
+        # bytes / HBM peak), over their measured time
+        "gemm_roofline_frac": round(gemm_roof_s / (gemm_ms * 1e-3), 4),
         "gather_scatter_frac_hbm": round(gs_bytes / (gs_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "metadata_us": round(1e3 * sum(per[n] for n in META_KERNELS), 1),
         # latency-bound: a few MB in three small launches
