@@ -27,7 +27,9 @@
         * 128) (GRBM_GUI_ACTIVE is summed over 8 XCDs of 128 SIMDs each),
         l2hit = TCC_HIT / (TCC_HIT + TCC_MISS), ta = TA_TA_BUSY /
         (GRBM_GUI_ACTIVE * 32) and tcp = TCP_PENDING_STALL_CYCLES /
-        (GRBM_GUI_ACTIVE * 32) (32 CUs per XCD).
+        (GRBM_GUI_ACTIVE * 32) (32 CUs per XCD), and mfma_gflop =
+        SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 / 1e9, the matrix-core work of one
+        launch.
 """
 from __future__ import annotations
 
@@ -103,6 +105,9 @@ def derived(c: dict) -> dict:
         "ta": ratio("TA_TA_BUSY_sum", "GRBM_GUI_ACTIVE", 32.0),
         "tcp": ratio("TCP_PENDING_STALL_CYCLES_sum", "GRBM_GUI_ACTIVE", 32.0),
         "lds_bankcf": c.get("SQ_LDS_BANK_CONFLICT"),
+        # SQ_INSTS_VALU_MFMA_MOPS_BF16 counts units of 512 FLOP
+        "mfma_gflop": (c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / 1e9
+                       if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c else None),
     }
 
 
@@ -163,7 +168,7 @@ def main(argv=None):
     if a.cmd == "counters":
         kernels = [tuple(k.split("=", 1)) for k in a.kernel]
         med = counter_medians(a.dirs, kernels)
-        cols = ("mfma", "l2hit", "ta", "tcp", "lds_bankcf")
+        cols = ("mfma", "l2hit", "ta", "tcp", "lds_bankcf", "mfma_gflop")
         print(f"{'kernel':28s} " + " ".join(f"{c:>10s}" for c in cols))
         for name, _ in kernels:
             d = derived(med[name])
@@ -171,7 +176,8 @@ def main(argv=None):
             for col in cols:
                 v = d[col]
                 cells.append(f"{'-':>10s}" if v is None else
-                             (f"{v:10.0f}" if col == "lds_bankcf" else f"{v:10.3f}"))
+                             (f"{v:10.0f}" if col == "lds_bankcf" else
+                              f"{v:10.2f}" if col == "mfma_gflop" else f"{v:10.3f}"))
             print(f"{name:28s} " + " ".join(cells))
         return 0
     if a.cmd == "stats":
