@@ -32,6 +32,8 @@ SMALL = [
     shrink(CONFIGS["sparse_e256"], T=16, H=128, F=128),           # most experts empty
     # the up-dgrad launch without the dw1/dw3 tail fill
     shrink(CONFIGS["fine_e64"], T=3584, H=2048, F=128, E=8, k=2),
+    # an expert of 17 row pairs: row groups of 6, 6 and 5
+    shrink(CONFIGS["fine_e64"], T=4300, H=128, F=256, E=1, k=1),
 ]
 
 

@@ -34,6 +34,12 @@ SMALL = [
     # 256 expected up-dgrad row tiles (one whole round of 256 CUs): the plain
     # up-dgrad launch, not the one that fills its last round with dw1/dw3 tiles
     shrink(CONFIGS["fine_e64"], T=3584, H=2048, F=128, E=8, k=2),
+    # experts with more than 8 row pairs, whose row tiles are split into
+    # groups of near-equal size: 17 pairs (6, 6, 5; the last pair half
+    # empty), two experts of 12 (6, 6), and skewed experts of 16, 13 and 11
+    shrink(CONFIGS["fine_e64"], T=4300, H=128, F=256, E=1, k=1),
+    shrink(CONFIGS["fine_e64"], T=3000, H=256, F=256, E=2, k=2),
+    shrink(CONFIGS["zipf_e64"], T=4096, H=128, F=128),
 ]
 
 
