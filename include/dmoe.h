@@ -262,10 +262,12 @@ int dmoe_router_backward(const dmoe_dims* dims, const float* logits,
 /* The metadata, forward and backward calls with per-kernel timing.  `events`
  * is NULL or an array of n+1 hipEvent_t; event i is recorded on `stream`
  * just before kernel i and event n after the last kernel, so the elapsed
- * time between events i and i+1 is kernel i's duration on the stream.  An
- * entry may be NULL: that record is skipped (each record puts a timestamp
- * between two kernels, so timing one kernel with two records disturbs the
- * sequence less than timing all of them).
+ * time between events i and i+1 is kernel i's duration on the stream plus
+ * the cost of one record (about 4.4 us on MI355X: the interval between two
+ * records with nothing between them).  An entry may be NULL: that record is
+ * skipped (each record puts a timestamp between two kernels, so timing one
+ * kernel with two records disturbs the sequence less than timing all of
+ * them).
  *   metadata (n = 3): histogram, scan, placement.
  *   forward  (n = 4): padded_gather, up projection + SiLU gate, down
  *                     projection, padded_scatter.
