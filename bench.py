@@ -242,8 +242,13 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--kernels", action="store_true",
                     help="also print the per-kernel table on stderr")
+    ap.add_argument("--gather", choices=("auto", "plain", "fused"), default="auto",
+                    help="plain: padded copy in the forward; fused: the gather "
+                         "inside the up projection's operand loads (bf16); auto: "
+                         "fused where the padded copy of x exceeds the last-level "
+                         "cache")
     ap.add_argument("--fused-gather", action="store_true",
-                    help="time the path with the gather fused into the up "
+                    help="same as --gather fused: time the path with the gather fused into the up "
                          "projection's operand loads (the backward gathers x_perm)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB "
@@ -282,7 +287,9 @@ def main():
     w1, w3, w2 = up(inp.w1), up(inp.w3), up(inp.w2)
     D = dm.Dims(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k,
                 dm.DMOE_F32 if cfg.dtype == "f32" else dm.DMOE_BF16)
-    fused = args.fused_gather and cfg.dtype == "bf16"
+    mode = "fused" if args.fused_gather else args.gather
+    fused = cfg.dtype == "bf16" and (
+        mode == "fused" or (mode == "auto" and dm.fused_gather_pays(D)))
     layer = dm.DMoELayer(D, dev, fused_gather=fused)
     fwd_kernels = [n for n in FWD_KERNELS if not (fused and n == "padded_gather")]
     bwd_kernels = list(BWD_KERNELS)

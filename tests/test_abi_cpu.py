@@ -174,3 +174,21 @@ def test_binding_rejects_cpu_tensors():
     assert dm.dmoe_max_tiles(D) == (8 + 127 * 2) // 128
     with pytest.raises(dm.DMoEError):
         dm.dmoe_max_tiles(dm.Dims(8, 100, 128, 2, 1, dm.DMOE_F32))
+
+
+def test_fused_gather_policy(lib):
+    """fused_gather="auto" fuses the gather where the padded copy of x
+    (P_max rows of H bf16) would not fit the 256 MB last-level cache."""
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    from workloads import CONFIGS
+    want = {"tiny_f32": False, "fine_e64": False, "zipf_e64": False,
+            "coarse_e8": False, "sparse_e256": True}
+    for name, fused in want.items():
+        c = CONFIGS[name]
+        d = dm.Dims(c.T, c.H, c.F, c.E, c.k,
+                    dm.DMOE_F32 if c.dtype == "f32" else dm.DMOE_BF16)
+        assert dm.fused_gather_pays(d) is fused, name
+    # x of 2 GB or more is beyond the fused entry points
+    big = dm.Dims(1 << 19, 2048, 1024, 64, 8, dm.DMOE_BF16)
+    assert dm.fused_gather_pays(big) is False
