@@ -24,10 +24,33 @@ constexpr int kRouterWaves = 4;                    // tokens per workgroup
 constexpr int kPerLane = kMaxExperts / kWave;      // logits per lane
 constexpr int kSumThreads = 1024;
 
-// (av, ai) comes before (bv, bi): a larger logit, or an equal one with a
-// lower expert id.
-__device__ __forceinline__ bool before(float av, int ai, float bv, int bi) {
-  return av > bv || (av == bv && ai < bi);
+// A finite float as an unsigned key with the same order (negative values
+// flipped whole, positive ones above them; -0 taken as +0, the two being
+// one value in a comparison); 0 is below every key.  Bitwise, so subnormal
+// logits keep their order whatever the float mode.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Maximum of v over the wave, in every lane.  Cross-lane moves by DPP (an
+// inclusive max-scan inside each row of 16 lanes by shifts of 1, 2, 4 and
+// 8, then row 15 to row 1 and 3, lane 31 to rows 2 and 3), so lane 63 ends
+// with the maximum; no LDS traffic.  Lanes whose source is outside the row
+// read 0, the identity.
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  const auto step = [](uint32_t x, uint32_t y) { return x > y ? x : y; };
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true));
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true));
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true));
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true));
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
+  v = step(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -55,26 +78,26 @@ router_forward_kernel(const float* __restrict__ logits, int64_t T, int E, int k,
     v[q] = live[q] ? row[e] : -FLT_MAX;
     sel[q] = 0.f;
   }
+  uint32_t key[kPerLane];
+#pragma unroll
+  for (int q = 0; q < kPerLane; ++q) key[q] = live[q] ? order_key(v[q]) : 0u;
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = INT32_MAX;                  // no candidate yet
+    // the largest remaining logit, then the lowest expert id holding it
+    // (expert q * 64 + lane: the first slot q with a holder, its lowest lane)
+    uint32_t lk = 0u;
 #pragma unroll
-    for (int q = 0; q < kPerLane; ++q)
-      if (live[q] && before(v[q], q * kWave + lane, bv, bi)) {
-        bv = v[q];
-        bi = q * kWave + lane;
-      }
+    for (int q = 0; q < kPerLane; ++q) lk = key[q] > lk ? key[q] : lk;
+    const uint32_t best = wave_umax(lk);
+    int bi = INT32_MAX;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, kWave);
-      const int oi = __shfl_xor(bi, off, kWave);
-      if (before(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
+    for (int q = kPerLane - 1; q >= 0; --q) {
+      const unsigned long long hold = __ballot(key[q] == best && best != 0u);
+      if (hold) bi = q * kWave + (__ffsll((long long)hold) - 1);
     }
+    const float bv = key_value(best);
 #pragma unroll
     for (int q = 0; q < kPerLane; ++q) {
+      if (q * kWave + lane == bi) key[q] = 0u;
       if (q * kWave + lane == bi) live[q] = false;
       if (q == j / kWave && lane == j % kWave) sel[q] = bv;
     }

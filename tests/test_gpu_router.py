@@ -108,3 +108,24 @@ def test_router_rejects_missing_zloss_buffers():
     w = torch.empty(cfg.T, cfg.k, device=dev)
     with pytest.raises(ValueError):
         dm.dmoe_router_forward(D, l, ids, w, zloss_coef=0.5)
+
+
+@pytest.mark.parametrize("E,k", [(64, 8), (256, 8), (100, 70)])
+def test_router_ids_on_signed_zeros_subnormals_and_extremes(E, k):
+    """Rows drawn from a handful of values, so that most of the top k are
+    ties: +0 and -0 (one value), subnormals of both signs, +-FLT_MAX and
+    ordinary values.  Ids must equal the oracle's stable order exactly."""
+    vals = np.array([0.0, -0.0, 1e-40, -1e-40, 2e-45, 1.5, -1.5, 3.0,
+                     np.finfo(np.float32).max, -np.finfo(np.float32).max],
+                    dtype=np.float32)
+    rng = np.random.default_rng(4242 + E)
+    T = 96
+    logits = vals[rng.integers(0, len(vals), size=(T, E))].astype(np.float32)
+    d_weights = rng.standard_normal((T, k)).astype(np.float32)
+    cfg = W.shrink(W.CONFIGS["sparse_e256"], T=T, E=E, k=k)
+    print(f"router extremes E={E} k={k}", flush=True)
+    ids, w, _, _, dl = _run(cfg, logits, d_weights, 0.0)
+    ref_ids, ref_w = R.router_forward(logits, k)
+    assert np.array_equal(ids.astype(np.int64), ref_ids), "top_experts differ"
+    assert_close(w, ref_w, TOL, "weights")
+    assert np.all(np.isfinite(dl))
