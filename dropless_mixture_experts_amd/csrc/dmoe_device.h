@@ -77,10 +77,19 @@ __device__ __forceinline__ void st16_nt(void* p, const u32x4& v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
+// Sum of v over the wave, in every lane, in a fixed order.  Cross-lane moves
+// by DPP, with no LDS traffic: an inclusive sum-scan inside each row of 16
+// lanes by shifts of 1, 2, 4 and 8 (a lane outside the row adds 0), then row
+// 0's lane 15 into row 1 and row 2's into row 3, then lane 31 into rows 2
+// and 3, so lane 63 holds the total.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // The gated SiLU of the expert FFN, silu(h1) * h3 with silu(z) = z / (1 +
