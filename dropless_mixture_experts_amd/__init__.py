@@ -67,7 +67,7 @@ class _Meta(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "tokens_per_expert", "bins", "padded_bins", "indices", "bin_ids",
         "row_of_entry", "tile_expert", "num_padded_rows", "status",
-        "pair_first", "num_pairs", "row_token")]
+        "pair_first", "num_pairs", "row_token", "xcd_first")]
 
 
 class _Saved(ctypes.Structure):
@@ -178,6 +178,7 @@ class Meta:
     pair_first: torch.Tensor
     num_pairs: torch.Tensor
     row_token: torch.Tensor
+    xcd_first: torch.Tensor
 
     def _c(self) -> _Meta:
         return _Meta(*[_ptr(getattr(self, f.name), torch.int32, f.name)
@@ -266,7 +267,7 @@ def _check_meta(dims: Dims, meta: Meta):
                        ("row_of_entry", n), ("tile_expert", dmoe_max_tiles(dims)),
                        ("num_padded_rows", 1), ("status", 1),
                        ("pair_first", dmoe_max_tiles(dims)), ("num_pairs", 1),
-                       ("row_token", 128 * dmoe_max_tiles(dims))):
+                       ("row_token", 128 * dmoe_max_tiles(dims)), ("xcd_first", 9)):
         _need(getattr(meta, name), name, size)
 
 
@@ -461,7 +462,7 @@ def allocate_meta(dims: Dims, device):
                 torch.empty(n, **i32), torch.empty(n, **i32), torch.empty(n, **i32),
                 torch.empty(nt, **i32), torch.empty(1, **i32), torch.empty(1, **i32),
                 torch.empty(nt, **i32), torch.empty(1, **i32),
-                torch.empty(128 * nt, **i32))
+                torch.empty(128 * nt, **i32), torch.empty(9, **i32))
     ws = torch.empty(dmoe_workspace_bytes(dims), dtype=torch.uint8, device=device)
     return meta, ws
 

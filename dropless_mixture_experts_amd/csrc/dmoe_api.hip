@@ -49,7 +49,8 @@ Shape shape_of(const dmoe_dims* d) {
 int check_meta(const dmoe_meta* m) {
   if (!m || !m->tokens_per_expert || !m->bins || !m->padded_bins || !m->indices ||
       !m->bin_ids || !m->row_of_entry || !m->tile_expert || !m->num_padded_rows ||
-      !m->status || !m->pair_first || !m->num_pairs || !m->row_token)
+      !m->status || !m->pair_first || !m->num_pairs || !m->row_token ||
+      !m->xcd_first)
     return DMOE_ERR_ARG;
   return DMOE_OK;
 }
@@ -57,7 +58,8 @@ int check_meta(const dmoe_meta* m) {
 MetaPtrs meta_ptrs(const dmoe_meta* m) {
   return MetaPtrs{m->tokens_per_expert, m->bins, m->padded_bins, m->indices,
                   m->bin_ids, m->row_of_entry, m->tile_expert, m->num_padded_rows,
-                  m->status, m->pair_first, m->num_pairs, m->row_token};
+                  m->status, m->pair_first, m->num_pairs, m->row_token,
+                  m->xcd_first};
 }
 
 // Records events[i] on the stream when timing is requested and the entry is

@@ -15,6 +15,7 @@ struct MetaPtrs {
   int32_t *tile_expert, *num_padded_rows, *status;
   int32_t *pair_first, *num_pairs;
   int32_t *row_token;
+  int32_t *xcd_first;
 };
 
 struct Shape {

@@ -676,31 +676,11 @@ struct UpDgrad {
 };
 
 // Weight-gradient tiles have K = the expert's padded rows, so equal tile
-// counts are not equal work under skewed routing.  Expert e goes to the XCD
-// holding the middle of its padded rows, min(7, 8 (start_e + n_e / 2) / P),
-// which gives each XCD about P / 8 rows and keeps every expert within one
-// L2; XCD x gets the experts [first(x), first(x + 1)).  One wave evaluates
-// all experts (E <= 256) with four loads per lane and counts with ballots.
-__device__ __forceinline__ int first_expert_of_xcd(int x, int E, const int32_t* tpe,
-                                                   const int32_t* padded_bins) {
-  if (x <= 0) return 0;
-  if (x >= 8) return E;
-  const int lane = threadIdx.x & 63;
-  const int64_t P = padded_bins[E - 1];
-  int count = 0;
-#pragma unroll
-  for (int q = 0; q < kMaxExperts / kWave; ++q) {
-    const int e = q * kWave + lane;
-    bool before = false;
-    if (e < E && P > 0) {
-      const int64_t n = round_up_block(tpe[e]);
-      const int64_t start = padded_bins[e] - n;
-      before = min<int64_t>(7, 8 * (start + n / 2) / P) < x;
-    }
-    count += __builtin_popcountll(__ballot(before));
-  }
-  return count;
-}
+// counts are not equal work under skewed routing.  XCD x computes the
+// experts [xcd_first[x], xcd_first[x + 1]), contiguous ranges that the
+// metadata chose to minimise the largest cost (an expert's 128-row blocks
+// + 1, for the epilogue of each of its tiles); every expert stays within one
+// L2.
 
 // dw2[e] = act[rows_e]^T dy_perm[rows_e] ([F,H]); zero for an empty expert.
 // A = 256 (or 128) hidden columns of dy_perm (u = h0), B = 256 (or 128) ffn
@@ -713,7 +693,7 @@ struct WgradDown {
   const bf16 *act, *dy_perm;
   int64_t H, F;
   int E;
-  const int32_t *tpe, *padded_bins;
+  const int32_t *tpe, *padded_bins, *xcd_first;
   bf16* dw2;
   __device__ uint32_t lda() const { return (uint32_t)(H * 2); }
   __device__ uint32_t ldb() const { return (uint32_t)(F * 2); }
@@ -723,8 +703,8 @@ struct WgradDown {
   __device__ int tiles_per_expert() const { return nh() * nf(); }
   __device__ int expert_steps(int e) const { return round_up_block(tpe[e]) / kKStep; }
   __device__ void xcd_range(int x, int& lo, int& hi) const {
-    lo = first_expert_of_xcd(x, E, tpe, padded_bins) * nh() * nf();
-    hi = first_expert_of_xcd(x + 1, E, tpe, padded_bins) * nh() * nf();
+    lo = xcd_first[x] * nh() * nf();
+    hi = xcd_first[x + 1] * nh() * nf();
   }
   __device__ void tile(int L, Job& j) const {
     // the tiles of one expert are consecutive: each XCD works on whole experts
@@ -771,7 +751,7 @@ struct WgradUp {
   const bf16 *x_perm, *dh1, *dh3;
   int64_t H, F;
   int E;
-  const int32_t *tpe, *padded_bins;
+  const int32_t *tpe, *padded_bins, *xcd_first;
   bf16 *dw1, *dw3;
   __device__ uint32_t lda() const { return (uint32_t)(F * 2); }
   __device__ uint32_t ldb() const { return (uint32_t)(H * 2); }
@@ -781,8 +761,8 @@ struct WgradUp {
   __device__ int tiles_per_expert() const { return nf() * nh(); }
   __device__ int expert_steps(int e) const { return round_up_block(tpe[e]) / kKStep; }
   __device__ void xcd_range(int x, int& lo, int& hi) const {
-    lo = first_expert_of_xcd(x, E, tpe, padded_bins) * nf() * nh();
-    hi = first_expert_of_xcd(x + 1, E, tpe, padded_bins) * nf() * nh();
+    lo = xcd_first[x] * nf() * nh();
+    hi = xcd_first[x + 1] * nf() * nh();
   }
   __device__ void tile(int L, Job& j) const {
     const int NF = nf(), NH = nh();
@@ -1272,11 +1252,13 @@ __global__ void __launch_bounds__(kThreads)
 up_dgrad_fill_kernel(const bf16* __restrict__ dh1, const bf16* __restrict__ dh3,
                      const bf16* __restrict__ w1, const bf16* __restrict__ w3,
                      const bf16* __restrict__ x_perm, int64_t H, int64_t F, int E,
-                     ROW_TILE_ARGS, const int32_t* __restrict__ tpe, bf16* dx_perm,
+                     ROW_TILE_ARGS, const int32_t* __restrict__ tpe,
+                     const int32_t* __restrict__ xcd_first, bf16* dx_perm,
                      bf16* __restrict__ dw1, bf16* __restrict__ dw3) {
   UpDgrad k1{dh1, dh3, w1, w3, H, F, dx_perm};
   k1.rt.init(tile_expert, pair_first, num_pairs, padded_bins, (int)((H + 255) / 256));
-  persistent_dual<kTailFill>(k1, WgradUp{x_perm, dh1, dh3, H, F, E, tpe, padded_bins, dw1, dw3});
+  persistent_dual<kTailFill>(
+      k1, WgradUp{x_perm, dh1, dh3, H, F, E, tpe, padded_bins, xcd_first, dw1, dw3});
 }
 
 // down dgrad + gate backward (dh1, dh3) and dw2 in one launch: both read
@@ -1285,21 +1267,24 @@ __global__ void __launch_bounds__(kThreads)
 down_dgrad_wgrad_down_kernel(const bf16* __restrict__ dy_perm, const bf16* __restrict__ w2,
                              const bf16* h1, const bf16* h3, const bf16* __restrict__ act,
                              int64_t H, int64_t F, int E, ROW_TILE_ARGS,
-                             const int32_t* __restrict__ tpe, bf16* dh1, bf16* dh3,
+                             const int32_t* __restrict__ tpe,
+                             const int32_t* __restrict__ xcd_first, bf16* dh1, bf16* dh3,
                              bf16* __restrict__ dw2) {
   DownDgrad k1{dy_perm, w2, h1, h3, H, F, dh1, dh3};
   k1.rt.init(tile_expert, pair_first, num_pairs, padded_bins, (int)((F + 255) / 256));
-  persistent_dual(k1, WgradDown{act, dy_perm, H, F, E, tpe, padded_bins, dw2});
+  persistent_dual(k1, WgradDown{act, dy_perm, H, F, E, tpe, padded_bins, xcd_first, dw2});
 }
 
 __global__ void __launch_bounds__(kThreads)
 wgrad_up_kernel(const bf16* __restrict__ dh1, const bf16* __restrict__ dh3,
                 const bf16* __restrict__ w1, const bf16* __restrict__ w3,
                 const bf16* __restrict__ x_perm, int64_t H, int64_t F, int E, ROW_TILE_ARGS,
-                const int32_t* __restrict__ tpe, int filled, bf16* dx_perm, bf16* __restrict__ dw1, bf16* __restrict__ dw3) {
+                const int32_t* __restrict__ tpe, const int32_t* __restrict__ xcd_first,
+                int filled, bf16* dx_perm, bf16* __restrict__ dw1, bf16* __restrict__ dw3) {
   UpDgrad k1{dh1, dh3, w1, w3, H, F, dx_perm};
   k1.rt.init(tile_expert, pair_first, num_pairs, padded_bins, (int)((H + 255) / 256));
-  persistent_dual<kRest>(k1, WgradUp{x_perm, dh1, dh3, H, F, E, tpe, padded_bins, dw1, dw3},
+  persistent_dual<kRest>(k1, WgradUp{x_perm, dh1, dh3, H, F, E, tpe, padded_bins, xcd_first,
+                                     dw1, dw3},
                          filled != 0);
 }
 
@@ -1388,7 +1373,7 @@ hipError_t launch_bf16_up_dgrad(const Shape& s, const void* dh1, const void* dh3
                        stream, cb<bf16>(dh1), cb<bf16>(dh3), cb<bf16>(w1), cb<bf16>(w3),
                        cb<bf16>(x_perm), s.H, s.F, s.E, m.tile_expert, m.pair_first,
                        m.num_pairs, m.padded_bins, m.tokens_per_expert,
-                       mb<bf16>(dx_perm), mb<bf16>(dw1), mb<bf16>(dw3));
+                       m.xcd_first, mb<bf16>(dx_perm), mb<bf16>(dw1), mb<bf16>(dw3));
   } else {
     hipLaunchKernelGGL(bfk::up_dgrad_kernel, persistent_grid(cdiv(s.H, 256) * s.max_tiles),
                        dim3(bfk::kThreads), 0, stream, cb<bf16>(dh1), cb<bf16>(dh3),
@@ -1408,7 +1393,7 @@ hipError_t launch_bf16_down_dgrad_wgrad_down(const Shape& s, const void* dy_perm
                      dim3(bfk::kThreads), 0, stream, cb<bf16>(dy_perm), cb<bf16>(w2),
                      cb<bf16>(h1), cb<bf16>(h3), cb<bf16>(act), s.H, s.F, s.E,
                      m.tile_expert, m.pair_first, m.num_pairs, m.padded_bins,
-                     m.tokens_per_expert, mb<bf16>(dh1), mb<bf16>(dh3),
+                     m.tokens_per_expert, m.xcd_first, mb<bf16>(dh1), mb<bf16>(dh3),
                      mb<bf16>(dw2));
   return hipGetLastError();
 }
@@ -1420,7 +1405,7 @@ hipError_t launch_bf16_wgrad_up(const Shape& s, const void* dh1, const void* dh3
   hipLaunchKernelGGL(bfk::wgrad_up_kernel, up_dgrad_grid(s), dim3(bfk::kThreads), 0, stream,
                      cb<bf16>(dh1), cb<bf16>(dh3), cb<bf16>(w1), cb<bf16>(w3),
                      cb<bf16>(x_perm), s.H, s.F, s.E, m.tile_expert, m.pair_first,
-                     m.num_pairs, m.padded_bins, m.tokens_per_expert,
+                     m.num_pairs, m.padded_bins, m.tokens_per_expert, m.xcd_first,
                      up_dgrad_fills_tail(s) ? 1 : 0, mb<bf16>(dx_perm), mb<bf16>(dw1),
                      mb<bf16>(dw3));
   return hipGetLastError();

@@ -77,8 +77,11 @@ meta_scan_kernel(int32_t* __restrict__ hist, const int32_t* __restrict__ err,
                  int32_t* __restrict__ status,
                  int32_t* __restrict__ pair_first,
                  int32_t* __restrict__ num_pairs,
-                 int32_t* __restrict__ row_token) {
+                 int32_t* __restrict__ row_token,
+                 int32_t* __restrict__ xcd_first) {
   __shared__ int32_t seg_tot[kScanThreads];
+  __shared__ int32_t nxt_s[kMaxExperts + 1];
+  __shared__ int32_t maxb_s, feas_s;
   __shared__ int32_t count_s[kMaxExperts];
   __shared__ int32_t start_s[kMaxExperts];
   __shared__ int32_t pend_s[kMaxExperts];
@@ -213,6 +216,61 @@ meta_scan_kernel(int32_t* __restrict__ hist, const int32_t* __restrict__ err,
     if (i < pc - c) row_token[pend_s[ee] - pc + c + i] = -1;
   }
   if (tid == 0) *status = bad_s ? kErrExpertId : 0;
+
+  // The experts whose weight-gradient tiles each XCD computes: 8 contiguous
+  // ranges with the least possible largest cost.  A tile of those products
+  // has K = its expert's padded rows plus an epilogue of about two K steps
+  // of 64, so an expert costs its 128-row blocks + 1 (an empty expert's
+  // tiles still write zeros).  Balancing rows alone measured worse than
+  // balancing this cost under skewed routing.  With total cost W and the
+  // largest expert cost M, the least maximum lies in [max(ceil(W / 8), M),
+  // ceil(W / 8) + M]: at the upper cap a greedy range that stops before E
+  // costs more than cap - M = ceil(W / 8), so 8 of them reach E.  Binary
+  // search on the cap; a cap is feasible when 8 greedy ranges reach E.
+  // nxt_s[s] is the greedy end of a range starting at expert s: the largest
+  // b with cost(s, b) <= cap, one binary search per thread.
+  if (tid == 0) maxb_s = 0;
+  __syncthreads();
+  if (tid < E) atomicMax(&maxb_s, round_up_block(count_s[tid]) / kBlock + 1);
+  __syncthreads();
+  const auto pre = [&](int b) { return b == 0 ? 0 : pend_s[b - 1] / kBlock + b; };
+  const int eighth = (P / kBlock + E + 7) / 8;
+  const auto greedy_ends = [&](int cap) {
+    for (int s0 = tid; s0 <= E; s0 += kScanThreads) {
+      const int lim = pre(s0) + cap;
+      int a = s0, z = E;
+      while (a < z) {
+        const int mid = (a + z + 1) >> 1;
+        if (pre(mid) <= lim) a = mid; else z = mid - 1;
+      }
+      nxt_s[s0] = a;
+    }
+  };
+  int lo = max(eighth, maxb_s), hi = eighth + maxb_s;
+  while (lo < hi) {                      // lo, hi are the same in every thread
+    const int cap = (lo + hi) >> 1;
+    greedy_ends(cap);
+    __syncthreads();
+    if (tid == 0) {
+      int b = 0;
+      for (int x = 0; x < 8 && b < E; ++x) b = nxt_s[b];
+      feas_s = b >= E;
+    }
+    __syncthreads();
+    if (feas_s) hi = cap; else lo = cap + 1;
+    __syncthreads();                     // nxt_s and feas_s are rewritten
+  }
+  greedy_ends(lo);
+  __syncthreads();
+  if (tid == 0) {
+    int b = 0;
+    xcd_first[0] = 0;
+    for (int x = 1; x < 8; ++x) {
+      b = b < E ? nxt_s[b] : E;
+      xcd_first[x] = b;
+    }
+    xcd_first[8] = E;
+  }
 }
 
 __global__ void __launch_bounds__(kMetaWaves * kWave)
@@ -317,7 +375,8 @@ hipError_t launch_metadata(int64_t n, int E, int k, int64_t max_tiles,
   hipLaunchKernelGGL(meta_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream,
                      hist, err, nchunks, E, Ecap, (int)max_tiles,
                      m.tokens_per_expert, m.bins, m.padded_bins, m.tile_expert,
-                     m.num_padded_rows, m.status, m.pair_first, m.num_pairs, m.row_token);
+                     m.num_padded_rows, m.status, m.pair_first, m.num_pairs, m.row_token,
+                     m.xcd_first);
   if (ev && ev[2] && (rc = hipEventRecord(ev[2], stream)) != hipSuccess) return rc;
   hipLaunchKernelGGL(meta_place_kernel, dim3(blocks), dim3(kMetaWaves * kWave), 0,
                      stream, ids, n, chunk, nchunks, E, k, nbits, hist,

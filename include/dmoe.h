@@ -105,7 +105,14 @@ typedef struct {
  *   row_token[max_tiles*128] the token whose row padded row p holds: a / k
  *                         for the entry a placed there (the §4.2 index rule
  *                         read from the row side), -1 for a pad row below P;
- *                         rows from P on are left untouched                */
+ *                         rows from P on are left untouched
+ *   xcd_first[9]          the experts whose weight-gradient tiles each of the
+ *                         8 XCDs (L2 domains) computes: [xcd_first[x],
+ *                         xcd_first[x+1]), xcd_first[0] = 0, xcd_first[8] = E;
+ *                         contiguous ranges whose largest cost is the
+ *                         least possible, an expert costing its 128-row
+ *                         blocks + 1 (a schedule, not part of the method's
+ *                         result)                                          */
 typedef struct {
   int32_t *tokens_per_expert, *bins, *padded_bins;
   int32_t *indices, *bin_ids, *row_of_entry;
@@ -115,6 +122,7 @@ typedef struct {
   int32_t *pair_first;
   int32_t *num_pairs;
   int32_t *row_token;
+  int32_t *xcd_first;
 } dmoe_meta;
 
 /* Activations kept from forward for backward, each [P_max, H] or [P_max, F]

@@ -66,19 +66,19 @@ def test_bad_dims_rejected(lib, kw, code):
     d = _dims(**kw)
     assert lib.dmoe_max_tiles(ctypes.byref(d)) == code
     assert lib.dmoe_workspace_bytes(ctypes.byref(d)) == code
-    meta = dm._Meta(*([ctypes.c_void_p(0x1000)] * 12))
+    meta = dm._Meta(*([ctypes.c_void_p(0x1000)] * 13))
     assert lib.dmoe_metadata(ctypes.byref(d), ctypes.c_void_p(0x1000),
                              ctypes.byref(meta), ctypes.c_void_p(0x1000), None) == code
 
 
 def test_null_pointers_rejected_before_launch(lib):
     d = _dims()
-    meta = dm._Meta(*([ctypes.c_void_p(0x1000)] * 12))
+    meta = dm._Meta(*([ctypes.c_void_p(0x1000)] * 13))
     assert lib.dmoe_metadata(ctypes.byref(d), None, ctypes.byref(meta),
                              ctypes.c_void_p(0x1000), None) == -1
     assert lib.dmoe_metadata(ctypes.byref(d), ctypes.c_void_p(0x1000),
                              ctypes.byref(meta), None, None) == -1
-    bad = dm._Meta(*([ctypes.c_void_p(0x1000)] * 11 + [None]))
+    bad = dm._Meta(*([ctypes.c_void_p(0x1000)] * 12 + [None]))
     assert lib.dmoe_metadata(ctypes.byref(d), ctypes.c_void_p(0x1000),
                              ctypes.byref(bad), ctypes.c_void_p(0x1000), None) == -1
     saved = dm._Saved(*([ctypes.c_void_p(0x1000)] * 4 + [None]))
@@ -110,7 +110,7 @@ def test_fused_gather_checks_before_launch(lib):
     """The fused gather is bf16 only, needs x below 2 GB and, in the
     backward, the forward's x; a meta without row_token is rejected."""
     p = ctypes.c_void_p(0x1000)
-    meta = dm._Meta(*([p] * 12))
+    meta = dm._Meta(*([p] * 13))
     saved = dm._Saved(None, p, p, p, p)          # no x_perm: allowed here
     scratch = dm._Scratch(p, p, p, p)
     f32 = _dims()
@@ -126,7 +126,7 @@ def test_fused_gather_checks_before_launch(lib):
     assert lib.dmoe_backward_fused_gather(ctypes.byref(bf), None, p, p, p, p, p,
                                           ctypes.byref(meta), ctypes.byref(saved),
                                           ctypes.byref(scratch), p, p, p, p, p, None) == -1
-    no_rt = dm._Meta(*([p] * 11 + [None]))
+    no_rt = dm._Meta(*([p] * 11 + [None, p]))
     assert lib.dmoe_forward_fused_gather(ctypes.byref(bf), p, p, p, p, p, ctypes.byref(no_rt),
                                          ctypes.byref(saved), p, None) == -1
     # the plain path needs x_perm, and so does the fused backward (it

@@ -11,7 +11,7 @@ import dropless_mixture_experts_amd as dm
 import oracle
 from workloads import CONFIGS, make_inputs
 
-from gpu_helpers import device
+from gpu_helpers import device, dims_of, up
 
 pytestmark = pytest.mark.gpu
 
@@ -138,3 +138,43 @@ def test_deterministic():
     b, _ = _run_meta(ids, 256)
     for key in KEYS:
         np.testing.assert_array_equal(a[key], b[key])
+
+
+def _least_max_partition(blocks, parts=8):
+    """The least possible largest sum over `parts` contiguous ranges of
+    `blocks`, by dynamic programming over split points (independent of the
+    kernel's binary search)."""
+    pre = np.concatenate([[0], np.cumsum(blocks)])
+    n = len(blocks)
+    INF = float("inf")
+    best = np.full((parts + 1, n + 1), INF)
+    best[0][0] = 0
+    for j in range(1, parts + 1):
+        for i in range(n + 1):
+            cand = [max(best[j - 1][s], pre[i] - pre[s]) for s in range(i + 1)]
+            best[j][i] = min(cand)
+    return best[parts][n]
+
+
+@pytest.mark.parametrize("name", ["fine_e64", "zipf_e64", "zipf_e64_empty", "sparse_e256",
+                                  "coarse_e8", "tiny_f32"])
+def test_weight_gradient_xcd_ranges_are_optimal(name):
+    """xcd_first splits the experts into 8 contiguous ranges whose largest
+    cost is the least possible, an expert costing its 128-row blocks + 1."""
+    cfg = CONFIGS[name]
+    inp = make_inputs(cfg, with_weights=False, with_dy=False)
+    print(f"xcd ranges {name}", flush=True)
+    dev = device()
+    D = dims_of(cfg)
+    meta, ws = dm.allocate_meta(D, dev)
+    dm.dmoe_metadata(D, up(inp.top_experts, torch.int32, dev), meta, ws)
+    torch.cuda.synchronize()
+    xf = meta.xcd_first.cpu().numpy().astype(np.int64)
+    blocks = (meta.padded_bins.cpu().numpy().astype(np.int64)
+              - np.concatenate([[0], meta.padded_bins.cpu().numpy()[:-1]])) // 128
+    assert xf[0] == 0 and xf[8] == cfg.E
+    assert np.all(np.diff(xf) >= 0)
+    cost = blocks + 1
+    loads = [int(cost[xf[x]:xf[x + 1]].sum()) for x in range(8)]
+    assert sum(loads) == int(cost.sum())
+    assert max(loads) == _least_max_partition(cost.tolist())
