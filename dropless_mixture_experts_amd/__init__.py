@@ -10,6 +10,7 @@ Entry points mirror the C names::
 
     dmoe_max_tiles(dims)            -> int
     dmoe_workspace_bytes(dims)      -> int
+    dmoe_schedule_bytes(dims)       -> int
     dmoe_metadata(dims, top_experts, meta, ws)
     dmoe_forward(dims, x, weights, w1, w3, w2, meta, saved, y)
     dmoe_backward(dims, dy, weights, w1, w3, w2, meta, saved, scratch,
@@ -24,6 +25,7 @@ from __future__ import annotations
 
 import ctypes
 import dataclasses
+import functools
 import os
 from typing import Optional
 
@@ -32,7 +34,8 @@ import torch
 __all__ = [
     "DMOE_F32", "DMOE_BF16", "DMoEError", "DMoELibraryMissing", "Dims",
     "Meta", "Saved", "GradScratch", "library_path", "load_library",
-    "dmoe_max_tiles", "dmoe_workspace_bytes", "dmoe_metadata", "dmoe_forward",
+    "dmoe_max_tiles", "dmoe_workspace_bytes", "dmoe_schedule_bytes",
+    "dmoe_metadata", "dmoe_forward",
     "dmoe_backward", "dmoe_padded_gather", "dmoe_padded_scatter",
     "dmoe_router_forward", "dmoe_router_backward",
     "dmoe_status_string", "allocate", "allocate_meta", "DMoELayer",
@@ -67,7 +70,7 @@ class _Meta(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "tokens_per_expert", "bins", "padded_bins", "indices", "bin_ids",
         "row_of_entry", "tile_expert", "num_padded_rows", "status",
-        "pair_first", "num_pairs", "row_token", "xcd_first")]
+        "row_token", "schedule")]
 
 
 class _Saved(ctypes.Structure):
@@ -103,6 +106,8 @@ def load_library() -> ctypes.CDLL:
     lib.dmoe_max_tiles.restype = ctypes.c_int64
     lib.dmoe_workspace_bytes.argtypes = [P(_Dims)]
     lib.dmoe_workspace_bytes.restype = ctypes.c_int64
+    lib.dmoe_schedule_bytes.argtypes = [P(_Dims)]
+    lib.dmoe_schedule_bytes.restype = ctypes.c_int64
     lib.dmoe_metadata.argtypes = [P(_Dims), vp, P(_Meta), vp, vp]
     lib.dmoe_metadata.restype = ctypes.c_int
     lib.dmoe_forward.argtypes = [P(_Dims), vp, vp, vp, vp, vp, P(_Meta),
@@ -175,13 +180,12 @@ class Meta:
     tile_expert: torch.Tensor
     num_padded_rows: torch.Tensor
     status: torch.Tensor
-    pair_first: torch.Tensor
-    num_pairs: torch.Tensor
     row_token: torch.Tensor
-    xcd_first: torch.Tensor
+    schedule: torch.Tensor      # opaque: dmoe_schedule_bytes(dims) bytes
 
     def _c(self) -> _Meta:
-        return _Meta(*[_ptr(getattr(self, f.name), torch.int32, f.name)
+        return _Meta(*[_ptr(getattr(self, f.name),
+                            None if f.name == "schedule" else torch.int32, f.name)
                        for f in dataclasses.fields(self)])
 
 
@@ -248,27 +252,47 @@ def dmoe_status_string(code: int) -> str:
         return f"status {code}"
 
 
+@functools.lru_cache(maxsize=256)
+def _sizes(dims: Dims):
+    """(max_tiles, workspace bytes, schedule bytes) of dims, from the library
+    (cached: these depend on the sizes only)."""
+    lib = load_library()
+    d = dims._c()
+    out = []
+    for fn, name in ((lib.dmoe_max_tiles, "dmoe_max_tiles"),
+                     (lib.dmoe_workspace_bytes, "dmoe_workspace_bytes"),
+                     (lib.dmoe_schedule_bytes, "dmoe_schedule_bytes")):
+        v = fn(ctypes.byref(d))
+        _check(v if v < 0 else 0, name)
+        out.append(int(v))
+    return tuple(out)
+
+
 def dmoe_max_tiles(dims: Dims) -> int:
-    v = load_library().dmoe_max_tiles(ctypes.byref(dims._c()))
-    _check(v if v < 0 else 0, "dmoe_max_tiles")
-    return int(v)
+    return _sizes(dims)[0]
 
 
 def dmoe_workspace_bytes(dims: Dims) -> int:
-    v = load_library().dmoe_workspace_bytes(ctypes.byref(dims._c()))
-    _check(v if v < 0 else 0, "dmoe_workspace_bytes")
-    return int(v)
+    return _sizes(dims)[1]
+
+
+def dmoe_schedule_bytes(dims: Dims) -> int:
+    return _sizes(dims)[2]
 
 
 def _check_meta(dims: Dims, meta: Meta):
     n = dims.T * dims.k
+    nt, _, sb = _sizes(dims)
     for name, size in (("tokens_per_expert", dims.E), ("bins", dims.E),
                        ("padded_bins", dims.E), ("indices", n), ("bin_ids", n),
-                       ("row_of_entry", n), ("tile_expert", dmoe_max_tiles(dims)),
+                       ("row_of_entry", n), ("tile_expert", nt),
                        ("num_padded_rows", 1), ("status", 1),
-                       ("pair_first", dmoe_max_tiles(dims)), ("num_pairs", 1),
-                       ("row_token", 128 * dmoe_max_tiles(dims)), ("xcd_first", 9)):
+                       ("row_token", 128 * nt)):
         _need(getattr(meta, name), name, size)
+    s = meta.schedule
+    if s.numel() * s.element_size() < sb:
+        raise ValueError(f"schedule: needs at least {sb} bytes, has "
+                         f"{s.numel() * s.element_size()}")
 
 
 def _ev(events, n):
@@ -288,11 +312,12 @@ def dmoe_metadata(dims: Dims, top_experts: torch.Tensor, meta: Meta,
     _need(top_experts, "top_experts", dims.T * dims.k)
     _check_meta(dims, meta)
     _need(ws, "ws", dmoe_workspace_bytes(dims) // ws.element_size())
-    _check(lib.dmoe_metadata_timed(ctypes.byref(dims._c()),
-                                   _ptr(top_experts, torch.int32, "top_experts"),
-                                   ctypes.byref(meta._c()), _ptr(ws, None, "ws"),
-                                   _stream(top_experts, stream), _ev(events, 3)),
-           "dmoe_metadata")
+    args = (ctypes.byref(dims._c()), _ptr(top_experts, torch.int32, "top_experts"),
+            ctypes.byref(meta._c()), _ptr(ws, None, "ws"), _stream(top_experts, stream))
+    if events is None:
+        _check(lib.dmoe_metadata(*args), "dmoe_metadata")
+    else:
+        _check(lib.dmoe_metadata_timed(*args, _ev(events, 3)), "dmoe_metadata_timed")
 
 
 def _pmax(dims: Dims) -> int:
@@ -319,13 +344,16 @@ def dmoe_forward(dims: Dims, x, weights, w1, w3, w2, meta: Meta, saved: Saved,
     for t, n, s in need:
         _need(t, n, s)
     _check_meta(dims, meta)
-    fn = lib.dmoe_forward_fused_gather_timed if fused_gather else lib.dmoe_forward_timed
-    _check(fn(
-        ctypes.byref(dims._c()), _ptr(x, dt, "x"),
-        _ptr(weights, torch.float32, "weights"), _ptr(w1, dt, "w1"),
-        _ptr(w3, dt, "w3"), _ptr(w2, dt, "w2"), ctypes.byref(meta._c()),
-        ctypes.byref(saved._c(dt)), _ptr(y, dt, "y"), _stream(x, stream),
-        _ev(events, 3 if fused_gather else 4)), "dmoe_forward")
+    args = (ctypes.byref(dims._c()), _ptr(x, dt, "x"),
+            _ptr(weights, torch.float32, "weights"), _ptr(w1, dt, "w1"),
+            _ptr(w3, dt, "w3"), _ptr(w2, dt, "w2"), ctypes.byref(meta._c()),
+            ctypes.byref(saved._c(dt)), _ptr(y, dt, "y"), _stream(x, stream))
+    name = "dmoe_forward_fused_gather" if fused_gather else "dmoe_forward"
+    if events is None:
+        _check(getattr(lib, name)(*args), name)
+    else:
+        _check(getattr(lib, name + "_timed")(*args, _ev(events, 3 if fused_gather else 4)),
+               name + "_timed")
 
 
 def dmoe_backward(dims: Dims, dy, weights, w1, w3, w2, meta: Meta, saved: Saved,
@@ -355,22 +383,26 @@ def dmoe_backward(dims: Dims, dy, weights, w1, w3, w2, meta: Meta, saved: Saved,
                     (scratch.dx_perm, "dx_perm", pm * H)):
         _need(t, n, s)
     _check_meta(dims, meta)
+    args = [ctypes.byref(dims._c()), _ptr(dy, dt, "dy"),
+            _ptr(weights, torch.float32, "weights"), _ptr(w1, dt, "w1"),
+            _ptr(w3, dt, "w3"), _ptr(w2, dt, "w2"), ctypes.byref(meta._c()),
+            ctypes.byref(saved._c(dt)), ctypes.byref(scratch._c(dt)),
+            _ptr(dx, dt, "dx"), _ptr(dw1, dt, "dw1"), _ptr(dw3, dt, "dw3"),
+            _ptr(dw2, dt, "dw2"), _ptr(d_weights, torch.float32, "d_weights"),
+            _stream(dy, stream)]
     if x is not None:
         _need(x, "x", T * H)
-        fn = lambda *a: lib.dmoe_backward_fused_gather_timed(a[0], _ptr(x, dt, "x"), *a[1:])
+        name = "dmoe_backward_fused_gather"
+        args.insert(1, _ptr(x, dt, "x"))
     elif recompute:
-        fn = lib.dmoe_backward_recompute_timed
+        name = "dmoe_backward_recompute"
     else:
-        fn = lib.dmoe_backward_timed
-    _check(fn(
-        ctypes.byref(dims._c()), _ptr(dy, dt, "dy"),
-        _ptr(weights, torch.float32, "weights"), _ptr(w1, dt, "w1"),
-        _ptr(w3, dt, "w3"), _ptr(w2, dt, "w2"), ctypes.byref(meta._c()),
-        ctypes.byref(saved._c(dt)), ctypes.byref(scratch._c(dt)),
-        _ptr(dx, dt, "dx"), _ptr(dw1, dt, "dw1"), _ptr(dw3, dt, "dw3"),
-        _ptr(dw2, dt, "dw2"), _ptr(d_weights, torch.float32, "d_weights"),
-        _stream(dy, stream), _ev(events, 6 if recompute or x is not None else 5)),
-        "dmoe_backward")
+        name = "dmoe_backward"
+    if events is None:
+        _check(getattr(lib, name)(*args), name)
+    else:
+        _check(getattr(lib, name + "_timed")(
+            *args, _ev(events, 6 if recompute or x is not None else 5)), name + "_timed")
 
 
 def dmoe_padded_gather(dims: Dims, x, meta: Meta, x_perm, stream=None) -> None:
@@ -456,14 +488,14 @@ class Buffers:
 def allocate_meta(dims: Dims, device):
     """The metadata arrays and the metadata workspace for `dims`."""
     n, E = dims.T * dims.k, dims.E
-    nt = dmoe_max_tiles(dims)
+    nt, ws_bytes, sched_bytes = _sizes(dims)
     i32 = dict(dtype=torch.int32, device=device)
     meta = Meta(torch.empty(E, **i32), torch.empty(E, **i32), torch.empty(E, **i32),
                 torch.empty(n, **i32), torch.empty(n, **i32), torch.empty(n, **i32),
                 torch.empty(nt, **i32), torch.empty(1, **i32), torch.empty(1, **i32),
-                torch.empty(nt, **i32), torch.empty(1, **i32),
-                torch.empty(128 * nt, **i32), torch.empty(9, **i32))
-    ws = torch.empty(dmoe_workspace_bytes(dims), dtype=torch.uint8, device=device)
+                torch.empty(128 * nt, **i32),
+                torch.empty(sched_bytes, dtype=torch.uint8, device=device))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
     return meta, ws
 
 

@@ -26,7 +26,12 @@ int check_dims(const dmoe_dims* d) {
   return DMOE_OK;
 }
 
-// The row-block GEMMs put the 128-row block index on grid dimension y.
+// The fp32 products launch one block per tile on a 2-D or 3-D grid: the
+// row-block kernels put the 128-row block index on grid dimension y, and the
+// weight gradients put cdiv(H, 128) (dw1/dw3) or cdiv(F, 128) (dw2) there.
+// The bf16 engine launches a 1-D persistent grid and has no such limit; the
+// row-block bound is kept for both so that one shape is valid or not
+// whatever the dtype.
 constexpr int64_t kMaxGridY = 65535;
 
 int check_gemm_dims(const dmoe_dims* d) {
@@ -34,7 +39,10 @@ int check_gemm_dims(const dmoe_dims* d) {
   if (rc != DMOE_OK) return rc;
   const int64_t n = d->T * (int64_t)d->k;
   const int64_t tiles = (n + 127 * (int64_t)(d->E < n ? d->E : n)) / DMOE_BLOCK;
-  return tiles > kMaxGridY ? DMOE_ERR_UNSUPPORTED : DMOE_OK;
+  if (tiles > kMaxGridY) return DMOE_ERR_UNSUPPORTED;
+  if (d->dtype == DMOE_F32 && ((d->H + 127) / 128 > kMaxGridY || (d->F + 127) / 128 > kMaxGridY))
+    return DMOE_ERR_UNSUPPORTED;
+  return DMOE_OK;
 }
 
 int64_t max_tiles_of(const dmoe_dims* d) {
@@ -49,18 +57,21 @@ Shape shape_of(const dmoe_dims* d) {
 int check_meta(const dmoe_meta* m) {
   if (!m || !m->tokens_per_expert || !m->bins || !m->padded_bins || !m->indices ||
       !m->bin_ids || !m->row_of_entry || !m->tile_expert || !m->num_padded_rows ||
-      !m->status || !m->pair_first || !m->num_pairs || !m->row_token ||
-      !m->xcd_first)
+      !m->status || !m->row_token || !m->schedule)
     return DMOE_ERR_ARG;
   return DMOE_OK;
 }
 
-MetaPtrs meta_ptrs(const dmoe_meta* m) {
+// The schedule's tables sit at fixed offsets of its buffer (dmoe_internal.h).
+MetaPtrs meta_ptrs(const dmoe_meta* m, int64_t max_tiles) {
+  int32_t* sched = static_cast<int32_t*>(m->schedule);
   return MetaPtrs{m->tokens_per_expert, m->bins, m->padded_bins, m->indices,
                   m->bin_ids, m->row_of_entry, m->tile_expert, m->num_padded_rows,
-                  m->status, m->pair_first, m->num_pairs, m->row_token,
-                  m->xcd_first};
+                  m->status, sched, sched + max_tiles, m->row_token,
+                  sched + max_tiles + 1};
 }
+
+MetaPtrs meta_ptrs(const dmoe_meta* m, const dmoe_dims* d) { return meta_ptrs(m, max_tiles_of(d)); }
 
 // Records events[i] on the stream when timing is requested and the entry is
 // not NULL.
@@ -92,6 +103,12 @@ int64_t dmoe_workspace_bytes(const dmoe_dims* dims) {
   return dmoe::meta_workspace_bytes(dims->T * (int64_t)dims->k, dims->E);
 }
 
+int64_t dmoe_schedule_bytes(const dmoe_dims* dims) {
+  const int rc = check_dims(dims);
+  if (rc != DMOE_OK) return rc;
+  return dmoe::schedule_bytes(max_tiles_of(dims));
+}
+
 int dmoe_metadata_timed(const dmoe_dims* dims, const int32_t* top_experts,
                         const dmoe_meta* meta, void* ws, hipStream_t stream,
                         hipEvent_t* events) {
@@ -100,7 +117,7 @@ int dmoe_metadata_timed(const dmoe_dims* dims, const int32_t* top_experts,
   if ((rc = check_meta(meta)) != DMOE_OK) return rc;
   if (!top_experts || !ws) return DMOE_ERR_ARG;
   DMOE_TRY(dmoe::launch_metadata(dims->T * (int64_t)dims->k, dims->E, dims->k, max_tiles_of(dims),
-                                 top_experts, meta_ptrs(meta), ws, stream, events));
+                                 top_experts, meta_ptrs(meta, dims), ws, stream, events));
   return DMOE_OK;
 }
 
@@ -136,7 +153,7 @@ int forward_impl(const dmoe_dims* dims, const void* x, const float* weights, con
       !saved->h1 || !saved->h3 || !saved->act || !saved->y_perm)
     return DMOE_ERR_ARG;
   const Shape s = shape_of(dims);
-  const MetaPtrs m = meta_ptrs(meta);
+  const MetaPtrs m = meta_ptrs(meta, dims);
   Recorder rec{ev, stream};
   int i = 0;
   if (!fused) {
@@ -209,7 +226,7 @@ int backward_impl(const dmoe_dims* dims, const void* x, const void* dy, const fl
       !scratch->dh3 || !scratch->dx_perm)
     return DMOE_ERR_ARG;
   const Shape s = shape_of(dims);
-  const MetaPtrs m = meta_ptrs(meta);
+  const MetaPtrs m = meta_ptrs(meta, dims);
   Recorder rec{ev, stream};
   int i = 0;
   if (recompute) {
@@ -314,7 +331,7 @@ int dmoe_padded_gather(const dmoe_dims* dims, const void* x, const dmoe_meta* me
   if (rc != DMOE_OK) return rc;
   if ((rc = check_meta(meta)) != DMOE_OK) return rc;
   if (!x || !x_perm) return DMOE_ERR_ARG;
-  DMOE_TRY(dmoe::launch_padded_gather(shape_of(dims), x, meta_ptrs(meta), x_perm, stream));
+  DMOE_TRY(dmoe::launch_padded_gather(shape_of(dims), x, meta_ptrs(meta, dims), x_perm, stream));
   return DMOE_OK;
 }
 
@@ -325,7 +342,7 @@ int dmoe_padded_scatter(const dmoe_dims* dims, const void* src_perm,
   if (rc != DMOE_OK) return rc;
   if ((rc = check_meta(meta)) != DMOE_OK) return rc;
   if (!src_perm || !out) return DMOE_ERR_ARG;
-  DMOE_TRY(dmoe::launch_padded_scatter(shape_of(dims), src_perm, weights, meta_ptrs(meta),
+  DMOE_TRY(dmoe::launch_padded_scatter(shape_of(dims), src_perm, weights, meta_ptrs(meta, dims),
                                        out, stream));
   return DMOE_OK;
 }
@@ -360,7 +377,7 @@ const char* dmoe_status_string(int status) {
     case DMOE_OK: return "ok";
     case DMOE_ERR_ARG: return "invalid argument (null pointer, non-positive size, k > E or too many entries)";
     case DMOE_ERR_SHAPE: return "H and F must be multiples of 128";
-    case DMOE_ERR_UNSUPPORTED: return "unsupported (E > 256, dtype, H/F too large, or more than 65535 row blocks)";
+    case DMOE_ERR_UNSUPPORTED: return "unsupported (E > 256, dtype, H/F too large, or more than 65535 row blocks or, for fp32, 128-column blocks)";
     case DMOE_ERR_HIP: return "HIP kernel launch failed";
     case DMOE_ERR_EXPERT_ID: return "an expert id is outside [0, E)";
     default: return "unknown dmoe status";

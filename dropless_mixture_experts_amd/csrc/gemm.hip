@@ -1,4 +1,6 @@
-// Grouped GEMM over expert-tagged 128-row tiles (gfx950 MFMA).
+// Grouped GEMM over expert-tagged 128-row tiles (gfx950 MFMA), fp32.  The
+// launch_gemm_* entry points below route bf16 to the engine of
+// gemm_bf16.hip; the kernels of this file run the fp32 layer.
 //
 // MegaBlocks chapter "02 · dropless MoE 与 block-sparse 重构" §2-§3: once each
 // expert's rows are padded to a multiple of 128, every 128-row block of the
@@ -17,17 +19,17 @@
 //     side) x 128 "B rows" (token rows, or the m dimension of a weight
 //     gradient).  Each wave owns 128 x 64 = 8 x 4 MFMA 16x16 tiles.
 //   * LDS holds both operands K-contiguous, 64 bytes of K per row per stage
-//     (32 bf16 / 16 fp32) plus 16 bytes of padding, which spreads the eight
+//     (16 fp32) plus 16 bytes of padding, which spreads the eight
 //     rows read by consecutive lanes over distinct banks.  Two stages: the
 //     next K slice is fetched into registers while the MFMAs consume the
 //     current one, then stored into the other stage (one barrier per step).
 //   * An operand whose source has K contiguous is copied 16 bytes per lane.
 //     One whose source has the row dimension contiguous ([K][N] weights,
-//     and both operands of the weight gradients) is read in 8x4 (bf16) or
-//     4x4 (fp32) micro-blocks and transposed in registers before the LDS
-//     store, so every MFMA operand is one 16-byte LDS read per lane.
-//   * bf16: v_mfma_f32_16x16x32_bf16, one per 16x16 tile per 64-byte K slice.
-//     fp32: four v_mfma_f32_16x16x4_f32 per slice (full fp32 products).
+//     and both operands of the weight gradients) is read in 4x4 micro-blocks
+//     and transposed in registers before the LDS store, so every MFMA
+//     operand is one 16-byte LDS read per lane.
+//   * Four v_mfma_f32_16x16x4_f32 per 16x16 tile and 64-byte K slice (full
+//     fp32 products).
 //     Lane l of a 16x16 accumulator holds 4 consecutive A rows
 //     (4*(l/16) + 0..3) of B row l%16, so the output's contiguous
 //     dimension sits on the A side and each lane stores 4 adjacent elements.
@@ -89,40 +91,6 @@ template <typename T, int ROWS> struct Loader<T, false, ROWS> {
   }
 };
 
-// Row-contiguous bf16 source: each thread reads 8 K-rows x 4 columns (8 bytes
-// per row) and writes 4 LDS rows of 8 consecutive K values.
-template <int ROWS> struct Loader<bf16, true, ROWS> {
-  u32x2 v[8];
-  __device__ __forceinline__ bool active(bool has1, int tid) const {
-    return (ROWS == 256 || tid < 128) && (tid < 128 || has1);
-  }
-  __device__ __forceinline__ void load(const Operand& op, int ks, int tid) {
-    if (!active(op.has1, tid)) return;
-    const int half = tid >> 7, mb = tid & 127, kblk = mb >> 5, nblk = mb & 31;
-    const char* base = (half ? op.p1 : op.p0) +
-                       (int64_t)(ks * KStep<bf16>::elems + kblk * 8) * op.ld + nblk * 8;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      v[kk] = *reinterpret_cast<const u32x2*>(base + (int64_t)kk * op.ld);
-  }
-  __device__ __forceinline__ void store(char* lds, int tid, bool has1) const {
-    if (!active(has1, tid)) return;
-    const int half = tid >> 7, mb = tid & 127, kblk = mb >> 5, nblk = mb & 31;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int sh = (c & 1) * 16;
-      u32x4 o;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t lo = ((c < 2 ? v[2 * q].x : v[2 * q].y) >> sh) & 0xffffu;
-        const uint32_t hi = ((c < 2 ? v[2 * q + 1].x : v[2 * q + 1].y) >> sh) & 0xffffu;
-        o[q] = lo | (hi << 16);
-      }
-      *reinterpret_cast<u32x4*>(lds + (half * 128 + nblk * 4 + c) * kLdsRow + kblk * 16) = o;
-    }
-  }
-};
-
 // Row-contiguous fp32 source: 4 K-rows x 4 columns per thread.
 template <int ROWS> struct Loader<float, true, ROWS> {
   u32x4 v[4];
@@ -154,26 +122,6 @@ __device__ __forceinline__ int a_row(int i, int wm) { return (i >> 2) * 128 + wm
 __device__ __forceinline__ int b_row(int j, int wn) { return wn * 64 + j * 16; }
 
 template <typename T> struct Mma;
-template <> struct Mma<bf16> {
-  __device__ __forceinline__ static void stage(Acc& acc, const char* lds, int wm, int wn,
-                                               int lane, bool has1) {
-    const char* la = lds;
-    const char* lb = lds + kLdsA;
-    const int lrow = lane & 15, lk = (lane >> 4) * 16;
-    bf16x8 b[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      b[j] = *reinterpret_cast<const bf16x8*>(lb + (b_row(j, wn) + lrow) * kLdsRow + lk);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i >= 4 && !has1) break;
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(la + (a_row(i, wm) + lrow) * kLdsRow + lk);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[i][j], 0, 0, 0);
-    }
-  }
-};
 template <> struct Mma<float> {
   __device__ __forceinline__ static void stage(Acc& acc, const char* lds, int wm, int wn,
                                                int lane, bool has1) {
@@ -239,21 +187,9 @@ template <typename T> __device__ __forceinline__ void store4(T* p, const f32x4& 
 template <> __device__ __forceinline__ void store4<float>(float* p, const f32x4& v) {
   *reinterpret_cast<f32x4*>(p) = v;
 }
-template <> __device__ __forceinline__ void store4<bf16>(bf16* p, const f32x4& v) {
-  const uint32_t a = __builtin_bit_cast(uint16_t, from_f32<bf16>(v[0])) |
-                     ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<bf16>(v[1])) << 16);
-  const uint32_t b = __builtin_bit_cast(uint16_t, from_f32<bf16>(v[2])) |
-                     ((uint32_t)__builtin_bit_cast(uint16_t, from_f32<bf16>(v[3])) << 16);
-  *reinterpret_cast<u32x2*>(p) = u32x2{a, b};
-}
 template <typename T> __device__ __forceinline__ f32x4 load4(const T* p);
 template <> __device__ __forceinline__ f32x4 load4<float>(const float* p) {
   return *reinterpret_cast<const f32x4*>(p);
-}
-template <> __device__ __forceinline__ f32x4 load4<bf16>(const bf16* p) {
-  const u32x2 u = *reinterpret_cast<const u32x2*>(p);
-  return f32x4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-               __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
 }
 
 

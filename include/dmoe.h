@@ -68,7 +68,9 @@ typedef enum {
   DMOE_ERR_ARG = -1,         /* null pointer, non-positive size, k > E, T*k >= 2^31 */
   DMOE_ERR_SHAPE = -2,       /* F % 128 != 0 (MegaBlocks §5) or H % 128 != 0 */
   DMOE_ERR_UNSUPPORTED = -3, /* E > 256, an unknown dtype, H or F > 2^24, or
-                                (forward/backward) more than 65535 row blocks */
+                                (forward/backward) more than 65535 row blocks,
+                                or for fp32 more than 65535 128-column blocks
+                                of H or F */
   DMOE_ERR_HIP = -4,         /* a kernel launch failed */
   DMOE_ERR_EXPERT_ID = -5    /* device-side: an expert id outside [0,E) */
 } dmoe_status;
@@ -84,45 +86,36 @@ typedef struct {
 } dmoe_dims;
 
 /* Routing metadata, written by dmoe_metadata and read by the other calls
- * (MegaBlocks §4.1-§4.3).  All device int32 arrays owned by the caller.
- *   tokens_per_expert[E]  histogram of the expert ids
- *   bins[E]               inclusive cumsum of tokens_per_expert
- *   padded_bins[E]        inclusive cumsum of round_up(tokens_per_expert, 128)
- *   indices[T*k]          stable sort of the entries by expert: indices[s] = a
- *   bin_ids[T*k]          expert of the s-th sorted entry
- *   row_of_entry[T*k]     padded row of entry a:
+ * (MegaBlocks §4.1-§4.3).  Device arrays owned by the caller.
+ *   tokens_per_expert[E]  int32, histogram of the expert ids
+ *   bins[E]               int32, inclusive cumsum of tokens_per_expert
+ *   padded_bins[E]        int32, inclusive cumsum of round_up(tokens_per_expert, 128)
+ *   indices[T*k]          int32, stable sort of the entries by expert: indices[s] = a
+ *   bin_ids[T*k]          int32, expert of the s-th sorted entry
+ *   row_of_entry[T*k]     int32, padded row of entry a:
  *                         (s - bins[e-1]) + padded_bins[e-1], both starts 0 at e=0
- *   tile_expert[max_tiles] expert owning 128-row block r; -1 for r >= P/128
- *   num_padded_rows[1]    P = padded_bins[E-1]
- *   status[1]             0, or DMOE_ERR_EXPERT_ID
- *   pair_first[max_tiles] the row blocks grouped for the matrix products:
- *                         group s starts at block pair_first[s] and also
- *                         takes the next block when that block belongs to
- *                         the same expert (each expert's blocks are paired
- *                         in order; an odd last block stays single); -1
- *                         past the last group
- *   num_pairs[1]          number of groups
- *   row_token[max_tiles*128] the token whose row padded row p holds: a / k
- *                         for the entry a placed there (the §4.2 index rule
- *                         read from the row side), -1 for a pad row below P;
- *                         rows from P on are left untouched
- *   xcd_first[9]          the experts whose weight-gradient tiles each of the
- *                         8 XCDs (L2 domains) computes: [xcd_first[x],
- *                         xcd_first[x+1]), xcd_first[0] = 0, xcd_first[8] = E;
- *                         contiguous ranges whose largest cost is the
- *                         least possible, an expert costing its 128-row
- *                         blocks + 1 (a schedule, not part of the method's
- *                         result)                                          */
+ *   tile_expert[max_tiles] int32, expert owning 128-row block r; -1 for r >= P/128
+ *   num_padded_rows[1]    int32, P = padded_bins[E-1]
+ *   status[1]             int32, 0, or DMOE_ERR_EXPERT_ID
+ *   row_token[max_tiles*128] int32, the token whose row padded row p holds:
+ *                         a / k for the entry a placed there (the §4.2 index
+ *                         rule read from the row side), -1 for a pad row
+ *                         below P; rows from P on are left untouched
+ *   schedule              opaque, dmoe_schedule_bytes(dims) bytes: the order
+ *                         in which the grouped matrix products take their
+ *                         tiles, derived from the counts by dmoe_metadata and
+ *                         read by the forward and backward calls.  It is not
+ *                         part of the method's result; its layout is private
+ *                         to the library and may change without changing
+ *                         this struct.                                         */
 typedef struct {
   int32_t *tokens_per_expert, *bins, *padded_bins;
   int32_t *indices, *bin_ids, *row_of_entry;
   int32_t *tile_expert;
   int32_t *num_padded_rows;
   int32_t *status;
-  int32_t *pair_first;
-  int32_t *num_pairs;
   int32_t *row_token;
-  int32_t *xcd_first;
+  void *schedule;
 } dmoe_meta;
 
 /* Activations kept from forward for backward, each [P_max, H] or [P_max, F]
@@ -146,10 +139,18 @@ typedef struct {
  * dims. */
 int64_t dmoe_max_tiles(const dmoe_dims* dims);
 
-/* Bytes of device workspace `ws` that dmoe_metadata needs (per-chunk
- * expert histograms and error flags).  The other entry points take no
- * workspace.  Returns a negative dmoe_status on bad dims. */
+/* Bytes of device workspace `ws` that dmoe_metadata needs: per-chunk
+ * expert histograms and error flags, scratch that is dead once the call's
+ * kernels have run (the same ws may serve other work afterwards, in stream
+ * order).  The forward and backward calls need no workspace: no product is
+ * split along K and no reduction uses atomics, so there are no partial
+ * results to keep.  At most 4 210 688 bytes (4096 chunks x (256 + 1) int32).
+ * Returns a negative dmoe_status on bad dims. */
 int64_t dmoe_workspace_bytes(const dmoe_dims* dims);
+
+/* Bytes of dmoe_meta.schedule for these dims (a few KB: 4 * (max_tiles + 10)
+ * rounded up to 256).  Returns a negative dmoe_status on bad dims. */
+int64_t dmoe_schedule_bytes(const dmoe_dims* dims);
 
 /* Routing metadata (MegaBlocks §4.1 sort / histogram / cumsum and round_up,
  * §4.2 padded row of each entry, §4.3 row block -> expert).

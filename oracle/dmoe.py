@@ -53,8 +53,8 @@ BLOCK = 128
 __all__ = [
     "BLOCK", "round_up", "max_tiles", "metadata", "metadata_counting_sort",
     "padded_gather", "row_token", "padded_scatter", "silu", "sigmoid", "forward_loop",
-    "backward_loop", "forward_padded", "backward_padded", "sampled_rows",
-    "sampled_dw",
+    "backward_loop", "forward_padded", "backward_padded", "layer_by_expert",
+    "sampled_rows", "sampled_dw",
 ]
 
 
@@ -305,6 +305,28 @@ def _expert_rows(md, e):
     return start, end
 
 
+def _expert_forward(xp, W1, W3, W2):
+    """One expert's padded rows through its FFN ([MB] §3: the row blocks of
+    an expert touch only that expert's weights; [FL] gated SiLU)."""
+    h1 = xp @ W1
+    h3 = xp @ W3
+    act = silu(h1) * h3
+    return h1, h3, act, act @ W2
+
+
+def _expert_backward(xp, h1, h3, act, dyp, W1, W3, W2):
+    """The backward of ``_expert_forward`` for upstream dyp (the expert's
+    rows of dY_perm): dA = dY w2^T, the gated-SiLU derivative
+    (d silu(u)/du = s (1 + u (1 - s)), s = sigmoid(u)), dw2 = A^T dY,
+    dw1 = X^T dH1, dw3 = X^T dH3, dX = dH1 w1^T + dH3 w3^T."""
+    da = dyp @ W2.T
+    s = sigmoid(h1)
+    dh3 = da * h1 * s
+    dh1 = da * h3 * s * (1.0 + h1 * (1.0 - s))
+    return dict(dh1=dh1, dh3=dh3, dx_perm=dh1 @ W1.T + dh3 @ W3.T,
+                dw1=xp.T @ dh1, dw3=xp.T @ dh3, dw2=act.T @ dyp)
+
+
 def forward_padded(x, top_experts, weights, w1, w3, w2, md=None):
     """Forward through the padded layout, as in [MB] §4.5.
 
@@ -326,10 +348,8 @@ def forward_padded(x, top_experts, weights, w1, w3, w2, md=None):
         r0, r1 = _expert_rows(md, e)
         if r1 == r0:
             continue
-        h1[r0:r1] = xp[r0:r1] @ _f64(w1[e])
-        h3[r0:r1] = xp[r0:r1] @ _f64(w3[e])
-        act[r0:r1] = silu(h1[r0:r1]) * h3[r0:r1]
-        yp[r0:r1] = act[r0:r1] @ _f64(w2[e])
+        h1[r0:r1], h3[r0:r1], act[r0:r1], yp[r0:r1] = _expert_forward(
+            xp[r0:r1], _f64(w1[e]), _f64(w3[e]), _f64(w2[e]))
     y = padded_scatter(yp, md, weights, T, k)
     return y, dict(md=md, x_perm=xp, h1=h1, h3=h3, act=act, y_perm=yp)
 
@@ -369,18 +389,61 @@ def backward_padded(x, top_experts, weights, w1, w3, w2, dy, saved=None):
         r0, r1 = _expert_rows(md, e)
         if r1 == r0:
             continue
-        W1, W3, W2 = _f64(w1[e]), _f64(w3[e]), _f64(w2[e])
-        da = dyp[r0:r1] @ W2.T
-        s = sigmoid(h1[r0:r1])
-        dh3[r0:r1] = da * h1[r0:r1] * s
-        dh1[r0:r1] = da * h3[r0:r1] * s * (1.0 + h1[r0:r1] * (1.0 - s))
-        dw2[e] = act[r0:r1].T @ dyp[r0:r1]
-        dw1[e] = xp[r0:r1].T @ dh1[r0:r1]
-        dw3[e] = xp[r0:r1].T @ dh3[r0:r1]
-        dxp[r0:r1] = dh1[r0:r1] @ W1.T + dh3[r0:r1] @ W3.T
+        g = _expert_backward(xp[r0:r1], h1[r0:r1], h3[r0:r1], act[r0:r1], dyp[r0:r1],
+                             _f64(w1[e]), _f64(w3[e]), _f64(w2[e]))
+        dh1[r0:r1], dh3[r0:r1], dxp[r0:r1] = g["dh1"], g["dh3"], g["dx_perm"]
+        dw1[e], dw3[e], dw2[e] = g["dw1"], g["dw3"], g["dw2"]
     dx = dxp[rows].reshape(T, k, H).sum(axis=1)
     return dict(dx=dx, dw1=dw1, dw3=dw3, dw2=dw2, d_weights=d_weights,
                 dy_perm=dyp, dh1=dh1, dh3=dh3, dx_perm=dxp)
+
+
+def layer_by_expert(x, top_experts, weights, w1, w3, w2, dy, out, md=None):
+    """The forward and backward of ``forward_padded`` / ``backward_padded``,
+    one expert at a time, for layers too large to hold every fp64
+    intermediate at once.
+
+    Yields, per expert e in order, a dict with its padded row range
+    ``rows`` = (r0, r1), its rows of x_perm, h1, h3, act, y_perm, dy_perm,
+    dh1, dh3, dx_perm (pad rows zero, as in the padded layout) and dw1[e],
+    dw3[e], dw2[e] (zeros for an empty expert).  Meanwhile it adds each
+    real row's share into ``out["y"]`` [T,H] and ``out["dx"]`` [T,H] and
+    writes ``out["d_weights"]`` [T,k] (fp64 arrays the caller provides,
+    zero-filled): the weighted scatter with the top-k sum and the gather's
+    backward of [MB] §4.2, and the routing-weight gradient
+    <dy[a // k], y_perm[row_of_entry[a]]>.  When the generator is exhausted,
+    those three arrays hold y, dx and d_weights.
+    """
+    ids = np.asarray(top_experts)
+    T, k = ids.shape
+    E, H, F = np.shape(w1)
+    if md is None:
+        md = metadata(ids, E)
+    wflat = _f64(weights).reshape(-1)
+    rows = md["row_of_entry"]
+    for e in range(E):
+        r0, r1 = _expert_rows(md, e)
+        n = r1 - r0
+        if n == 0:
+            yield dict(e=e, rows=(r0, r1), dw1=np.zeros((H, F)), dw3=np.zeros((H, F)),
+                       dw2=np.zeros((F, H)))
+            continue
+        ent = md["indices"][md["bins"][e] - md["tokens_per_expert"][e]:md["bins"][e]]
+        loc = rows[ent] - r0                 # the entries' rows within the expert
+        tok = ent // k
+        xp = np.zeros((n, H))
+        xp[loc] = _f64(x[tok])
+        W1, W3, W2 = _f64(w1[e]), _f64(w3[e]), _f64(w2[e])
+        h1, h3, act, yp = _expert_forward(xp, W1, W3, W2)
+        dyt = _f64(dy[tok])
+        dyp = np.zeros((n, H))
+        dyp[loc] = dyt * wflat[ent][:, None]
+        g = _expert_backward(xp, h1, h3, act, dyp, W1, W3, W2)
+        np.add.at(out["y"], tok, yp[loc] * wflat[ent][:, None])
+        np.add.at(out["dx"], tok, g["dx_perm"][loc])
+        out["d_weights"].reshape(-1)[ent] = np.einsum("ah,ah->a", dyt, yp[loc])
+        yield dict(e=e, rows=(r0, r1), x_perm=xp, h1=h1, h3=h3, act=act, y_perm=yp,
+                   dy_perm=dyp, **g)
 
 
 # --------------------------------------------------------------------------

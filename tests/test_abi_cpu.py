@@ -29,7 +29,8 @@ def lib():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("dmoe_metadata", "dmoe_forward", "dmoe_backward", "dmoe_max_tiles",
-              "dmoe_workspace_bytes", "dmoe_padded_gather", "dmoe_padded_scatter",
+              "dmoe_workspace_bytes", "dmoe_schedule_bytes", "dmoe_padded_gather",
+              "dmoe_padded_scatter",
               "dmoe_status_string", "dmoe_router_forward", "dmoe_router_backward",
               "dmoe_backward_recompute", "dmoe_backward_recompute_timed",
               "dmoe_forward_fused_gather", "dmoe_backward_fused_gather"):
@@ -52,8 +53,14 @@ def test_max_tiles_and_workspace(lib):
     # floor((1024 + 127*8)/128) = floor(2040/128) = 15
     assert lib.dmoe_max_tiles(ctypes.byref(d)) == 15
     assert lib.dmoe_workspace_bytes(ctypes.byref(d)) > 0
+    # the schedule: 15 + 10 int32, rounded up to 256 bytes
+    assert lib.dmoe_schedule_bytes(ctypes.byref(d)) == 256
     d = _dims(T=16384, H=1536, F=256, E=256, k=8)
     assert lib.dmoe_max_tiles(ctypes.byref(d)) == (131072 + 127 * 256) // 128
+    assert lib.dmoe_schedule_bytes(ctypes.byref(d)) >= 4 * ((131072 + 127 * 256) // 128 + 10)
+    # the largest workspace: 4096 chunks of E = 256 counts and a flag each
+    big = _dims(T=268_000_000, k=8, E=256)
+    assert 0 < lib.dmoe_workspace_bytes(ctypes.byref(big)) <= 4096 * 257 * 4
     d = _dims(T=1, k=1, E=256)           # min(E, T*k) = 1
     assert lib.dmoe_max_tiles(ctypes.byref(d)) == 1
 
@@ -66,19 +73,20 @@ def test_bad_dims_rejected(lib, kw, code):
     d = _dims(**kw)
     assert lib.dmoe_max_tiles(ctypes.byref(d)) == code
     assert lib.dmoe_workspace_bytes(ctypes.byref(d)) == code
-    meta = dm._Meta(*([ctypes.c_void_p(0x1000)] * 13))
+    assert lib.dmoe_schedule_bytes(ctypes.byref(d)) == code
+    meta = dm._Meta(*([ctypes.c_void_p(0x1000)] * 11))
     assert lib.dmoe_metadata(ctypes.byref(d), ctypes.c_void_p(0x1000),
                              ctypes.byref(meta), ctypes.c_void_p(0x1000), None) == code
 
 
 def test_null_pointers_rejected_before_launch(lib):
     d = _dims()
-    meta = dm._Meta(*([ctypes.c_void_p(0x1000)] * 13))
+    meta = dm._Meta(*([ctypes.c_void_p(0x1000)] * 11))
     assert lib.dmoe_metadata(ctypes.byref(d), None, ctypes.byref(meta),
                              ctypes.c_void_p(0x1000), None) == -1
     assert lib.dmoe_metadata(ctypes.byref(d), ctypes.c_void_p(0x1000),
                              ctypes.byref(meta), None, None) == -1
-    bad = dm._Meta(*([ctypes.c_void_p(0x1000)] * 12 + [None]))
+    bad = dm._Meta(*([ctypes.c_void_p(0x1000)] * 10 + [None]))   # no schedule
     assert lib.dmoe_metadata(ctypes.byref(d), ctypes.c_void_p(0x1000),
                              ctypes.byref(bad), ctypes.c_void_p(0x1000), None) == -1
     saved = dm._Saved(*([ctypes.c_void_p(0x1000)] * 4 + [None]))
@@ -110,7 +118,7 @@ def test_fused_gather_checks_before_launch(lib):
     """The fused gather is bf16 only, needs x below 2 GB and, in the
     backward, the forward's x; a meta without row_token is rejected."""
     p = ctypes.c_void_p(0x1000)
-    meta = dm._Meta(*([p] * 13))
+    meta = dm._Meta(*([p] * 11))
     saved = dm._Saved(None, p, p, p, p)          # no x_perm: allowed here
     scratch = dm._Scratch(p, p, p, p)
     f32 = _dims()
@@ -126,7 +134,7 @@ def test_fused_gather_checks_before_launch(lib):
     assert lib.dmoe_backward_fused_gather(ctypes.byref(bf), None, p, p, p, p, p,
                                           ctypes.byref(meta), ctypes.byref(saved),
                                           ctypes.byref(scratch), p, p, p, p, p, None) == -1
-    no_rt = dm._Meta(*([p] * 11 + [None, p]))
+    no_rt = dm._Meta(*([p] * 9 + [None, p]))
     assert lib.dmoe_forward_fused_gather(ctypes.byref(bf), p, p, p, p, p, ctypes.byref(no_rt),
                                          ctypes.byref(saved), p, None) == -1
     # the plain path needs x_perm, and so does the fused backward (it

@@ -1,9 +1,10 @@
 """Forward + backward of the whole layer on the GPU vs the fp64 oracle.
 
-Small cases (several 128-row tiles, ragged tails, empty experts) compare
-every output and every intermediate element by element.  Full-size cases run
-the exact call sequence the benchmark times and compare sampled outputs that
-the oracle computes one by one from the per-entry definition."""
+Small cases (several 128-row tiles, ragged tails, empty experts) and every
+workload at full size compare every output and every intermediate element by
+element; at full size the oracle runs one expert at a time
+(oracle.layer_by_expert), and sampled outputs that it computes one by one
+from the per-entry definition give a second opinion."""
 import numpy as np
 import pytest
 import torch
@@ -144,41 +145,53 @@ def _picks(inp, md, rng, n=24):
 LARGE = shrink(CONFIGS["fine_e64"], T=32768, H=8192, F=128)
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "fine_e64", "zipf_e64",
-                                  "zipf_e64_empty", "coarse_e8", "sparse_e256",
-                                  "large_over_4gb"])
-def test_full_size_sampled(name):
-    cfg = LARGE if name == "large_over_4gb" else CONFIGS[name]
-    inp = make_inputs(cfg)
-    print(f"full {name}", flush=True)
-    r = Run(inp)
-    if name == "large_over_4gb":
-        assert r.P * cfg.H * 2 > (1 << 32)
-        f = Run(inp, fused_gather=True)
-        assert torch.equal(f.y, r.y)
-        for key in OUTS:
-            assert torch.equal(f.g[key], r.g[key]), key
-        del f
-    tol = TOL[cfg.dtype]
-    md = oracle.metadata(inp.top_experts, cfg.E, len(r.meta.tile_expert))
-    got_md = r.meta_np()
-    for key in ("tokens_per_expert", "bins", "padded_bins", "indices", "bin_ids",
-                "row_of_entry", "tile_expert"):
-        np.testing.assert_array_equal(got_md[key], md[key], err_msg=key)
-    P = md["P"]
-    assert r.P == P
-    # x_perm: every real row is the token row, every pad row zero
-    a = np.arange(cfg.T * cfg.k)
-    rows = torch.from_numpy(md["row_of_entry"]).to(r.dev)
-    src = torch.from_numpy(a // cfg.k).to(r.dev)
-    assert torch.equal(r.saved.x_perm[rows], r.x[src])
-    pad = torch.ones(P, dtype=torch.bool, device=r.dev)
-    pad[rows] = False
-    for t in (r.saved.x_perm, r.saved.h1, r.saved.h3, r.saved.act, r.saved.y_perm,
-              r.scratch.dy_perm, r.scratch.dh1, r.scratch.dh3, r.scratch.dx_perm):
-        assert int(torch.count_nonzero(t[:P][pad])) == 0
-    for t in (r.y, r.g["dx"], r.g["dw1"], r.g["dw3"], r.g["dw2"], r.g["d_weights"]):
-        assert bool(torch.isfinite(t).all())
+def _elementwise(r, inp, md, tol, name):
+    """Every output and every intermediate below P, element by element,
+    against the oracle taken one expert at a time: metadata bit-exact, x_perm
+    bit-exact, the rest within tol * max|ref| of each whole tensor."""
+    cfg = inp.cfg
+    out = dict(y=np.zeros((cfg.T, cfg.H)), dx=np.zeros((cfg.T, cfg.H)),
+               d_weights=np.zeros((cfg.T, cfg.k)))
+    worst = {}
+
+    def note(key, got, ref):
+        err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+        scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+        assert np.all(np.isfinite(got)), f"{name} {key}: non-finite values"
+        e0, s0 = worst.get(key, (0.0, 0.0))
+        worst[key] = (max(e0, err), max(s0, scale))
+
+    bufs = {"h1": r.saved.h1, "h3": r.saved.h3, "act": r.saved.act,
+            "y_perm": r.saved.y_perm, "dy_perm": r.scratch.dy_perm,
+            "dh1": r.scratch.dh1, "dh3": r.scratch.dh3, "dx_perm": r.scratch.dx_perm}
+    for res in oracle.layer_by_expert(inp.x, inp.top_experts, inp.weights, inp.w1,
+                                      inp.w3, inp.w2, inp.dy, out, md=md):
+        e, (r0, r1) = res["e"], res["rows"]
+        for key in ("dw1", "dw3", "dw2"):
+            got = down(r.g[key][e])
+            if r1 == r0:
+                assert np.all(got == 0.0), f"{name} {key}[{e}]: empty expert not zero"
+            note(key, got, res[key])
+        if r1 == r0:
+            continue
+        assert np.array_equal(down(r.saved.x_perm[r0:r1]), res["x_perm"]), \
+            f"{name} x_perm rows of expert {e}"
+        for key, t in bufs.items():
+            note(key, down(t[r0:r1]), res[key])
+    note("y", down(r.y), out["y"])
+    note("dx", down(r.g["dx"]), out["dx"])
+    note("d_weights", down(r.g["d_weights"]), out["d_weights"])
+    for key, (err, scale) in sorted(worst.items()):
+        print(f"  {name} {key}: max err {err:.3e}, max|ref| {scale:.3e}", flush=True)
+        assert err <= tol * scale, f"{name} {key}: max err {err:.3e} > {tol} * {scale:.3e}"
+    assert set(worst) == {"dw1", "dw3", "dw2", "y", "dx", "d_weights", *bufs}
+
+
+def _sampled(r, inp, md, tol, name):
+    """A second opinion from the per-entry definition: rows of y and dx,
+    d_weights of a few tokens, and single weight-gradient elements, each
+    computed on its own by the oracle."""
+    cfg = inp.cfg
     rng = np.random.default_rng(17)
     toks = sorted(set([0, cfg.T - 1] + list(rng.integers(0, cfg.T, 22))))
     ref = oracle.sampled_rows(inp.x, inp.top_experts, inp.weights, inp.w1, inp.w3,
@@ -198,5 +211,59 @@ def test_full_size_sampled(name):
         scale = float(np.max(np.abs(want[sel])))
         err = float(np.max(np.abs(got - want[sel])))
         assert err <= tol * scale, f"{name} {nm}: {err:.3e} > {tol}*{scale:.3e}"
-        empty = [i for i in sel if md["tokens_per_expert"][picks[i][1]] == 0]
-        assert all(float(r.g[nm][picks[i][1]].abs().max()) == 0.0 for i in empty)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["tiny_f32", "fine_e64", "zipf_e64",
+                                  "zipf_e64_empty", "coarse_e8", "sparse_e256",
+                                  "large_over_4gb"])
+def test_full_size(name):
+    """The launch sequence the benchmark times, at the workload's full size:
+    every output and intermediate element by element against the oracle,
+    plus sampled per-entry values as a second opinion."""
+    cfg = LARGE if name == "large_over_4gb" else CONFIGS[name]
+    inp = make_inputs(cfg)
+    print(f"full {name}", flush=True)
+    r = Run(inp)
+    if name == "large_over_4gb":
+        assert r.P * cfg.H * 2 > (1 << 32)
+        f = Run(inp, fused_gather=True)
+        assert torch.equal(f.y, r.y)
+        for key in OUTS:
+            assert torch.equal(f.g[key], r.g[key]), key
+        del f
+    tol = TOL[cfg.dtype]
+    md = oracle.metadata(inp.top_experts, cfg.E, len(r.meta.tile_expert))
+    got_md = r.meta_np()
+    for key in ("tokens_per_expert", "bins", "padded_bins", "indices", "bin_ids",
+                "row_of_entry", "tile_expert"):
+        np.testing.assert_array_equal(got_md[key], md[key], err_msg=key)
+    P = md["P"]
+    assert r.P == P
+    # pad rows of every padded buffer are exact zeros
+    rows = torch.from_numpy(md["row_of_entry"]).to(r.dev)
+    pad = torch.ones(P, dtype=torch.bool, device=r.dev)
+    pad[rows] = False
+    for t in (r.saved.x_perm, r.saved.h1, r.saved.h3, r.saved.act, r.saved.y_perm,
+              r.scratch.dy_perm, r.scratch.dh1, r.scratch.dh3, r.scratch.dx_perm):
+        assert int(torch.count_nonzero(t[:P][pad])) == 0
+    _sampled(r, inp, md, tol, name)
+    _elementwise(r, inp, md, tol, name)
+
+
+def test_full_size_runs_are_bitwise_identical():
+    """Two runs of the whole layer at the headline size agree bit for bit in
+    every output, every saved activation and every backward intermediate (no
+    reduction uses atomics)."""
+    inp = make_inputs(CONFIGS["fine_e64"])
+    print("bitwise fine_e64", flush=True)
+    a = Run(inp)
+    b = Run(inp)
+    assert torch.equal(a.y, b.y)
+    for key in OUTS:
+        assert torch.equal(a.g[key], b.g[key]), key
+    P = a.P
+    for name in ("x_perm", "h1", "h3", "act", "y_perm"):
+        assert torch.equal(getattr(a.saved, name)[:P], getattr(b.saved, name)[:P]), name
+    for name in ("dy_perm", "dh1", "dh3", "dx_perm"):
+        assert torch.equal(getattr(a.scratch, name)[:P], getattr(b.scratch, name)[:P]), name

@@ -11,7 +11,7 @@ import dropless_mixture_experts_amd as dm
 import oracle
 from workloads import CONFIGS, make_inputs
 
-from gpu_helpers import device, dims_of, up
+from gpu_helpers import device, dims_of, schedule_tables, up
 
 pytestmark = pytest.mark.gpu
 
@@ -36,8 +36,9 @@ def _run_meta(ids_np, E, dtype=dm.DMOE_BF16, H=128, F=128):
     out = {k: getattr(meta, k).cpu().numpy().astype(np.int64) for k in KEYS}
     out["P"] = int(meta.num_padded_rows.item())
     out["status"] = int(meta.status.item())
-    out["pair_first"] = meta.pair_first.cpu().numpy().astype(np.int64)
-    out["num_pairs"] = int(meta.num_pairs.item())
+    sched = schedule_tables(meta, dm.dmoe_max_tiles(D))
+    out["pair_first"] = sched["pair_first"]
+    out["num_pairs"] = sched["num_pairs"]
     out["row_token"] = meta.row_token.cpu().numpy().astype(np.int64)
     return out, dm.dmoe_max_tiles(D)
 
@@ -169,7 +170,7 @@ def test_weight_gradient_xcd_ranges_are_optimal(name):
     meta, ws = dm.allocate_meta(D, dev)
     dm.dmoe_metadata(D, up(inp.top_experts, torch.int32, dev), meta, ws)
     torch.cuda.synchronize()
-    xf = meta.xcd_first.cpu().numpy().astype(np.int64)
+    xf = schedule_tables(meta, dm.dmoe_max_tiles(D))["xcd_first"]
     blocks = (meta.padded_bins.cpu().numpy().astype(np.int64)
               - np.concatenate([[0], meta.padded_bins.cpu().numpy()[:-1]])) // 128
     assert xf[0] == 0 and xf[8] == cfg.E

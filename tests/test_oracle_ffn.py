@@ -206,3 +206,38 @@ def test_sampled_outputs_match_full_backward():
     vals = oracle.sampled_dw(**L, dy=dy, picks=picks)
     for (name, e, i, j), v in zip(picks, vals):
         assert abs(v - g[name][e][i, j]) <= 1e-12 * max(1.0, abs(v))
+
+
+@pytest.mark.parametrize("T,H,F,E,k,distinct", [
+    (40, 8, 6, 5, 2, True),      # most experts under one 128-row block
+    (300, 4, 3, 3, 2, True),     # experts of several blocks
+    (30, 5, 4, 7, 1, True),      # some experts empty
+    (200, 3, 5, 2, 3, False),    # duplicate ids in a token's row
+])
+def test_layer_by_expert_equals_padded_pipeline(T, H, F, E, k, distinct):
+    """The expert-at-a-time form gives every padded intermediate, every
+    weight gradient and y, dx, d_weights of the whole-layer padded form."""
+    rng = np.random.default_rng(T + 7 * E)
+    L = _rand_layer(rng, T, H, F, E, k, distinct)
+    dy = rng.standard_normal((T, H))
+    y, sv = oracle.forward_padded(**L)
+    g = oracle.backward_padded(**L, dy=dy, saved=sv)
+    out = dict(y=np.zeros((T, H)), dx=np.zeros((T, H)), d_weights=np.zeros((T, k)))
+    seen = []
+    for r in oracle.layer_by_expert(**L, dy=dy, out=out):
+        e, (r0, r1) = r["e"], r["rows"]
+        seen.append(e)
+        for key in ("dw1", "dw3", "dw2"):
+            np.testing.assert_allclose(r[key], g[key][e], rtol=1e-12, atol=1e-12)
+        if r1 == r0:
+            continue
+        for key, ref in (("x_perm", sv["x_perm"]), ("h1", sv["h1"]), ("h3", sv["h3"]),
+                         ("act", sv["act"]), ("y_perm", sv["y_perm"]),
+                         ("dy_perm", g["dy_perm"]), ("dh1", g["dh1"]),
+                         ("dh3", g["dh3"]), ("dx_perm", g["dx_perm"])):
+            np.testing.assert_allclose(r[key], ref[r0:r1], rtol=1e-12, atol=1e-12,
+                                       err_msg=key)
+    assert seen == list(range(E))
+    np.testing.assert_allclose(out["y"], y, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(out["dx"], g["dx"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(out["d_weights"], g["d_weights"], rtol=1e-12, atol=1e-12)
