@@ -35,7 +35,7 @@ __all__ = [
     "DMOE_F32", "DMOE_BF16", "DMoEError", "DMoELibraryMissing", "Dims",
     "Meta", "Saved", "GradScratch", "library_path", "load_library",
     "dmoe_max_tiles", "dmoe_workspace_bytes", "dmoe_schedule_bytes",
-    "dmoe_metadata", "dmoe_forward",
+    "dmoe_metadata", "dmoe_metadata_noalloc", "dmoe_forward",
     "dmoe_backward", "dmoe_padded_gather", "dmoe_padded_scatter",
     "dmoe_router_forward", "dmoe_router_backward",
     "dmoe_status_string", "allocate", "allocate_meta", "DMoELayer",
@@ -110,6 +110,8 @@ def load_library() -> ctypes.CDLL:
     lib.dmoe_schedule_bytes.restype = ctypes.c_int64
     lib.dmoe_metadata.argtypes = [P(_Dims), vp, P(_Meta), vp, vp]
     lib.dmoe_metadata.restype = ctypes.c_int
+    lib.dmoe_metadata_noalloc.argtypes = [P(_Dims), vp, P(_Meta), vp]
+    lib.dmoe_metadata_noalloc.restype = ctypes.c_int
     lib.dmoe_forward.argtypes = [P(_Dims), vp, vp, vp, vp, vp, P(_Meta),
                                  P(_Saved), vp, vp]
     lib.dmoe_forward.restype = ctypes.c_int
@@ -318,6 +320,20 @@ def dmoe_metadata(dims: Dims, top_experts: torch.Tensor, meta: Meta,
         _check(lib.dmoe_metadata(*args), "dmoe_metadata")
     else:
         _check(lib.dmoe_metadata_timed(*args, _ev(events, 3)), "dmoe_metadata_timed")
+
+
+def dmoe_metadata_noalloc(dims: Dims, top_experts: torch.Tensor, meta: Meta,
+                          stream=None) -> None:
+    """dmoe_metadata with its workspace in the library's own device array
+    (no ws argument, nothing allocated); see include/dmoe.h for the limit
+    and for calls that overlap on one GPU."""
+    lib = load_library()
+    _need(top_experts, "top_experts", dims.T * dims.k)
+    _check_meta(dims, meta)
+    _check(lib.dmoe_metadata_noalloc(ctypes.byref(dims._c()),
+                                     _ptr(top_experts, torch.int32, "top_experts"),
+                                     ctypes.byref(meta._c()), _stream(top_experts, stream)),
+           "dmoe_metadata_noalloc")
 
 
 def _pmax(dims: Dims) -> int:

@@ -1,8 +1,16 @@
 // C ABI of the dMoE layer: argument checks and the launch sequence of each
 // entry point.  Every check here runs on the host before anything is
 // enqueued; nothing is allocated and nothing waits on the device.
+#include <mutex>
+
 #include "../../include/dmoe.h"
 #include "dmoe_internal.h"
+
+// Workspace of dmoe_metadata_noalloc: the metadata's per-chunk histograms
+// and error flags for callers that cannot allocate.  The largest workspace
+// any valid dims need: at most 4096 chunks of E <= 256 counts and one flag
+// each.  Each GPU the library runs on holds one copy until the process ends.
+static __device__ __align__(256) char scratch[4096 * (256 + 1) * 4];
 
 
 namespace {
@@ -124,6 +132,52 @@ int dmoe_metadata_timed(const dmoe_dims* dims, const int32_t* top_experts,
 int dmoe_metadata(const dmoe_dims* dims, const int32_t* top_experts,
                   const dmoe_meta* meta, void* ws, hipStream_t stream) {
   return dmoe_metadata_timed(dims, top_experts, meta, ws, stream, nullptr);
+}
+
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of this GPU's copy of `scratch`, looked up once per
+// device with that device current.  In host code `scratch` names a host-side
+// stand-in, not device memory, so it is never passed to a kernel itself.
+int scratch_of_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DMOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return DMOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+      return DMOE_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dmoe_metadata_noalloc(const dmoe_dims* dims, const int32_t* top_experts,
+                          const dmoe_meta* meta, hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc != DMOE_OK) return rc;
+  if ((rc = check_meta(meta)) != DMOE_OK) return rc;
+  if (!top_experts) return DMOE_ERR_ARG;
+  if (dmoe::meta_workspace_bytes(dims->T * (int64_t)dims->k, dims->E) >
+      (int64_t)sizeof(scratch))
+    return DMOE_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if ((rc = scratch_of_current_device(&ws)) != DMOE_OK) return rc;
+  DMOE_TRY(dmoe::launch_metadata(dims->T * (int64_t)dims->k, dims->E, dims->k, max_tiles_of(dims),
+                                 top_experts, meta_ptrs(meta, dims), ws, stream, nullptr));
+  return DMOE_OK;
 }
 
 }  // extern "C"

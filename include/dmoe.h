@@ -160,6 +160,20 @@ int64_t dmoe_schedule_bytes(const dmoe_dims* dims);
 int dmoe_metadata(const dmoe_dims* dims, const int32_t* top_experts,
                   const dmoe_meta* meta, void* ws, hipStream_t stream);
 
+/* dmoe_metadata without the workspace argument, for callers that cannot
+ * allocate device memory at all (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  Same results as
+ * dmoe_metadata, bit for bit.  The workspace is a 4 210 688-byte array in
+ * the library's own device memory (one per GPU, held until the process
+ * ends), which this call neither allocates nor frees.  Every call on one
+ * GPU uses that GPU's one array: calls that may overlap in time on one GPU
+ * (different streams, or different host threads without stream order
+ * between them) race and give unspecified metadata; calls in the order of
+ * one stream do not.  Dims whose workspace would exceed the array return
+ * DMOE_ERR_UNSUPPORTED (none do under the limits DMOE_ERR_ARG enforces). */
+int dmoe_metadata_noalloc(const dmoe_dims* dims, const int32_t* top_experts,
+                          const dmoe_meta* meta, hipStream_t stream);
+
 /* Forward: padded_gather (MegaBlocks §4.2) -> per-128-row-block gated-SiLU
  * up projection (the sdd of §3, GLU variant of §5) -> down projection (the
  * dsd of §3) -> padded_scatter with the routing weights and the top-k sum
