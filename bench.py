@@ -10,17 +10,20 @@ Prints ONE JSON line with tokens/s, the per-kernel times (HIP events that
 the library records between its kernels: around every kernel in an untimed
 pass, and around the dominant kernel in the timed steps, each interval less
 the measured cost of one record), the roofline of the dominant kernel and
-the CPU oracle's rate on the host.
+the CPU oracle's rate on the host.  The same line carries a compact record
+of the other seeded workloads (``workloads``), the step with the
+activation-lean backward (``lean_backward``) and cold-cache figures.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+                    [--workloads zipf_e64,coarse_e8,... | none]
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import statistics
 import sys
-import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -148,20 +151,6 @@ def cpu_literal_loop(inp, threads, max_tokens=64, budget_s=20.0):
                        f"{n} tokens of the workload, one token per call: {dt:.2f} s")}
 
 
-def gpu_sclk_mhz():
-    """The shader clock the amdgpu kernel driver reports as current (sysfs
-    pp_dpm_sclk, the level marked '*'), or None where it is not readable."""
-    import glob
-    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
-        try:
-            for line in open(f):
-                if "*" in line:
-                    return int(line.split(":")[1].strip().lower().split("mhz")[0])
-        except (OSError, ValueError, IndexError):
-            continue
-    return None
-
-
 def event_overhead_ms(stream, n=40):
     """Median interval between two HIP event records with nothing between
     them on the stream: what every bracketed interval carries on top of
@@ -233,13 +222,271 @@ def router_time(dm, cfg, dev, stream, steps):
     return round(e0.elapsed_time(e1) * 1e3 / steps, 1)
 
 
+
+def saved_bytes_per_token(cfg, P):
+    """Bytes of activations kept from the forward for the backward, per
+    token: the plain backward keeps x_perm, h1, h3, act and y_perm; the
+    activation recompute drops act; the lean backward keeps y_perm only (it
+    rebuilds the rest from x, which the caller holds anyway)."""
+    s = 4 if cfg.dtype == "f32" else 2
+    H, F = cfg.H, cfg.F
+    per_row = {"plain": 2 * H + 3 * F, "recompute_act": 2 * H + 2 * F, "lean": H}
+    return {k: round(v * s * P / cfg.T, 1) for k, v in per_row.items()}
+
+
+class Layer:
+    """One workload resident on the GPU with its buffers and the step."""
+
+    def __init__(self, dm, cfg, dev, gather="auto", inputs=None):
+        import numpy as np
+        import torch
+        from workloads import make_inputs
+        self.dm, self.cfg, self.dev = dm, cfg, dev
+        self.inp = inputs if inputs is not None else make_inputs(cfg)
+        dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
+        up = lambda a, d=dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(d)
+        inp = self.inp
+        self.x, self.dy = up(inp.x), up(inp.dy)
+        self.ids = up(inp.top_experts, torch.int32)
+        self.w = up(inp.weights, torch.float32)
+        self.w1, self.w3, self.w2 = up(inp.w1), up(inp.w3), up(inp.w2)
+        self.D = dm.Dims(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k,
+                         dm.DMOE_F32 if cfg.dtype == "f32" else dm.DMOE_BF16)
+        self.fused = cfg.dtype == "bf16" and (
+            gather == "fused" or (gather == "auto" and dm.fused_gather_pays(self.D)))
+        self.layer = dm.DMoELayer(self.D, dev, fused_gather=self.fused)
+        self.fwd_kernels = [n for n in FWD_KERNELS if not (self.fused and n == "padded_gather")]
+        self.bwd_kernels = list(BWD_KERNELS)
+        if self.fused:   # the backward gathers x_perm right before the up dgrad
+            self.bwd_kernels.insert(self.bwd_kernels.index("gemm_up_dgrad"), "padded_gather")
+        self.y = torch.empty(cfg.T, cfg.H, dtype=dt, device=dev)
+        self.grads = dict(dx=torch.empty(cfg.T, cfg.H, dtype=dt, device=dev),
+                          dw1=torch.empty_like(self.w1), dw3=torch.empty_like(self.w3),
+                          dw2=torch.empty_like(self.w2),
+                          d_weights=torch.empty(cfg.T, cfg.k, dtype=torch.float32,
+                                                device=dev))
+        self.stream = torch.cuda.current_stream(dev)
+        self.phases = (META_KERNELS, self.fwd_kernels, self.bwd_kernels)
+        self.names = META_KERNELS + self.fwd_kernels + self.bwd_kernels
+
+    def step(self, ev=None, lean=False, stream="fixed"):
+        """Metadata + forward + backward.  stream=None: torch's current
+        stream at call time (for graph capture)."""
+        st = self.stream if stream == "fixed" else None
+        L = self.layer
+        L.metadata(self.ids, st, ev[0] if ev else None)
+        L.forward(self.x, self.ids, self.w, self.w1, self.w3, self.w2, y=self.y, stream=st,
+                  run_metadata=False, events=ev[1] if ev else None)
+        L.backward(self.dy, self.w, self.w1, self.w3, self.w2, grads=self.grads, stream=st,
+                   events=ev[2] if ev else None, lean=lean)
+
+    def padded_rows(self):
+        import torch
+        torch.cuda.synchronize()
+        assert int(self.layer.buf.meta.status.item()) == 0
+        return int(self.layer.buf.meta.num_padded_rows.item())
+
+    def per_kernel(self, n, ovh, flush=None):
+        """Mean ms of every kernel over n untimed steps with an event around
+        every kernel, less one record's cost; flush(): called before each
+        step, outside the events (cold-cache pass)."""
+        import torch
+        from dropless_mixture_experts_amd.hip_events import EventArray
+        raw = {k: 0.0 for k in self.names}
+        evs = [tuple(EventArray(len(ks) + 1) for ks in self.phases) for _ in range(n)]
+        torch.cuda.synchronize()
+        for ev in evs:            # back to back, as in the timed steps
+            if flush:
+                flush()
+            self.step(ev)
+        torch.cuda.synchronize()
+        for ev in evs:
+            for arr, ks in zip(ev, self.phases):
+                for j, k in enumerate(ks):
+                    raw[k] += arr.elapsed_ms(j, j + 1) / n
+                arr.close()
+        return raw, {k: max(raw[k] - ovh, 0.0) for k in self.names}
+
+    def timed(self, K, dom=None, lean=False):
+        """Wall time of K back-to-back steps between two synchronizations;
+        with dom, two event records around that kernel in every step.
+        Returns (ms per step, the mean raw event interval of dom)."""
+        import torch
+        from dropless_mixture_experts_amd.hip_events import EventArray
+        evs = []
+        if dom is not None:
+            dph = next(i for i, ks in enumerate(self.phases) if dom in ks)
+            dj = self.phases[dph].index(dom)
+            for _ in range(K):
+                ev = [None, None, None]
+                ev[dph] = EventArray(len(self.phases[dph]) + 1, only=(dj, dj + 1))
+                evs.append(tuple(ev))
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            self.step(evs[i] if evs else None, lean=lean)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / K
+        dom_raw = None
+        if evs:
+            dom_raw = sum(ev[dph].elapsed_ms(dj, dj + 1) for ev in evs) / K
+            for ev in evs:
+                ev[dph].close()
+        return ms, dom_raw
+
+    def graph_ms(self, K, replays=3):
+        """ms per step when one whole step (metadata, forward, backward) is
+        captured as a HIP graph and replayed K times back to back."""
+        import torch
+        side = torch.cuda.Stream(self.dev)
+        side.wait_stream(torch.cuda.current_stream(self.dev))
+        with torch.cuda.stream(side):
+            for _ in range(2):
+                self.step(stream=None)
+        torch.cuda.current_stream(self.dev).wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step(stream=None)
+        torch.cuda.synchronize()
+        best = None
+        for _ in range(replays):
+            t0 = time.perf_counter()
+            for _ in range(K):
+                g.replay()
+            torch.cuda.synchronize()
+            ms = (time.perf_counter() - t0) * 1e3 / K
+            best = ms if best is None else min(best, ms)
+        del g
+        return best
+
+    def close(self):
+        import torch
+        for n in ("x", "dy", "ids", "w", "w1", "w3", "w2", "y", "grads", "layer", "inp"):
+            setattr(self, n, None)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def summarise(cfg, P, per, fused):
+    """The per-kernel table and the step's fractions from per-kernel ms."""
+    peak = PEAK_F32_TFLOPS if cfg.dtype == "f32" else PEAK_BF16_TFLOPS
+    work = kernel_work(cfg, P, fused)
+    names = list(per)
+    table = {}
+    for n in names:
+        fl, by = work[n]
+        t = per[n] * 1e-3
+        table[n] = {"ms": round(per[n], 4),
+                    "tflops": round(fl / t / 1e12, 1) if fl and t > 0 else None,
+                    "gbs": round(by / t / 1e9, 1) if t > 0 else None,
+                    "roofline_frac": (round(roof_time(fl, by, peak) / t, 4)
+                                      if t > 0 else None)}
+    gemms = [n for n in names if n.startswith("gemm")]
+    gemm_ms = sum(per[n] for n in gemms)
+    gemm_roof_s = sum(roof_time(*work[n], peak) for n in gemms)
+    gs = [n for n in ("padded_gather", "padded_scatter", "scatter_backward",
+                      "gather_backward") if n in names]
+    gs_ms = sum(per[n] for n in gs)
+    gs_bytes = sum(work[n][1] for n in gs)
+    executed_flop = 18.0 * P * cfg.H * cfg.F
+    return table, {
+        "gemm_executed_frac_peak": round(executed_flop / (gemm_ms * 1e-3) / 1e12 / peak, 4),
+        # the GEMMs' time at their per-kernel roofline, max(FLOP / peak,
+        # bytes / HBM peak), over their measured time
+        "gemm_roofline_frac": round(gemm_roof_s / (gemm_ms * 1e-3), 4),
+        "gather_scatter_frac_hbm": round(gs_bytes / (gs_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "metadata_us": round(1e3 * sum(per[n] for n in META_KERNELS), 1),
+        # latency-bound: a few MB in three small launches
+        "metadata_frac_hbm": round(sum(work[n][1] for n in META_KERNELS)
+                                   / (sum(per[n] for n in META_KERNELS) * 1e-3) / 1e9
+                                   / PEAK_HBM_GBS, 5),
+    }
+
+
+def roofline(cfg, P, fused, dom, dom_ms):
+    """The roofline object of kernel dom, run in dom_ms per launch."""
+    peak = PEAK_F32_TFLOPS if cfg.dtype == "f32" else PEAK_BF16_TFLOPS
+    fl, by = kernel_work(cfg, P, fused)[dom]
+    # the binding roof at the kernel's arithmetic intensity (algorithmic FLOP
+    # per unique byte): the matrix cores above the ridge, HBM below it
+    ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    intensity = fl / by if fl else 0.0
+    t = dom_ms * 1e-3
+    if fl and intensity >= ridge:
+        achieved = fl / t / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": None}
+    else:
+        achieved = by / t / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
+    roof["intensity_flop_per_byte"] = round(intensity, 1)
+    roof["ridge_flop_per_byte"] = round(ridge, 1)
+    if fl:
+        roof["tflops"] = round(fl / t / 1e12, 1)
+        roof["tflops_frac_of_mfma_peak"] = round(fl / t / 1e12 / peak, 4)
+        # the kernel against its own roofline time, max(FLOP / peak, bytes / HBM)
+        roof["frac_of_roofline_time"] = round(roof_time(fl, by, peak) / t, 4)
+    roof["launch_ms"] = round(dom_ms, 4)
+    roof["algorithmic_bytes_per_launch"] = by
+    roof["algorithmic_flop_per_launch"] = fl
+    roof["traffic"] = committed_traffic(dom, cfg.name)
+    return roof
+
+
+def other_workload(dm, name, dev, args, ovh):
+    """Compact record of one more workload: its step, GEMM fractions and
+    the roofline of its dominant kernel."""
+    from workloads import CONFIGS
+    cfg = CONFIGS[name]
+    t0 = time.perf_counter()
+    L = Layer(dm, cfg, dev, gather=args.gather)
+    t_in = time.perf_counter() - t0
+    print(f"bench: workload {name} (inputs {t_in:.1f} s)", file=sys.stderr, flush=True)
+    K, W = 10, 3
+    for _ in range(W):
+        L.step()
+    P = L.padded_rows()
+    _, per = L.per_kernel(3, ovh)
+    dom = max(L.names, key=lambda n: per[n])
+    ms, dom_raw = L.timed(K, dom)
+    table, fr = summarise(cfg, P, per, L.fused)
+    peak = PEAK_F32_TFLOPS if cfg.dtype == "f32" else PEAK_BF16_TFLOPS
+    useful = 18.0 * cfg.T * cfg.k * cfg.H * cfg.F / (ms * 1e-3) / 1e12
+    rec = {"config": {"T": cfg.T, "H": cfg.H, "F": cfg.F, "E": cfg.E, "k": cfg.k,
+                      "dtype": cfg.dtype, "routing": cfg.routing, "P": P,
+                      "gather": "fused" if L.fused else "plain"},
+           "steps": K, "warmup": W, "ms_per_step": round(ms, 4),
+           "tokens_s": round(cfg.T / (ms * 1e-3), 1),
+           "useful_tflops": round(useful, 1), "useful_frac_peak": round(useful / peak, 4),
+           **fr,
+           "roofline": roofline(cfg, P, L.fused, dom, dom_raw - ovh),
+           "kernels": {n: table[n]["ms"] for n in L.names}}
+    if cfg.dtype == "f32" or cfg.T * cfg.k <= 4096:
+        # small layers are bound by the host's launches: the same step
+        # captured once as a HIP graph and replayed
+        g = L.graph_ms(K)
+        rec["graph_replay"] = {"ms_per_step": round(g, 4),
+                               "tokens_s": round(cfg.T / (g * 1e-3), 1)}
+    L.close()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="fine_e64")
+    ap.add_argument("--workloads", default="zipf_e64,coarse_e8,sparse_e256,tiny_f32",
+                    help="comma-separated other workloads reported under 'workloads' "
+                         "(10 steps each), or 'none'")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-lean", action="store_true",
+                    help="skip the step with the activation-lean backward")
     ap.add_argument("--kernels", action="store_true",
                     help="also print the per-kernel table on stderr")
     ap.add_argument("--gather", choices=("auto", "plain", "fused"), default="auto",
@@ -248,8 +495,7 @@ def main():
                          "fused where the padded copy of x exceeds the last-level "
                          "cache")
     ap.add_argument("--fused-gather", action="store_true",
-                    help="same as --gather fused: time the path with the gather fused into the up "
-                         "projection's operand loads (the backward gathers x_perm)")
+                    help="same as --gather fused")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="after timing, run a plain device copy of this many MiB "
                          "three times (reference for hardware byte counters)")
@@ -262,13 +508,13 @@ def main():
     if world != 1:
         print("bench.py is single-process: WORLD_SIZE must be 1", file=sys.stderr)
         sys.exit(2)
+    if args.fused_gather:
+        args.gather = "fused"
 
-    import numpy as np
     import torch
 
     import dropless_mixture_experts_amd as dm
-    from dropless_mixture_experts_amd.hip_events import EventArray
-    from workloads import CONFIGS, make_inputs
+    from workloads import CONFIGS
 
     if not torch.cuda.is_available():
         print("bench.py needs an MI355X GPU", file=sys.stderr)
@@ -276,163 +522,32 @@ def main():
     dm.load_library()   # fail loudly if the HIP library is not built
     dev = torch.device("cuda:0")
     cfg = CONFIGS[args.workload]
-    t_gen = time.perf_counter()
-    inp = make_inputs(cfg)
-    t_gen = time.perf_counter() - t_gen
-    dt = torch.float32 if cfg.dtype == "f32" else torch.bfloat16
-    up = lambda a, d=dt: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(d)
-    x, dy = up(inp.x), up(inp.dy)
-    ids = up(inp.top_experts, torch.int32)
-    w = up(inp.weights, torch.float32)
-    w1, w3, w2 = up(inp.w1), up(inp.w3), up(inp.w2)
-    D = dm.Dims(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k,
-                dm.DMOE_F32 if cfg.dtype == "f32" else dm.DMOE_BF16)
-    mode = "fused" if args.fused_gather else args.gather
-    fused = cfg.dtype == "bf16" and (
-        mode == "fused" or (mode == "auto" and dm.fused_gather_pays(D)))
-    layer = dm.DMoELayer(D, dev, fused_gather=fused)
-    fwd_kernels = [n for n in FWD_KERNELS if not (fused and n == "padded_gather")]
-    bwd_kernels = list(BWD_KERNELS)
-    if fused:   # the backward gathers x_perm right before the up dgrad
-        bwd_kernels.insert(bwd_kernels.index("gemm_up_dgrad"), "padded_gather")
-    y = torch.empty(cfg.T, cfg.H, dtype=dt, device=dev)
-    grads = dict(dx=torch.empty(cfg.T, cfg.H, dtype=dt, device=dev),
-                 dw1=torch.empty_like(w1), dw3=torch.empty_like(w3),
-                 dw2=torch.empty_like(w2),
-                 d_weights=torch.empty(cfg.T, cfg.k, dtype=torch.float32, device=dev))
-    stream = torch.cuda.current_stream(dev)
-
-    def step(ev=None):
-        layer.metadata(ids, stream, ev[0] if ev else None)
-        layer.forward(x, ids, w, w1, w3, w2, y=y, stream=stream, run_metadata=False,
-                      events=ev[1] if ev else None)
-        layer.backward(dy, w, w1, w3, w2, grads=grads, stream=stream,
-                       events=ev[2] if ev else None)
-
+    L = Layer(dm, cfg, dev, gather=args.gather)
+    stream = L.stream
+    print(f"bench: workload {cfg.name}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    P = int(layer.buf.meta.num_padded_rows.item())
-    assert int(layer.buf.meta.status.item()) == 0
-
+        L.step()
+    P = L.padded_rows()
     K = args.steps
-    phases = (META_KERNELS, fwd_kernels, bwd_kernels)
-    names = META_KERNELS + fwd_kernels + bwd_kernels
 
     # Per-kernel table: a pass of its own, outside the timed region, with an
     # event around every kernel (each record puts a timestamp between two
     # kernels, ~5 us each at 15 per step).
-    KP = max(3, min(K, 10))
-    evs = [tuple(EventArray(len(ks) + 1) for ks in phases) for _ in range(KP)]
-    for i in range(KP):
-        step(evs[i])
-    torch.cuda.synchronize()
-    raw = {n: 0.0 for n in names}
-    for ev in evs:
-        for arr, ks in zip(ev, phases):
-            for j, n in enumerate(ks):
-                raw[n] += arr.elapsed_ms(j, j + 1) / KP
-            arr.close()
-    # every interval carries one record's cost; kernel durations are the
-    # intervals less the interval between two records with nothing between
     ovh = event_overhead_ms(stream)
-    per = {n: max(raw[n] - ovh, 0.0) for n in names}
-    dom = max(names, key=lambda n: per[n])
-    dph = next(i for i, ks in enumerate(phases) if dom in ks)
-    dj = phases[dph].index(dom)
-
+    KP = max(3, min(K, 10))
+    raw, per = L.per_kernel(KP, ovh)
+    dom = max(L.names, key=lambda n: per[n])
     # The timed region: K steps with two event records, around the dominant
     # kernel, whose duration the roofline takes from here.
-    evs = []
-    for _ in range(K):
-        ev = [None, None, None]
-        ev[dph] = EventArray(len(phases[dph]) + 1, only=(dj, dj + 1))
-        evs.append(tuple(ev))
-    # The shader clock is sampled every ~1 ms by a thread of its own while the
-    # steps run: a sysfs read of it takes about a millisecond, so polling it
-    # in the wait for the last step would notice the end late.
-    sclk = []
-    stop = threading.Event()
-
-    def sample():
-        while not stop.is_set() and len(sclk) < 1000:
-            c = gpu_sclk_mhz()
-            if c is None:
-                break
-            sclk.append(c)
-            stop.wait(0.001)
-
-    sampler = threading.Thread(target=sample, daemon=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(evs[i])
-        if i == 0:
-            sampler.start()        # while the first step runs
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    stop.set()
-    sampler.join()
-    dom_raw_ms = sum(ev[dph].elapsed_ms(dj, dj + 1) for ev in evs) / K
-    dom_ms = dom_raw_ms - ovh
-    for ev in evs:
-        ev[dph].close()
-
-    ms = elapsed * 1e3 / K
+    ms, dom_raw = L.timed(K, dom)
     tokens_s = cfg.T / (ms * 1e-3)
-    useful_flop = 18.0 * cfg.T * cfg.k * cfg.H * cfg.F
-    executed_flop = 18.0 * P * cfg.H * cfg.F
     peak = PEAK_F32_TFLOPS if cfg.dtype == "f32" else PEAK_BF16_TFLOPS
-    useful_tf = useful_flop / (ms * 1e-3) / 1e12
-    work = kernel_work(cfg, P, fused)
-    table = {}
-    for n in names:
-        fl, by = work[n]
-        t = per[n] * 1e-3
-        table[n] = {"ms": round(per[n], 4), "interval_ms": round(raw[n], 4),
-                    "tflops": round(fl / t / 1e12, 1) if fl and t > 0 else None,
-                    "gbs": round(by / t / 1e9, 1) if t > 0 else None,
-                    "roofline_frac": (round(roof_time(fl, by, peak) / t, 4)
-                                      if t > 0 else None)}
-    gemms = [n for n in names if n.startswith("gemm")]
-    gemm_ms = sum(per[n] for n in gemms)
-    gemm_roof_s = sum(roof_time(*work[n], peak) for n in gemms)
-    gs = [n for n in ("padded_gather", "padded_scatter", "scatter_backward",
-                      "gather_backward") if n in names]
-    gs_ms = sum(per[n] for n in gs)
-    gs_bytes = sum(work[n][1] for n in gs)
-    fl, by = work[dom]
-    # the binding roof at the kernel's arithmetic intensity (algorithmic FLOP
-    # per unique byte): the matrix cores above the ridge, HBM below it
-    ridge = peak * 1e12 / (PEAK_HBM_GBS * 1e9)
-    intensity = fl / by if fl else 0.0
-    t_dom = dom_ms * 1e-3
-    if fl and intensity >= ridge:
-        achieved = fl / t_dom / 1e12
-        roof = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 1),
-                "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": None}
-    else:
-        achieved = by / t_dom / 1e9
-        roof = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None}
-    roof["intensity_flop_per_byte"] = round(intensity, 1)
-    roof["ridge_flop_per_byte"] = round(ridge, 1)
-    if fl:
-        roof["tflops"] = round(fl / t_dom / 1e12, 1)
-        roof["tflops_frac_of_mfma_peak"] = round(fl / t_dom / 1e12 / peak, 4)
-    if fl and sclk:
-        # the published peak assumes the 2.4 GHz top clock; the matrix cores
-        # scale with the clock the chip holds under this load
-        at_clk = peak * (sorted(sclk)[len(sclk) // 2] / 2400.0)
-        roof["mfma_peak_at_median_sclk"] = round(at_clk, 1)
-        roof["tflops_frac_at_median_sclk"] = round(fl / t_dom / 1e12 / at_clk, 4)
-    roof["launch_ms"] = round(dom_ms, 4)
-    roof["event_interval_ms"] = round(dom_raw_ms, 4)
-    roof["algorithmic_bytes_per_launch"] = by
-    roof["algorithmic_flop_per_launch"] = fl
-    roof["traffic"] = committed_traffic(dom, cfg.name)
+    useful_tf = 18.0 * cfg.T * cfg.k * cfg.H * cfg.F / (ms * 1e-3) / 1e12
+    table, fr = summarise(cfg, P, per, L.fused)
+    for n in L.names:
+        table[n]["interval_ms"] = round(raw[n], 4)
+    roof = roofline(cfg, P, L.fused, dom, dom_raw - ovh)
+    roof["event_interval_ms"] = round(dom_raw, 4)
 
     out = {
         "metric": METRIC,
@@ -450,22 +565,10 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "F": cfg.F,
                    "E": cfg.E, "k": cfg.k, "routing": cfg.routing, "P": P,
                    "gather": ("fused into the up projection's loads; gathered in the "
-                              "backward" if fused else "padded copy in the forward")},
+                              "backward" if L.fused else "padded copy in the forward")},
         "useful_tflops": round(useful_tf, 1),
         "useful_frac_peak": round(useful_tf / peak, 4),
-        "gemm_executed_frac_peak": round(executed_flop / (gemm_ms * 1e-3) / 1e12 / peak, 4),
-        # the GEMMs' time at their per-kernel roofline, max(FLOP / peak,
-        # bytes / HBM peak), over their measured time
-        "gemm_roofline_frac": round(gemm_roof_s / (gemm_ms * 1e-3), 4),
-        "gather_scatter_frac_hbm": round(gs_bytes / (gs_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "metadata_us": round(1e3 * sum(per[n] for n in META_KERNELS), 1),
-        # latency-bound: a few MB in three small launches
-        "metadata_frac_hbm": round(sum(work[n][1] for n in META_KERNELS)
-                                   / (sum(per[n] for n in META_KERNELS) * 1e-3) / 1e9
-                                   / PEAK_HBM_GBS, 5),
-        "sclk_mhz_during_timing": ({"samples": len(sclk), "min": min(sclk),
-                                    "median": sorted(sclk)[len(sclk) // 2],
-                                    "max": max(sclk)} if sclk else None),
+        **fr,
         "roofline": roof,
         "kernels": table,
         "event_overhead_us": round(ovh * 1e3, 2),
@@ -475,13 +578,36 @@ def main():
                          f"records with nothing between them"),
     }
     out["router_us"] = router_time(dm, cfg, dev, stream, K)
-    cold = cold_steps(step, stream, min(K, 10))
+    if not args.no_lean:
+        lean_ms, _ = L.timed(K, lean=True)
+        out["lean_backward"] = {
+            "ms_per_step": round(lean_ms, 4),
+            "tokens_s": round(cfg.T / (lean_ms * 1e-3), 1),
+            "saved_activation_bytes_per_token": saved_bytes_per_token(cfg, P),
+            "note": ("metadata + forward + dmoe_backward_lean, which rebuilds x_perm, h1, h3 "
+                     "and act from x: only y_perm is kept from forward to backward"),
+        }
+    # Cold cache: each step after a 512 MB write that evicts the 256 MB
+    # last-level cache, timed as a whole and, in a pass of its own, per kernel.
+    flush_buf = torch.empty(512 << 18, dtype=torch.float32, device=dev)
+    flush = lambda: flush_buf.fill_(1.0)
+    cold = cold_steps(L.step, stream, min(K, 10))
+    _, cper = L.per_kernel(5, ovh, flush=flush)
+    _, cfr = summarise(cfg, P, cper, L.fused)
+    del flush_buf
+    gs = [n for n in ("padded_gather", "padded_scatter", "scatter_backward",
+                      "gather_backward") if n in L.names]
     out["cold_cache"] = {"ms_per_step_median": round(cold, 4),
                          "tokens_s": round(cfg.T / (cold * 1e-3), 1),
-                         "note": "last-level cache flushed by a 512 MB write before each step"}
+                         "gather_scatter_frac_hbm": cfr["gather_scatter_frac_hbm"],
+                         "kernels_ms": {n: round(cper[n], 4) for n in L.names},
+                         "gather_scatter_ms": {n: round(cper[n], 4) for n in gs},
+                         "note": ("last-level cache flushed by a 512 MB write before each "
+                                  "step; per-kernel figures from 5 such steps with an event "
+                                  "around every kernel")}
     if args.kernels:
-        for n in names:
-            print(f"{n:22s} {table[n]}", file=sys.stderr)
+        for n in L.names:
+            print(f"{n:28s} {table[n]}", file=sys.stderr)
     if args.calibrate_copy_mb:
         nbytes = args.calibrate_copy_mb << 20
         src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
@@ -490,7 +616,14 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         out["calibration_copy_bytes"] = nbytes
+        del src, dst
+    inp = L.inp
+    L.close()
+    others = [n for n in args.workloads.split(",") if n and n != "none" and n != cfg.name]
+    if others:
+        out["workloads"] = {n: other_workload(dm, n, dev, args, ovh) for n in others}
     if not args.no_cpu:
+        print("bench: CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp)
     else:
         out["cpu_baseline"] = None

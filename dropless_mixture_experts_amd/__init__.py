@@ -139,6 +139,10 @@ def load_library() -> ctypes.CDLL:
     lib.dmoe_forward_fused_gather.restype = ctypes.c_int
     lib.dmoe_forward_fused_gather_timed.argtypes = lib.dmoe_forward_timed.argtypes
     lib.dmoe_forward_fused_gather_timed.restype = ctypes.c_int
+    lib.dmoe_backward_lean.argtypes = [P(_Dims), vp] + lib.dmoe_backward.argtypes[1:]
+    lib.dmoe_backward_lean.restype = ctypes.c_int
+    lib.dmoe_backward_lean_timed.argtypes = [P(_Dims), vp] + lib.dmoe_backward_timed.argtypes[1:]
+    lib.dmoe_backward_lean_timed.restype = ctypes.c_int
     lib.dmoe_backward_fused_gather.argtypes = [P(_Dims), vp] + lib.dmoe_backward.argtypes[1:]
     lib.dmoe_backward_fused_gather.restype = ctypes.c_int
     lib.dmoe_backward_fused_gather_timed.argtypes = ([P(_Dims), vp]
@@ -375,15 +379,19 @@ def dmoe_forward(dims: Dims, x, weights, w1, w3, w2, meta: Meta, saved: Saved,
 def dmoe_backward(dims: Dims, dy, weights, w1, w3, w2, meta: Meta, saved: Saved,
                   scratch: GradScratch, dx, dw1, dw3, dw2, d_weights,
                   stream=None, events=None, recompute: bool = False,
-                  x=None) -> None:
+                  x=None, lean: bool = False) -> None:
     """Backward of the layer; see include/dmoe.h.  `events`: optional
-    EventArray of 6 events (7 with recompute or x) for per-kernel timing.
-    recompute: saved.act is scratch on entry and is rebuilt from h1 and h3
-    (dmoe_backward_recompute).  x: the forward's input, after the
-    fused-gather forward (dmoe_backward_fused_gather): saved.x_perm is then
-    scratch on entry and is gathered from x first."""
+    EventArray of 6 events (7 with recompute or x, 8 with lean) for
+    per-kernel timing.  recompute: saved.act is scratch on entry and is
+    rebuilt from h1 and h3 (dmoe_backward_recompute).  x: the forward's
+    input; alone, after the fused-gather forward (dmoe_backward_fused_gather):
+    saved.x_perm is then scratch on entry and is gathered from x first.
+    lean (needs x): saved.x_perm, h1, h3 and act are all scratch on entry and
+    are rebuilt from x (dmoe_backward_lean); only saved.y_perm is kept."""
     if x is not None and recompute:
         raise ValueError("the fused gather has no recompute variant")
+    if lean and (x is None or recompute):
+        raise ValueError("lean needs the forward's x and excludes recompute")
     lib = load_library()
     dt = dims.torch_dtype
     T, H, F, E, k = dims.T, dims.H, dims.F, dims.E, dims.k
@@ -408,7 +416,7 @@ def dmoe_backward(dims: Dims, dy, weights, w1, w3, w2, meta: Meta, saved: Saved,
             _stream(dy, stream)]
     if x is not None:
         _need(x, "x", T * H)
-        name = "dmoe_backward_fused_gather"
+        name = "dmoe_backward_lean" if lean else "dmoe_backward_fused_gather"
         args.insert(1, _ptr(x, dt, "x"))
     elif recompute:
         name = "dmoe_backward_recompute"
@@ -418,7 +426,8 @@ def dmoe_backward(dims: Dims, dy, weights, w1, w3, w2, meta: Meta, saved: Saved,
         _check(getattr(lib, name)(*args), name)
     else:
         _check(getattr(lib, name + "_timed")(
-            *args, _ev(events, 6 if recompute or x is not None else 5)), name + "_timed")
+            *args, _ev(events, 7 if lean else 6 if recompute or x is not None else 5)),
+            name + "_timed")
 
 
 def dmoe_padded_gather(dims: Dims, x, meta: Meta, x_perm, stream=None) -> None:
@@ -587,11 +596,13 @@ class DMoELayer:
                             device=self.device)
         dmoe_forward(self.dims, x, weights, w1, w3, w2, self.buf.meta,
                      self.buf.saved, y, stream, events, self.fused_gather)
-        self._x = x if self.fused_gather else None
+        self._x = x
         return y
 
     def backward(self, dy, weights, w1, w3, w2, grads=None, stream=None,
-                 events=None, recompute=False):
+                 events=None, recompute=False, lean=False):
+        """lean: rebuild x_perm, h1, h3 and act from the forward's x
+        (dmoe_backward_lean) instead of reading them."""
         d = self.dims
         if grads is None:
             fl = dict(dtype=d.torch_dtype, device=self.device)
@@ -601,12 +612,12 @@ class DMoELayer:
                          dw2=torch.empty(d.E, d.F, d.H, **fl),
                          d_weights=torch.empty(d.T, d.k, dtype=torch.float32,
                                                device=self.device))
-        if self.fused_gather and self._x is None:
-            raise RuntimeError("fused_gather: backward needs a forward first")
+        if (self.fused_gather or lean) and self._x is None:
+            raise RuntimeError("backward needs the forward's x: run forward first")
         dmoe_backward(d, dy, weights, w1, w3, w2, self.buf.meta, self.buf.saved,
                       self.buf.scratch, grads["dx"], grads["dw1"], grads["dw3"],
                       grads["dw2"], grads["d_weights"], stream, events, recompute,
-                      self._x)
+                      self._x if (self.fused_gather or lean) else None, lean)
         return grads
 
 

@@ -261,18 +261,28 @@ int dmoe_forward(const dmoe_dims* dims, const void* x, const float* weights,
 
 namespace {
 
-// The backward of the layer; with `recompute`, act is rebuilt from h1 and h3
-// first, and with a non-null x (after the fused-gather forward) x_perm is
-// gathered from x before the up dgrad.  Each such kernel has an event of its
-// own in launch order.
+// What the backward rebuilds before its own kernels.
+enum class Rebuild {
+  kNone,     // every saved activation is the forward's
+  kAct,      // act = silu(h1) * h3 from the saved h1, h3
+  kFromX,    // x_perm, h1, h3 and act from the forward's input x
+};
+
+// The backward of the layer.  kAct rebuilds act from h1 and h3 first;
+// kFromX gathers x_perm from x and reruns the up projection (the forward's
+// kernels on the forward's input, so the same bits) first.  Otherwise a
+// non-null x (after the fused-gather forward) has x_perm gathered from x
+// before the up dgrad.  Each such kernel has an event of its own in launch
+// order.
 int backward_impl(const dmoe_dims* dims, const void* x, const void* dy, const float* weights,
                   const void* w1, const void* w3, const void* w2, const dmoe_meta* meta,
                   const dmoe_saved* saved, const dmoe_grad_scratch* scratch, void* dx,
                   void* dw1, void* dw3, void* dw2, float* d_weights, hipStream_t stream,
-                  hipEvent_t* ev, bool recompute) {
+                  hipEvent_t* ev, Rebuild rebuild) {
   int rc = check_gemm_dims(dims);
   if (rc != DMOE_OK) return rc;
-  if (x && (rc = check_fused(dims)) != DMOE_OK) return rc;
+  if (x && rebuild != Rebuild::kFromX && (rc = check_fused(dims)) != DMOE_OK) return rc;
+  if (rebuild == Rebuild::kFromX && !x) return DMOE_ERR_ARG;
   if ((rc = check_meta(meta)) != DMOE_OK) return rc;
   if (!dy || !weights || !w1 || !w3 || !w2 || !saved || !scratch || !dx || !dw1 ||
       !dw3 || !dw2 || !d_weights || !saved->x_perm || !saved->h1 || !saved->h3 ||
@@ -283,10 +293,16 @@ int backward_impl(const dmoe_dims* dims, const void* x, const void* dy, const fl
   const MetaPtrs m = meta_ptrs(meta, dims);
   Recorder rec{ev, stream};
   int i = 0;
-  if (recompute) {
+  if (rebuild == Rebuild::kAct) {
     // before the down dgrad, which may overwrite h1 and h3 (dh1, dh3 alias)
     DMOE_TRY(rec(i++));
     DMOE_TRY(dmoe::launch_recompute_act(s, saved->h1, saved->h3, m, saved->act, stream));
+  } else if (rebuild == Rebuild::kFromX) {
+    DMOE_TRY(rec(i++));
+    DMOE_TRY(dmoe::launch_padded_gather(s, x, m, saved->x_perm, stream));
+    DMOE_TRY(rec(i++));
+    DMOE_TRY(dmoe::launch_gemm_up(s, saved->x_perm, nullptr, w1, w3, m, saved->h1, saved->h3,
+                                  saved->act, stream));
   }
   // Order matters for the permitted aliases: dy_perm is last read by the
   // down-projection weight gradient, before dx_perm is written.
@@ -298,7 +314,7 @@ int backward_impl(const dmoe_dims* dims, const void* x, const void* dy, const fl
                                                    saved->h3, saved->act, m, scratch->dh1,
                                                    scratch->dh3, dw2, stream));
   DMOE_TRY(rec(i++));
-  if (x) {
+  if (x && rebuild != Rebuild::kFromX) {
     // the forward did not keep x_perm: gather it for the products that read
     // it (dw1/dw3, some of them in the up dgrad's launch)
     DMOE_TRY(dmoe::launch_padded_gather(s, x, m, saved->x_perm, stream));
@@ -328,7 +344,7 @@ int dmoe_backward_timed(const dmoe_dims* dims, const void* dy, const float* weig
                         void* dw3, void* dw2, float* d_weights, hipStream_t stream,
                         hipEvent_t* ev) {
   return backward_impl(dims, nullptr, dy, weights, w1, w3, w2, meta, saved, scratch, dx, dw1,
-                       dw3, dw2, d_weights, stream, ev, false);
+                       dw3, dw2, d_weights, stream, ev, Rebuild::kNone);
 }
 
 int dmoe_backward(const dmoe_dims* dims, const void* dy, const float* weights,
@@ -337,7 +353,7 @@ int dmoe_backward(const dmoe_dims* dims, const void* dy, const float* weights,
                   const dmoe_grad_scratch* scratch, void* dx, void* dw1,
                   void* dw3, void* dw2, float* d_weights, hipStream_t stream) {
   return backward_impl(dims, nullptr, dy, weights, w1, w3, w2, meta, saved, scratch, dx, dw1,
-                       dw3, dw2, d_weights, stream, nullptr, false);
+                       dw3, dw2, d_weights, stream, nullptr, Rebuild::kNone);
 }
 
 int dmoe_backward_recompute_timed(const dmoe_dims* dims, const void* dy, const float* weights,
@@ -347,7 +363,7 @@ int dmoe_backward_recompute_timed(const dmoe_dims* dims, const void* dy, const f
                                   void* dw3, void* dw2, float* d_weights, hipStream_t stream,
                                   hipEvent_t* ev) {
   return backward_impl(dims, nullptr, dy, weights, w1, w3, w2, meta, saved, scratch, dx, dw1,
-                       dw3, dw2, d_weights, stream, ev, true);
+                       dw3, dw2, d_weights, stream, ev, Rebuild::kAct);
 }
 
 int dmoe_backward_recompute(const dmoe_dims* dims, const void* dy, const float* weights,
@@ -356,7 +372,25 @@ int dmoe_backward_recompute(const dmoe_dims* dims, const void* dy, const float* 
                             const dmoe_grad_scratch* scratch, void* dx, void* dw1,
                             void* dw3, void* dw2, float* d_weights, hipStream_t stream) {
   return backward_impl(dims, nullptr, dy, weights, w1, w3, w2, meta, saved, scratch, dx, dw1,
-                       dw3, dw2, d_weights, stream, nullptr, true);
+                       dw3, dw2, d_weights, stream, nullptr, Rebuild::kAct);
+}
+
+int dmoe_backward_lean_timed(const dmoe_dims* dims, const void* x, const void* dy,
+                             const float* weights, const void* w1, const void* w3,
+                             const void* w2, const dmoe_meta* meta, const dmoe_saved* saved,
+                             const dmoe_grad_scratch* scratch, void* dx, void* dw1, void* dw3,
+                             void* dw2, float* d_weights, hipStream_t stream, hipEvent_t* ev) {
+  return backward_impl(dims, x, dy, weights, w1, w3, w2, meta, saved, scratch, dx, dw1, dw3, dw2,
+                       d_weights, stream, ev, Rebuild::kFromX);
+}
+
+int dmoe_backward_lean(const dmoe_dims* dims, const void* x, const void* dy,
+                       const float* weights, const void* w1, const void* w3, const void* w2,
+                       const dmoe_meta* meta, const dmoe_saved* saved,
+                       const dmoe_grad_scratch* scratch, void* dx, void* dw1, void* dw3,
+                       void* dw2, float* d_weights, hipStream_t stream) {
+  return backward_impl(dims, x, dy, weights, w1, w3, w2, meta, saved, scratch, dx, dw1, dw3, dw2,
+                       d_weights, stream, nullptr, Rebuild::kFromX);
 }
 
 int dmoe_backward_fused_gather_timed(const dmoe_dims* dims, const void* x, const void* dy,
@@ -367,7 +401,7 @@ int dmoe_backward_fused_gather_timed(const dmoe_dims* dims, const void* x, const
                                      hipStream_t stream, hipEvent_t* ev) {
   if (!x) return DMOE_ERR_ARG;
   return backward_impl(dims, x, dy, weights, w1, w3, w2, meta, saved, scratch, dx, dw1, dw3, dw2,
-                       d_weights, stream, ev, false);
+                       d_weights, stream, ev, Rebuild::kNone);
 }
 
 int dmoe_backward_fused_gather(const dmoe_dims* dims, const void* x, const void* dy,

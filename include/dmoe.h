@@ -211,6 +211,26 @@ int dmoe_backward_recompute(const dmoe_dims* dims, const void* dy, const float* 
                             const dmoe_grad_scratch* scratch, void* dx, void* dw1,
                             void* dw3, void* dw2, float* d_weights, hipStream_t stream);
 
+/* The backward for callers that keep only y_perm of the forward's saved
+ * activations: the memory-optimized MLP of the MegaBlocks chapter (§4.4)
+ * taken to the whole up projection.  x is the forward's input [T,H], which
+ * the caller holds anyway.  saved->x_perm, h1, h3 and act are scratch on
+ * entry (their memory may serve other work between forward and backward);
+ * the call first gathers x_perm from x and reruns the up projection into
+ * h1, h3 and act -- the forward's kernels on the forward's input, so the
+ * same bits -- then runs the backward of dmoe_backward.  saved->y_perm must
+ * hold the forward's y_perm (the routing-weight gradient reads it).  Every
+ * result and every buffer is then bit-identical to dmoe_forward +
+ * dmoe_backward on the same inputs.  Kept between forward and backward: H
+ * elements per padded row instead of 2H + 3F.  Costs one more up
+ * projection (4 P H F flops) and one more gather.  Either forward may
+ * precede it. */
+int dmoe_backward_lean(const dmoe_dims* dims, const void* x, const void* dy,
+                       const float* weights, const void* w1, const void* w3, const void* w2,
+                       const dmoe_meta* meta, const dmoe_saved* saved,
+                       const dmoe_grad_scratch* scratch, void* dx, void* dw1, void* dw3,
+                       void* dw2, float* d_weights, hipStream_t stream);
+
 /* The forward with the gather fused into the up projection's operand loads
  * (bf16 only), and its backward.  Fine-grained experts are bound by memory
  * IO, and overlapping that IO with the products is how the pages' own
@@ -300,6 +320,8 @@ int dmoe_router_backward(const dmoe_dims* dims, const float* logits,
  *                     first dw1/dw3 tiles), gather backward (dx), dw1 + dw3.
  *   backward_recompute (n = 6): the activation recompute, then the five
  *                     kernels of the backward.
+ *   backward_lean (n = 7): padded_gather (x_perm), up projection + SiLU
+ *                     gate, then the five kernels of the backward.
  *   forward_fused_gather (n = 3): the forward's kernels but padded_gather.
  *   backward_fused_gather (n = 6): scatter backward, down dgrad + dw2,
  *                     padded_gather (x_perm), up dgrad, gather backward,
@@ -324,6 +346,12 @@ int dmoe_backward_recompute_timed(const dmoe_dims* dims, const void* dy, const f
                                   const dmoe_grad_scratch* scratch, void* dx, void* dw1,
                                   void* dw3, void* dw2, float* d_weights, hipStream_t stream,
                                   hipEvent_t* events);
+
+int dmoe_backward_lean_timed(const dmoe_dims* dims, const void* x, const void* dy,
+                             const float* weights, const void* w1, const void* w3,
+                             const void* w2, const dmoe_meta* meta, const dmoe_saved* saved,
+                             const dmoe_grad_scratch* scratch, void* dx, void* dw1, void* dw3,
+                             void* dw2, float* d_weights, hipStream_t stream, hipEvent_t* events);
 
 int dmoe_forward_fused_gather_timed(const dmoe_dims* dims, const void* x, const float* weights,
                                     const void* w1, const void* w3, const void* w2,

@@ -123,6 +123,45 @@ def test_backward_recompute_is_bitwise_identical(name, dims, lean):
         assert torch.equal(g[key], a.g[key]), key
 
 
+@pytest.mark.parametrize("name,dims,aliased,fused", [
+    ("zipf_e64_empty", dict(T=600, H=256, F=256), False, False),
+    ("zipf_e64_empty", dict(T=600, H=256, F=256), True, False),
+    ("coarse_e8", dict(T=1024, H=512, F=1024), True, True),
+    ("tiny_f32", {}, False, False),
+    ("fine_e64", {}, False, False),
+    ("sparse_e256", {}, True, True),
+], ids=["zipf_empty", "zipf_empty_aliased", "coarse_aliased_fused", "tiny_f32",
+        "fine_e64_full", "sparse_e256_full_aliased_fused"])
+def test_backward_lean_is_bitwise_identical(name, dims, aliased, fused):
+    """dmoe_backward_lean with x_perm, h1, h3 and act overwritten by NaN
+    after the forward (only y_perm kept) gives the plain backward's results
+    bit for bit, and rebuilds the four buffers as the forward wrote them."""
+    cfg = shrink(CONFIGS[name], **dims) if dims else CONFIGS[name]
+    inp = make_inputs(cfg)
+    print(f"lean {cfg.name} aliased={aliased} fused={fused}", flush=True)
+    a = Run(inp, lean=aliased)
+    b = Run(inp, lean=aliased, backward=False, fused_gather=fused)
+    P = b.P
+    fwd = {n: getattr(b.saved, n)[:P].clone() for n in ("h1", "h3", "act")}
+    for n in ("x_perm", "h1", "h3", "act"):
+        getattr(b.saved, n).fill_(float("nan"))
+    dy = up(inp.dy, torch_dtype(cfg), b.dev)
+    g = b.layer.backward(dy, b.w, b.w1, b.w3, b.w2, lean=True)
+    torch.cuda.synchronize()
+    assert torch.equal(b.y, a.y)
+    for key in OUTS:
+        assert torch.equal(g[key], a.g[key]), key
+    # the rebuilt x_perm, and (where the backward does not overwrite them
+    # with dh1/dh3) h1 and h3; act is never overwritten
+    assert torch.equal(b.saved.x_perm[:P], a.saved.x_perm[:P])
+    assert torch.equal(b.saved.act[:P], fwd["act"])
+    if not aliased:
+        assert torch.equal(b.saved.h1[:P], fwd["h1"])
+        assert torch.equal(b.saved.h3[:P], fwd["h3"])
+    for n in ("dy_perm", "dh1", "dh3", "dx_perm"):
+        assert torch.equal(getattr(b.scratch, n)[:P], getattr(a.scratch, n)[:P]), n
+
+
 def _picks(inp, md, rng, n=24):
     cfg = inp.cfg
     counts = md["tokens_per_expert"]

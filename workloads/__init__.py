@@ -30,6 +30,7 @@ Recipe (one numpy stream per tensor, spawned from ``SeedSequence(1000+id)``):
 from __future__ import annotations
 
 import dataclasses
+from concurrent.futures import ThreadPoolExecutor
 from typing import Dict, Optional
 
 import numpy as np
@@ -168,15 +169,20 @@ def make_inputs(cfg: Config, seed: Optional[int] = None,
         ids, w = _route_zipf(rl, rz, T, E, k, cfg.zipf_s, cfg.zero_ranks)
     else:
         ids, w = _route_gauss(rl, T, E, k)
-    x = _normal(rx, (T, H), 1.0, cfg.dtype)
+    # one stream per tensor: the draws are independent, so they run side by
+    # side (numpy releases the GIL while it fills and rounds large arrays)
+    jobs = {"x": (rx, (T, H), 1.0)}
     if with_weights:
-        w1 = _normal(r1, (E, H, F), cfg.std1, cfg.dtype)
-        w3 = _normal(r3, (E, H, F), cfg.std1, cfg.dtype)
-        w2 = _normal(r2, (E, F, H), cfg.std2, cfg.dtype)
-    else:
-        w1 = w3 = w2 = None
-    dy = _normal(rdy, (T, H), 1.0, cfg.dtype) if with_dy else None
-    return Inputs(cfg, x, ids, w, w1, w3, w2, dy)
+        jobs.update(w1=(r1, (E, H, F), cfg.std1), w3=(r3, (E, H, F), cfg.std1),
+                    w2=(r2, (E, F, H), cfg.std2))
+    if with_dy:
+        jobs["dy"] = (rdy, (T, H), 1.0)
+    with ThreadPoolExecutor(len(jobs)) as ex:
+        futs = {n: ex.submit(_normal, r, shape, std, cfg.dtype)
+                for n, (r, shape, std) in jobs.items()}
+        out = {n: f.result() for n, f in futs.items()}
+    return Inputs(cfg, out["x"], ids, w, out.get("w1"), out.get("w3"), out.get("w2"),
+                  out.get("dy"))
 
 
 def make_logits(cfg: Config, seed: Optional[int] = None, ties: bool = False):
