@@ -34,12 +34,12 @@ int check_dims(const dmoe_dims* d) {
   return DMOE_OK;
 }
 
-// The fp32 products launch one block per tile on a 2-D or 3-D grid: the
-// row-block kernels put the 128-row block index on grid dimension y, and the
-// weight gradients put cdiv(H, 128) (dw1/dw3) or cdiv(F, 128) (dw2) there.
-// The bf16 engine launches a 1-D persistent grid and has no such limit; the
-// row-block bound is kept for both so that one shape is valid or not
-// whatever the dtype.
+// The fp32 products launch one block per 64 x 64 tile on a 2-D or 3-D
+// grid: the row-block kernels put two 64-row tiles per 128-row block on grid
+// dimension y, and the weight gradients put cdiv(H, 64) (dw1/dw3) or
+// cdiv(F, 64) (dw2) there, with cdiv(F, 32) on x for dw1/dw3.  The bf16
+// engine launches a 1-D persistent grid; its own bound is the 65535 row
+// blocks kept for both dtypes.
 constexpr int64_t kMaxGridY = 65535;
 
 int check_gemm_dims(const dmoe_dims* d) {
@@ -48,7 +48,8 @@ int check_gemm_dims(const dmoe_dims* d) {
   const int64_t n = d->T * (int64_t)d->k;
   const int64_t tiles = (n + 127 * (int64_t)(d->E < n ? d->E : n)) / DMOE_BLOCK;
   if (tiles > kMaxGridY) return DMOE_ERR_UNSUPPORTED;
-  if (d->dtype == DMOE_F32 && ((d->H + 127) / 128 > kMaxGridY || (d->F + 127) / 128 > kMaxGridY))
+  if (d->dtype == DMOE_F32 &&
+      (2 * tiles > kMaxGridY || (d->H + 63) / 64 > kMaxGridY || (d->F + 63) / 64 > kMaxGridY))
     return DMOE_ERR_UNSUPPORTED;
   return DMOE_OK;
 }
@@ -465,7 +466,7 @@ const char* dmoe_status_string(int status) {
     case DMOE_OK: return "ok";
     case DMOE_ERR_ARG: return "invalid argument (null pointer, non-positive size, k > E or too many entries)";
     case DMOE_ERR_SHAPE: return "H and F must be multiples of 128";
-    case DMOE_ERR_UNSUPPORTED: return "unsupported (E > 256, dtype, H/F too large, or more than 65535 row blocks or, for fp32, 128-column blocks)";
+    case DMOE_ERR_UNSUPPORTED: return "unsupported (E > 256, dtype, H/F too large, or too many row or column blocks for the launch grid)";
     case DMOE_ERR_HIP: return "HIP kernel launch failed";
     case DMOE_ERR_EXPERT_ID: return "an expert id is outside [0, E)";
     default: return "unknown dmoe status";

@@ -1,4 +1,4 @@
-// Grouped GEMM over expert-tagged 128-row tiles (gfx950 MFMA), fp32.  The
+// Grouped GEMM over expert-tagged 128-row blocks (gfx950 MFMA), fp32.  The
 // launch_gemm_* entry points below route bf16 to the engine of
 // gemm_bf16.hip; the kernels of this file run the fp32 layer.
 //
@@ -8,156 +8,173 @@
 // sparse product whose non-zero blocks are exactly (row block r, the columns
 // of expert tile_expert[r]).  The sdd product (x_perm w1, x_perm w3) and the
 // dsd product (act w2) are computed here as one launch each over all row
-// blocks, each block reading its own expert's weights; §5's GLU variant
+// blocks, each tile reading its own expert's weights; §5's GLU variant
 // shares the row-block -> expert map.  The backward products (dgrad of both
 // projections and the per-expert weight gradients, whose contraction runs
 // over the expert's padded row range) use the same tile engine.
 //
-// Tile engine
-//   * 256 threads = 4 waves (2 x 2).  A block computes a 256 x 128 output
-//     tile: 256 "A rows" along the output's contiguous dimension (weights
-//     side) x 128 "B rows" (token rows, or the m dimension of a weight
-//     gradient).  Each wave owns 128 x 64 = 8 x 4 MFMA 16x16 tiles.
-//   * LDS holds both operands K-contiguous, 64 bytes of K per row per stage
-//     (16 fp32) plus 16 bytes of padding, which spreads the eight
-//     rows read by consecutive lanes over distinct banks.  Two stages: the
-//     next K slice is fetched into registers while the MFMAs consume the
-//     current one, then stored into the other stage (one barrier per step).
+// Tile engine.  The fp32 layer is small (its products are a few hundred
+// MFLOP), so tiles are small too, to spread one product over many CUs:
+//   * 256 threads = 4 waves (2 x 2).  A block computes a 64 x 64 output
+//     tile: 64 "A rows" along the output's contiguous dimension (weights
+//     side) x 64 "B rows" (token rows, or the m dimension of a weight
+//     gradient).  The A rows are two halves of 32 from two sources (w1 and
+//     w3 columns in the up projection, so the SiLU gate pairs them in
+//     registers; consecutive columns elsewhere).  Each wave owns 16 rows of
+//     each A half x 32 B rows: 2 x 2 MFMA 16x16 tiles.
+//   * LDS holds both operands K-contiguous, 128 bytes of K per row per stage
+//     (32 fp32) plus 16 bytes of padding, which spreads the rows read by
+//     consecutive lanes over distinct banks.  32 K per stage halves the
+//     number of steps, each of which waits once for its global loads.  Two stages: the next K slice
+//     is fetched into registers while the MFMAs consume the current one,
+//     then stored into the other stage (one barrier per step).
 //   * An operand whose source has K contiguous is copied 16 bytes per lane.
 //     One whose source has the row dimension contiguous ([K][N] weights,
 //     and both operands of the weight gradients) is read in 4x4 micro-blocks
 //     and transposed in registers before the LDS store, so every MFMA
 //     operand is one 16-byte LDS read per lane.
 //   * Four v_mfma_f32_16x16x4_f32 per 16x16 tile and 64-byte K slice (full
-//     fp32 products).
-//     Lane l of a 16x16 accumulator holds 4 consecutive A rows
-//     (4*(l/16) + 0..3) of B row l%16, so the output's contiguous
+//     fp32 products).  Lane l of a 16x16 accumulator holds 4 consecutive A
+//     rows (4*(l/16) + 0..3) of B row l%16, so the output's contiguous
 //     dimension sits on the A side and each lane stores 4 adjacent elements.
-//   * The up projection puts w1 columns [f0, f0+128) in A rows 0..127 and the
-//     same w3 columns in A rows 128..255, so each lane holds matching h1 and
-//     h3 values and the SiLU gate is applied in the epilogue.
 #include "dmoe_device.h"
 #include "dmoe_internal.h"
 
 namespace dmoe {
 
 constexpr int kGemmThreads = 256;
-constexpr int kTileA = 256;
-constexpr int kTileB = 128;
-constexpr int kKBytes = 64;
+constexpr int kTileA = 64;                 // A rows: two halves of kHalfA
+constexpr int kHalfA = kTileA / 2;
+constexpr int kTileB = 64;                 // B rows, from one source
+constexpr int kKElems = 32;                // fp32 K per stage
+constexpr int kKBytes = kKElems * 4;
 constexpr int kLdsRow = kKBytes + 16;
 constexpr int kLdsA = kTileA * kLdsRow;
 constexpr int kLdsB = kTileB * kLdsRow;
 constexpr int kLdsStage = kLdsA + kLdsB;
+constexpr int kBPerBlock = kBlock / kTileB;   // B tiles per 128-row block
 
-template <typename T> struct KStep { static constexpr int elems = kKBytes / (int)sizeof(T); };
-
-// One operand's source: tile rows [0,128) start at p0 and rows [128,256) at
-// p1 (A side only).  `ld` is the byte distance between consecutive source
-// rows.  For a K-contiguous source a tile row is a source row; for a
-// transposed source a tile row is a source column and K runs down the rows.
+// One operand's source.  A: tile rows [0, half) start at p0 and rows
+// [half, 2 half) at p1 (present when has1).  B: all rows from p0 (half =
+// kTileB).  `ld` is the byte distance between consecutive source rows.  For
+// a K-contiguous source a tile row is a source row; for a transposed source
+// a tile row is a source column and K runs down the rows.
 struct Operand {
   const char* p0;
   const char* p1;
   int64_t ld;
+  int half;
   bool has1;
 };
 
-template <typename T, bool TRANS, int ROWS> struct Loader;
+template <bool TRANS, int ROWS> struct Loader;
 
 // K-contiguous source: 16 bytes per lane, 4 lanes per 64-byte row slice.
-template <typename T, int ROWS> struct Loader<T, false, ROWS> {
-  static constexpr int kChunks = ROWS * (kKBytes / 16) / kGemmThreads;
+template <int ROWS> struct Loader<false, ROWS> {
+  static constexpr int kSegs = kKBytes / 16;                 // 16-byte segments per row
+  static constexpr int kChunks = ROWS * kSegs / kGemmThreads;
+  static_assert(kChunks >= 1 && ROWS * kSegs % kGemmThreads == 0, "tile/block mismatch");
   u32x4 r[kChunks];
+  __device__ __forceinline__ bool live(const Operand& op, int row) const {
+    return row < op.half || op.has1;
+  }
   __device__ __forceinline__ void load(const Operand& op, int ks, int tid) {
 #pragma unroll
     for (int q = 0; q < kChunks; ++q) {
       const int c = tid + q * kGemmThreads;
-      const int row = c >> 2, seg = c & 3;
-      const bool hi = row >= 128;
-      if (hi && !op.has1) continue;
-      const char* base = hi ? op.p1 : op.p0;
-      r[q] = ld16(base + (int64_t)(row & 127) * op.ld + (int64_t)ks * kKBytes + seg * 16);
+      const int row = c / kSegs, seg = c % kSegs;
+      if (!live(op, row)) continue;
+      const char* base = row < op.half ? op.p0 + (int64_t)row * op.ld
+                                       : op.p1 + (int64_t)(row - op.half) * op.ld;
+      r[q] = ld16(base + (int64_t)ks * kKBytes + seg * 16);
     }
   }
-  __device__ __forceinline__ void store(char* lds, int tid, bool has1) const {
+  __device__ __forceinline__ void store(char* lds, const Operand& op, int tid) const {
 #pragma unroll
     for (int q = 0; q < kChunks; ++q) {
       const int c = tid + q * kGemmThreads;
-      const int row = c >> 2, seg = c & 3;
-      if (row >= 128 && !has1) continue;
+      const int row = c / kSegs, seg = c % kSegs;
+      if (!live(op, row)) continue;
       *reinterpret_cast<u32x4*>(lds + row * kLdsRow + seg * 16) = r[q];
     }
   }
 };
 
-// Row-contiguous fp32 source: 4 K-rows x 4 columns per thread.
-template <int ROWS> struct Loader<float, true, ROWS> {
+// Row-contiguous source: thread t reads 4 K-rows x 4 columns (16 bytes per
+// K-row) and writes 4 LDS rows of 4 consecutive K values.
+template <int ROWS> struct Loader<true, ROWS> {
+  static constexpr int kNBlk = ROWS / 4;      // 4-column blocks per K-row
+  static constexpr int kThreads = kNBlk * (kKElems / 4);
+  static_assert(kThreads <= kGemmThreads, "one micro-block per thread");
   u32x4 v[4];
-  __device__ __forceinline__ bool active(bool has1, int tid) const {
-    return (ROWS == 256 || tid < 128) && (tid < 128 || has1);
+  __device__ __forceinline__ bool active(const Operand& op, int tid) const {
+    return tid < kThreads && ((tid % kNBlk) * 4 < op.half || op.has1);
   }
   __device__ __forceinline__ void load(const Operand& op, int ks, int tid) {
-    if (!active(op.has1, tid)) return;
-    const int half = tid >> 7, mb = tid & 127, kblk = mb >> 5, nblk = mb & 31;
-    const char* base = (half ? op.p1 : op.p0) +
-                       (int64_t)(ks * KStep<float>::elems + kblk * 4) * op.ld + nblk * 16;
+    if (!active(op, tid)) return;
+    const int kblk = tid / kNBlk, n0 = (tid % kNBlk) * 4;
+    const char* col = n0 < op.half ? op.p0 + n0 * 4 : op.p1 + (n0 - op.half) * 4;
+    const char* base = col + (int64_t)(ks * kKElems + kblk * 4) * op.ld;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) v[kk] = ld16(base + (int64_t)kk * op.ld);
   }
-  __device__ __forceinline__ void store(char* lds, int tid, bool has1) const {
-    if (!active(has1, tid)) return;
-    const int half = tid >> 7, mb = tid & 127, kblk = mb >> 5, nblk = mb & 31;
+  __device__ __forceinline__ void store(char* lds, const Operand& op, int tid) const {
+    if (!active(op, tid)) return;
+    const int kblk = tid / kNBlk, n0 = (tid % kNBlk) * 4;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const u32x4 o = {v[0][c], v[1][c], v[2][c], v[3][c]};
-      *reinterpret_cast<u32x4*>(lds + (half * 128 + nblk * 4 + c) * kLdsRow + kblk * 16) = o;
+      *reinterpret_cast<u32x4*>(lds + (n0 + c) * kLdsRow + kblk * 16) = o;
     }
   }
 };
 
-typedef f32x4 Acc[8][4];
+typedef f32x4 Acc[2][2];
 
-__device__ __forceinline__ int a_row(int i, int wm) { return (i >> 2) * 128 + wm * 64 + (i & 3) * 16; }
-__device__ __forceinline__ int b_row(int j, int wn) { return wn * 64 + j * 16; }
+// 16-row subtiles of wave (wm, wn): A subtile i in A half i, B subtile j.
+__device__ __forceinline__ int a_row(int i, int wm) { return i * kHalfA + wm * 16; }
+__device__ __forceinline__ int b_row(int j, int wn) { return wn * 32 + j * 16; }
 
-template <typename T> struct Mma;
-template <> struct Mma<float> {
-  __device__ __forceinline__ static void stage(Acc& acc, const char* lds, int wm, int wn,
-                                               int lane, bool has1) {
-    const char* la = lds;
-    const char* lb = lds + kLdsA;
-    const int lrow = lane & 15, lk = (lane >> 4) * 16;
-    f32x4 b[4];
+__device__ __forceinline__ void mma_stage(Acc& acc, const char* lds, int wm, int wn, int lane,
+                                          bool has1) {
+  const char* la = lds;
+  const char* lb = lds + kLdsA;
+  const int lrow = lane & 15;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+  for (int kk = 0; kk < kKElems / 16; ++kk) {
+    // lanes of group l/16 hold K 16 kk + 4 (l/16) + 0..3; MFMA s takes the
+    // s-th of them, so the four MFMAs cover the 16 K of this sub-step
+    const int lk = kk * 64 + (lane >> 4) * 16;
+    f32x4 b[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
       b[j] = *reinterpret_cast<const f32x4*>(lb + (b_row(j, wn) + lrow) * kLdsRow + lk);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (i >= 4 && !has1) break;
+    for (int i = 0; i < 2; ++i) {
+      if (i == 1 && !has1) break;
       const f32x4 a = *reinterpret_cast<const f32x4*>(la + (a_row(i, wm) + lrow) * kLdsRow + lk);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int s = 0; s < 4; ++s)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[j][s], acc[i][j], 0, 0, 0);
     }
   }
-};
+}
 
-// acc += A_tile . B_tile^T over `ksteps` 64-byte K slices.
-template <typename T, bool ATR, bool BTR>
+// acc += A_tile . B_tile^T over `ksteps` K slices of kKElems.
+template <bool ATR, bool BTR>
 __device__ __forceinline__ void mainloop(Acc& acc, const Operand& A, const Operand& B,
                                          int ksteps, char* lds) {
   if (ksteps <= 0) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w >> 1, wn = w & 1;
-  Loader<T, ATR, kTileA> la;
-  Loader<T, BTR, kTileB> lb;
+  Loader<ATR, kTileA> la;
+  Loader<BTR, kTileB> lb;
   la.load(A, 0, tid);
   lb.load(B, 0, tid);
-  la.store(lds, tid, A.has1);
-  lb.store(lds + kLdsA, tid, false);
+  la.store(lds, A, tid);
+  lb.store(lds + kLdsA, B, tid);
   __syncthreads();
   for (int ks = 0; ks < ksteps; ++ks) {
     char* cur = lds + (ks & 1) * kLdsStage;
@@ -167,10 +184,10 @@ __device__ __forceinline__ void mainloop(Acc& acc, const Operand& A, const Opera
       la.load(A, ks + 1, tid);
       lb.load(B, ks + 1, tid);
     }
-    Mma<T>::stage(acc, cur, wm, wn, lane, A.has1);
+    mma_stage(acc, cur, wm, wn, lane, A.has1);
     if (more) {
-      la.store(nxt, tid, A.has1);
-      lb.store(nxt + kLdsA, tid, false);
+      la.store(nxt, A, tid);
+      lb.store(nxt + kLdsA, B, tid);
     }
     __syncthreads();
   }
@@ -178,88 +195,90 @@ __device__ __forceinline__ void mainloop(Acc& acc, const Operand& A, const Opera
 
 __device__ __forceinline__ void zero(Acc& acc) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-template <typename T> __device__ __forceinline__ void store4(T* p, const f32x4& v);
-template <> __device__ __forceinline__ void store4<float>(float* p, const f32x4& v) {
+__device__ __forceinline__ void store4(float* p, const f32x4& v) {
   *reinterpret_cast<f32x4*>(p) = v;
 }
-template <typename T> __device__ __forceinline__ f32x4 load4(const T* p);
-template <> __device__ __forceinline__ f32x4 load4<float>(const float* p) {
+__device__ __forceinline__ f32x4 load4(const float* p) {
   return *reinterpret_cast<const f32x4*>(p);
 }
 
-
-#define GEMM_PROLOGUE                                        \
-  __shared__ __attribute__((aligned(16))) char lds[2 * kLdsStage]; \
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6; \
-  const int wm = w >> 1, wn = w & 1;                         \
-  const int lr = (lane >> 4) * 4, lc = lane & 15;            \
+#define GEMM_PROLOGUE                                                \
+  __shared__ __attribute__((aligned(16))) char lds[2 * kLdsStage];   \
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;        \
+  const int wm = w >> 1, wn = w & 1;                                 \
+  const int lr = (lane >> 4) * 4, lc = lane & 15;                    \
   (void)lr; (void)lc;
 
-// h1 = x_perm w1[e], h3 = x_perm w3[e], act = silu(h1) * h3 for one 128-row
-// block and 128 ffn columns.  grid = (F/128, max_tiles).
-template <typename T>
-__global__ void __launch_bounds__(kGemmThreads)
-gemm_up_kernel(const T* __restrict__ x_perm, const T* __restrict__ w1,
-               const T* __restrict__ w3, int64_t H, int64_t F,
-               const int32_t* __restrict__ tile_expert, T* __restrict__ h1,
-               T* __restrict__ h3, T* __restrict__ act) {
-  GEMM_PROLOGUE
-  const int64_t mt = blockIdx.y, f0 = (int64_t)blockIdx.x * 128;
-  const int e = tile_expert[mt];
-  if (e < 0) return;
-  const int64_t wofs = (int64_t)e * H * F + f0;
-  const Operand A{reinterpret_cast<const char*>(w1 + wofs),
-                  reinterpret_cast<const char*>(w3 + wofs), F * (int64_t)sizeof(T), true};
-  const Operand B{reinterpret_cast<const char*>(x_perm + mt * kBlock * H), nullptr,
-                  H * (int64_t)sizeof(T), false};
-  Acc acc;
-  zero(acc);
-  mainloop<T, true, false>(acc, A, B, (int)(H / KStep<T>::elems), lds);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t p = mt * kBlock + b_row(j, wn) + lc;
-      const int64_t f = f0 + a_row(i, wm) + lr;
-      const f32x4 v1 = acc[i][j], v3 = acc[i + 4][j];
-      f32x4 a;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) a[r] = gated_silu(v1[r], v3[r]);
-      store4(h1 + p * F + f, v1);
-      store4(h3 + p * F + f, v3);
-      store4(act + p * F + f, a);
-    }
+// The B tile of the row-block products: 64 rows of a 128-row block.
+__device__ __forceinline__ bool row_tile(const int32_t* tile_expert, int64_t& p0, int& e) {
+  const int64_t bt = blockIdx.y;
+  e = tile_expert[bt / kBPerBlock];
+  p0 = bt * kTileB;
+  return e >= 0;
 }
 
-// y_perm = act w2[e].  grid = (ceil(H/256), max_tiles).
-template <typename T>
+// h1 = x_perm w1[e], h3 = x_perm w3[e], act = silu(h1) * h3 for 64 rows and
+// 32 ffn columns (w1 columns in A half 0, the same w3 columns in A half 1).
+// grid = (F/32, 2 max_tiles).
 __global__ void __launch_bounds__(kGemmThreads)
-gemm_down_kernel(const T* __restrict__ act, const T* __restrict__ w2, int64_t H,
-                 int64_t F, const int32_t* __restrict__ tile_expert,
-                 T* __restrict__ y_perm) {
+gemm_up_kernel(const float* __restrict__ x_perm, const float* __restrict__ w1,
+               const float* __restrict__ w3, int64_t H, int64_t F,
+               const int32_t* __restrict__ tile_expert, float* __restrict__ h1,
+               float* __restrict__ h3, float* __restrict__ act) {
   GEMM_PROLOGUE
-  const int64_t mt = blockIdx.y, h0 = (int64_t)blockIdx.x * kTileA;
-  const int e = tile_expert[mt];
-  if (e < 0) return;
-  const T* wb = w2 + (int64_t)e * F * H + h0;
-  const Operand A{reinterpret_cast<const char*>(wb), reinterpret_cast<const char*>(wb + 128),
-                  H * (int64_t)sizeof(T), h0 + 128 < H};
-  const Operand B{reinterpret_cast<const char*>(act + mt * kBlock * F), nullptr,
-                  F * (int64_t)sizeof(T), false};
+  int64_t p0;
+  int e;
+  if (!row_tile(tile_expert, p0, e)) return;
+  const int64_t f0 = (int64_t)blockIdx.x * kHalfA;
+  const int64_t wofs = (int64_t)e * H * F + f0;
+  const Operand A{reinterpret_cast<const char*>(w1 + wofs),
+                  reinterpret_cast<const char*>(w3 + wofs), F * 4, kHalfA, true};
+  const Operand B{reinterpret_cast<const char*>(x_perm + p0 * H), nullptr, H * 4, kTileB, false};
   Acc acc;
   zero(acc);
-  mainloop<T, true, false>(acc, A, B, (int)(F / KStep<T>::elems), lds);
+  mainloop<true, false>(acc, A, B, (int)(H / kKElems), lds);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (i >= 4 && !A.has1) break;
+  for (int j = 0; j < 2; ++j) {
+    const int64_t p = p0 + b_row(j, wn) + lc;
+    const int64_t f = f0 + a_row(0, wm) + lr;
+    const f32x4 v1 = acc[0][j], v3 = acc[1][j];
+    f32x4 a;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t p = mt * kBlock + b_row(j, wn) + lc;
+    for (int r = 0; r < 4; ++r) a[r] = gated_silu(v1[r], v3[r]);
+    store4(h1 + p * F + f, v1);
+    store4(h3 + p * F + f, v3);
+    store4(act + p * F + f, a);
+  }
+}
+
+// y_perm = act w2[e] for 64 rows and 64 hidden columns.  grid = (H/64, 2 max_tiles).
+__global__ void __launch_bounds__(kGemmThreads)
+gemm_down_kernel(const float* __restrict__ act, const float* __restrict__ w2, int64_t H,
+                 int64_t F, const int32_t* __restrict__ tile_expert,
+                 float* __restrict__ y_perm) {
+  GEMM_PROLOGUE
+  int64_t p0;
+  int e;
+  if (!row_tile(tile_expert, p0, e)) return;
+  const int64_t h0 = (int64_t)blockIdx.x * kTileA;
+  const float* wb = w2 + (int64_t)e * F * H + h0;
+  const Operand A{reinterpret_cast<const char*>(wb), reinterpret_cast<const char*>(wb + kHalfA),
+                  H * 4, kHalfA, h0 + kHalfA < H};
+  const Operand B{reinterpret_cast<const char*>(act + p0 * F), nullptr, F * 4, kTileB, false};
+  Acc acc;
+  zero(acc);
+  mainloop<true, false>(acc, A, B, (int)(F / kKElems), lds);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (i == 1 && !A.has1) break;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int64_t p = p0 + b_row(j, wn) + lc;
       store4(y_perm + p * H + h0 + a_row(i, wm) + lr, acc[i][j]);
     }
   }
@@ -267,30 +286,35 @@ gemm_down_kernel(const T* __restrict__ act, const T* __restrict__ w2, int64_t H,
 
 // dA = dy_perm w2[e]^T, then the gate's backward:
 // dh3 = dA * silu(h1), dh1 = dA * h3 * s * (1 + h1 (1 - s)), s = sigmoid(h1).
-// grid = (ceil(F/256), max_tiles).
-template <typename T>
-__global__ void __launch_bounds__(kGemmThreads)
-gemm_down_dgrad_kernel(const T* __restrict__ dy_perm, const T* __restrict__ w2,
-                       const T* h1, const T* h3, int64_t H, int64_t F,
-                       const int32_t* __restrict__ tile_expert, T* dh1, T* dh3) {
-  GEMM_PROLOGUE
-  const int64_t mt = blockIdx.y, fb = (int64_t)blockIdx.x * kTileA;
-  const int e = tile_expert[mt];
+// 64 rows and 64 ffn columns.
+// (bx, by): the tile's grid coordinates.
+__device__ __forceinline__ void down_dgrad_tile(const float* __restrict__ dy_perm,
+                                                const float* __restrict__ w2, const float* h1,
+                                                const float* h3, int64_t H, int64_t F,
+                                                const int32_t* __restrict__ tile_expert,
+                                                float* dh1, float* dh3, int bx, int by,
+                                                char* lds) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wn = w & 1, wm = w >> 1;
+  const int lr = (lane >> 4) * 4, lc = lane & 15;
+  const int e = tile_expert[by / kBPerBlock];
   if (e < 0) return;
-  const T* wb = w2 + (int64_t)e * F * H + fb * H;
-  const Operand A{reinterpret_cast<const char*>(wb), reinterpret_cast<const char*>(wb + 128 * H),
-                  H * (int64_t)sizeof(T), fb + 128 < F};
-  const Operand B{reinterpret_cast<const char*>(dy_perm + mt * kBlock * H), nullptr,
-                  H * (int64_t)sizeof(T), false};
+  const int64_t p0 = (int64_t)by * kTileB;
+  const int64_t fb = (int64_t)bx * kTileA;
+  const float* wb = w2 + (int64_t)e * F * H + fb * H;
+  const Operand A{reinterpret_cast<const char*>(wb),
+                  reinterpret_cast<const char*>(wb + kHalfA * H), H * 4, kHalfA,
+                  fb + kHalfA < F};
+  const Operand B{reinterpret_cast<const char*>(dy_perm + p0 * H), nullptr, H * 4, kTileB, false};
   Acc acc;
   zero(acc);
-  mainloop<T, false, false>(acc, A, B, (int)(H / KStep<T>::elems), lds);
+  mainloop<false, false>(acc, A, B, (int)(H / kKElems), lds);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (i >= 4 && !A.has1) break;
+  for (int i = 0; i < 2; ++i) {
+    if (i == 1 && !A.has1) break;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t p = mt * kBlock + b_row(j, wn) + lc;
+    for (int j = 0; j < 2; ++j) {
+      const int64_t p = p0 + b_row(j, wn) + lc;
       const int64_t o = p * F + fb + a_row(i, wm) + lr;
       const f32x4 g1 = load4(h1 + o), g3 = load4(h3 + o);
       f32x4 d1, d3;
@@ -307,42 +331,40 @@ gemm_down_dgrad_kernel(const T* __restrict__ dy_perm, const T* __restrict__ w2,
   }
 }
 
-// dx_perm = dh1 w1[e]^T + dh3 w3[e]^T.  grid = (ceil(H/256), max_tiles).
-template <typename T>
+// dx_perm = dh1 w1[e]^T + dh3 w3[e]^T for 64 rows and 64 hidden columns.
+// grid = (H/64, 2 max_tiles).
 __global__ void __launch_bounds__(kGemmThreads)
-gemm_up_dgrad_kernel(const T* __restrict__ dh1, const T* __restrict__ dh3,
-                     const T* __restrict__ w1, const T* __restrict__ w3, int64_t H,
-                     int64_t F, const int32_t* __restrict__ tile_expert,
-                     T* dx_perm) {
+gemm_up_dgrad_kernel(const float* __restrict__ dh1, const float* __restrict__ dh3,
+                     const float* __restrict__ w1, const float* __restrict__ w3, int64_t H,
+                     int64_t F, const int32_t* __restrict__ tile_expert, float* dx_perm) {
   GEMM_PROLOGUE
-  const int64_t mt = blockIdx.y, h0 = (int64_t)blockIdx.x * kTileA;
-  const int e = tile_expert[mt];
-  if (e < 0) return;
+  int64_t p0;
+  int e;
+  if (!row_tile(tile_expert, p0, e)) return;
+  const int64_t h0 = (int64_t)blockIdx.x * kTileA;
   const int64_t wofs = (int64_t)e * H * F + h0 * F;
-  const bool has1 = h0 + 128 < H;
-  const int ks = (int)(F / KStep<T>::elems);
+  const bool has1 = h0 + kHalfA < H;
+  const int ks = (int)(F / kKElems);
   Acc acc;
   zero(acc);
   {
     const Operand A{reinterpret_cast<const char*>(w1 + wofs),
-                    reinterpret_cast<const char*>(w1 + wofs + 128 * F), F * (int64_t)sizeof(T), has1};
-    const Operand B{reinterpret_cast<const char*>(dh1 + mt * kBlock * F), nullptr,
-                    F * (int64_t)sizeof(T), false};
-    mainloop<T, false, false>(acc, A, B, ks, lds);
+                    reinterpret_cast<const char*>(w1 + wofs + kHalfA * F), F * 4, kHalfA, has1};
+    const Operand B{reinterpret_cast<const char*>(dh1 + p0 * F), nullptr, F * 4, kTileB, false};
+    mainloop<false, false>(acc, A, B, ks, lds);
   }
   {
     const Operand A{reinterpret_cast<const char*>(w3 + wofs),
-                    reinterpret_cast<const char*>(w3 + wofs + 128 * F), F * (int64_t)sizeof(T), has1};
-    const Operand B{reinterpret_cast<const char*>(dh3 + mt * kBlock * F), nullptr,
-                    F * (int64_t)sizeof(T), false};
-    mainloop<T, false, false>(acc, A, B, ks, lds);
+                    reinterpret_cast<const char*>(w3 + wofs + kHalfA * F), F * 4, kHalfA, has1};
+    const Operand B{reinterpret_cast<const char*>(dh3 + p0 * F), nullptr, F * 4, kTileB, false};
+    mainloop<false, false>(acc, A, B, ks, lds);
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (i >= 4 && !has1) break;
+  for (int i = 0; i < 2; ++i) {
+    if (i == 1 && !has1) break;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t p = mt * kBlock + b_row(j, wn) + lc;
+    for (int j = 0; j < 2; ++j) {
+      const int64_t p = p0 + b_row(j, wn) + lc;
       store4(dx_perm + p * H + h0 + a_row(i, wm) + lr, acc[i][j]);
     }
   }
@@ -356,68 +378,94 @@ __device__ __forceinline__ void expert_rows(int e, const int32_t* tpe,
 }
 
 // dw2[e] = act[rows_e]^T dy_perm[rows_e]  ([F,H]); zero for an empty expert.
-// grid = (ceil(H/256), F/128, E).
-template <typename T>
-__global__ void __launch_bounds__(kGemmThreads)
-gemm_wgrad_down_kernel(const T* __restrict__ act, const T* __restrict__ dy_perm,
-                       int64_t H, int64_t F, const int32_t* __restrict__ tpe,
-                       const int32_t* __restrict__ padded_bins, T* __restrict__ dw2) {
-  GEMM_PROLOGUE
-  const int64_t h0 = (int64_t)blockIdx.x * kTileA, f0 = (int64_t)blockIdx.y * 128;
-  const int e = blockIdx.z;
+// 64 ffn x 64 hidden columns; (bx, by, e): the tile's grid coordinates.
+__device__ __forceinline__ void wgrad_down_tile(const float* __restrict__ act,
+                                                const float* __restrict__ dy_perm, int64_t H,
+                                                int64_t F, const int32_t* __restrict__ tpe,
+                                                const int32_t* __restrict__ padded_bins,
+                                                float* __restrict__ dw2, int bx, int by, int e,
+                                                char* lds) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wn = w & 1, wm = w >> 1;
+  const int lr = (lane >> 4) * 4, lc = lane & 15;
+  const int64_t h0 = (int64_t)bx * kTileA, f0 = (int64_t)by * kTileB;
   int64_t start;
   int n;
   expert_rows(e, tpe, padded_bins, start, n);
-  const T* ab = dy_perm + start * H + h0;
-  const Operand A{reinterpret_cast<const char*>(ab), reinterpret_cast<const char*>(ab + 128),
-                  H * (int64_t)sizeof(T), h0 + 128 < H};
-  const Operand B{reinterpret_cast<const char*>(act + start * F + f0), nullptr,
-                  F * (int64_t)sizeof(T), false};
+  const float* ab = dy_perm + start * H + h0;
+  const Operand A{reinterpret_cast<const char*>(ab), reinterpret_cast<const char*>(ab + kHalfA),
+                  H * 4, kHalfA, h0 + kHalfA < H};
+  const Operand B{reinterpret_cast<const char*>(act + start * F + f0), nullptr, F * 4, kTileB,
+                  false};
   Acc acc;
   zero(acc);
-  mainloop<T, true, true>(acc, A, B, n / KStep<T>::elems, lds);
-  T* out = dw2 + (int64_t)e * F * H;
+  mainloop<true, true>(acc, A, B, n / kKElems, lds);
+  float* out = dw2 + (int64_t)e * F * H;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (i >= 4 && !A.has1) break;
+  for (int i = 0; i < 2; ++i) {
+    if (i == 1 && !A.has1) break;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       const int64_t f = f0 + b_row(j, wn) + lc;
       store4(out + f * H + h0 + a_row(i, wm) + lr, acc[i][j]);
     }
   }
 }
 
-// dw1[e] = x_perm[rows_e]^T dh1[rows_e], dw3[e] = x_perm[rows_e]^T dh3[rows_e]
-// ([H,F] each); zero for an empty expert.  grid = (F/128, H/128, E).
-template <typename T>
+// down dgrad + gate backward and dw2 in one launch (neither reads what the
+// other writes): blocks [0, nd) are dgrad tiles ((F/64) x (2 max_tiles),
+// x fastest), the rest dw2 tiles ((H/64) x (F/64) x E).
 __global__ void __launch_bounds__(kGemmThreads)
-gemm_wgrad_up_kernel(const T* __restrict__ x_perm, const T* __restrict__ dh1,
-                     const T* __restrict__ dh3, int64_t H, int64_t F,
+gemm_down_dgrad_wgrad_down_kernel(const float* __restrict__ dy_perm,
+                                  const float* __restrict__ w2, const float* h1,
+                                  const float* h3, const float* __restrict__ act, int64_t H,
+                                  int64_t F, const int32_t* __restrict__ tile_expert,
+                                  const int32_t* __restrict__ tpe,
+                                  const int32_t* __restrict__ padded_bins, float* dh1,
+                                  float* dh3, float* __restrict__ dw2, int nd) {
+  __shared__ __attribute__((aligned(16))) char lds[2 * kLdsStage];
+  const int b = (int)blockIdx.x;
+  if (b < nd) {
+    const int fx = (int)((F + kTileA - 1) / kTileA);
+    down_dgrad_tile(dy_perm, w2, h1, h3, H, F, tile_expert, dh1, dh3, b % fx, b / fx, lds);
+  } else {
+    const int hx = (int)((H + kTileA - 1) / kTileA), fy = (int)((F + kTileB - 1) / kTileB);
+    const int r = b - nd;
+    wgrad_down_tile(act, dy_perm, H, F, tpe, padded_bins, dw2, r % hx, (r / hx) % fy,
+                    r / (hx * fy), lds);
+  }
+}
+
+// dw1[e] = x_perm[rows_e]^T dh1[rows_e], dw3[e] = x_perm[rows_e]^T dh3[rows_e]
+// ([H,F] each); zero for an empty expert.  32 ffn columns of each (A halves)
+// x 64 hidden rows.  grid = (F/32, H/64, E).
+__global__ void __launch_bounds__(kGemmThreads)
+gemm_wgrad_up_kernel(const float* __restrict__ x_perm, const float* __restrict__ dh1,
+                     const float* __restrict__ dh3, int64_t H, int64_t F,
                      const int32_t* __restrict__ tpe,
-                     const int32_t* __restrict__ padded_bins, T* __restrict__ dw1,
-                     T* __restrict__ dw3) {
+                     const int32_t* __restrict__ padded_bins, float* __restrict__ dw1,
+                     float* __restrict__ dw3) {
   GEMM_PROLOGUE
-  const int64_t f0 = (int64_t)blockIdx.x * 128, h0 = (int64_t)blockIdx.y * 128;
+  const int64_t f0 = (int64_t)blockIdx.x * kHalfA, h0 = (int64_t)blockIdx.y * kTileB;
   const int e = blockIdx.z;
   int64_t start;
   int n;
   expert_rows(e, tpe, padded_bins, start, n);
   const Operand A{reinterpret_cast<const char*>(dh1 + start * F + f0),
-                  reinterpret_cast<const char*>(dh3 + start * F + f0), F * (int64_t)sizeof(T), true};
-  const Operand B{reinterpret_cast<const char*>(x_perm + start * H + h0), nullptr,
-                  H * (int64_t)sizeof(T), false};
+                  reinterpret_cast<const char*>(dh3 + start * F + f0), F * 4, kHalfA, true};
+  const Operand B{reinterpret_cast<const char*>(x_perm + start * H + h0), nullptr, H * 4,
+                  kTileB, false};
   Acc acc;
   zero(acc);
-  mainloop<T, true, true>(acc, A, B, n / KStep<T>::elems, lds);
+  mainloop<true, true>(acc, A, B, n / kKElems, lds);
   const int64_t eo = (int64_t)e * H * F;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       const int64_t h = h0 + b_row(j, wn) + lc;
-      const int64_t f = f0 + a_row(i & 3, wm) + lr;
-      store4((i < 4 ? dw1 : dw3) + eo + h * F + f, acc[i][j]);
+      const int64_t f = f0 + a_row(0, wm) + lr;
+      store4((i == 0 ? dw1 : dw3) + eo + h * F + f, acc[i][j]);
     }
 }
 
@@ -426,13 +474,16 @@ static unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b);
 template <typename T> static const T* cp(const void* p) { return static_cast<const T*>(p); }
 template <typename T> static T* mp(void* p) { return static_cast<T*>(p); }
 
+// B tiles of the row-block products: kBPerBlock per 128-row block.
+static unsigned row_tiles(const Shape& s) { return (unsigned)(s.max_tiles * kBPerBlock); }
+
 hipError_t launch_gemm_up(const Shape& s, const void* x_perm, const void* x, const void* w1,
                           const void* w3, const MetaPtrs& m, void* h1, void* h3,
                           void* act, hipStream_t stream) {
-  const dim3 grid(cdiv(s.F, 128), (unsigned)s.max_tiles);
   if (s.bf16) return launch_bf16_up(s, x_perm, x, w1, w3, m, h1, h3, act, stream);
   if (x) return hipErrorNotSupported;   // rows from x: bf16 engine only
-  hipLaunchKernelGGL(gemm_up_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
+  const dim3 grid(cdiv(s.F, kHalfA), row_tiles(s));
+  hipLaunchKernelGGL(gemm_up_kernel, grid, dim3(kGemmThreads), 0, stream,
                      cp<float>(x_perm), cp<float>(w1), cp<float>(w3), s.H, s.F,
                      m.tile_expert, mp<float>(h1), mp<float>(h3), mp<float>(act));
   return hipGetLastError();
@@ -440,30 +491,11 @@ hipError_t launch_gemm_up(const Shape& s, const void* x_perm, const void* x, con
 
 hipError_t launch_gemm_down(const Shape& s, const void* act, const void* w2,
                             const MetaPtrs& m, void* y_perm, hipStream_t stream) {
-  const dim3 grid(cdiv(s.H, kTileA), (unsigned)s.max_tiles);
   if (s.bf16) return launch_bf16_down(s, act, w2, m, y_perm, stream);
-  hipLaunchKernelGGL(gemm_down_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
+  const dim3 grid(cdiv(s.H, kTileA), row_tiles(s));
+  hipLaunchKernelGGL(gemm_down_kernel, grid, dim3(kGemmThreads), 0, stream,
                      cp<float>(act), cp<float>(w2), s.H, s.F, m.tile_expert,
                      mp<float>(y_perm));
-  return hipGetLastError();
-}
-
-static hipError_t f32_down_dgrad(const Shape& s, const void* dy_perm, const void* w2,
-                                 const void* h1, const void* h3, const MetaPtrs& m, void* dh1,
-                                 void* dh3, hipStream_t stream) {
-  const dim3 grid(cdiv(s.F, kTileA), (unsigned)s.max_tiles);
-  hipLaunchKernelGGL(gemm_down_dgrad_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
-                     cp<float>(dy_perm), cp<float>(w2), cp<float>(h1), cp<float>(h3),
-                     s.H, s.F, m.tile_expert, mp<float>(dh1), mp<float>(dh3));
-  return hipGetLastError();
-}
-
-static hipError_t f32_wgrad_down(const Shape& s, const void* act, const void* dy_perm,
-                                 const MetaPtrs& m, void* dw2, hipStream_t stream) {
-  const dim3 grid(cdiv(s.H, kTileA), cdiv(s.F, 128), (unsigned)s.E);
-  hipLaunchKernelGGL(gemm_wgrad_down_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
-                     cp<float>(act), cp<float>(dy_perm), s.H, s.F, m.tokens_per_expert,
-                     m.padded_bins, mp<float>(dw2));
   return hipGetLastError();
 }
 
@@ -474,9 +506,13 @@ hipError_t launch_gemm_down_dgrad_wgrad_down(const Shape& s, const void* dy_perm
   if (s.bf16)
     return launch_bf16_down_dgrad_wgrad_down(s, dy_perm, w2, h1, h3, act, m, dh1, dh3, dw2,
                                              stream);
-  const hipError_t err = f32_down_dgrad(s, dy_perm, w2, h1, h3, m, dh1, dh3, stream);
-  if (err != hipSuccess) return err;
-  return f32_wgrad_down(s, act, dy_perm, m, dw2, stream);
+  const unsigned nd = cdiv(s.F, kTileA) * row_tiles(s);
+  const unsigned nw = cdiv(s.H, kTileA) * cdiv(s.F, kTileB) * (unsigned)s.E;
+  hipLaunchKernelGGL(gemm_down_dgrad_wgrad_down_kernel, dim3(nd + nw), dim3(kGemmThreads), 0,
+                     stream, cp<float>(dy_perm), cp<float>(w2), cp<float>(h1), cp<float>(h3),
+                     cp<float>(act), s.H, s.F, m.tile_expert, m.tokens_per_expert,
+                     m.padded_bins, mp<float>(dh1), mp<float>(dh3), mp<float>(dw2), (int)nd);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_up_dgrad(const Shape& s, const void* dh1, const void* dh3,
@@ -485,8 +521,8 @@ hipError_t launch_gemm_up_dgrad(const Shape& s, const void* dh1, const void* dh3
                                 hipStream_t stream) {
   if (s.bf16)
     return launch_bf16_up_dgrad(s, dh1, dh3, w1, w3, x_perm, m, dx_perm, dw1, dw3, stream);
-  const dim3 grid(cdiv(s.H, kTileA), (unsigned)s.max_tiles);
-  hipLaunchKernelGGL(gemm_up_dgrad_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
+  const dim3 grid(cdiv(s.H, kTileA), row_tiles(s));
+  hipLaunchKernelGGL(gemm_up_dgrad_kernel, grid, dim3(kGemmThreads), 0, stream,
                      cp<float>(dh1), cp<float>(dh3), cp<float>(w1), cp<float>(w3), s.H,
                      s.F, m.tile_expert, mp<float>(dx_perm));
   return hipGetLastError();
@@ -498,8 +534,8 @@ hipError_t launch_gemm_wgrad_up(const Shape& s, const void* dh1, const void* dh3
                                 hipStream_t stream) {
   if (s.bf16)
     return launch_bf16_wgrad_up(s, dh1, dh3, w1, w3, x_perm, m, dx_perm, dw1, dw3, stream);
-  const dim3 grid(cdiv(s.F, 128), cdiv(s.H, 128), (unsigned)s.E);
-  hipLaunchKernelGGL(gemm_wgrad_up_kernel<float>, grid, dim3(kGemmThreads), 0, stream,
+  const dim3 grid(cdiv(s.F, kHalfA), cdiv(s.H, kTileB), (unsigned)s.E);
+  hipLaunchKernelGGL(gemm_wgrad_up_kernel, grid, dim3(kGemmThreads), 0, stream,
                      cp<float>(x_perm), cp<float>(dh1), cp<float>(dh3), s.H, s.F,
                      m.tokens_per_expert, m.padded_bins, mp<float>(dw1), mp<float>(dw3));
   return hipGetLastError();

@@ -25,6 +25,8 @@
         under the DIRs (one rocprofv3 --pmc pass each), per kernel, and the
         derived figures: mfma = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE
         * 128) (GRBM_GUI_ACTIVE is summed over 8 XCDs of 128 SIMDs each),
+        clock_ghz = GRBM_GUI_ACTIVE / (8 * dispatch duration) (the
+        effective shader clock; needs the rows' timestamps),
         l2hit = TCC_HIT / (TCC_HIT + TCC_MISS), ta = TA_TA_BUSY /
         (GRBM_GUI_ACTIVE * 32) and tcp = TCP_PENDING_STALL_CYCLES /
         (GRBM_GUI_ACTIVE * 32) (32 CUs per XCD), and mfma_gflop =
@@ -80,15 +82,26 @@ def _counter(directory: str, counter: str, kernel_re: str):
 
 
 def counter_medians(dirs, kernels):
-    """{name: {counter: median over dispatches}} for (name, regex) pairs."""
+    """{name: {counter: median over dispatches}} for (name, regex) pairs.
+    Where the rows carry dispatch timestamps, "clock_ghz" is the median over
+    dispatches of GRBM_GUI_ACTIVE / (8 * duration): the effective shader
+    clock while the kernel ran (GRBM_GUI_ACTIVE counts busy cycles of each
+    of the 8 XCDs and sums them)."""
     rows = [r for d in dirs for r in _rows(d, "*counter_collection.csv")]
     out = {}
     for name, rx in kernels:
         per = {}
+        clk = []
         for r in rows:
             if re.search(rx, r["Kernel_Name"]):
                 per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                if r["Counter_Name"] == "GRBM_GUI_ACTIVE" and r.get("Start_Timestamp"):
+                    ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                    if ns > 0:
+                        clk.append(float(r["Counter_Value"]) / 8.0 / ns)
         out[name] = {c: statistics.median(v) for c, v in per.items()}
+        if clk:
+            out[name]["clock_ghz"] = statistics.median(clk)
     return out
 
 
@@ -105,6 +118,7 @@ def derived(c: dict) -> dict:
         "ta": ratio("TA_TA_BUSY_sum", "GRBM_GUI_ACTIVE", 32.0),
         "tcp": ratio("TCP_PENDING_STALL_CYCLES_sum", "GRBM_GUI_ACTIVE", 32.0),
         "lds_bankcf": c.get("SQ_LDS_BANK_CONFLICT"),
+        "clock_ghz": c.get("clock_ghz"),
         # SQ_INSTS_VALU_MFMA_MOPS_BF16 counts units of 512 FLOP
         "mfma_gflop": (c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / 1e9
                        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in c else None),
@@ -168,7 +182,7 @@ def main(argv=None):
     if a.cmd == "counters":
         kernels = [tuple(k.split("=", 1)) for k in a.kernel]
         med = counter_medians(a.dirs, kernels)
-        cols = ("mfma", "l2hit", "ta", "tcp", "lds_bankcf", "mfma_gflop")
+        cols = ("mfma", "l2hit", "ta", "tcp", "lds_bankcf", "mfma_gflop", "clock_ghz")
         print(f"{'kernel':28s} " + " ".join(f"{c:>10s}" for c in cols))
         for name, _ in kernels:
             d = derived(med[name])

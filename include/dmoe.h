@@ -68,9 +68,9 @@ typedef enum {
   DMOE_ERR_ARG = -1,         /* null pointer, non-positive size, k > E, T*k >= 2^31 */
   DMOE_ERR_SHAPE = -2,       /* F % 128 != 0 (MegaBlocks §5) or H % 128 != 0 */
   DMOE_ERR_UNSUPPORTED = -3, /* E > 256, an unknown dtype, H or F > 2^24, or
-                                (forward/backward) more than 65535 row blocks,
-                                or for fp32 more than 65535 128-column blocks
-                                of H or F */
+                                (forward/backward) more than 65535 row blocks;
+                                for fp32, more than 32767 row blocks or 65535
+                                64-column blocks of H or F */
   DMOE_ERR_HIP = -4,         /* a kernel launch failed */
   DMOE_ERR_EXPERT_ID = -5    /* device-side: an expert id outside [0,E) */
 } dmoe_status;
