@@ -37,7 +37,8 @@ __all__ = [
     "dmoe_max_tiles", "dmoe_workspace_bytes", "dmoe_schedule_bytes",
     "dmoe_metadata", "dmoe_metadata_noalloc", "dmoe_forward",
     "dmoe_backward", "dmoe_padded_gather", "dmoe_padded_scatter",
-    "dmoe_router_forward", "dmoe_router_backward",
+    "dmoe_router_forward", "dmoe_router_backward", "dmoe_token_round",
+    "dmoe_token_round_workspace_bytes",
     "dmoe_status_string", "allocate", "allocate_meta", "DMoELayer",
     "dmoe_autograd", "fused_gather_pays",
 ]
@@ -148,6 +149,10 @@ def load_library() -> ctypes.CDLL:
     lib.dmoe_backward_fused_gather_timed.argtypes = ([P(_Dims), vp]
                                                      + lib.dmoe_backward_timed.argtypes[1:])
     lib.dmoe_backward_fused_gather_timed.restype = ctypes.c_int
+    lib.dmoe_token_round_workspace_bytes.argtypes = [P(_Dims)]
+    lib.dmoe_token_round_workspace_bytes.restype = ctypes.c_int64
+    lib.dmoe_token_round.argtypes = [P(_Dims), vp, ctypes.c_int32, vp, vp, vp, vp]
+    lib.dmoe_token_round.restype = ctypes.c_int
     lib.dmoe_router_forward.argtypes = [P(_Dims), vp, ctypes.c_float, vp, vp, vp, vp, vp]
     lib.dmoe_router_forward.restype = ctypes.c_int
     lib.dmoe_router_backward.argtypes = [P(_Dims), vp, vp, vp, vp, ctypes.c_float, vp, vp]
@@ -479,6 +484,31 @@ def dmoe_router_forward(dims: Dims, logits, top_experts, weights, zloss_coef: fl
         _ptr(weights, torch.float32, "weights"), _ptr(z, torch.float32, "z"),
         _ptr(zloss, torch.float32, "zloss"), _stream(logits, stream)),
         "dmoe_router_forward")
+
+
+def dmoe_token_round_workspace_bytes(dims: Dims) -> int:
+    v = load_library().dmoe_token_round_workspace_bytes(ctypes.byref(dims._c()))
+    _check(v if v < 0 else 0, "dmoe_token_round_workspace_bytes")
+    return int(v)
+
+
+def dmoe_token_round(dims: Dims, logits, top_experts, weights, ws, tile_rows: int = 128,
+                     stream=None) -> None:
+    """Tile-aware token rounding of the top-k routing; see include/dmoe.h.
+
+    logits [T,E] fp32; dims.k = k routed slots (k < E); writes top_experts
+    [T,k+1] int32 (-1 for an empty slot) and weights [T,k+1] fp32.  The
+    layer then runs on these slots with Dims(..., k=k+1)."""
+    lib = load_library()
+    k1 = dims.k + 1
+    _need(logits, "logits", dims.T * dims.E)
+    _need(top_experts, "top_experts", dims.T * k1)
+    _need(weights, "weights", dims.T * k1)
+    _need(ws, "ws", dmoe_token_round_workspace_bytes(dims) // ws.element_size())
+    _check(lib.dmoe_token_round(
+        ctypes.byref(dims._c()), _ptr(logits, torch.float32, "logits"), ctypes.c_int32(tile_rows),
+        _ptr(top_experts, torch.int32, "top_experts"), _ptr(weights, torch.float32, "weights"),
+        _ptr(ws, None, "ws"), _stream(logits, stream)), "dmoe_token_round")
 
 
 def dmoe_router_backward(dims: Dims, logits, top_experts, weights, d_weights, d_logits,

@@ -461,6 +461,42 @@ int dmoe_router_backward(const dmoe_dims* dims, const float* logits,
   return DMOE_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Token rounding: the layer's checks, and k < E (a candidate per token)
+// with k + 1 slots per token within the limits of the metadata.
+int check_round(const dmoe_dims* d) {
+  const int rc = check_dims(d);
+  if (rc != DMOE_OK) return rc;
+  if (d->k >= d->E) return DMOE_ERR_ARG;
+  const int64_t n1 = d->T * (int64_t)(d->k + 1);
+  if (n1 >= (int64_t(1) << 31) || n1 + 127 * (int64_t)d->E >= (int64_t(1) << 31))
+    return DMOE_ERR_ARG;
+  return DMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t dmoe_token_round_workspace_bytes(const dmoe_dims* dims) {
+  const int rc = check_round(dims);
+  if (rc != DMOE_OK) return rc;
+  return dmoe::token_round_workspace_bytes(dims->T, dims->E, dims->k);
+}
+
+int dmoe_token_round(const dmoe_dims* dims, const float* logits, int32_t tile_rows,
+                     int32_t* top_experts, float* weights, void* ws, hipStream_t stream) {
+  const int rc = check_round(dims);
+  if (rc != DMOE_OK) return rc;
+  if (!logits || !top_experts || !weights || !ws || tile_rows < 1) return DMOE_ERR_ARG;
+  DMOE_TRY(dmoe::launch_token_round(shape_of(dims), logits, tile_rows, top_experts, weights, ws,
+                                    stream));
+  return DMOE_OK;
+}
+
 const char* dmoe_status_string(int status) {
   switch (status) {
     case DMOE_OK: return "ok";

@@ -62,6 +62,12 @@ hipError_t launch_scatter_backward(const Shape& s, const void* dy,
                                    const MetaPtrs& m, void* dy_perm,
                                    float* d_weights, hipStream_t stream);
 
+// token_round.hip: tile-aware token rounding of the router's top-k (s.k
+// routed slots, outputs [T, s.k + 1]); M rows per tile.
+int64_t token_round_workspace_bytes(int64_t T, int E, int k);
+hipError_t launch_token_round(const Shape& s, const float* logits, int M, int32_t* out_ids,
+                              float* out_w, void* ws, hipStream_t stream);
+
 // activation.hip: act = silu(h1) * h3 over rows [0, P) (backward recompute)
 hipError_t launch_recompute_act(const Shape& s, const void* h1, const void* h3,
                                 const MetaPtrs& m, void* act, hipStream_t stream);

@@ -12,7 +12,8 @@
 //
 // Three launches, stream-ordered, no host synchronisation:
 //   meta_hist   one wave per chunk of entries: expert histogram of the chunk
-//               (LDS counters) and an invalid-id flag.
+//               (LDS counters) and an invalid-id flag (-1 is no error: an
+//               empty slot, routed nowhere).
 //   meta_scan   one workgroup: per-expert totals, bins / padded_bins / P,
 //               each chunk's starting sorted position per expert, the
 //               block -> expert table, the pairs of row blocks that the
@@ -53,7 +54,7 @@ meta_hist_kernel(const int32_t* __restrict__ ids, int64_t n, int64_t chunk,
       const int e = ids[a];
       if (e >= 0 && e < E)
         atomicAdd(&cnt[w][e], 1);   // integer count: order does not matter
-      else
+      else if (e != -1)             // -1: an empty slot, routed nowhere
         bad = 1;
     }
   }
@@ -69,7 +70,8 @@ meta_hist_kernel(const int32_t* __restrict__ ids, int64_t n, int64_t chunk,
 // seg-th range of chunks; Ecap (a power of two >= E) experts x S segments.
 __global__ void __launch_bounds__(kScanThreads)
 meta_scan_kernel(int32_t* __restrict__ hist, const int32_t* __restrict__ err,
-                 int nchunks, int E, int Ecap, int max_tiles,
+                 int nchunks, int E, int Ecap, int max_tiles, int64_t n,
+                 int32_t* __restrict__ indices, int32_t* __restrict__ bin_ids,
                  int32_t* __restrict__ tokens_per_expert,
                  int32_t* __restrict__ bins, int32_t* __restrict__ padded_bins,
                  int32_t* __restrict__ tile_expert,
@@ -86,7 +88,7 @@ meta_scan_kernel(int32_t* __restrict__ hist, const int32_t* __restrict__ err,
   __shared__ int32_t start_s[kMaxExperts];
   __shared__ int32_t pend_s[kMaxExperts];
   __shared__ int32_t pair_s[kMaxExperts];   // first group of each expert
-  __shared__ int32_t P_s, S_s, bad_s;
+  __shared__ int32_t P_s, S_s, bad_s, N_s;
   const int tid = threadIdx.x;
   const int S = kScanThreads / Ecap;
   const int e = tid % Ecap, seg = tid / Ecap;
@@ -161,6 +163,7 @@ meta_scan_kernel(int32_t* __restrict__ hist, const int32_t* __restrict__ err,
     if (tid == kWave - 1) {
       P_s = pi;
       S_s = gi;
+      N_s = ci;
       *num_padded_rows = pi;
       *num_pairs = gi;
     }
@@ -216,6 +219,12 @@ meta_scan_kernel(int32_t* __restrict__ hist, const int32_t* __restrict__ err,
     if (i < pc - c) row_token[pend_s[ee] - pc + c + i] = -1;
   }
   if (tid == 0) *status = bad_s ? kErrExpertId : 0;
+  // The sorted arrays list the routed entries only: past their total (less
+  // than n when some slots are empty or invalid) they hold -1.
+  for (int64_t i = N_s + (int64_t)tid; i < n; i += kScanThreads) {
+    indices[i] = -1;
+    bin_ids[i] = -1;
+  }
 
   // The experts whose weight-gradient tiles each XCD computes: 8 contiguous
   // ranges with the least possible largest cost.  A tile of those products
@@ -373,7 +382,7 @@ hipError_t launch_metadata(int64_t n, int E, int k, int64_t max_tiles,
                      stream, ids, n, chunk, nchunks, E, hist, err);
   if (ev && ev[1] && (rc = hipEventRecord(ev[1], stream)) != hipSuccess) return rc;
   hipLaunchKernelGGL(meta_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream,
-                     hist, err, nchunks, E, Ecap, (int)max_tiles,
+                     hist, err, nchunks, E, Ecap, (int)max_tiles, n, m.indices, m.bin_ids,
                      m.tokens_per_expert, m.bins, m.padded_bins, m.tile_expert,
                      m.num_padded_rows, m.status, m.pair_first, m.num_pairs, m.row_token,
                      m.xcd_first);

@@ -76,7 +76,7 @@ padded_gather_kernel(const T* __restrict__ x, int64_t ntok, int64_t H, int k, in
     }
     for (int j = 0; j < k; ++j) {
       const int row = rows[j];
-      if (row < 0) continue;     // an invalid expert id: no row
+      if (row < 0) continue;     // an empty slot (or an invalid id): no row
       char* dst = out + (int64_t)row * rowb;
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
@@ -176,7 +176,10 @@ scatter_backward_kernel(const T* __restrict__ dy, const T* __restrict__ y_perm,
     return;
   }
   const int row = row_of_entry[a];
-  if (row < 0) return;           // an invalid expert id: no row
+  if (row < 0) {                 // an empty slot (or an invalid id): no row
+    if (lane == 0) d_weights[a] = 0.f;
+    return;
+  }
   const char* g = reinterpret_cast<const char*>(dy) + (a / k) * rowb;
   const char* yp = reinterpret_cast<const char*>(y_perm) + (int64_t)row * rowb;
   char* dst = out + (int64_t)row * rowb;

@@ -29,6 +29,12 @@
  *   dtype.  w1, w3, dw1, dw3: [E,H,F].  w2, dw2: [E,F,H].  The floating
  *   arrays other than weights/d_weights are all of `dims->dtype`.
  * - Entry numbering.  Entry a = t*k + j is slot j of token t.
+ * - Empty slots.  An expert id of -1 is an empty slot: the entry is routed
+ *   nowhere (row_of_entry = -1, no padded row), adds nothing to y or dx and
+ *   gets d_weights = 0, so a token may use fewer than k experts (for
+ *   instance after dmoe_token_round).  The sorted arrays (indices, bin_ids)
+ *   list the routed entries only and hold -1 past them, and bins[E-1] is
+ *   their number.
  * - Padded rows.  P = padded_bins[E-1] is known only on the device
  *   (meta.num_padded_rows).  Buffers with padded rows are sized for
  *   P_max = 128 * dmoe_max_tiles(dims) rows.  Rows in [P, P_max) are left
@@ -42,7 +48,8 @@
  *   reproducible run to run.
  * - Errors.  Argument and shape errors are detected on the host before any
  *   launch and returned as a negative dmoe_status; nothing is enqueued then.
- *   An expert id outside [0,E) is a data error found on the device:
+ *   An expert id outside [0,E) other than -1 is a data error found on the
+ *   device:
  *   dmoe_metadata stores DMOE_ERR_EXPERT_ID in meta.status (0 otherwise),
  *   the offending entries get row_of_entry = -1 and contribute nothing;
  *   other outputs are then unspecified.  The caller reads meta.status after
@@ -90,7 +97,8 @@ typedef struct {
  *   tokens_per_expert[E]  int32, histogram of the expert ids
  *   bins[E]               int32, inclusive cumsum of tokens_per_expert
  *   padded_bins[E]        int32, inclusive cumsum of round_up(tokens_per_expert, 128)
- *   indices[T*k]          int32, stable sort of the entries by expert: indices[s] = a
+ *   indices[T*k]          int32, stable sort of the routed entries by expert:
+ *                         indices[s] = a; -1 past the routed entries
  *   bin_ids[T*k]          int32, expert of the s-th sorted entry
  *   row_of_entry[T*k]     int32, padded row of entry a:
  *                         (s - bins[e-1]) + padded_bins[e-1], both starts 0 at e=0
@@ -301,6 +309,29 @@ int dmoe_router_backward(const dmoe_dims* dims, const float* logits,
                          const int32_t* top_experts, const float* weights,
                          const float* d_weights, float zloss_coef, float* d_logits,
                          hipStream_t stream);
+
+/* Tile-aware token rounding of the router's choice ("SonicMoE: Accelerating
+ * MoE with IO and Tile-aware Optimizations", abstract: round each expert's
+ * token count to the grouped GEMM's tile instead of padding it).  The page
+ * gives no rule; this one is taken: each token is routed to its k largest
+ * logits (the order of dmoe_router_forward) and its (k+1)-th largest is
+ * its candidate; an expert with c routed tokens and r = c mod tile_rows > 0
+ * takes its tile_rows - r best candidates (largest logit, then lower token
+ * id) when tile_rows - r < r and it has that many, and otherwise drops its
+ * r worst routed tokens (smallest logit, then higher token id).
+ *   logits [T,E] fp32, finite; dims->k = k routed slots, 1 <= k < E.
+ *   top_experts [T,k+1] int32: slot j < k the j-th routed expert or -1 when
+ *     dropped; slot k the candidate when taken, else -1.
+ *   weights [T,k+1] fp32: the softmax over the logits of the occupied slots,
+ *     0 in empty slots (all 0 for a token left with no expert).
+ *   ws: dmoe_token_round_workspace_bytes(dims) bytes of scratch.
+ * Every expert then has a multiple of tile_rows tokens; with tile_rows =
+ * 128 the layer called on these slots (dims->k = k + 1) computes no pad
+ * rows.  Bit-reproducible.  DMOE_ERR_ARG for k >= E, tile_rows < 1, null
+ * pointers, or T*(k+1) at 2^31 or more. */
+int64_t dmoe_token_round_workspace_bytes(const dmoe_dims* dims);
+int dmoe_token_round(const dmoe_dims* dims, const float* logits, int32_t tile_rows,
+                     int32_t* top_experts, float* weights, void* ws, hipStream_t stream);
 
 /* The metadata, forward and backward calls with per-kernel timing.  `events`
  * is NULL or an array of n+1 hipEvent_t; event i is recorded on `stream`

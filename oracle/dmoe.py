@@ -34,6 +34,10 @@ Readings where the pages are silent or garbled (each is used below):
 * R6: the sort is stable: ties keep ascending ``a``.
 * R7: ``round_up(0) = 0``: an empty expert gets no rows and no tile.
 * R9: the top-k reduction is a plain sum over j (the oracle does not round).
+* R26: an expert id of -1 is an empty slot: the entry is routed nowhere,
+  gets no padded row (row_of_entry = -1), adds nothing to y or dx and has a
+  routing-weight gradient of 0.  The sorted arrays list the routed entries
+  only and hold -1 past them.  Token rounding leaves such slots.
 * w1, w3 are stored ``[E,H,F]`` and w2 ``[E,F,H]``.
 
 Pins (tests/test_oracle_*.py): hand-derived metadata fixtures, a pure-Python
@@ -96,20 +100,25 @@ def metadata(top_experts, num_experts: int, n_tiles: Optional[int] = None
     """
     ids = np.asarray(top_experts).reshape(-1).astype(np.int64)
     E = int(num_experts)
-    if ids.size and (ids.min() < 0 or ids.max() >= E):
+    if ids.size and (ids.min() < -1 or ids.max() >= E):
         raise ValueError("expert id out of range")
     n = ids.size
-    counts = np.bincount(ids, minlength=E).astype(np.int64)
-    indices = np.argsort(ids, kind="stable").astype(np.int64)   # R6
-    bin_ids = ids[indices]
+    routed = np.nonzero(ids >= 0)[0]        # R26: -1 is an empty slot
+    nv = routed.size
+    counts = np.bincount(ids[routed], minlength=E).astype(np.int64)
+    order = routed[np.argsort(ids[routed], kind="stable")]      # R6
+    indices = np.full(n, -1, dtype=np.int64)
+    indices[:nv] = order
+    bin_ids = np.full(n, -1, dtype=np.int64)
+    bin_ids[:nv] = ids[order]
     bins = np.cumsum(counts)
     padded = round_up(counts)
     padded_bins = np.cumsum(padded)
     bins_start = bins - counts              # R1: exclusive starts
     padded_start = padded_bins - padded
-    s = np.arange(n, dtype=np.int64)
-    row_of_entry = np.empty(n, dtype=np.int64)
-    row_of_entry[indices] = padded_start[bin_ids] + (s - bins_start[bin_ids])
+    s = np.arange(nv, dtype=np.int64)
+    row_of_entry = np.full(n, -1, dtype=np.int64)
+    row_of_entry[order] = padded_start[ids[order]] + (s - bins_start[ids[order]])
     P = int(padded_bins[-1]) if E else 0
     if n_tiles is None:
         n_tiles = P // BLOCK
@@ -132,7 +141,8 @@ def metadata_counting_sort(top_experts, num_experts: int,
     E = int(num_experts)
     counts = [0] * E
     for e in ids:
-        counts[e] += 1
+        if e >= 0:
+            counts[e] += 1
     bins, padded_bins = [], []
     run = prun = 0
     for e in range(E):
@@ -144,10 +154,12 @@ def metadata_counting_sort(top_experts, num_experts: int,
     pstart = [padded_bins[e] - ((counts[e] + BLOCK - 1) // BLOCK) * BLOCK
               for e in range(E)]
     fill = [0] * E
-    indices = [0] * len(ids)
-    bin_ids = [0] * len(ids)
-    row_of_entry = [0] * len(ids)
+    indices = [-1] * len(ids)
+    bin_ids = [-1] * len(ids)
+    row_of_entry = [-1] * len(ids)
     for a, e in enumerate(ids):
+        if e == -1:                          # R26: an empty slot
+            continue
         s = start[e] + fill[e]
         indices[s] = a
         bin_ids[s] = e
@@ -182,8 +194,8 @@ def padded_gather(x, md, k: int) -> np.ndarray:
     """
     x = _f64(x)
     out = np.zeros((md["P"], x.shape[1]), dtype=np.float64)
-    a = np.arange(md["row_of_entry"].size)
-    out[md["row_of_entry"]] = x[a // k]
+    a = np.nonzero(md["row_of_entry"] >= 0)[0]          # routed entries (R26)
+    out[md["row_of_entry"][a]] = x[a // k]
     return out
 
 
@@ -197,8 +209,8 @@ def row_token(md, k: int) -> np.ndarray:
     straight from x.  Length P.
     """
     out = np.full(md["P"], -1, dtype=np.int64)
-    a = np.arange(md["row_of_entry"].size)
-    out[md["row_of_entry"]] = a // k
+    a = np.nonzero(md["row_of_entry"] >= 0)[0]          # routed entries (R26)
+    out[md["row_of_entry"][a]] = a // k
     return out
 
 
@@ -208,7 +220,10 @@ def padded_scatter(y_perm, md, weights, T: int, k: int) -> np.ndarray:
     over the k slots of a token."""
     y_perm = _f64(y_perm)
     w = _f64(weights).reshape(-1)
-    rows = y_perm[md["row_of_entry"]] * w[:, None]        # entry a's term
+    roe = md["row_of_entry"]
+    rows = np.zeros((roe.size, y_perm.shape[1]))
+    a = np.nonzero(roe >= 0)[0]                          # an empty slot adds 0 (R26)
+    rows[a] = y_perm[roe[a]] * w[a, None]                 # entry a's term
     return rows.reshape(T, k, -1).sum(axis=1)
 
 
@@ -245,6 +260,8 @@ def forward_loop(x, top_experts, weights, w1, w3, w2):
     for t in range(T):
         for j in range(k):
             e = int(ids[t, j])
+            if e < 0:                        # R26: an empty slot
+                continue
             u1 = x[t] @ _f64(w1[e])
             u3 = x[t] @ _f64(w3[e])
             act = silu(u1) * u3
@@ -274,6 +291,8 @@ def backward_loop(x, top_experts, weights, w1, w3, w2, dy):
     for t in range(T):
         for j in range(k):
             e = int(ids[t, j])
+            if e < 0:                        # R26: an empty slot
+                continue
             W1, W3, W2 = _f64(w1[e]), _f64(w3[e]), _f64(w2[e])
             u1 = x[t] @ W1
             u3 = x[t] @ W3
@@ -374,12 +393,13 @@ def backward_padded(x, top_experts, weights, w1, w3, w2, dy, saved=None):
     dy = _f64(dy)
     P, H = md["P"], dy.shape[1]
     F = np.shape(w1)[2]
-    a = np.arange(T * k)
     rows = md["row_of_entry"]
+    a = np.nonzero(rows >= 0)[0]             # routed entries (R26)
     dyp = np.zeros((P, H))
-    dyp[rows] = dy[a // k] * w[:, None]
-    d_weights = np.einsum("ah,ah->a", dy[a // k], saved["y_perm"][rows]
-                          ).reshape(T, k)
+    dyp[rows[a]] = dy[a // k] * w[a, None]
+    d_weights = np.zeros(T * k)
+    d_weights[a] = np.einsum("ah,ah->a", dy[a // k], saved["y_perm"][rows[a]])
+    d_weights = d_weights.reshape(T, k)
     dh1, dh3, dxp = np.zeros((P, F)), np.zeros((P, F)), np.zeros((P, H))
     dw1 = np.zeros(np.shape(w1))
     dw3 = np.zeros(np.shape(w3))
@@ -393,7 +413,9 @@ def backward_padded(x, top_experts, weights, w1, w3, w2, dy, saved=None):
                              _f64(w1[e]), _f64(w3[e]), _f64(w2[e]))
         dh1[r0:r1], dh3[r0:r1], dxp[r0:r1] = g["dh1"], g["dh3"], g["dx_perm"]
         dw1[e], dw3[e], dw2[e] = g["dw1"], g["dw3"], g["dw2"]
-    dx = dxp[rows].reshape(T, k, H).sum(axis=1)
+    terms = np.zeros((T * k, H))
+    terms[a] = dxp[rows[a]]
+    dx = terms.reshape(T, k, H).sum(axis=1)
     return dict(dx=dx, dw1=dw1, dw3=dw3, dw2=dw2, d_weights=d_weights,
                 dy_perm=dyp, dh1=dh1, dh3=dh3, dx_perm=dxp)
 
@@ -465,7 +487,8 @@ def sampled_rows(x, top_experts, weights, w1, w3, w2, dy,
     by_expert: Dict[int, list] = {}
     for t in tokens:
         for j in range(k):
-            by_expert.setdefault(int(ids[t, j]), []).append((t, j))
+            if int(ids[t, j]) >= 0:          # R26: an empty slot adds nothing
+                by_expert.setdefault(int(ids[t, j]), []).append((t, j))
     for e, ents in sorted(by_expert.items()):
         W1, W3, W2 = _f64(w1[e]), _f64(w3[e]), _f64(w2[e])
         for t, j in ents:

@@ -241,3 +241,42 @@ def test_layer_by_expert_equals_padded_pipeline(T, H, F, E, k, distinct):
     np.testing.assert_allclose(out["y"], y, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(out["dx"], g["dx"], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(out["d_weights"], g["d_weights"], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("impl", ["loop", "padded", "by_expert"])
+def test_empty_slot_is_a_zero_weight_entry(impl):
+    """An empty slot (expert id -1) adds to y, dx, dw1, dw3 and dw2 exactly
+    what an entry of routing weight 0 adds, i.e. nothing, and its
+    routing-weight gradient is 0; the other slots' gradients are unchanged."""
+    rng = np.random.default_rng(21)
+    T, H, F, E, k = 40, 6, 5, 4, 3
+    L = _rand_layer(rng, T, H, F, E, k)
+    dy = rng.standard_normal((T, H))
+    empty = rng.random((T, k)) < 0.35
+    Lz = dict(L, weights=np.where(empty, 0.0, L["weights"]))
+    Le = dict(L, top_experts=np.where(empty, -1, L["top_experts"]).astype(np.int32))
+
+    def run(layer):
+        if impl == "loop":
+            y, _ = oracle.forward_loop(**layer)
+            return y, oracle.backward_loop(**layer, dy=dy)
+        if impl == "padded":
+            y, sv = oracle.forward_padded(**layer)
+            return y, oracle.backward_padded(**layer, dy=dy, saved=sv)
+        out = dict(y=np.zeros((T, H)), dx=np.zeros((T, H)), d_weights=np.zeros((T, k)))
+        g = {key: np.zeros(np.shape(layer[w])) for key, w in
+             (("dw1", "w1"), ("dw3", "w3"), ("dw2", "w2"))}
+        for r in oracle.layer_by_expert(**layer, dy=dy, out=out):
+            for key in g:
+                g[key][r["e"]] = r[key]
+        g.update(dx=out["dx"], d_weights=out["d_weights"])
+        return out["y"], g
+
+    yz, gz = run(Lz)
+    ye, ge = run(Le)
+    np.testing.assert_allclose(ye, yz, rtol=1e-12, atol=1e-13)
+    for key in ("dx", "dw1", "dw3", "dw2"):
+        np.testing.assert_allclose(ge[key], gz[key], rtol=1e-12, atol=1e-13, err_msg=key)
+    assert np.all(ge["d_weights"][empty] == 0.0)
+    np.testing.assert_allclose(ge["d_weights"][~empty], gz["d_weights"][~empty],
+                               rtol=1e-12, atol=1e-13)

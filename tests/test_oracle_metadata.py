@@ -114,6 +114,40 @@ def test_duplicate_ids_in_one_token_are_separate_entries():
 def test_out_of_range_id_rejected():
     with pytest.raises(ValueError):
         oracle.metadata(np.array([[3]]), 3)
+    with pytest.raises(ValueError):
+        oracle.metadata(np.array([[-2]]), 3)
+
+
+@pytest.mark.parametrize("T,k,E,seed", [(1, 1, 1, 0), (50, 3, 4, 1), (300, 8, 16, 2),
+                                        (129, 2, 3, 3)])
+def test_empty_slots(T, k, E, seed):
+    """Slots holding -1 are routed nowhere: the routed entries alone give
+    the same metadata as a layer without those slots, the sorted arrays end
+    in -1, and the counting sort agrees."""
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(0, E, (T, k)).astype(np.int32)
+    ids[rng.random((T, k)) < 0.3] = -1
+    if seed == 0:
+        ids[:] = -1                          # nothing routed at all
+    nt = oracle.max_tiles(T, k, E)
+    a = oracle.metadata(ids, E, nt)
+    b = oracle.metadata_counting_sort(ids, E, nt)
+    for key in KEYS:
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+    flat = ids.reshape(-1)
+    routed = np.nonzero(flat >= 0)[0]
+    nv = routed.size
+    assert a["bins"][-1] == nv
+    np.testing.assert_array_equal(np.sort(a["indices"][:nv]), routed)
+    assert np.all(a["indices"][nv:] == -1) and np.all(a["bin_ids"][nv:] == -1)
+    assert np.array_equal(a["row_of_entry"] < 0, flat < 0)
+    # the routed entries alone, as a one-slot layer of nv "tokens" in order
+    c = oracle.metadata(flat[routed].reshape(nv, 1), E, nt)
+    for key in ("tokens_per_expert", "bins", "padded_bins", "tile_expert"):
+        np.testing.assert_array_equal(a[key], c[key], err_msg=key)
+    np.testing.assert_array_equal(a["row_of_entry"][routed], c["row_of_entry"])
+    np.testing.assert_array_equal(a["indices"][:nv], routed[c["indices"][:nv]])
+    assert a["P"] == c["P"]
 
 
 @pytest.mark.parametrize("k", [1, 2, 3, 8])
