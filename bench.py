@@ -475,6 +475,65 @@ def other_workload(dm, name, dev, args, ovh):
     return rec
 
 
+def token_rounding(dm, name, dev, args, ovh, topk_ms):
+    """The layer's step on tile-aware token-rounded routing against top-k
+    on the same logits: the rounding's own time, the padded rows, and the
+    step.  topk_ms: the top-k step of this workload, if measured here."""
+    import dataclasses
+    import numpy as np
+    import torch
+    from workloads import CONFIGS, make_inputs, make_logits
+    cfg = CONFIGS[name]
+    logits, _ = make_logits(cfg)
+    D = dm.Dims(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, dm.DMOE_F32)
+    l = torch.from_numpy(logits).to(dev)
+    ids = torch.empty(cfg.T, cfg.k + 1, dtype=torch.int32, device=dev)
+    w = torch.empty(cfg.T, cfg.k + 1, dtype=torch.float32, device=dev)
+    ws = torch.empty(dm.dmoe_token_round_workspace_bytes(D), dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        dm.dmoe_token_round(D, l, ids, w, ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dm.dmoe_token_round(D, l, ids, w, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    round_us = e0.elapsed_time(e1) * 1e3 / 10
+    inp = make_inputs(cfg)
+    rcfg = cfg.replace(k=cfg.k + 1)
+    inp = dataclasses.replace(inp, cfg=rcfg, top_experts=ids.cpu().numpy(),
+                              weights=w.cpu().numpy())
+    L = Layer(dm, rcfg, dev, gather=args.gather, inputs=inp)
+    for _ in range(3):
+        L.step()
+    P = L.padded_rows()
+    ms, _ = L.timed(10)
+    if topk_ms is None:
+        T = Layer(dm, cfg, dev, gather=args.gather, inputs=make_inputs(cfg))
+        for _ in range(3):
+            T.step()
+        topk_P = T.padded_rows()
+        topk_ms, _ = T.timed(10)
+        T.close()
+    else:
+        topk_P = None
+    occupied = int((L.ids >= 0).sum().item())
+    L.close()
+    rec = {"workload": name, "tile_rows": 128, "round_us": round(round_us, 1),
+           "entries": occupied, "entries_topk": cfg.T * cfg.k, "P": P,
+           "ms_per_step": round(ms, 4), "tokens_s": round(cfg.T / (ms * 1e-3), 1),
+           "topk_ms_per_step": round(topk_ms, 4),
+           "speedup_vs_topk": round(topk_ms / ms, 3),
+           "note": ("metadata + forward + backward on the token-rounded slots (k + 1 per token, "
+                    "empty slots -1), against the same step on top-k routing; the rounding's "
+                    "own time (router top-(k+1), metadata of the k + 1 slots, selection) is "
+                    "round_us, outside the step like the router's")}
+    if topk_P is not None:
+        rec["P_topk"] = topk_P
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -484,6 +543,9 @@ def main():
     ap.add_argument("--workloads", default="zipf_e64,coarse_e8,sparse_e256,tiny_f32",
                     help="comma-separated other workloads reported under 'workloads' "
                          "(10 steps each), or 'none'")
+    ap.add_argument("--rounding", default="sparse_e256",
+                    help="workload on which to time the layer on tile-aware token-rounded "
+                         "routing against top-k, or 'none'")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-lean", action="store_true",
                     help="skip the step with the activation-lean backward")
@@ -622,6 +684,15 @@ def main():
     others = [n for n in args.workloads.split(",") if n and n != "none" and n != cfg.name]
     if others:
         out["workloads"] = {n: other_workload(dm, n, dev, args, ovh) for n in others}
+    if args.rounding != "none":
+        print(f"bench: token rounding on {args.rounding}", file=sys.stderr, flush=True)
+        known = (out.get("workloads", {}).get(args.rounding, {}).get("ms_per_step")
+                 if args.rounding != cfg.name else ms)
+        out["token_rounding"] = token_rounding(dm, args.rounding, dev, args, ovh, known)
+        if known is not None:
+            P_topk = (P if args.rounding == cfg.name
+                      else out["workloads"][args.rounding]["config"]["P"])
+            out["token_rounding"]["P_topk"] = P_topk
     if not args.no_cpu:
         print("bench: CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp)
