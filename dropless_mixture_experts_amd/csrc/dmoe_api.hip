@@ -76,8 +76,7 @@ MetaPtrs meta_ptrs(const dmoe_meta* m, int64_t max_tiles) {
   int32_t* sched = static_cast<int32_t*>(m->schedule);
   return MetaPtrs{m->tokens_per_expert, m->bins, m->padded_bins, m->indices,
                   m->bin_ids, m->row_of_entry, m->tile_expert, m->num_padded_rows,
-                  m->status, sched, sched + max_tiles, m->row_token,
-                  sched + max_tiles + 1};
+                  m->status, sched, sched + max_tiles, m->row_token};
 }
 
 MetaPtrs meta_ptrs(const dmoe_meta* m, const dmoe_dims* d) { return meta_ptrs(m, max_tiles_of(d)); }

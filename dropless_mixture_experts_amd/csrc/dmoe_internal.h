@@ -9,7 +9,7 @@ namespace dmoe {
 constexpr int kMaxExperts = 256;
 constexpr int kErrExpertId = -5;   // matches DMOE_ERR_EXPERT_ID
 
-// The metadata arrays, and the three tables of the opaque schedule buffer
+// The metadata arrays, and the two tables of the opaque schedule buffer
 // (dmoe_meta.schedule), which holds, as int32:
 //   [0, max_tiles)              pair_first: group s of row blocks starts at
 //                               block pair_first[s] and also takes the next
@@ -17,23 +17,17 @@ constexpr int kErrExpertId = -5;   // matches DMOE_ERR_EXPERT_ID
 //                               (each expert's blocks paired in order, an
 //                               odd last one single); -1 past the last group
 //   [max_tiles]                 num_pairs: the number of groups
-//   [max_tiles + 1, + 10)       xcd_first[9]: the experts whose weight-
-//                               gradient tiles XCD x computes are
-//                               [xcd_first[x], xcd_first[x + 1])
 struct MetaPtrs {
   int32_t *tokens_per_expert, *bins, *padded_bins;
   int32_t *indices, *bin_ids, *row_of_entry;
   int32_t *tile_expert, *num_padded_rows, *status;
   int32_t *pair_first, *num_pairs;
   int32_t *row_token;
-  int32_t *xcd_first;
 };
-
-constexpr int kXcdTable = 9;
 
 // Bytes of the schedule buffer for max_tiles 128-row blocks.
 inline int64_t schedule_bytes(int64_t max_tiles) {
-  return ((max_tiles + 1 + kXcdTable) * 4 + 255) / 256 * 256;
+  return ((max_tiles + 1) * 4 + 255) / 256 * 256;
 }
 
 struct Shape {

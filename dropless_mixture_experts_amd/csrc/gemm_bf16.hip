@@ -676,11 +676,36 @@ struct UpDgrad {
 };
 
 // Weight-gradient tiles have K = the expert's padded rows, so equal tile
-// counts are not equal work under skewed routing.  XCD x computes the
-// experts [xcd_first[x], xcd_first[x + 1]), contiguous ranges that the
-// metadata chose to minimise the largest cost (an expert's 128-row blocks
-// + 1, for the epilogue of each of its tiles); every expert stays within one
-// L2.
+// counts are not equal work under skewed routing.  Expert e costs its 128-row
+// blocks + 1 (its K steps plus an epilogue of about two K steps, in units of
+// two K steps), so that the experts before e cost pre(e) = padded_bins[e - 1]
+// / 128 + e and all of them W = pre(E).  The tiles of expert e are
+// consecutive in the tile order and share its cost equally; XCD x computes
+// the tiles whose cost lies in [x W / 8, (x + 1) W / 8), so every XCD gets
+// an eighth of the work up to one tile, and an expert may straddle two XCDs
+// (both then fetch its rows: one expert per boundary).  Every block of every
+// launch derives the same ranges from padded_bins.
+struct CostSplit {
+  const int32_t* padded_bins;
+  int E;
+  __device__ int pre(int e) const { return e == 0 ? 0 : padded_bins[e - 1] / kBlock + e; }
+  // the tile that holds cost position c, or E * tpe for c >= W
+  __device__ int tile_at(int64_t c, int tpe) const {
+    if (c >= pre(E)) return E * tpe;
+    int a = 0, z = E - 1;                 // the last expert with pre(e) <= c
+    while (a < z) {
+      const int mid = (a + z + 1) >> 1;
+      if (pre(mid) <= c) a = mid; else z = mid - 1;
+    }
+    const int p0 = pre(a);
+    return a * tpe + (int)((c - p0) * tpe / (pre(a + 1) - p0));
+  }
+  __device__ void range(int x, int tpe, int& lo, int& hi) const {
+    const int64_t W = pre(E);
+    lo = tile_at(x * W / 8, tpe);
+    hi = tile_at((x + 1) * W / 8, tpe);
+  }
+};
 
 // dw2[e] = act[rows_e]^T dy_perm[rows_e] ([F,H]); zero for an empty expert.
 // A = 256 (or 128) hidden columns of dy_perm (u = h0), B = 256 (or 128) ffn
@@ -693,7 +718,7 @@ struct WgradDown {
   const bf16 *act, *dy_perm;
   int64_t H, F;
   int E;
-  const int32_t *tpe, *padded_bins, *xcd_first;
+  const int32_t *tpe, *padded_bins;
   bf16* dw2;
   __device__ uint32_t lda() const { return (uint32_t)(H * 2); }
   __device__ uint32_t ldb() const { return (uint32_t)(F * 2); }
@@ -703,8 +728,7 @@ struct WgradDown {
   __device__ int tiles_per_expert() const { return nh() * nf(); }
   __device__ int expert_steps(int e) const { return round_up_block(tpe[e]) / kKStep; }
   __device__ void xcd_range(int x, int& lo, int& hi) const {
-    lo = xcd_first[x] * nh() * nf();
-    hi = xcd_first[x + 1] * nh() * nf();
+    CostSplit{padded_bins, E}.range(x, tiles_per_expert(), lo, hi);
   }
   __device__ void tile(int L, Job& j) const {
     // the tiles of one expert are consecutive: each XCD works on whole experts
@@ -751,7 +775,7 @@ struct WgradUp {
   const bf16 *x_perm, *dh1, *dh3;
   int64_t H, F;
   int E;
-  const int32_t *tpe, *padded_bins, *xcd_first;
+  const int32_t *tpe, *padded_bins;
   bf16 *dw1, *dw3;
   __device__ uint32_t lda() const { return (uint32_t)(F * 2); }
   __device__ uint32_t ldb() const { return (uint32_t)(H * 2); }
@@ -761,8 +785,7 @@ struct WgradUp {
   __device__ int tiles_per_expert() const { return nf() * nh(); }
   __device__ int expert_steps(int e) const { return round_up_block(tpe[e]) / kKStep; }
   __device__ void xcd_range(int x, int& lo, int& hi) const {
-    lo = xcd_first[x] * nf() * nh();
-    hi = xcd_first[x + 1] * nf() * nh();
+    CostSplit{padded_bins, E}.range(x, tiles_per_expert(), lo, hi);
   }
   __device__ void tile(int L, Job& j) const {
     const int NF = nf(), NH = nh();
@@ -1117,18 +1140,20 @@ struct DualSched {
   int rho;          // this block's place in the phase-B order
   int c1, cA, cB;   // this block's tiles of K1, of phase A, of phase B
 
-  // The longest prefix of K2's tiles from `lo` (an expert boundary) that,
-  // dealt round-robin over `nb` blocks, gives no block more than `gap` K
-  // steps: ceil(n / nb) tiles of at most the largest cost among them.
+  // The longest prefix of K2's tiles [lo, hi) that, dealt round-robin over
+  // `nb` blocks, gives no block more than `gap` K steps: ceil(n / nb) tiles
+  // of at most the largest cost among them.  lo and hi may fall inside an
+  // expert's tiles.
   __device__ static int prefix_tiles(const K2& k2, int lo, int hi, int nb, int gap) {
     const int tpe = k2.tiles_per_expert();
     int n = 0, cmax = 1;
     for (int e = lo / tpe; e * tpe < hi; ++e) {
+      const int avail = min(hi, (e + 1) * tpe) - max(lo, e * tpe);   // e's tiles in [lo, hi)
       cmax = max(cmax, k2.expert_steps(e) + K2::kEpiSteps);
       const int cap = (gap / cmax) * nb;   // tiles allowed at this cost
       if (cap <= n) break;
-      if (cap < n + tpe) return cap;
-      n += tpe;
+      if (cap < n + avail) return cap;
+      n += avail;
     }
     return n;
   }
@@ -1252,13 +1277,12 @@ __global__ void __launch_bounds__(kThreads)
 up_dgrad_fill_kernel(const bf16* __restrict__ dh1, const bf16* __restrict__ dh3,
                      const bf16* __restrict__ w1, const bf16* __restrict__ w3,
                      const bf16* __restrict__ x_perm, int64_t H, int64_t F, int E,
-                     ROW_TILE_ARGS, const int32_t* __restrict__ tpe,
-                     const int32_t* __restrict__ xcd_first, bf16* dx_perm,
+                     ROW_TILE_ARGS, const int32_t* __restrict__ tpe, bf16* dx_perm,
                      bf16* __restrict__ dw1, bf16* __restrict__ dw3) {
   UpDgrad k1{dh1, dh3, w1, w3, H, F, dx_perm};
   k1.rt.init(tile_expert, pair_first, num_pairs, padded_bins, (int)((H + 255) / 256));
   persistent_dual<kTailFill>(
-      k1, WgradUp{x_perm, dh1, dh3, H, F, E, tpe, padded_bins, xcd_first, dw1, dw3});
+      k1, WgradUp{x_perm, dh1, dh3, H, F, E, tpe, padded_bins, dw1, dw3});
 }
 
 // down dgrad + gate backward (dh1, dh3) and dw2 in one launch: both read
@@ -1267,24 +1291,21 @@ __global__ void __launch_bounds__(kThreads)
 down_dgrad_wgrad_down_kernel(const bf16* __restrict__ dy_perm, const bf16* __restrict__ w2,
                              const bf16* h1, const bf16* h3, const bf16* __restrict__ act,
                              int64_t H, int64_t F, int E, ROW_TILE_ARGS,
-                             const int32_t* __restrict__ tpe,
-                             const int32_t* __restrict__ xcd_first, bf16* dh1, bf16* dh3,
+                             const int32_t* __restrict__ tpe, bf16* dh1, bf16* dh3,
                              bf16* __restrict__ dw2) {
   DownDgrad k1{dy_perm, w2, h1, h3, H, F, dh1, dh3};
   k1.rt.init(tile_expert, pair_first, num_pairs, padded_bins, (int)((F + 255) / 256));
-  persistent_dual(k1, WgradDown{act, dy_perm, H, F, E, tpe, padded_bins, xcd_first, dw2});
+  persistent_dual(k1, WgradDown{act, dy_perm, H, F, E, tpe, padded_bins, dw2});
 }
 
 __global__ void __launch_bounds__(kThreads)
 wgrad_up_kernel(const bf16* __restrict__ dh1, const bf16* __restrict__ dh3,
                 const bf16* __restrict__ w1, const bf16* __restrict__ w3,
                 const bf16* __restrict__ x_perm, int64_t H, int64_t F, int E, ROW_TILE_ARGS,
-                const int32_t* __restrict__ tpe, const int32_t* __restrict__ xcd_first,
-                int filled, bf16* dx_perm, bf16* __restrict__ dw1, bf16* __restrict__ dw3) {
+                const int32_t* __restrict__ tpe, int filled, bf16* dx_perm, bf16* __restrict__ dw1, bf16* __restrict__ dw3) {
   UpDgrad k1{dh1, dh3, w1, w3, H, F, dx_perm};
   k1.rt.init(tile_expert, pair_first, num_pairs, padded_bins, (int)((H + 255) / 256));
-  persistent_dual<kRest>(k1, WgradUp{x_perm, dh1, dh3, H, F, E, tpe, padded_bins, xcd_first,
-                                     dw1, dw3},
+  persistent_dual<kRest>(k1, WgradUp{x_perm, dh1, dh3, H, F, E, tpe, padded_bins, dw1, dw3},
                          filled != 0);
 }
 
@@ -1372,8 +1393,8 @@ hipError_t launch_bf16_up_dgrad(const Shape& s, const void* dh1, const void* dh3
     hipLaunchKernelGGL(bfk::up_dgrad_fill_kernel, up_dgrad_grid(s), dim3(bfk::kThreads), 0,
                        stream, cb<bf16>(dh1), cb<bf16>(dh3), cb<bf16>(w1), cb<bf16>(w3),
                        cb<bf16>(x_perm), s.H, s.F, s.E, m.tile_expert, m.pair_first,
-                       m.num_pairs, m.padded_bins, m.tokens_per_expert,
-                       m.xcd_first, mb<bf16>(dx_perm), mb<bf16>(dw1), mb<bf16>(dw3));
+                       m.num_pairs, m.padded_bins, m.tokens_per_expert, mb<bf16>(dx_perm),
+                       mb<bf16>(dw1), mb<bf16>(dw3));
   } else {
     hipLaunchKernelGGL(bfk::up_dgrad_kernel, persistent_grid(cdiv(s.H, 256) * s.max_tiles),
                        dim3(bfk::kThreads), 0, stream, cb<bf16>(dh1), cb<bf16>(dh3),
@@ -1393,8 +1414,7 @@ hipError_t launch_bf16_down_dgrad_wgrad_down(const Shape& s, const void* dy_perm
                      dim3(bfk::kThreads), 0, stream, cb<bf16>(dy_perm), cb<bf16>(w2),
                      cb<bf16>(h1), cb<bf16>(h3), cb<bf16>(act), s.H, s.F, s.E,
                      m.tile_expert, m.pair_first, m.num_pairs, m.padded_bins,
-                     m.tokens_per_expert, m.xcd_first, mb<bf16>(dh1), mb<bf16>(dh3),
-                     mb<bf16>(dw2));
+                     m.tokens_per_expert, mb<bf16>(dh1), mb<bf16>(dh3), mb<bf16>(dw2));
   return hipGetLastError();
 }
 
@@ -1405,7 +1425,7 @@ hipError_t launch_bf16_wgrad_up(const Shape& s, const void* dh1, const void* dh3
   hipLaunchKernelGGL(bfk::wgrad_up_kernel, up_dgrad_grid(s), dim3(bfk::kThreads), 0, stream,
                      cb<bf16>(dh1), cb<bf16>(dh3), cb<bf16>(w1), cb<bf16>(w3),
                      cb<bf16>(x_perm), s.H, s.F, s.E, m.tile_expert, m.pair_first,
-                     m.num_pairs, m.padded_bins, m.tokens_per_expert, m.xcd_first,
+                     m.num_pairs, m.padded_bins, m.tokens_per_expert,
                      up_dgrad_fills_tail(s) ? 1 : 0, mb<bf16>(dx_perm), mb<bf16>(dw1),
                      mb<bf16>(dw3));
   return hipGetLastError();

@@ -194,7 +194,7 @@ hipError_t launch_token_round(const Shape& s, const float* logits, int M, int32_
   int32_t* active = i32(2);
   int32_t* sched = i32(13);
   const MetaPtrs m{i32(3), i32(4), i32(5), i32(6), i32(7), i32(8), i32(9), i32(10), i32(11),
-                   sched, sched + L.mt, i32(12), sched + L.mt + 1};
+                   sched, sched + L.mt, i32(12)};
   Shape s1 = s;
   s1.k = s.k + 1;
   hipError_t err = launch_router_forward(s1, logits, 0.0f, ids1, w1, nullptr, nullptr, stream);

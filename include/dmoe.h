@@ -156,7 +156,7 @@ int64_t dmoe_max_tiles(const dmoe_dims* dims);
  * Returns a negative dmoe_status on bad dims. */
 int64_t dmoe_workspace_bytes(const dmoe_dims* dims);
 
-/* Bytes of dmoe_meta.schedule for these dims (a few KB: 4 * (max_tiles + 10)
+/* Bytes of dmoe_meta.schedule for these dims (a few KB: 4 * (max_tiles + 1)
  * rounded up to 256).  Returns a negative dmoe_status on bad dims. */
 int64_t dmoe_schedule_bytes(const dmoe_dims* dims);
 

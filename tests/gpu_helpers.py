@@ -27,11 +27,10 @@ def dims_of(cfg):
 
 def schedule_tables(meta, max_tiles):
     """The tables the library keeps in the opaque meta.schedule buffer, in
-    its private layout (int32: pair_first[max_tiles], num_pairs, then
-    xcd_first[9]); for tests of that schedule only."""
+    its private layout (int32: pair_first[max_tiles], then num_pairs); for
+    tests of that schedule only."""
     s = meta.schedule.view(torch.int32).cpu().numpy().astype(np.int64)
-    return dict(pair_first=s[:max_tiles], num_pairs=int(s[max_tiles]),
-                xcd_first=s[max_tiles + 1:max_tiles + 10])
+    return dict(pair_first=s[:max_tiles], num_pairs=int(s[max_tiles]))
 
 
 def up(a, dt, dev):
