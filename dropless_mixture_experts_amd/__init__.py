@@ -177,11 +177,36 @@ class Dims:
         return _TORCH[self.dtype]
 
     def _c(self) -> _Dims:
-        return _Dims(self.T, self.H, self.F, self.E, self.k, self.dtype)
+        return _dims_struct(self)
+
+
+@functools.lru_cache(maxsize=256)
+def _dims_struct(dims: "Dims") -> _Dims:
+    # the library only reads the struct, so one per dims serves every call
+    return _Dims(dims.T, dims.H, dims.F, dims.E, dims.k, dims.dtype)
+
+
+class _Buffers:
+    """Base of the buffer sets passed to the library (Meta, Saved,
+    GradScratch): their ctypes struct is built and validated once and kept
+    until a field is assigned.  The tensors themselves must not be resized
+    or re-pointed in place (resize_, set_) while the struct is in use."""
+
+    def __setattr__(self, name, value):
+        self.__dict__.pop("_struct", None)
+        self.__dict__.pop("_checked", None)
+        object.__setattr__(self, name, value)
+
+    def _cached(self, dt, build):
+        c = self.__dict__.get("_struct")
+        if c is None or c[0] != dt:
+            c = (dt, build())
+            self.__dict__["_struct"] = c
+        return c[1]
 
 
 @dataclasses.dataclass
-class Meta:
+class Meta(_Buffers):
     tokens_per_expert: torch.Tensor
     bins: torch.Tensor
     padded_bins: torch.Tensor
@@ -195,13 +220,13 @@ class Meta:
     schedule: torch.Tensor      # opaque: dmoe_schedule_bytes(dims) bytes
 
     def _c(self) -> _Meta:
-        return _Meta(*[_ptr(getattr(self, f.name),
-                            None if f.name == "schedule" else torch.int32, f.name)
-                       for f in dataclasses.fields(self)])
+        return self._cached(None, lambda: _Meta(*[
+            _ptr(getattr(self, f.name), None if f.name == "schedule" else torch.int32, f.name)
+            for f in dataclasses.fields(self)]))
 
 
 @dataclasses.dataclass
-class Saved:
+class Saved(_Buffers):
     x_perm: Optional[torch.Tensor]      # may be None for the fused-gather forward
     h1: torch.Tensor
     h3: torch.Tensor
@@ -209,20 +234,20 @@ class Saved:
     y_perm: torch.Tensor
 
     def _c(self, dt) -> _Saved:
-        return _Saved(*[_ptr(getattr(self, f.name), dt, f.name)
-                        for f in dataclasses.fields(self)])
+        return self._cached(dt, lambda: _Saved(*[
+            _ptr(getattr(self, f.name), dt, f.name) for f in dataclasses.fields(self)]))
 
 
 @dataclasses.dataclass
-class GradScratch:
+class GradScratch(_Buffers):
     dy_perm: torch.Tensor
     dh1: torch.Tensor
     dh3: torch.Tensor
     dx_perm: torch.Tensor
 
     def _c(self, dt) -> _Scratch:
-        return _Scratch(*[_ptr(getattr(self, f.name), dt, f.name)
-                          for f in dataclasses.fields(self)])
+        return self._cached(dt, lambda: _Scratch(*[
+            _ptr(getattr(self, f.name), dt, f.name) for f in dataclasses.fields(self)]))
 
 
 def _ptr(t: Optional[torch.Tensor], dtype: Optional[torch.dtype], name: str):
@@ -292,6 +317,9 @@ def dmoe_schedule_bytes(dims: Dims) -> int:
 
 
 def _check_meta(dims: Dims, meta: Meta):
+    # once per dims until a field of meta is assigned
+    if meta.__dict__.get("_checked") == dims:
+        return
     n = dims.T * dims.k
     nt, _, sb = _sizes(dims)
     for name, size in (("tokens_per_expert", dims.E), ("bins", dims.E),
@@ -304,6 +332,7 @@ def _check_meta(dims: Dims, meta: Meta):
     if s.numel() * s.element_size() < sb:
         raise ValueError(f"schedule: needs at least {sb} bytes, has "
                          f"{s.numel() * s.element_size()}")
+    meta.__dict__["_checked"] = dims
 
 
 def _ev(events, n):
