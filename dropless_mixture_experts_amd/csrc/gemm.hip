@@ -321,7 +321,7 @@ __device__ __forceinline__ void down_dgrad_tile(const float* __restrict__ dy_per
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float da = acc[i][j][r];
-        const float s = 1.0f / (1.0f + __expf(-g1[r]));
+        const float s = sigmoid(g1[r]);
         d3[r] = da * g1[r] * s;
         d1[r] = da * g3[r] * s * (1.0f + g1[r] * (1.0f - s));
       }

@@ -620,7 +620,7 @@ struct DownDgrad {
           f32x4 v1, v3;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float sg = 1.0f / (1.0f + __expf(-x1[r]));
+            const float sg = sigmoid(x1[r]);
             v3[r] = da[r] * x1[r] * sg;
             v1[r] = da[r] * x3[r] * sg * (1.0f + x1[r] * (1.0f - sg));
           }
