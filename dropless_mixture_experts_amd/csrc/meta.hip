@@ -10,12 +10,14 @@
 // token count and overflowed shared memory at 64 experts; here on-chip memory
 // is O(E) (at most ~5 KB at E = 256) whatever T is.
 //
-// Three launches, stream-ordered, no host synchronisation:
+// Four launches, stream-ordered, no host synchronisation:
 //   meta_hist   one wave per chunk of entries: expert histogram of the chunk
 //               (LDS counters) and an invalid-id flag (-1 is no error: an
 //               empty slot, routed nowhere).
-//   meta_scan   one workgroup: per-expert totals, bins / padded_bins / P,
-//               each chunk's starting sorted position per expert, the
+//   meta_count  kCountExperts experts per workgroup: each expert's total and
+//               each chunk's first position among that expert's entries
+//               (a scan over the chunks, independent per expert).
+//   meta_scan   one workgroup: bins / padded_bins / P from the totals, the
 //               block -> expert table, the pairs of row blocks that the
 //               matrix products process together, the status word.
 //   meta_place  one wave per chunk: stable rank of every entry among the
@@ -36,6 +38,7 @@ namespace dmoe {
 constexpr int kMetaWaves = 4;  // waves (chunks) per workgroup
 constexpr int kScanThreads = 1024;
 constexpr int kScanBatch = 8;   // chunk counts a scan thread loads at once
+constexpr int kCountExperts = 8;  // experts per meta_count workgroup
 
 __global__ void __launch_bounds__(kMetaWaves * kWave)
 meta_hist_kernel(const int32_t* __restrict__ ids, int64_t n, int64_t chunk,
@@ -66,35 +69,24 @@ meta_hist_kernel(const int32_t* __restrict__ ids, int64_t n, int64_t chunk,
   }
 }
 
-// One workgroup of 1024 threads.  Thread (e, seg) owns expert e over the
-// seg-th range of chunks; Ecap (a power of two >= E) experts x S segments.
+// kCountExperts experts per workgroup of 1024 threads: thread (el, seg)
+// owns expert e = kCountExperts * blockIdx.x + el over the seg-th of S =
+// 1024 / kCountExperts ranges of chunks.  It sums its range, the workgroup
+// scans the S range sums of each expert (Hillis-Steele in LDS), and the
+// thread writes each chunk's first position among expert e's entries over
+// the chunk's count in hist; the last range writes the expert's total.
 __global__ void __launch_bounds__(kScanThreads)
-meta_scan_kernel(int32_t* __restrict__ hist, const int32_t* __restrict__ err,
-                 int nchunks, int E, int Ecap, int max_tiles, int64_t n,
-                 int32_t* __restrict__ indices, int32_t* __restrict__ bin_ids,
-                 int32_t* __restrict__ tokens_per_expert,
-                 int32_t* __restrict__ bins, int32_t* __restrict__ padded_bins,
-                 int32_t* __restrict__ tile_expert,
-                 int32_t* __restrict__ num_padded_rows,
-                 int32_t* __restrict__ status,
-                 int32_t* __restrict__ pair_first,
-                 int32_t* __restrict__ num_pairs,
-                 int32_t* __restrict__ row_token) {
+meta_count_kernel(int32_t* __restrict__ hist, int nchunks, int E,
+                  int32_t* __restrict__ tokens_per_expert) {
   __shared__ int32_t seg_tot[kScanThreads];
-  __shared__ int32_t count_s[kMaxExperts];
-  __shared__ int32_t start_s[kMaxExperts];
-  __shared__ int32_t pend_s[kMaxExperts];
-  __shared__ int32_t pair_s[kMaxExperts];   // first group of each expert
-  __shared__ int32_t P_s, S_s, bad_s, N_s;
+  constexpr int S = kScanThreads / kCountExperts;
   const int tid = threadIdx.x;
-  const int S = kScanThreads / Ecap;
-  const int e = tid % Ecap, seg = tid / Ecap;
+  const int el = tid % kCountExperts, seg = tid / kCountExperts;
+  const int e = blockIdx.x * kCountExperts + el;
   const int seg_len = (nchunks + S - 1) / S;
   const int c0 = min(nchunks, seg * seg_len);
   const int c1 = min(nchunks, c0 + seg_len);
-
-  // Batches of kScanBatch independent loads, so a thread waits for memory
-  // once per batch rather than once per chunk.
+  // batches of kScanBatch independent loads: one wait for memory per batch
   int sum = 0;
   if (e < E)
     for (int cb = c0; cb < c1; cb += kScanBatch) {
@@ -106,15 +98,54 @@ meta_scan_kernel(int32_t* __restrict__ hist, const int32_t* __restrict__ err,
       for (int i = 0; i < kScanBatch; ++i) sum += v[i];
     }
   seg_tot[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < S; off <<= 1) {
+    const int u = seg >= off ? seg_tot[tid - off * kCountExperts] : 0;
+    __syncthreads();
+    seg_tot[tid] += u;
+    __syncthreads();
+  }
+  if (e >= E) return;
+  int run = seg_tot[tid] - sum;            // entries of e in ranges 0..seg-1
+  for (int cb = c0; cb < c1; cb += kScanBatch) {
+    int v[kScanBatch];
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i)
+      v[i] = cb + i < c1 ? hist[(int64_t)(cb + i) * E + e] : 0;
+#pragma unroll
+    for (int i = 0; i < kScanBatch; ++i)
+      if (cb + i < c1) {
+        hist[(int64_t)(cb + i) * E + e] = run;
+        run += v[i];
+      }
+  }
+  if (seg == S - 1) tokens_per_expert[e] = run;
+}
+
+// One workgroup of 1024 threads, from the expert totals of meta_count.
+__global__ void __launch_bounds__(kScanThreads)
+meta_scan_kernel(const int32_t* __restrict__ err, int nchunks, int E, int max_tiles,
+                 int64_t n,
+                 int32_t* __restrict__ indices, int32_t* __restrict__ bin_ids,
+                 int32_t* __restrict__ tokens_per_expert,
+                 int32_t* __restrict__ bins, int32_t* __restrict__ padded_bins,
+                 int32_t* __restrict__ tile_expert,
+                 int32_t* __restrict__ num_padded_rows,
+                 int32_t* __restrict__ status,
+                 int32_t* __restrict__ pair_first,
+                 int32_t* __restrict__ num_pairs,
+                 int32_t* __restrict__ row_token) {
+  __shared__ int32_t count_s[kMaxExperts];
+  __shared__ int32_t start_s[kMaxExperts];
+  __shared__ int32_t pend_s[kMaxExperts];
+  __shared__ int32_t pair_s[kMaxExperts];   // first group of each expert
+  __shared__ int32_t P_s, S_s, bad_s, N_s;
+  const int tid = threadIdx.x;
   if (tid == 0) bad_s = 0;
   __syncthreads();
   for (int c = tid; c < nchunks; c += kScanThreads)
     if (err[c]) bad_s = 1;                 // every writer stores the same 1
-  if (tid < E) {
-    int tot = 0;
-    for (int s = 0; s < S; ++s) tot += seg_tot[s * Ecap + tid];
-    count_s[tid] = tot;
-  }
+  if (tid < E) count_s[tid] = tokens_per_expert[tid];
   __syncthreads();
 
   // Inclusive scans over experts of the counts and the rounded-up counts:
@@ -152,7 +183,6 @@ meta_scan_kernel(int32_t* __restrict__ hist, const int32_t* __restrict__ err,
         prun += pc[i];
         grun += gp[i];
         pend_s[ee] = prun;
-        tokens_per_expert[ee] = c[i];
         bins[ee] = crun;
         padded_bins[ee] = prun;
       }
@@ -167,23 +197,6 @@ meta_scan_kernel(int32_t* __restrict__ hist, const int32_t* __restrict__ err,
   }
   __syncthreads();
 
-  // Each chunk's first sorted position per expert (exclusive, global).
-  if (e < E) {
-    int run = start_s[e];
-    for (int s = 0; s < seg; ++s) run += seg_tot[s * Ecap + e];
-    for (int cb = c0; cb < c1; cb += kScanBatch) {
-      int v[kScanBatch];
-#pragma unroll
-      for (int i = 0; i < kScanBatch; ++i)
-        v[i] = cb + i < c1 ? hist[(int64_t)(cb + i) * E + e] : 0;
-#pragma unroll
-      for (int i = 0; i < kScanBatch; ++i)
-        if (cb + i < c1) {
-          hist[(int64_t)(cb + i) * E + e] = run;
-          run += v[i];
-        }
-    }
-  }
   // 128-row block r -> its expert: the first e with padded_bins[e] > 128 r.
   const int P = P_s;
   for (int r = tid; r < max_tiles; r += kScanThreads) {
@@ -241,8 +254,9 @@ meta_place_kernel(const int32_t* __restrict__ ids, int64_t n, int64_t chunk,
     const int cnt = tokens_per_expert[i];
     shift_s[i] = (padded_bins[i] - round_up_block(cnt)) - (bins[i] - cnt);
   }
-  if (c < nchunks)
-    for (int i = lane; i < E; i += kWave) run[w][i] = chunk_start[(int64_t)c * E + i];
+  if (c < nchunks)   // the chunk's first position among expert i's entries, made global
+    for (int i = lane; i < E; i += kWave)
+      run[w][i] = chunk_start[(int64_t)c * E + i] + (bins[i] - tokens_per_expert[i]);
   __syncthreads();
   if (c >= nchunks) return;
 
@@ -275,19 +289,15 @@ meta_place_kernel(const int32_t* __restrict__ ids, int64_t n, int64_t chunk,
   }
 }
 
-static int expert_cap(int E) {
-  int Ecap = 1;
-  while (Ecap < E) Ecap <<= 1;
-  return Ecap;
-}
-
 int64_t meta_chunk(int64_t n, int E) {
   // A multiple of 64 entries per wave.  meta_hist and meta_place walk a chunk
-  // per wave (n / chunks entries, 64 at a time); each thread of meta_scan
-  // walks chunks / S chunks of one expert (S = 1024 / Ecap threads per
-  // expert).  About sqrt(n S / 16) chunks balances the two, counting a
-  // 64-entry step of the placement as 4 scan loads; at most 4096 chunks.
-  const double S = (double)(kScanThreads / expert_cap(E));
+  // per wave (n / chunks entries, 64 at a time); each thread of meta_count
+  // walks chunks / S chunks of one expert (S = 1024 / kCountExperts threads
+  // per expert).  About sqrt(n S / 16) chunks balances the two, counting a
+  // 64-entry step of the placement as 4 loads of the count; at most 4096
+  // chunks.  E only bounds the workspace (chunks x E counts).
+  (void)E;
+  const double S = (double)(kScanThreads / kCountExperts);
   const int64_t target =
       std::max<int64_t>(1, std::min<int64_t>(4096, (int64_t)std::sqrt((double)n * S / 16.0)));
   int64_t c = (n + target - 1) / target;
@@ -313,8 +323,6 @@ hipError_t launch_metadata(int64_t n, int E, int k, int64_t max_tiles,
   const int nchunks = meta_nchunks(n, E);
   int32_t* hist = static_cast<int32_t*>(ws);
   int32_t* err = hist + (int64_t)nchunks * E;
-  int Ecap = 1;
-  while (Ecap < E) Ecap <<= 1;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   const int blocks = (nchunks + kMetaWaves - 1) / kMetaWaves;
@@ -323,8 +331,10 @@ hipError_t launch_metadata(int64_t n, int E, int k, int64_t max_tiles,
   hipLaunchKernelGGL(meta_hist_kernel, dim3(blocks), dim3(kMetaWaves * kWave), 0,
                      stream, ids, n, chunk, nchunks, E, hist, err);
   if (ev && ev[1] && (rc = hipEventRecord(ev[1], stream)) != hipSuccess) return rc;
+  hipLaunchKernelGGL(meta_count_kernel, dim3((E + kCountExperts - 1) / kCountExperts),
+                     dim3(kScanThreads), 0, stream, hist, nchunks, E, m.tokens_per_expert);
   hipLaunchKernelGGL(meta_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream,
-                     hist, err, nchunks, E, Ecap, (int)max_tiles, n, m.indices, m.bin_ids,
+                     err, nchunks, E, (int)max_tiles, n, m.indices, m.bin_ids,
                      m.tokens_per_expert, m.bins, m.padded_bins, m.tile_expert,
                      m.num_padded_rows, m.status, m.pair_first, m.num_pairs, m.row_token);
   if (ev && ev[2] && (rc = hipEventRecord(ev[2], stream)) != hipSuccess) return rc;

@@ -45,6 +45,26 @@ __device__ __forceinline__ uint64_t tr_key(float logit, int64_t t) {
   return ((uint64_t)tr_order(logit) << 32) | (uint64_t)(~(uint32_t)t);
 }
 
+// Inclusive sum over the 256 threads of the workgroup, in thread order: a
+// shuffle scan inside each wave, then the totals of the waves before.
+__device__ __forceinline__ int tr_block_scan(int v, int32_t* wave_tot) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off, 64);
+    if (lane >= off) v += u;
+  }
+  if (lane == 63) wave_tot[w] = v;
+  __syncthreads();
+  for (int i = 0; i < w; ++i) v += wave_tot[i];
+  return v;
+}
+
+// Keys of one expert's selected entries kept in LDS across the radix
+// passes when they fit; beyond that each pass recomputes them from global
+// memory (same keys, same result).
+constexpr int kTrCache = 4096;
+
 // One workgroup per expert e.  Its entries (from every one of the k1 = k + 1
 // slots) are indices[bins[e] - cnt, bins[e]); slot j = a % k1 < k is routed,
 // j = k the candidate.  active[a] is written for every entry of e, so for
@@ -53,15 +73,17 @@ __global__ void __launch_bounds__(kTrThreads)
 tr_select_kernel(const float* __restrict__ logits, int E, int k1, int M,
                  const int32_t* __restrict__ tpe, const int32_t* __restrict__ bins,
                  const int32_t* __restrict__ indices, int32_t* __restrict__ active) {
-  __shared__ int32_t cnt_s[2];
+  __shared__ int32_t cnt_s[3];
   __shared__ int32_t hist[256];
+  __shared__ int32_t wave_tot[kTrThreads / 64];
   __shared__ uint64_t prefix_s;
   __shared__ int32_t rank_s;
+  __shared__ uint64_t keys_s[kTrCache];
   const int e = blockIdx.x, tid = threadIdx.x;
   const int cnt = tpe[e];
   const int start = bins[e] - cnt;
   const int k = k1 - 1;
-  if (tid < 2) cnt_s[tid] = 0;
+  if (tid < 3) cnt_s[tid] = 0;
   __syncthreads();
   int cr = 0, cc = 0;
   for (int s = tid; s < cnt; s += kTrThreads) {
@@ -81,28 +103,52 @@ tr_select_kernel(const float* __restrict__ logits, int E, int k1, int M,
     // key (drop those up to it), or the up-th largest candidate key (take
     // those from it)
     const bool want_cand = mode == 1;
+    const int nsel = want_cand ? cands : routed;
+    const bool cached = nsel <= kTrCache;
+    if (cached) {
+      // the selected keys, compacted in any order (a selection does not
+      // depend on it)
+      for (int s = tid; s < cnt; s += kTrThreads) {
+        const int a = indices[start + s];
+        if ((a % k1 == k) != want_cand) continue;
+        const int64_t t = a / k1;
+        keys_s[atomicAdd(&cnt_s[2], 1)] = tr_key(logits[t * E + e], t);
+      }
+    }
     if (tid == 0) {
       prefix_s = 0;
       rank_s = mode == 2 ? r - 1 : cands - up;
     }
     uint64_t mask = 0;
     for (int shift = 56; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 256; i += kTrThreads) hist[i] = 0;
+      hist[tid] = 0;
       __syncthreads();
       const uint64_t prefix = prefix_s;
-      for (int s = tid; s < cnt; s += kTrThreads) {
-        const int a = indices[start + s];
-        if ((a % k1 == k) != want_cand) continue;
-        const int64_t t = a / k1;
-        const uint64_t key = tr_key(logits[t * E + e], t);
-        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+      const int q = rank_s;
+      if (cached) {
+        for (int s = tid; s < nsel; s += kTrThreads) {
+          const uint64_t key = keys_s[s];
+          if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+        }
+      } else {
+        for (int s = tid; s < cnt; s += kTrThreads) {
+          const int a = indices[start + s];
+          if ((a % k1 == k) != want_cand) continue;
+          const int64_t t = a / k1;
+          const uint64_t key = tr_key(logits[t * E + e], t);
+          if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+        }
       }
       __syncthreads();
-      if (tid == 0) {
-        int q = rank_s, d = 0;
-        while (d < 255 && q >= hist[d]) q -= hist[d++];   // the rank lies in digit d
-        rank_s = q;
-        prefix_s = prefix | ((uint64_t)d << shift);
+      // digit d holds rank q when the counts below it sum to at most q and
+      // with it to more than q (the last digit takes any remainder)
+      const int v = hist[tid];
+      const int incl = tr_block_scan(v, wave_tot);
+      const int excl = incl - v;
+      __syncthreads();                    // every thread has read prefix_s and rank_s
+      if (excl <= q && (q < incl || tid == 255)) {
+        rank_s = q - excl;
+        prefix_s = prefix | ((uint64_t)tid << shift);
       }
       mask |= (uint64_t)255 << shift;
       __syncthreads();
