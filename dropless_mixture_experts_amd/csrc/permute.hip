@@ -150,55 +150,84 @@ padded_scatter_kernel(const T* __restrict__ src_perm,
   }
 }
 
-// Waves [0, ntok * k): entry a = t*k + j on padded row p gets
-// dy_perm[p] = w[a] * dy[t] and d_weights[a] = <dy[t], y_perm[p]>.  The waves
-// run in entry order, so the k waves of a token run side by side and read
-// dy[t] from HBM once.  Waves [ntok * k, ntok * k + 127 E): zero the pad rows
-// of dy_perm.
+// Waves [0, ntok): token t, for each entry a = t*k + j on padded row p,
+// writes dy_perm[p] = w[a] * dy[t] and d_weights[a] = <dy[t], y_perm[p]>.
+// The entries go four at a time; per pass a lane holds four 16-byte columns
+// of dy[t] and of the four y_perm rows (20 loads in flight), so dy[t] is read
+// once per four entries.  Each dot accumulates a lane's columns in ascending
+// order and is summed over the wave in a fixed order (run-to-run identical).
+// Waves [ntok, ntok + 127 E): zero the pad rows of dy_perm.
 template <typename T>
 __global__ void __launch_bounds__(kRowsPerBlock * kWave)
 scatter_backward_kernel(const T* __restrict__ dy, const T* __restrict__ y_perm,
-                        const float* __restrict__ weights, int64_t nent, int64_t H, int k,
+                        const float* __restrict__ weights, int64_t ntok, int64_t H, int k,
                         int E, const int32_t* __restrict__ row_of_entry,
                         const int32_t* __restrict__ tpe,
                         const int32_t* __restrict__ padded_bins,
                         T* __restrict__ dy_perm, float* __restrict__ d_weights) {
   using V = Vec16<T>;
   const int lane = threadIdx.x % kWave;
-  const int64_t a = wave_index();
+  const int64_t t = wave_index();
   const int64_t vecs = H * (int64_t)sizeof(T) / 16;
   const int64_t rowb = H * (int64_t)sizeof(T);
   char* out = reinterpret_cast<char*>(dy_perm);
-  if (a >= nent) {
-    if (a - nent >= (int64_t)E * kPadWaves) return;
-    const int64_t p = pad_row(a - nent, tpe, padded_bins);
+  if (t >= ntok) {
+    if (t - ntok >= (int64_t)E * kPadWaves) return;
+    const int64_t p = pad_row(t - ntok, tpe, padded_bins);
     if (p >= 0) zero_row(out + p * rowb, vecs, lane);
     return;
   }
-  const int row = row_of_entry[a];
-  if (row < 0) {                 // an empty slot (or an invalid id): no row
-    if (lane == 0) d_weights[a] = 0.f;
-    return;
-  }
-  const char* g = reinterpret_cast<const char*>(dy) + (a / k) * rowb;
-  const char* yp = reinterpret_cast<const char*>(y_perm) + (int64_t)row * rowb;
-  char* dst = out + (int64_t)row * rowb;
-  const float wt = weights[a];
-  float dot = 0.f;
-#pragma unroll 4
-  for (int64_t v = lane; v < vecs; v += kWave) {
-    float gf[V::N], yf[V::N], o[V::N];
-    V::unpack(ld16(g + v * 16), gf);
-    V::unpack(ld16_nt(yp + v * 16), yf);
+  const char* g = reinterpret_cast<const char*>(dy) + t * rowb;
+  const char* yp = reinterpret_cast<const char*>(y_perm);
+  const int32_t* rows = row_of_entry + t * k;
+  for (int j0 = 0; j0 < k; j0 += 4) {
+    int row[4];
+    float wt[4], dot[4];
 #pragma unroll
-    for (int i = 0; i < V::N; ++i) {
-      o[i] = wt * gf[i];
-      dot = __builtin_fmaf(gf[i], yf[i], dot);
+    for (int u = 0; u < 4; ++u) {
+      const int j = j0 + u;
+      row[u] = j < k ? rows[j] : -1;     // -1: past k, or an empty slot
+      wt[u] = row[u] >= 0 ? weights[t * k + j] : 0.f;
+      dot[u] = 0.f;
     }
-    st16(dst + v * 16, V::pack(o));
+    for (int64_t v0 = lane; v0 < vecs; v0 += 4 * kWave) {
+      u32x4 gd[4], yd[4][4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        gd[c] = v0 + c * kWave < vecs ? ld16(g + (v0 + c * kWave) * 16) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const char* src = yp + (int64_t)(row[u] >= 0 ? row[u] : 0) * rowb;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          yd[u][c] = row[u] >= 0 && v0 + c * kWave < vecs ? ld16_nt(src + (v0 + c * kWave) * 16)
+                                                          : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (v0 + c * kWave >= vecs) break;
+        float gf[V::N];
+        V::unpack(gd[c], gf);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (row[u] < 0) continue;
+          float yf[V::N], o[V::N];
+          V::unpack(yd[u][c], yf);
+#pragma unroll
+          for (int i = 0; i < V::N; ++i) {
+            o[i] = wt[u] * gf[i];
+            dot[u] = __builtin_fmaf(gf[i], yf[i], dot[u]);
+          }
+          st16(out + (int64_t)row[u] * rowb + (v0 + c * kWave) * 16, V::pack(o));
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float d = wave_sum(dot[u]);
+      if (lane == 0 && j0 + u < k) d_weights[t * k + j0 + u] = row[u] >= 0 ? d : 0.f;
+    }
   }
-  dot = wave_sum(dot);
-  if (lane == 0) d_weights[a] = dot;
 }
 
 static unsigned blocks_for(int64_t rows) {
@@ -243,16 +272,16 @@ hipError_t launch_scatter_backward(const Shape& s, const void* dy,
                                    const void* y_perm, const float* weights,
                                    const MetaPtrs& m, void* dy_perm,
                                    float* d_weights, hipStream_t stream) {
-  const dim3 grid(blocks_for(s.T * s.k + (int64_t)s.E * kPadWaves)), block(kRowsPerBlock * kWave);
+  const dim3 grid(blocks_for(s.T + (int64_t)s.E * kPadWaves)), block(kRowsPerBlock * kWave);
   if (s.bf16)
     hipLaunchKernelGGL(scatter_backward_kernel<bf16>, grid, block, 0, stream,
                        static_cast<const bf16*>(dy), static_cast<const bf16*>(y_perm),
-                       weights, s.T * s.k, s.H, s.k, s.E, m.row_of_entry, m.tokens_per_expert,
+                       weights, s.T, s.H, s.k, s.E, m.row_of_entry, m.tokens_per_expert,
                        m.padded_bins, static_cast<bf16*>(dy_perm), d_weights);
   else
     hipLaunchKernelGGL(scatter_backward_kernel<float>, grid, block, 0, stream,
                        static_cast<const float*>(dy), static_cast<const float*>(y_perm),
-                       weights, s.T * s.k, s.H, s.k, s.E, m.row_of_entry, m.tokens_per_expert,
+                       weights, s.T, s.H, s.k, s.E, m.row_of_entry, m.tokens_per_expert,
                        m.padded_bins, static_cast<float*>(dy_perm), d_weights);
   return hipGetLastError();
 }
