@@ -9,3 +9,4 @@ from .dmoe import *  # noqa: F401,F403
 from .dmoe import __all__  # noqa: F401
 from . import router  # noqa: F401  (the router in front of the layer)
 from . import token_round as rounding  # noqa: F401  (tile-aware token rounding)
+from . import moa  # noqa: F401  (dMoA map / reduce)
