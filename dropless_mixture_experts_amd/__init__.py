@@ -157,6 +157,15 @@ def load_library() -> ctypes.CDLL:
     lib.dmoe_router_forward.restype = ctypes.c_int
     lib.dmoe_router_backward.argtypes = [P(_Dims), vp, vp, vp, vp, ctypes.c_float, vp, vp]
     lib.dmoe_router_backward.restype = ctypes.c_int
+    lib.dmoe_moa_map.argtypes = [P(_Dims), vp, vp, P(_Meta), vp, vp, vp, vp]
+    lib.dmoe_moa_map.restype = ctypes.c_int
+    lib.dmoe_moa_reduce.argtypes = [P(_Dims), vp, vp, vp, P(_Meta), vp, vp, vp, vp]
+    lib.dmoe_moa_reduce.restype = ctypes.c_int
+    lib.dmoe_moa_reduce_backward.argtypes = [P(_Dims), vp, vp, vp, P(_Meta), vp, vp, vp, vp,
+                                             vp, vp, vp, vp]
+    lib.dmoe_moa_reduce_backward.restype = ctypes.c_int
+    lib.dmoe_moa_map_backward.argtypes = [P(_Dims), vp, vp, P(_Meta), vp, vp, vp, vp, vp, vp]
+    lib.dmoe_moa_map_backward.restype = ctypes.c_int
     lib.dmoe_status_string.argtypes = [ctypes.c_int]
     lib.dmoe_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -538,6 +547,138 @@ def dmoe_token_round(dims: Dims, logits, top_experts, weights, ws, tile_rows: in
         ctypes.byref(dims._c()), _ptr(logits, torch.float32, "logits"), ctypes.c_int32(tile_rows),
         _ptr(top_experts, torch.int32, "top_experts"), _ptr(weights, torch.float32, "weights"),
         _ptr(ws, None, "ws"), _stream(logits, stream)), "dmoe_token_round")
+
+
+# --------------------------------------------------------------------------
+# dMoA: the map / reduce pair of mixture of attention heads (bf16)
+# --------------------------------------------------------------------------
+
+def dmoe_moa_map(dims: Dims, x, w1, meta: Meta, x_perm, q_perm, q, stream=None) -> None:
+    """q [T*k, F] = x[t] @ w1[e] per routed slot; x_perm [P_max, H] is kept
+    for the backward.  See include/dmoe.h."""
+    lib = load_library()
+    dt, pm = dims.torch_dtype, _pmax(dims)
+    T, H, F, E, k = dims.T, dims.H, dims.F, dims.E, dims.k
+    for t, n, sz in ((x, "x", T * H), (w1, "w1", E * H * F), (x_perm, "x_perm", pm * H),
+                     (q_perm, "q_perm", pm * F), (q, "q", T * k * F)):
+        _need(t, n, sz)
+    _check_meta(dims, meta)
+    _check(lib.dmoe_moa_map(ctypes.byref(dims._c()), _ptr(x, dt, "x"), _ptr(w1, dt, "w1"),
+                            ctypes.byref(meta._c()), _ptr(x_perm, dt, "x_perm"),
+                            _ptr(q_perm, dt, "q_perm"), _ptr(q, dt, "q"), _stream(x, stream)),
+           "dmoe_moa_map")
+
+
+def dmoe_moa_reduce(dims: Dims, y, weights, w2, meta: Meta, y_perm, o_perm, out,
+                    stream=None) -> None:
+    """out [T, H] = sum_j weights[t, j] * y[t*k+j] @ w2[e]; y_perm and o_perm
+    are kept for the backward.  See include/dmoe.h."""
+    lib = load_library()
+    dt, pm = dims.torch_dtype, _pmax(dims)
+    T, H, F, E, k = dims.T, dims.H, dims.F, dims.E, dims.k
+    for t, n, sz in ((y, "y", T * k * F), (weights, "weights", T * k), (w2, "w2", E * F * H),
+                     (y_perm, "y_perm", pm * F), (o_perm, "o_perm", pm * H),
+                     (out, "out", T * H)):
+        _need(t, n, sz)
+    _check_meta(dims, meta)
+    _check(lib.dmoe_moa_reduce(ctypes.byref(dims._c()), _ptr(y, dt, "y"),
+                               _ptr(weights, torch.float32, "weights"), _ptr(w2, dt, "w2"),
+                               ctypes.byref(meta._c()), _ptr(y_perm, dt, "y_perm"),
+                               _ptr(o_perm, dt, "o_perm"), _ptr(out, dt, "out"),
+                               _stream(y, stream)), "dmoe_moa_reduce")
+
+
+def dmoe_moa_reduce_backward(dims: Dims, dout, weights, w2, meta: Meta, y_perm, o_perm,
+                             do_perm, dy_perm, dy, dw2, d_weights, stream=None) -> None:
+    """Gradients of dmoe_moa_reduce; see include/dmoe.h."""
+    lib = load_library()
+    dt, pm = dims.torch_dtype, _pmax(dims)
+    T, H, F, E, k = dims.T, dims.H, dims.F, dims.E, dims.k
+    for t, n, sz in ((dout, "dout", T * H), (weights, "weights", T * k),
+                     (w2, "w2", E * F * H), (y_perm, "y_perm", pm * F),
+                     (o_perm, "o_perm", pm * H), (do_perm, "do_perm", pm * H),
+                     (dy_perm, "dy_perm", pm * F), (dy, "dy", T * k * F),
+                     (dw2, "dw2", E * F * H), (d_weights, "d_weights", T * k)):
+        _need(t, n, sz)
+    _check_meta(dims, meta)
+    _check(lib.dmoe_moa_reduce_backward(
+        ctypes.byref(dims._c()), _ptr(dout, dt, "dout"), _ptr(weights, torch.float32, "weights"),
+        _ptr(w2, dt, "w2"), ctypes.byref(meta._c()), _ptr(y_perm, dt, "y_perm"),
+        _ptr(o_perm, dt, "o_perm"), _ptr(do_perm, dt, "do_perm"), _ptr(dy_perm, dt, "dy_perm"),
+        _ptr(dy, dt, "dy"), _ptr(dw2, dt, "dw2"), _ptr(d_weights, torch.float32, "d_weights"),
+        _stream(dout, stream)), "dmoe_moa_reduce_backward")
+
+
+def dmoe_moa_map_backward(dims: Dims, dq, w1, meta: Meta, x_perm, dq_perm, dx_perm, dx, dw1,
+                          stream=None) -> None:
+    """Gradients of dmoe_moa_map; see include/dmoe.h."""
+    lib = load_library()
+    dt, pm = dims.torch_dtype, _pmax(dims)
+    T, H, F, E, k = dims.T, dims.H, dims.F, dims.E, dims.k
+    for t, n, sz in ((dq, "dq", T * k * F), (w1, "w1", E * H * F), (x_perm, "x_perm", pm * H),
+                     (dq_perm, "dq_perm", pm * F), (dx_perm, "dx_perm", pm * H),
+                     (dx, "dx", T * H), (dw1, "dw1", E * H * F)):
+        _need(t, n, sz)
+    _check_meta(dims, meta)
+    _check(lib.dmoe_moa_map_backward(
+        ctypes.byref(dims._c()), _ptr(dq, dt, "dq"), _ptr(w1, dt, "w1"), ctypes.byref(meta._c()),
+        _ptr(x_perm, dt, "x_perm"), _ptr(dq_perm, dt, "dq_perm"), _ptr(dx_perm, dt, "dx_perm"),
+        _ptr(dx, dt, "dx"), _ptr(dw1, dt, "dw1"), _stream(dq, stream)), "dmoe_moa_map_backward")
+
+
+class DMoALayer:
+    """map / reduce of mixture of attention heads on preallocated buffers:
+    metadata(top_experts), then map(x), attention outside, reduce(y), and
+    their backward in reverse (reduce_backward, then map_backward)."""
+
+    def __init__(self, dims: Dims, device="cuda"):
+        if dims.dtype != DMOE_BF16:
+            raise DMoEError(-3, "DMoALayer (bf16 only)")
+        self.dims = dims
+        self.device = torch.device(device)
+        self.meta, self.ws = allocate_meta(dims, device)
+        pm = _pmax(dims)
+        fl = dict(dtype=dims.torch_dtype, device=device)
+        H, F = dims.H, dims.F
+        self.x_perm = torch.empty(pm, H, **fl)
+        self.y_perm = torch.empty(pm, F, **fl)
+        self.o_perm = torch.empty(pm, H, **fl)
+        self.perm_f = torch.empty(pm, F, **fl)     # q_perm, dy_perm, dq_perm (scratch)
+        self.perm_h = torch.empty(pm, H, **fl)     # do_perm, dx_perm (scratch)
+
+    def metadata(self, top_experts, stream=None):
+        dmoe_metadata(self.dims, top_experts, self.meta, self.ws, stream)
+
+    def map(self, x, w1, stream=None):
+        d = self.dims
+        q = torch.empty(d.T * d.k, d.F, dtype=d.torch_dtype, device=self.device)
+        dmoe_moa_map(d, x, w1, self.meta, self.x_perm, self.perm_f, q, stream)
+        return q
+
+    def reduce(self, y, weights, w2, stream=None):
+        d = self.dims
+        out = torch.empty(d.T, d.H, dtype=d.torch_dtype, device=self.device)
+        dmoe_moa_reduce(d, y, weights, w2, self.meta, self.y_perm, self.o_perm, out, stream)
+        return out
+
+    def reduce_backward(self, dout, weights, w2, stream=None):
+        d = self.dims
+        fl = dict(dtype=d.torch_dtype, device=self.device)
+        dy = torch.empty(d.T * d.k, d.F, **fl)
+        dw2 = torch.empty(d.E, d.F, d.H, **fl)
+        dwt = torch.empty(d.T, d.k, dtype=torch.float32, device=self.device)
+        dmoe_moa_reduce_backward(d, dout, weights, w2, self.meta, self.y_perm, self.o_perm,
+                                 self.perm_h, self.perm_f, dy, dw2, dwt, stream)
+        return dy, dw2, dwt
+
+    def map_backward(self, dq, w1, stream=None):
+        d = self.dims
+        fl = dict(dtype=d.torch_dtype, device=self.device)
+        dx = torch.empty(d.T, d.H, **fl)
+        dw1 = torch.empty(d.E, d.H, d.F, **fl)
+        dmoe_moa_map_backward(d, dq, w1, self.meta, self.x_perm, self.perm_f, self.perm_h,
+                              dx, dw1, stream)
+        return dx, dw1
 
 
 def dmoe_router_backward(dims: Dims, logits, top_experts, weights, d_weights, d_logits,

@@ -508,4 +508,95 @@ const char* dmoe_status_string(int status) {
   }
 }
 
+// ---- dMoA map / reduce (mixture of attention heads) ------------------------
+
+}  // extern "C"
+
+namespace {
+
+// bf16 only: the grouped products run on the bf16 engine.
+int check_moa(const dmoe_dims* d) {
+  const int rc = check_gemm_dims(d);
+  if (rc != DMOE_OK) return rc;
+  return d->dtype == DMOE_BF16 ? DMOE_OK : DMOE_ERR_UNSUPPORTED;
+}
+
+// The same shape with H and F exchanged: a product whose K and N are the
+// other way round than in the dMoE layer's.
+Shape swapped(Shape s) {
+  const int64_t h = s.H;
+  s.H = s.F;
+  s.F = h;
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dmoe_moa_map(const dmoe_dims* dims, const void* x, const void* w1, const dmoe_meta* meta,
+                 void* x_perm, void* q_perm, void* q, hipStream_t stream) {
+  int rc = check_moa(dims);
+  if (rc != DMOE_OK) return rc;
+  if ((rc = check_meta(meta)) != DMOE_OK) return rc;
+  if (!x || !w1 || !x_perm || !q_perm || !q) return DMOE_ERR_ARG;
+  const Shape s = shape_of(dims);
+  const MetaPtrs m = meta_ptrs(meta, dims);
+  DMOE_TRY(dmoe::launch_padded_gather(s, x, m, x_perm, stream));
+  DMOE_TRY(dmoe::launch_bf16_down(swapped(s), x_perm, w1, m, q_perm, stream));
+  DMOE_TRY(dmoe::launch_slot_unpermute(s, s.F, q_perm, m, q, stream));
+  return DMOE_OK;
+}
+
+int dmoe_moa_reduce(const dmoe_dims* dims, const void* y, const float* weights, const void* w2,
+                    const dmoe_meta* meta, void* y_perm, void* o_perm, void* out,
+                    hipStream_t stream) {
+  int rc = check_moa(dims);
+  if (rc != DMOE_OK) return rc;
+  if ((rc = check_meta(meta)) != DMOE_OK) return rc;
+  if (!y || !weights || !w2 || !y_perm || !o_perm || !out) return DMOE_ERR_ARG;
+  const Shape s = shape_of(dims);
+  const MetaPtrs m = meta_ptrs(meta, dims);
+  DMOE_TRY(dmoe::launch_slot_permute(s, s.F, y, m, y_perm, stream));
+  DMOE_TRY(dmoe::launch_bf16_down(s, y_perm, w2, m, o_perm, stream));
+  DMOE_TRY(dmoe::launch_padded_scatter(s, o_perm, weights, m, out, stream));
+  return DMOE_OK;
+}
+
+int dmoe_moa_reduce_backward(const dmoe_dims* dims, const void* dout, const float* weights,
+                             const void* w2, const dmoe_meta* meta, const void* y_perm,
+                             const void* o_perm, void* do_perm, void* dy_perm, void* dy,
+                             void* dw2, float* d_weights, hipStream_t stream) {
+  int rc = check_moa(dims);
+  if (rc != DMOE_OK) return rc;
+  if ((rc = check_meta(meta)) != DMOE_OK) return rc;
+  if (!dout || !weights || !w2 || !y_perm || !o_perm || !do_perm || !dy_perm || !dy || !dw2 ||
+      !d_weights)
+    return DMOE_ERR_ARG;
+  const Shape s = shape_of(dims);
+  const MetaPtrs m = meta_ptrs(meta, dims);
+  DMOE_TRY(dmoe::launch_scatter_backward(s, dout, o_perm, weights, m, do_perm, d_weights,
+                                         stream));
+  DMOE_TRY(dmoe::launch_bf16_dgrad(swapped(s), do_perm, w2, m, dy_perm, stream));
+  DMOE_TRY(dmoe::launch_bf16_wgrad(s, y_perm, do_perm, m, dw2, stream));
+  DMOE_TRY(dmoe::launch_slot_unpermute(s, s.F, dy_perm, m, dy, stream));
+  return DMOE_OK;
+}
+
+int dmoe_moa_map_backward(const dmoe_dims* dims, const void* dq, const void* w1,
+                          const dmoe_meta* meta, const void* x_perm, void* dq_perm,
+                          void* dx_perm, void* dx, void* dw1, hipStream_t stream) {
+  int rc = check_moa(dims);
+  if (rc != DMOE_OK) return rc;
+  if ((rc = check_meta(meta)) != DMOE_OK) return rc;
+  if (!dq || !w1 || !x_perm || !dq_perm || !dx_perm || !dx || !dw1) return DMOE_ERR_ARG;
+  const Shape s = shape_of(dims);
+  const MetaPtrs m = meta_ptrs(meta, dims);
+  DMOE_TRY(dmoe::launch_slot_permute(s, s.F, dq, m, dq_perm, stream));
+  DMOE_TRY(dmoe::launch_bf16_dgrad(s, dq_perm, w1, m, dx_perm, stream));
+  DMOE_TRY(dmoe::launch_padded_scatter(s, dx_perm, nullptr, m, dx, stream));
+  DMOE_TRY(dmoe::launch_bf16_wgrad(swapped(s), x_perm, dq_perm, m, dw1, stream));
+  return DMOE_OK;
+}
+
 }  // extern "C"

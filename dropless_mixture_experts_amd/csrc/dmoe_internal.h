@@ -55,6 +55,12 @@ hipError_t launch_scatter_backward(const Shape& s, const void* dy,
                                    const void* y_perm, const float* weights,
                                    const MetaPtrs& m, void* dy_perm,
                                    float* d_weights, hipStream_t stream);
+// Slot order (T*k rows of W elements) <-> padded order: out[a] = src_perm[row(a)]
+// (zeros for an empty slot); dst_perm[row(a)] = src[a] with the pad rows zeroed.
+hipError_t launch_slot_unpermute(const Shape& s, int64_t W, const void* src_perm,
+                                 const MetaPtrs& m, void* out, hipStream_t stream);
+hipError_t launch_slot_permute(const Shape& s, int64_t W, const void* src, const MetaPtrs& m,
+                               void* dst_perm, hipStream_t stream);
 
 // token_round.hip: tile-aware token rounding of the router's top-k (s.k
 // routed slots, outputs [T, s.k + 1]); M rows per tile.
@@ -118,5 +124,12 @@ hipError_t launch_bf16_wgrad_up(const Shape& s, const void* dh1, const void* dh3
                                 const void* w1, const void* w3, const void* x_perm,
                                 const MetaPtrs& m, void* dx_perm, void* dw1, void* dw3,
                                 hipStream_t stream);
+// A single grouped linear map y = x w[e] (w [E, H, F]): its dgrad
+// dx_perm [P, H] = dy_perm [P, F] w[e]^T, and its weight gradient in the
+// layout of dw2: dw [E, F, H] = x_perm [P, F]^T dy_perm [P, H].
+hipError_t launch_bf16_dgrad(const Shape& s, const void* dy_perm, const void* w,
+                             const MetaPtrs& m, void* dx_perm, hipStream_t stream);
+hipError_t launch_bf16_wgrad(const Shape& s, const void* x_perm, const void* dy_perm,
+                             const MetaPtrs& m, void* dw, hipStream_t stream);
 
 }  // namespace dmoe

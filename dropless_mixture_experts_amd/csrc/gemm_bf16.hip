@@ -636,7 +636,9 @@ struct DownDgrad {
   }
 };
 
-// dx_perm = dh1 w1[e]^T + dh3 w3[e]^T: two K segments into one accumulator.
+// dx_perm = dh1 w1[e]^T + dh3 w3[e]^T: two K segments into one accumulator
+// (one, dh1 w1[e]^T, when `two` is false: the dgrad of a single grouped
+// linear map).
 struct UpDgrad {
   static constexpr bool kLateStep1 = false;
   static constexpr bool kUsesFreeStage = false;
@@ -646,16 +648,17 @@ struct UpDgrad {
   int64_t H, F;
   bf16* dx_perm;
   RowTiles rt;
+  bool two = true;
   __device__ uint32_t lda() const { return (uint32_t)(F * 2); }
   __device__ uint32_t ldb() const { return (uint32_t)(F * 2); }
   static constexpr int kEpiSteps = 2;
-  __device__ int tile_steps() const { return (int)(2 * F / kKStep); }
+  __device__ int tile_steps() const { return (int)((two ? 2 : 1) * F / kKStep); }
   __device__ void xcd_range(int x, int& lo, int& hi) const { rt.xcd_range(x, lo, hi); }
   __device__ void tile(int L, Job& j) const {
     rt.get(L, j);
     j.fa = j.v * 256 + 256 <= H;
     j.nk = (int)(F / kKStep);
-    j.steps = 2 * j.nk;
+    j.steps = two ? 2 * j.nk : j.nk;
   }
   __device__ void operands(const Job& j, int seg, const char*& a0, const char*& a1,
                            const char*& b0, const char*& b1) const {
@@ -1309,6 +1312,26 @@ wgrad_up_kernel(const bf16* __restrict__ dh1, const bf16* __restrict__ dh3,
                          filled != 0);
 }
 
+// dx_perm = dy_perm w[e]^T for a single grouped linear map y = x w[e]
+// (w [E, H, F], dy_perm [P, F], dx_perm [P, H]).
+__global__ void __launch_bounds__(kThreads)
+dgrad_kernel(const bf16* __restrict__ dy_perm, const bf16* __restrict__ w, int64_t H,
+             int64_t F, ROW_TILE_ARGS, bf16* dx_perm) {
+  UpDgrad k{dy_perm, dy_perm, w, w, H, F, dx_perm};
+  k.two = false;
+  k.rt.init(tile_expert, pair_first, num_pairs, padded_bins, (int)((H + 255) / 256));
+  persistent(k);
+}
+
+// dw[e] = x_perm[rows_e]^T dy_perm[rows_e] for y = x w[e] (x_perm [P, F],
+// dy_perm [P, H], dw [E, F, H]), zero for an empty expert.
+__global__ void __launch_bounds__(kThreads)
+wgrad_down_kernel(const bf16* __restrict__ x_perm, const bf16* __restrict__ dy_perm, int64_t H,
+                  int64_t F, int E, const int32_t* __restrict__ tpe,
+                  const int32_t* __restrict__ padded_bins, bf16* __restrict__ dw) {
+  persistent(WgradDown{x_perm, dy_perm, H, F, E, tpe, padded_bins, dw});
+}
+
 }  // namespace bfk
 
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -1428,6 +1451,26 @@ hipError_t launch_bf16_wgrad_up(const Shape& s, const void* dh1, const void* dh3
                      m.num_pairs, m.padded_bins, m.tokens_per_expert,
                      up_dgrad_fills_tail(s) ? 1 : 0, mb<bf16>(dx_perm), mb<bf16>(dw1),
                      mb<bf16>(dw3));
+  return hipGetLastError();
+}
+
+// dx_perm [P, H] = dy_perm [P, F] w[e]^T with w [E, H, F].
+hipError_t launch_bf16_dgrad(const Shape& s, const void* dy_perm, const void* w,
+                             const MetaPtrs& m, void* dx_perm, hipStream_t stream) {
+  hipLaunchKernelGGL(bfk::dgrad_kernel, persistent_grid(cdiv(s.H, 256) * s.max_tiles),
+                     dim3(bfk::kThreads), 0, stream, cb<bf16>(dy_perm), cb<bf16>(w), s.H, s.F,
+                     m.tile_expert, m.pair_first, m.num_pairs, m.padded_bins,
+                     mb<bf16>(dx_perm));
+  return hipGetLastError();
+}
+
+// dw [E, F, H] = x_perm [P, F]^T dy_perm [P, H] per expert.
+hipError_t launch_bf16_wgrad(const Shape& s, const void* x_perm, const void* dy_perm,
+                             const MetaPtrs& m, void* dw, hipStream_t stream) {
+  hipLaunchKernelGGL(bfk::wgrad_down_kernel,
+                     persistent_grid(cdiv(s.H, 256) * cdiv(s.F, 256) * s.E),
+                     dim3(bfk::kThreads), 0, stream, cb<bf16>(x_perm), cb<bf16>(dy_perm), s.H,
+                     s.F, s.E, m.tokens_per_expert, m.padded_bins, mb<bf16>(dw));
   return hipGetLastError();
 }
 

@@ -230,6 +230,82 @@ scatter_backward_kernel(const T* __restrict__ dy, const T* __restrict__ y_perm,
   }
 }
 
+// Slot order <-> padded order, one row per entry, no weights and no sum
+// (the map / reduce pair of mixture of attention heads: the
+// "yikangshen/megablocks" README feeds attention with k queries per token
+// and reduces the k attention outputs).  Rows are W elements wide.
+//
+// slot_unpermute: waves [0, nent): out[a] = src_perm[row_of_entry[a]], zeros
+// for an empty slot (row -1).
+template <typename T>
+__global__ void __launch_bounds__(kRowsPerBlock * kWave)
+slot_unpermute_kernel(const T* __restrict__ src_perm, int64_t nent, int64_t W,
+                      const int32_t* __restrict__ row_of_entry, T* __restrict__ out) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t a = wave_index();
+  if (a >= nent) return;
+  const int64_t vecs = W * (int64_t)sizeof(T) / 16;
+  const int64_t rowb = W * (int64_t)sizeof(T);
+  char* dst = reinterpret_cast<char*>(out) + a * rowb;
+  const int row = row_of_entry[a];
+  if (row < 0) {
+    zero_row(dst, vecs, lane);
+    return;
+  }
+  const char* src = reinterpret_cast<const char*>(src_perm) + (int64_t)row * rowb;
+  for (int64_t v0 = lane; v0 < vecs; v0 += kWave * kUnroll) {
+    u32x4 r[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t v = v0 + u * kWave;
+      if (v < vecs) r[u] = ld16_nt(src + v * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t v = v0 + u * kWave;
+      if (v < vecs) st16(dst + v * 16, r[u]);
+    }
+  }
+}
+
+// slot_permute: waves [0, nent): dst_perm[row_of_entry[a]] = src[a] (nothing
+// for an empty slot); waves [nent, nent + 127 E): zero the pad rows.
+template <typename T>
+__global__ void __launch_bounds__(kRowsPerBlock * kWave)
+slot_permute_kernel(const T* __restrict__ src, int64_t nent, int64_t W, int E,
+                    const int32_t* __restrict__ row_of_entry,
+                    const int32_t* __restrict__ tpe,
+                    const int32_t* __restrict__ padded_bins, T* __restrict__ dst_perm) {
+  const int lane = threadIdx.x % kWave;
+  const int64_t a = wave_index();
+  const int64_t vecs = W * (int64_t)sizeof(T) / 16;
+  const int64_t rowb = W * (int64_t)sizeof(T);
+  char* out = reinterpret_cast<char*>(dst_perm);
+  if (a >= nent) {
+    if (a - nent >= (int64_t)E * kPadWaves) return;
+    const int64_t p = pad_row(a - nent, tpe, padded_bins);
+    if (p >= 0) zero_row(out + p * rowb, vecs, lane);
+    return;
+  }
+  const int row = row_of_entry[a];
+  if (row < 0) return;
+  const char* s = reinterpret_cast<const char*>(src) + a * rowb;
+  char* d = out + (int64_t)row * rowb;
+  for (int64_t v0 = lane; v0 < vecs; v0 += kWave * kUnroll) {
+    u32x4 r[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t v = v0 + u * kWave;
+      if (v < vecs) r[u] = ld16_nt(s + v * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t v = v0 + u * kWave;
+      if (v < vecs) st16(d + v * 16, r[u]);
+    }
+  }
+}
+
 static unsigned blocks_for(int64_t rows) {
   return (unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock);
 }
@@ -283,6 +359,36 @@ hipError_t launch_scatter_backward(const Shape& s, const void* dy,
                        static_cast<const float*>(dy), static_cast<const float*>(y_perm),
                        weights, s.T, s.H, s.k, s.E, m.row_of_entry, m.tokens_per_expert,
                        m.padded_bins, static_cast<float*>(dy_perm), d_weights);
+  return hipGetLastError();
+}
+
+hipError_t launch_slot_unpermute(const Shape& s, int64_t W, const void* src_perm,
+                                 const MetaPtrs& m, void* out, hipStream_t stream) {
+  const int64_t n = s.T * s.k;
+  const dim3 grid(blocks_for(n)), block(kRowsPerBlock * kWave);
+  if (s.bf16)
+    hipLaunchKernelGGL(slot_unpermute_kernel<bf16>, grid, block, 0, stream,
+                       static_cast<const bf16*>(src_perm), n, W, m.row_of_entry,
+                       static_cast<bf16*>(out));
+  else
+    hipLaunchKernelGGL(slot_unpermute_kernel<float>, grid, block, 0, stream,
+                       static_cast<const float*>(src_perm), n, W, m.row_of_entry,
+                       static_cast<float*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_slot_permute(const Shape& s, int64_t W, const void* src, const MetaPtrs& m,
+                               void* dst_perm, hipStream_t stream) {
+  const int64_t n = s.T * s.k;
+  const dim3 grid(blocks_for(n + (int64_t)s.E * kPadWaves)), block(kRowsPerBlock * kWave);
+  if (s.bf16)
+    hipLaunchKernelGGL(slot_permute_kernel<bf16>, grid, block, 0, stream,
+                       static_cast<const bf16*>(src), n, W, s.E, m.row_of_entry,
+                       m.tokens_per_expert, m.padded_bins, static_cast<bf16*>(dst_perm));
+  else
+    hipLaunchKernelGGL(slot_permute_kernel<float>, grid, block, 0, stream,
+                       static_cast<const float*>(src), n, W, s.E, m.row_of_entry,
+                       m.tokens_per_expert, m.padded_bins, static_cast<float*>(dst_perm));
   return hipGetLastError();
 }
 

@@ -395,6 +395,55 @@ int dmoe_backward_fused_gather_timed(const dmoe_dims* dims, const void* x, const
                                      void* dx, void* dw1, void* dw3, void* dw2, float* d_weights,
                                      hipStream_t stream, hipEvent_t* events);
 
+/* ---- dMoA: the map / reduce pair of mixture of attention heads ---------------
+ *
+ * "yikangshen/megablocks" README (the dMoA example): a causal self-attention
+ * whose query projection is a dMoA layer built from the plain MLP expert
+ * with no activation and no bias.  map(x) gives each token k query vectors,
+ * one per routed expert; attention (not part of this library) turns them
+ * into k outputs; reduce(y) projects each output with its expert and sums
+ * the k slots with the routing weights.  Reading taken (the README prints no
+ * formula): expert e is w1[e] [H, F] and w2[e] [F, H];
+ *     map:    q[t*k + j]  = x[t] w1[e(t, j)]                   (no weight)
+ *     reduce: out[t]      = sum_j weights[t*k + j] * y[t*k + j] w2[e(t, j)]
+ * An empty slot (id -1) maps to a zero row and adds nothing.  The routing
+ * and its metadata are the dMoE layer's (dmoe_metadata), so the pages'
+ * padded layout and grouped products serve both.  The README's example has
+ * F = H.
+ *
+ * bf16 only (DMOE_ERR_UNSUPPORTED for fp32); the dims rules of
+ * dmoe_forward otherwise.  All pointers are device memory owned by the
+ * caller; P_max = 128 * dmoe_max_tiles(dims).  Slot-order arrays have
+ * T*k rows in entry order a = t*k + j.  Nothing is allocated, nothing
+ * waits on the host, and argument errors return before any launch.
+ *
+ * dmoe_moa_map:     x [T, H] -> q [T*k, F].  x_perm [P_max, H] is written
+ *                   (the padded copy of x, saved for dmoe_moa_map_backward);
+ *                   q_perm [P_max, F] is scratch.
+ * dmoe_moa_reduce:  y [T*k, F], weights fp32 [T*k] -> out [T, H].
+ *                   y_perm [P_max, F] and o_perm [P_max, H] are written and
+ *                   saved for dmoe_moa_reduce_backward.
+ * dmoe_moa_reduce_backward: dout [T, H] -> dy [T*k, F] (zero rows for empty
+ *                   slots), dw2 [E, F, H] (zero for an empty expert),
+ *                   d_weights fp32 [T*k] (<dout[t], y[t*k+j] w2[e]>, 0 for
+ *                   an empty slot).  do_perm [P_max, H] and dy_perm
+ *                   [P_max, F] are scratch.
+ * dmoe_moa_map_backward: dq [T*k, F] -> dx [T, H], dw1 [E, H, F].
+ *                   x_perm is the one dmoe_moa_map wrote; dq_perm [P_max, F]
+ *                   and dx_perm [P_max, H] are scratch. */
+int dmoe_moa_map(const dmoe_dims* dims, const void* x, const void* w1, const dmoe_meta* meta,
+                 void* x_perm, void* q_perm, void* q, hipStream_t stream);
+int dmoe_moa_reduce(const dmoe_dims* dims, const void* y, const float* weights, const void* w2,
+                    const dmoe_meta* meta, void* y_perm, void* o_perm, void* out,
+                    hipStream_t stream);
+int dmoe_moa_reduce_backward(const dmoe_dims* dims, const void* dout, const float* weights,
+                             const void* w2, const dmoe_meta* meta, const void* y_perm,
+                             const void* o_perm, void* do_perm, void* dy_perm, void* dy,
+                             void* dw2, float* d_weights, hipStream_t stream);
+int dmoe_moa_map_backward(const dmoe_dims* dims, const void* dq, const void* w1,
+                          const dmoe_meta* meta, const void* x_perm, void* dq_perm,
+                          void* dx_perm, void* dx, void* dw1, hipStream_t stream);
+
 /* Static text for a dmoe_status value. */
 const char* dmoe_status_string(int status);
 

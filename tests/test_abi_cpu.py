@@ -201,3 +201,28 @@ def test_fused_gather_policy(lib):
     # x of 2 GB or more is beyond the fused entry points
     big = dm.Dims(1 << 19, 2048, 1024, 64, 8, dm.DMOE_BF16)
     assert dm.fused_gather_pays(big) is False
+
+
+def test_moa_checks_before_launch(lib):
+    """dMoA map/reduce: bf16 only, null pointers and bad dims rejected on the
+    host."""
+    p = ctypes.c_void_p(0x1000)
+    meta = dm._Meta(*([p] * 11))
+    f32 = _dims()
+    bf = _dims(dtype=dm.DMOE_BF16)
+    args_map = (p, p, ctypes.byref(meta), p, p, p, None)
+    assert lib.dmoe_moa_map(ctypes.byref(f32), *args_map) == -3
+    assert lib.dmoe_moa_map(ctypes.byref(bf), None, p, ctypes.byref(meta), p, p, p, None) == -1
+    assert lib.dmoe_moa_reduce(ctypes.byref(f32), p, p, p, ctypes.byref(meta), p, p, p,
+                               None) == -3
+    assert lib.dmoe_moa_reduce(ctypes.byref(bf), p, None, p, ctypes.byref(meta), p, p, p,
+                               None) == -1
+    assert lib.dmoe_moa_reduce_backward(ctypes.byref(bf), p, p, p, ctypes.byref(meta), p, p, p,
+                                        p, p, p, None, None) == -1
+    assert lib.dmoe_moa_map_backward(ctypes.byref(bf), p, p, ctypes.byref(meta), p, p, p, p,
+                                     None, None) == -1
+    bad = _dims(F=200, dtype=dm.DMOE_BF16)
+    assert lib.dmoe_moa_map(ctypes.byref(bad), *args_map) == -2
+    no_sched = dm._Meta(*([p] * 10 + [None]))
+    assert lib.dmoe_moa_map(ctypes.byref(bf), p, p, ctypes.byref(no_sched), p, p, p,
+                            None) == -1
