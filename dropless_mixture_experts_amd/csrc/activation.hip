@@ -31,7 +31,7 @@ recompute_act_kernel(const T* __restrict__ h1, const T* __restrict__ h3, int64_t
     V::unpack(ld16(h3 + i * V::N), b);
 #pragma unroll
     for (int r = 0; r < V::N; ++r) a[r] = gated_silu(a[r], b[r]);
-    st16(act + i * V::N, V::pack(a));
+    st16_nt(act + i * V::N, V::pack(a));
   }
 }
 
