@@ -61,17 +61,17 @@ template <> struct Vec16<bf16> {
   }
 };
 
-// 16-byte global load and store.  ld16_nt marks the line for early eviction:
+// 16-byte global loads and store.  ld16_nt marks the line for early eviction:
 // for rows that one wave reads once and nothing reads again soon (the
 // scatter's inputs), where it also lets the memory system stream them faster.
+// Every store of the row kernels is non-temporal (st16_nt): the next kernel,
+// not this one, reads what it writes, and without the hint the dirty lines
+// are written back under that kernel's loads.
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 __device__ __forceinline__ u32x4 ld16_nt(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-__device__ __forceinline__ void st16(void* p, const u32x4& v) {
-  *reinterpret_cast<u32x4*>(p) = v;
 }
 __device__ __forceinline__ void st16_nt(void* p, const u32x4& v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
