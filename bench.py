@@ -12,7 +12,9 @@ pass, and around the dominant kernel in the timed steps, each interval less
 the measured cost of one record), the roofline of the dominant kernel and
 the CPU oracle's rate on the host.  The same line carries a compact record
 of the other seeded workloads (``workloads``), the step with the
-activation-lean backward (``lean_backward``) and cold-cache figures.
+activation-lean backward (``lean_backward``), cold-cache figures, the layer
+on tile-aware token-rounded routing (``token_rounding``) and the dMoA map /
+reduce pair with its backward (``moa``).
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
                     [--workloads zipf_e64,coarse_e8,... | none]
@@ -69,6 +71,37 @@ def kernel_work(cfg, P, fused=False):
     w["gemm_up_dgrad"] = (4 * P * H * F, (2 * P * F + 2 * Ea * H * F + P * H) * s)
     w["gemm_wgrad_up"] = (4 * P * H * F, (P * H + 2 * P * F + 2 * Ea * H * F) * s)
     w["gather_backward"] = (0, (N * H + T * H) * s)
+    return w
+
+
+MOA_CALLS = ["moa_map", "moa_reduce", "moa_reduce_backward", "moa_map_backward"]
+
+
+def moa_work(cfg, P):
+    """Algorithmic FLOPs and bytes of each dMoA entry point for P padded rows
+    (bf16): the sum over the kernels the call launches, each counted as in
+    kernel_work (unique reads plus writes, weights once)."""
+    s = 2
+    T, H, F, E, k = cfg.T, cfg.H, cfg.F, cfg.E, cfg.k
+    N = T * k
+    w = {}
+    # gather x; q_perm = x_perm w1[e]; q in slot order
+    w["moa_map"] = (2 * P * H * F,
+                    ((T * H + P * H) + (P * H + E * H * F + P * F) + 2 * N * F) * s)
+    # y in padded order; o_perm = y_perm w2[e]; out = weighted top-k sum
+    w["moa_reduce"] = (2 * P * F * H,
+                       ((N * F + P * F) + (P * F + E * F * H + P * H) + (N * H + T * H)) * s
+                       + 4 * N)
+    # do_perm = w dout and d_weights; dy_perm = do_perm w2^T; dw2; dy in slot order
+    w["moa_reduce_backward"] = (
+        4 * P * F * H,
+        ((T * H + N * H + P * H) + (P * H + E * F * H + P * F) + (P * F + P * H + E * F * H)
+         + 2 * N * F) * s + 8 * N)
+    # dq in padded order; dx_perm = dq_perm w1^T; dx = unit top-k sum; dw1
+    w["moa_map_backward"] = (
+        4 * P * H * F,
+        ((N * F + P * F) + (P * F + E * H * F + P * H) + (N * H + T * H)
+         + (P * H + P * F + E * H * F)) * s)
     return w
 
 
@@ -221,6 +254,95 @@ def router_time(dm, cfg, dev, stream, steps):
     torch.cuda.synchronize()
     return round(e0.elapsed_time(e1) * 1e3 / steps, 1)
 
+
+
+def moa_leg(dm, dev, ovh, K=10, W=3):
+    """The dMoA map / reduce pair (mixture of attention heads) on moa_e16:
+    per step the metadata, map, reduce, reduce_backward and map_backward.
+    The attention between map and reduce is outside the library and not
+    timed; its output (y) and the map's upstream gradient (dq) are seeded
+    N(0,1) stand-ins of their shapes."""
+    import torch
+    from dropless_mixture_experts_amd.hip_events import EventArray
+    from workloads import CONFIGS, make_inputs
+    cfg = CONFIGS["moa_e16"]
+    inp = make_inputs(cfg)
+    print(f"bench: dMoA map/reduce on {cfg.name}", file=sys.stderr, flush=True)
+    D = dm.Dims(cfg.T, cfg.H, cfg.F, cfg.E, cfg.k, dm.DMOE_BF16)
+    L = dm.DMoALayer(D, dev)
+    bf = torch.bfloat16
+    up = lambda a, dt=bf: torch.from_numpy(a).to(dev).to(dt).contiguous()
+    x, w1, w2, dout = up(inp.x), up(inp.w1), up(inp.w2), up(inp.dy)
+    ids = up(inp.top_experts, torch.int32)
+    wts = up(inp.weights, torch.float32)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed_id)
+    y = torch.randn(cfg.T * cfg.k, cfg.F, generator=gen, device=dev).to(bf)
+    dq = torch.randn(cfg.T * cfg.k, cfg.F, generator=gen, device=dev).to(bf)
+    stream = torch.cuda.current_stream(dev)
+    calls = [lambda: L.map(x, w1), lambda: L.reduce(y, wts, w2),
+             lambda: L.reduce_backward(dout, wts, w2), lambda: L.map_backward(dq, w1)]
+
+    def step(ev=None):
+        L.metadata(ids)
+        for i, f in enumerate(calls):
+            if ev is not None:
+                ev.record(i, stream)
+            f()
+        if ev is not None:
+            ev.record(len(calls), stream)
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    P = int(L.meta.num_padded_rows.item())
+    evs = [EventArray(len(calls) + 1) for _ in range(K)]
+    for ev in evs:
+        step(ev)
+    torch.cuda.synchronize()
+    per = {n: max(sum(ev.elapsed_ms(i, i + 1) for ev in evs) / K - ovh, 0.0)
+           for i, n in enumerate(MOA_CALLS)}
+    for ev in evs:
+        ev.close()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / K
+    work = moa_work(cfg, P)
+    N = cfg.T * cfg.k
+    table = {}
+    for n in MOA_CALLS:
+        fl, by = work[n]
+        t = per[n] * 1e-3
+        table[n] = {"ms": round(per[n], 4), "tflops": round(fl / t / 1e12, 1),
+                    "gbs": round(by / t / 1e9, 1),
+                    "roofline_frac": round(roof_time(fl, by, PEAK_BF16_TFLOPS) / t, 4)}
+    dom = max(MOA_CALLS, key=lambda n: per[n])
+    fl, by = work[dom]
+    ai = fl / by
+    ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    t = per[dom] * 1e-3
+    roof = ({"call": dom, "bound": "hbm", "achieved": round(by / t / 1e9, 1),
+             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(by / t / 1e9 / PEAK_HBM_GBS, 4)}
+            if ai < ridge else
+            {"call": dom, "bound": "mfma", "achieved": round(fl / t / 1e12, 1),
+             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+             "frac": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4)})
+    roof["intensity_flop_per_byte"] = round(ai, 1)
+    gemm_flop = sum(work[n][0] for n in MOA_CALLS)
+    rec = {"config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "F": cfg.F, "E": cfg.E,
+                      "k": cfg.k, "dtype": cfg.dtype, "routing": cfg.routing, "P": P},
+           "steps": K, "warmup": W, "ms_per_step": round(ms, 4),
+           "tokens_s": round(cfg.T / (ms * 1e-3), 1),
+           "useful_tflops": round(12.0 * N * cfg.H * cfg.F / (ms * 1e-3) / 1e12, 1),
+           "gemm_executed_tflops": round(gemm_flop / (ms * 1e-3) / 1e12, 1),
+           "calls": table, "roofline": roof,
+           "note": ("metadata + map + reduce + reduce_backward + map_backward per step; the "
+                    "attention between map and reduce is not part of the library and not "
+                    "timed; per-call ms from K steps with an event around every call")}
+    del L
+    return rec
 
 
 def saved_bytes_per_token(cfg, P):
@@ -540,9 +662,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="fine_e64")
-    ap.add_argument("--workloads", default="zipf_e64,coarse_e8,sparse_e256,tiny_f32",
+    ap.add_argument("--workloads", default="zipf_e64,coarse_e8,sparse_e256,tiny_f32,moa_e16",
                     help="comma-separated other workloads reported under 'workloads' "
-                         "(10 steps each), or 'none'")
+                         "(10 steps each; moa_e16, the dMoA map / reduce pair, under "
+                         "'moa'), or 'none'")
     ap.add_argument("--rounding", default="sparse_e256",
                     help="workload on which to time the layer on tile-aware token-rounded "
                          "routing against top-k, or 'none'")
@@ -682,6 +805,10 @@ def main():
     inp = L.inp
     L.close()
     others = [n for n in args.workloads.split(",") if n and n != "none" and n != cfg.name]
+    if "moa_e16" in others:
+        # the dMoA map / reduce pair: its own record, not a dMoE layer's
+        others.remove("moa_e16")
+        out["moa"] = moa_leg(dm, dev, ovh)
     if others:
         out["workloads"] = {n: other_workload(dm, n, dev, args, ovh) for n in others}
     if args.rounding != "none":

@@ -54,6 +54,30 @@ def test_permutation_bytes_are_symmetric():
     assert w["padded_gather"][1] - w["gather_backward"][1] == (P - N) * cfg.H * 2
 
 
+def test_moa_work_model():
+    """The dMoA calls execute 12 P H F FLOPs in all (map and reduce 2 each,
+    their backward 4 each).  With H = F the map and the reduce move the
+    same bytes but for the reduce's fp32 routing weights.  Each backward
+    adds one weight-gradient product (P H + P F reads, E H F writes) to its
+    forward's traffic.  In the reduce's backward the scatter's backward also
+    writes the P padded rows of do_perm, and the slot unpermute moves 2 N
+    rows where the forward's slot permute moves N + P (net N H with H = F);
+    it reads the routing weights and writes d_weights (8 bytes per entry
+    against the forward's 4)."""
+    cfg = CONFIGS["moa_e16"]
+    assert cfg.H == cfg.F
+    P = 128 * (cfg.T * cfg.k // 128 + cfg.E)
+    w = bench.moa_work(cfg, P)
+    assert set(w) == set(bench.MOA_CALLS)
+    assert sum(w[n][0] for n in w) == 12 * P * cfg.H * cfg.F
+    T, H, F, E, k = cfg.T, cfg.H, cfg.F, cfg.E, cfg.k
+    N = T * k
+    assert w["moa_reduce"][1] - w["moa_map"][1] == 4 * N
+    wg = (P * H + P * F + E * H * F) * 2
+    assert w["moa_map_backward"][1] - w["moa_map"][1] == wg
+    assert w["moa_reduce_backward"][1] - w["moa_reduce"][1] == wg + N * H * 2 + 4 * N
+
+
 def test_roof_time_takes_the_binding_roof():
     # 1 GFLOP and 1 MB: MFMA-bound (0.4 us against 0.125 us)
     assert bench.roof_time(1e9, 1e6, 2500.0) == pytest.approx(1e9 / 2.5e15)

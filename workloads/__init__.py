@@ -82,6 +82,12 @@ CONFIGS: Dict[str, Config] = {
     # High-sparsity bf16 layer: T=16384, H=1536, F=256, E=256, top-8.
     "sparse_e256": Config("sparse_e256", 16384, 1536, 256, 256, 8, "bf16",
                           seed_id=5),
+    # Mixture of attention heads, the map / reduce pair: 2x2048 tokens, hidden
+    # 2048 for both halves (the "yikangshen/megablocks" README example sets
+    # ffn_hidden_size to hidden_size), 16 attention experts, top-4.  The pages
+    # give no sizes for it; w1 [E,H,F] and w2 [E,F,H] are the two halves, w3
+    # is drawn and not used.
+    "moa_e16": Config("moa_e16", 4096, 2048, 2048, 16, 4, "bf16", seed_id=6),
 }
 
 
