@@ -94,6 +94,15 @@ def test_mid_size_layer():
     _check(got, ref, top, "mid")
 
 
+@pytest.mark.timeout(900)
+def test_full_size_bench_workload():
+    """The moa_e16 layer that bench.py times (4096 tokens, H = F = 2048, 16
+    experts, top-4), every output and gradient element by element."""
+    cfg = CONFIGS["moa_e16"]
+    got, ref, top = _run(cfg, seed=3)
+    _check(got, ref, top, cfg.name)
+
+
 def test_run_to_run_bitwise():
     cfg = shrink(CONFIGS["fine_e64"], T=600, H=256, F=256, E=8, k=2)
     a, _, _ = _run(cfg, seed=2)
