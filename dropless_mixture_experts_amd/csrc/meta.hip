@@ -24,9 +24,11 @@
 //               chunk's entries of the same expert (64-lane ballots on the
 //               bits of the id + mbcnt), then writes indices, bin_ids,
 //               row_of_entry and the token of the entry's padded row
-//               (row_token; meta_scan marks the pad rows -1).  Ties keep
-//               ascending entry order, so the result is unique and
-//               bit-identical on every run.
+//               (row_token).  Ties keep ascending entry order, so the
+//               result is unique and bit-identical on every run.  Its
+//               workgroups also mark the pad rows of row_token -1 and fill
+//               the sorted arrays past the routed entries with -1: spread
+//               over the grid, not left to meta_scan's single workgroup.
 #include <algorithm>
 #include <cmath>
 
@@ -125,21 +127,17 @@ meta_count_kernel(int32_t* __restrict__ hist, int nchunks, int E,
 // One workgroup of 1024 threads, from the expert totals of meta_count.
 __global__ void __launch_bounds__(kScanThreads)
 meta_scan_kernel(const int32_t* __restrict__ err, int nchunks, int E, int max_tiles,
-                 int64_t n,
-                 int32_t* __restrict__ indices, int32_t* __restrict__ bin_ids,
                  int32_t* __restrict__ tokens_per_expert,
                  int32_t* __restrict__ bins, int32_t* __restrict__ padded_bins,
                  int32_t* __restrict__ tile_expert,
                  int32_t* __restrict__ num_padded_rows,
                  int32_t* __restrict__ status,
                  int32_t* __restrict__ pair_first,
-                 int32_t* __restrict__ num_pairs,
-                 int32_t* __restrict__ row_token) {
+                 int32_t* __restrict__ num_pairs) {
   __shared__ int32_t count_s[kMaxExperts];
-  __shared__ int32_t start_s[kMaxExperts];
   __shared__ int32_t pend_s[kMaxExperts];
   __shared__ int32_t pair_s[kMaxExperts];   // first group of each expert
-  __shared__ int32_t P_s, S_s, bad_s, N_s;
+  __shared__ int32_t P_s, S_s, bad_s;
   const int tid = threadIdx.x;
   if (tid == 0) bad_s = 0;
   __syncthreads();
@@ -177,7 +175,6 @@ meta_scan_kernel(const int32_t* __restrict__ err, int nchunks, int E, int max_ti
     for (int i = 0; i < 4; ++i) {
       const int ee = tid * 4 + i;
       if (ee < E) {
-        start_s[ee] = crun;
         pair_s[ee] = grun;
         crun += c[i];
         prun += pc[i];
@@ -190,7 +187,6 @@ meta_scan_kernel(const int32_t* __restrict__ err, int nchunks, int E, int max_ti
     if (tid == kWave - 1) {
       P_s = pi;
       S_s = gi;
-      N_s = ci;
       *num_padded_rows = pi;
       *num_pairs = gi;
     }
@@ -221,20 +217,7 @@ meta_scan_kernel(const int32_t* __restrict__ err, int nchunks, int E, int max_ti
     for (int q = 0; q < ng; ++q) pair_first[g0 + q] = t0 + 2 * q;
   }
   for (int r = S_s + tid; r < max_tiles; r += kScanThreads) pair_first[r] = -1;
-  // Pad rows hold no token: rows [pend - pc + c, pend) of each expert (at
-  // most 127 per expert, MegaBlocks §2).
-  for (int q = tid; q < E * (kBlock - 1); q += kScanThreads) {
-    const int ee = q / (kBlock - 1), i = q - ee * (kBlock - 1);
-    const int c = count_s[ee], pc = round_up_block(c);
-    if (i < pc - c) row_token[pend_s[ee] - pc + c + i] = -1;
-  }
   if (tid == 0) *status = bad_s ? kErrExpertId : 0;
-  // The sorted arrays list the routed entries only: past their total (less
-  // than n when some slots are empty or invalid) they hold -1.
-  for (int64_t i = N_s + (int64_t)tid; i < n; i += kScanThreads) {
-    indices[i] = -1;
-    bin_ids[i] = -1;
-  }
 }
 
 __global__ void __launch_bounds__(kMetaWaves * kWave)
@@ -257,6 +240,22 @@ meta_place_kernel(const int32_t* __restrict__ ids, int64_t n, int64_t chunk,
   if (c < nchunks)   // the chunk's first position among expert i's entries, made global
     for (int i = lane; i < E; i += kWave)
       run[w][i] = chunk_start[(int64_t)c * E + i] + (bins[i] - tokens_per_expert[i]);
+  // Pad rows hold no token: rows [padded_bins[e] - pc + cnt, padded_bins[e])
+  // of expert e, at most 127 (MegaBlocks §2); workgroup b takes experts b,
+  // b + gridDim.x, ...
+  for (int e = blockIdx.x; e < E; e += gridDim.x) {
+    const int cnt = tokens_per_expert[e], pc = round_up_block(cnt);
+    for (int i = threadIdx.x; i < pc - cnt; i += blockDim.x)
+      row_token[padded_bins[e] - pc + cnt + i] = -1;
+  }
+  // The sorted arrays list the routed entries only: past their total (less
+  // than n when some slots are empty or invalid) they hold -1.
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = bins[E - 1] + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += stride) {
+    indices[i] = -1;
+    bin_ids[i] = -1;
+  }
   __syncthreads();
   if (c >= nchunks) return;
 
@@ -334,9 +333,9 @@ hipError_t launch_metadata(int64_t n, int E, int k, int64_t max_tiles,
   hipLaunchKernelGGL(meta_count_kernel, dim3((E + kCountExperts - 1) / kCountExperts),
                      dim3(kScanThreads), 0, stream, hist, nchunks, E, m.tokens_per_expert);
   hipLaunchKernelGGL(meta_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream,
-                     err, nchunks, E, (int)max_tiles, n, m.indices, m.bin_ids,
+                     err, nchunks, E, (int)max_tiles,
                      m.tokens_per_expert, m.bins, m.padded_bins, m.tile_expert,
-                     m.num_padded_rows, m.status, m.pair_first, m.num_pairs, m.row_token);
+                     m.num_padded_rows, m.status, m.pair_first, m.num_pairs);
   if (ev && ev[2] && (rc = hipEventRecord(ev[2], stream)) != hipSuccess) return rc;
   hipLaunchKernelGGL(meta_place_kernel, dim3(blocks), dim3(kMetaWaves * kWave), 0,
                      stream, ids, n, chunk, nchunks, E, k, nbits, hist,
