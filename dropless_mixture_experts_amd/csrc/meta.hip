@@ -10,13 +10,15 @@
 // token count and overflowed shared memory at 64 experts; here on-chip memory
 // is O(E) (at most ~5 KB at E = 256) whatever T is.
 //
-// Four launches, stream-ordered, no host synchronisation:
+// Three or four launches, stream-ordered, no host synchronisation:
 //   meta_hist   one wave per chunk of entries: expert histogram of the chunk
 //               (LDS counters) and an invalid-id flag (-1 is no error: an
 //               empty slot, routed nowhere).
 //   meta_count  kCountExperts experts per workgroup: each expert's total and
 //               each chunk's first position among that expert's entries
-//               (a scan over the chunks, independent per expert).
+//               (a scan over the chunks, independent per expert).  Skipped
+//               when one workgroup covers every expert with one batch of
+//               loads per thread: meta_scan then does these scans itself.
 //   meta_scan   one workgroup: bins / padded_bins / P from the totals, the
 //               block -> expert table, the pairs of row blocks that the
 //               matrix products process together, the status word.
@@ -39,7 +41,7 @@ namespace dmoe {
 
 constexpr int kMetaWaves = 4;  // waves (chunks) per workgroup
 constexpr int kScanThreads = 1024;
-constexpr int kScanBatch = 8;   // chunk counts a scan thread loads at once
+constexpr int kScanBatch = 32;  // chunk counts a scan thread loads at once
 constexpr int kCountExperts = 8;  // experts per meta_count workgroup
 
 __global__ void __launch_bounds__(kMetaWaves * kWave)
@@ -71,62 +73,86 @@ meta_hist_kernel(const int32_t* __restrict__ ids, int64_t n, int64_t chunk,
   }
 }
 
-// kCountExperts experts per workgroup of 1024 threads: thread (el, seg)
-// owns expert e = kCountExperts * blockIdx.x + el over the seg-th of S =
-// 1024 / kCountExperts ranges of chunks.  It sums its range, the workgroup
-// scans the S range sums of each expert (Hillis-Steele in LDS), and the
-// thread writes each chunk's first position among expert e's entries over
-// the chunk's count in hist; the last range writes the expert's total.
-__global__ void __launch_bounds__(kScanThreads)
-meta_count_kernel(int32_t* __restrict__ hist, int nchunks, int E,
-                  int32_t* __restrict__ tokens_per_expert) {
-  __shared__ int32_t seg_tot[kScanThreads];
-  constexpr int S = kScanThreads / kCountExperts;
+// The chunk scan of experts [e0, e0 + ne) by one workgroup of 1024 threads
+// (ne <= 256): thread (el, seg) owns expert e0 + el over the seg-th of S =
+// 1024 / ne ranges of chunks (threads past S ne only join the barriers).  It
+// sums its range, the workgroup scans the S range sums of each expert
+// (Hillis-Steele in LDS, `seg_tot` of 1024 entries), and the thread writes
+// each chunk's first position among the expert's entries over the chunk's
+// count in hist; the last range writes the expert's total to
+// tokens_per_expert and, when `tot` is given, to tot[e0 + el] in LDS.
+// Ends with a barrier.
+__device__ __forceinline__ void scan_chunks(int32_t* __restrict__ hist, int nchunks, int E,
+                                            int e0, int ne, int32_t* seg_tot,
+                                            int32_t* __restrict__ tokens_per_expert,
+                                            int32_t* tot) {
+  const int S = kScanThreads / ne;
   const int tid = threadIdx.x;
-  const int el = tid % kCountExperts, seg = tid / kCountExperts;
-  const int e = blockIdx.x * kCountExperts + el;
+  const int el = tid % ne, seg = tid / ne;
+  const int e = e0 + el;
+  const bool mine = seg < S;
   const int seg_len = (nchunks + S - 1) / S;
   const int c0 = min(nchunks, seg * seg_len);
-  const int c1 = min(nchunks, c0 + seg_len);
-  // batches of kScanBatch independent loads: one wait for memory per batch
+  const int c1 = mine ? min(nchunks, c0 + seg_len) : c0;
+  // batches of kScanBatch independent loads: one wait for memory per batch;
+  // a range of one batch (the usual case) keeps its counts in registers for
+  // the second pass
   int sum = 0;
-  if (e < E)
-    for (int cb = c0; cb < c1; cb += kScanBatch) {
-      int v[kScanBatch];
-#pragma unroll
-      for (int i = 0; i < kScanBatch; ++i)
-        v[i] = cb + i < c1 ? hist[(int64_t)(cb + i) * E + e] : 0;
-#pragma unroll
-      for (int i = 0; i < kScanBatch; ++i) sum += v[i];
-    }
-  seg_tot[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < S; off <<= 1) {
-    const int u = seg >= off ? seg_tot[tid - off * kCountExperts] : 0;
-    __syncthreads();
-    seg_tot[tid] += u;
-    __syncthreads();
-  }
-  if (e >= E) return;
-  int run = seg_tot[tid] - sum;            // entries of e in ranges 0..seg-1
+  int v[kScanBatch];
   for (int cb = c0; cb < c1; cb += kScanBatch) {
-    int v[kScanBatch];
 #pragma unroll
     for (int i = 0; i < kScanBatch; ++i)
       v[i] = cb + i < c1 ? hist[(int64_t)(cb + i) * E + e] : 0;
 #pragma unroll
-    for (int i = 0; i < kScanBatch; ++i)
-      if (cb + i < c1) {
-        hist[(int64_t)(cb + i) * E + e] = run;
-        run += v[i];
-      }
+    for (int i = 0; i < kScanBatch; ++i) sum += v[i];
   }
-  if (seg == S - 1) tokens_per_expert[e] = run;
+  seg_tot[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < S; off <<= 1) {
+    const int u = seg >= off ? seg_tot[tid - off * ne] : 0;
+    __syncthreads();
+    seg_tot[tid] += u;
+    __syncthreads();
+  }
+  if (mine) {
+    int run = seg_tot[tid] - sum;            // entries of e in ranges 0..seg-1
+    const bool reload = c1 - c0 > kScanBatch;
+    for (int cb = c0; cb < c1; cb += kScanBatch) {
+      if (reload)
+#pragma unroll
+        for (int i = 0; i < kScanBatch; ++i)
+          v[i] = cb + i < c1 ? hist[(int64_t)(cb + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i)
+        if (cb + i < c1) {
+          hist[(int64_t)(cb + i) * E + e] = run;
+          run += v[i];
+        }
+    }
+    if (seg == S - 1) {
+      tokens_per_expert[e] = run;
+      if (tot) tot[e] = run;
+    }
+  }
+  __syncthreads();
 }
 
-// One workgroup of 1024 threads, from the expert totals of meta_count.
+// kCountExperts experts per workgroup; the chunk scans of different experts
+// are independent, so E / kCountExperts workgroups share them.
 __global__ void __launch_bounds__(kScanThreads)
-meta_scan_kernel(const int32_t* __restrict__ err, int nchunks, int E, int max_tiles,
+meta_count_kernel(int32_t* __restrict__ hist, int nchunks, int E,
+                  int32_t* __restrict__ tokens_per_expert) {
+  __shared__ int32_t seg_tot[kScanThreads];
+  const int e0 = blockIdx.x * kCountExperts;
+  scan_chunks(hist, nchunks, E, e0, min(kCountExperts, E - e0), seg_tot, tokens_per_expert,
+              nullptr);
+}
+
+// One workgroup of 1024 threads, from the expert totals of meta_count, or
+// (fuse_count) doing meta_count's chunk scans of all E experts itself first.
+__global__ void __launch_bounds__(kScanThreads)
+meta_scan_kernel(int32_t* __restrict__ hist, const int32_t* __restrict__ err, int nchunks,
+                 int E, int max_tiles, int fuse_count,
                  int32_t* __restrict__ tokens_per_expert,
                  int32_t* __restrict__ bins, int32_t* __restrict__ padded_bins,
                  int32_t* __restrict__ tile_expert,
@@ -138,12 +164,14 @@ meta_scan_kernel(const int32_t* __restrict__ err, int nchunks, int E, int max_ti
   __shared__ int32_t pend_s[kMaxExperts];
   __shared__ int32_t pair_s[kMaxExperts];   // first group of each expert
   __shared__ int32_t P_s, S_s, bad_s;
+  __shared__ int32_t seg_tot[kScanThreads];
   const int tid = threadIdx.x;
   if (tid == 0) bad_s = 0;
-  __syncthreads();
+  if (fuse_count) scan_chunks(hist, nchunks, E, 0, E, seg_tot, tokens_per_expert, count_s);
+  else __syncthreads();
   for (int c = tid; c < nchunks; c += kScanThreads)
     if (err[c]) bad_s = 1;                 // every writer stores the same 1
-  if (tid < E) count_s[tid] = tokens_per_expert[tid];
+  if (!fuse_count && tid < E) count_s[tid] = tokens_per_expert[tid];
   __syncthreads();
 
   // Inclusive scans over experts of the counts and the rounded-up counts:
@@ -330,10 +358,15 @@ hipError_t launch_metadata(int64_t n, int E, int k, int64_t max_tiles,
   hipLaunchKernelGGL(meta_hist_kernel, dim3(blocks), dim3(kMetaWaves * kWave), 0,
                      stream, ids, n, chunk, nchunks, E, hist, err);
   if (ev && ev[1] && (rc = hipEventRecord(ev[1], stream)) != hipSuccess) return rc;
-  hipLaunchKernelGGL(meta_count_kernel, dim3((E + kCountExperts - 1) / kCountExperts),
-                     dim3(kScanThreads), 0, stream, hist, nchunks, E, m.tokens_per_expert);
+  // When one workgroup covers every expert with one batch of loads per
+  // thread, the scan kernel takes the chunk scans too: one launch fewer.
+  const int segs = kScanThreads / E;
+  const bool fuse = (nchunks + segs - 1) / segs <= kScanBatch;
+  if (!fuse)
+    hipLaunchKernelGGL(meta_count_kernel, dim3((E + kCountExperts - 1) / kCountExperts),
+                       dim3(kScanThreads), 0, stream, hist, nchunks, E, m.tokens_per_expert);
   hipLaunchKernelGGL(meta_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream,
-                     err, nchunks, E, (int)max_tiles,
+                     hist, err, nchunks, E, (int)max_tiles, fuse ? 1 : 0,
                      m.tokens_per_expert, m.bins, m.padded_bins, m.tile_expert,
                      m.num_padded_rows, m.status, m.pair_first, m.num_pairs);
   if (ev && ev[2] && (rc = hipEventRecord(ev[2], stream)) != hipSuccess) return rc;
