@@ -577,8 +577,8 @@ int dmoe_moa_reduce_backward(const dmoe_dims* dims, const void* dout, const floa
   const MetaPtrs m = meta_ptrs(meta, dims);
   DMOE_TRY(dmoe::launch_scatter_backward(s, dout, o_perm, weights, m, do_perm, d_weights,
                                          stream));
-  DMOE_TRY(dmoe::launch_bf16_dgrad(swapped(s), do_perm, w2, m, dy_perm, stream));
-  DMOE_TRY(dmoe::launch_bf16_wgrad(s, y_perm, do_perm, m, dw2, stream));
+  DMOE_TRY(dmoe::launch_bf16_dgrad_wgrad(swapped(s), do_perm, w2, y_perm, m, dy_perm, dw2,
+                                          stream));
   DMOE_TRY(dmoe::launch_slot_unpermute(s, s.F, dy_perm, m, dy, stream));
   return DMOE_OK;
 }
@@ -593,9 +593,8 @@ int dmoe_moa_map_backward(const dmoe_dims* dims, const void* dq, const void* w1,
   const Shape s = shape_of(dims);
   const MetaPtrs m = meta_ptrs(meta, dims);
   DMOE_TRY(dmoe::launch_slot_permute(s, s.F, dq, m, dq_perm, stream));
-  DMOE_TRY(dmoe::launch_bf16_dgrad(s, dq_perm, w1, m, dx_perm, stream));
+  DMOE_TRY(dmoe::launch_bf16_dgrad_wgrad(s, dq_perm, w1, x_perm, m, dx_perm, dw1, stream));
   DMOE_TRY(dmoe::launch_padded_scatter(s, dx_perm, nullptr, m, dx, stream));
-  DMOE_TRY(dmoe::launch_bf16_wgrad(swapped(s), x_perm, dq_perm, m, dw1, stream));
   return DMOE_OK;
 }
 

@@ -125,11 +125,10 @@ hipError_t launch_bf16_wgrad_up(const Shape& s, const void* dh1, const void* dh3
                                 const MetaPtrs& m, void* dx_perm, void* dw1, void* dw3,
                                 hipStream_t stream);
 // A single grouped linear map y = x w[e] (w [E, H, F]): its dgrad
-// dx_perm [P, H] = dy_perm [P, F] w[e]^T, and its weight gradient in the
-// layout of dw2: dw [E, F, H] = x_perm [P, F]^T dy_perm [P, H].
-hipError_t launch_bf16_dgrad(const Shape& s, const void* dy_perm, const void* w,
-                             const MetaPtrs& m, void* dx_perm, hipStream_t stream);
-hipError_t launch_bf16_wgrad(const Shape& s, const void* x_perm, const void* dy_perm,
-                             const MetaPtrs& m, void* dw, hipStream_t stream);
+// dx_perm [P, H] = dy_perm [P, F] w[e]^T and its weight gradient
+// dw [E, H, F] = x_perm [P, H]^T dy_perm [P, F], in one launch.
+hipError_t launch_bf16_dgrad_wgrad(const Shape& s, const void* dy_perm, const void* w,
+                                   const void* x_perm, const MetaPtrs& m, void* dx_perm,
+                                   void* dw, hipStream_t stream);
 
 }  // namespace dmoe

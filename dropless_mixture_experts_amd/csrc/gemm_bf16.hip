@@ -1386,24 +1386,22 @@ wgrad_up_kernel(const bf16* __restrict__ dh1, const bf16* __restrict__ dh3,
                          filled != 0);
 }
 
-// dx_perm = dy_perm w[e]^T for a single grouped linear map y = x w[e]
-// (w [E, H, F], dy_perm [P, F], dx_perm [P, H]).
+// The dgrad and the weight gradient of a single grouped linear map y = x w[e]
+// (w [E, H, F]) in one launch, as the down dgrad and dw2 share one:
+// dx_perm [P, H] = dy_perm [P, F] w[e]^T and dw [E, H, F] = x_perm [P, H]^T
+// dy_perm [P, F] per expert (zero for an empty expert).  Both read dy_perm and
+// neither reads what the other writes, so the weight-gradient tiles fill the
+// dgrad's last round of row tiles.
 __global__ void __launch_bounds__(kThreads)
-dgrad_kernel(const bf16* __restrict__ dy_perm, const bf16* __restrict__ w, int64_t H,
-             int64_t F, ROW_TILE_ARGS, bf16* dx_perm) {
-  UpDgrad k{dy_perm, dy_perm, w, w, H, F, dx_perm};
-  k.two = false;
-  k.rt.init(tile_expert, pair_first, num_pairs, padded_bins, (int)((H + 255) / 256));
-  persistent(k);
-}
-
-// dw[e] = x_perm[rows_e]^T dy_perm[rows_e] for y = x w[e] (x_perm [P, F],
-// dy_perm [P, H], dw [E, F, H]), zero for an empty expert.
-__global__ void __launch_bounds__(kThreads)
-wgrad_down_kernel(const bf16* __restrict__ x_perm, const bf16* __restrict__ dy_perm, int64_t H,
-                  int64_t F, int E, const int32_t* __restrict__ tpe,
-                  const int32_t* __restrict__ padded_bins, bf16* __restrict__ dw) {
-  persistent(WgradDown{x_perm, dy_perm, H, F, E, tpe, padded_bins, dw});
+dgrad_wgrad_kernel(const bf16* __restrict__ dy_perm, const bf16* __restrict__ w,
+                   const bf16* __restrict__ x_perm, int64_t H, int64_t F, int E, ROW_TILE_ARGS,
+                   const int32_t* __restrict__ tpe, bf16* __restrict__ dx_perm,
+                   bf16* __restrict__ dw) {
+  UpDgrad k1{dy_perm, dy_perm, w, w, H, F, dx_perm};
+  k1.two = false;
+  k1.rt.init(tile_expert, pair_first, num_pairs, padded_bins, (int)((H + 255) / 256));
+  // WgradDown's (H, F) name its output dw [E, F, H]: here (F, H)
+  persistent_dual(k1, WgradDown{x_perm, dy_perm, F, H, E, tpe, padded_bins, dw});
 }
 
 }  // namespace bfk
@@ -1528,23 +1526,17 @@ hipError_t launch_bf16_wgrad_up(const Shape& s, const void* dh1, const void* dh3
   return hipGetLastError();
 }
 
-// dx_perm [P, H] = dy_perm [P, F] w[e]^T with w [E, H, F].
-hipError_t launch_bf16_dgrad(const Shape& s, const void* dy_perm, const void* w,
-                             const MetaPtrs& m, void* dx_perm, hipStream_t stream) {
-  hipLaunchKernelGGL(bfk::dgrad_kernel, persistent_grid(cdiv(s.H, 256) * s.max_tiles),
-                     dim3(bfk::kThreads), 0, stream, cb<bf16>(dy_perm), cb<bf16>(w), s.H, s.F,
+// dx_perm [P, H] = dy_perm [P, F] w[e]^T and dw [E, H, F] = x_perm [P, H]^T
+// dy_perm [P, F] per expert, with w [E, H, F], in one launch.
+hipError_t launch_bf16_dgrad_wgrad(const Shape& s, const void* dy_perm, const void* w,
+                                   const void* x_perm, const MetaPtrs& m, void* dx_perm,
+                                   void* dw, hipStream_t stream) {
+  const int64_t t1 = cdiv(s.H, 256) * s.max_tiles;
+  const int64_t t2 = cdiv(s.H, 256) * cdiv(s.F, 256) * s.E;
+  hipLaunchKernelGGL(bfk::dgrad_wgrad_kernel, persistent_grid(t1 + t2), dim3(bfk::kThreads), 0,
+                     stream, cb<bf16>(dy_perm), cb<bf16>(w), cb<bf16>(x_perm), s.H, s.F, s.E,
                      m.tile_expert, m.pair_first, m.num_pairs, m.padded_bins,
-                     mb<bf16>(dx_perm));
-  return hipGetLastError();
-}
-
-// dw [E, F, H] = x_perm [P, F]^T dy_perm [P, H] per expert.
-hipError_t launch_bf16_wgrad(const Shape& s, const void* x_perm, const void* dy_perm,
-                             const MetaPtrs& m, void* dw, hipStream_t stream) {
-  hipLaunchKernelGGL(bfk::wgrad_down_kernel,
-                     persistent_grid(cdiv(s.H, 256) * cdiv(s.F, 256) * s.E),
-                     dim3(bfk::kThreads), 0, stream, cb<bf16>(x_perm), cb<bf16>(dy_perm), s.H,
-                     s.F, s.E, m.tokens_per_expert, m.padded_bins, mb<bf16>(dw));
+                     m.tokens_per_expert, mb<bf16>(dx_perm), mb<bf16>(dw));
   return hipGetLastError();
 }
 
