@@ -1155,8 +1155,13 @@ __device__ __forceinline__ void engine(O& o, int total, TileOf&& tile_of, char* 
 
 // One block per CU.  XCD x = blockIdx % 8 owns the logical tiles [lo, hi)
 // that the product assigns it; its S blocks take them round-robin, so at any
-// time they work on S consecutive tiles.  Every branch that reaches a barrier is
-// uniform over the block.
+// time they work on S consecutive tiles.  In the 4x2 layout (kFlip) a last
+// round that would leave more than half of the blocks idle is dealt in
+// 128-row halves instead: blocks r < t take the first row block of the t
+// leftover tiles, blocks t..2t-1 the second one (none when the tile has a
+// single block).  A one-block tile keeps every SIMD busy with one wave and
+// fetches half the row operand, so it ends well before a whole tile would.
+// Every branch that reaches a barrier is uniform over the block.
 template <class K>
 __device__ __forceinline__ void persistent(const K& k) {
   __shared__ __attribute__((aligned(16))) char lds[kLds];
@@ -1167,7 +1172,26 @@ __device__ __forceinline__ void persistent(const K& k) {
   k.xcd_range(x, lo, hi);
   lo = (int)uniform((uint32_t)lo);
   hi = (int)uniform((uint32_t)hi);
-  const int total = hi - lo > r ? (hi - lo - r + S - 1) / S : 0;
+  int full = hi - lo, tail = 0;      // tiles dealt whole; leftover tiles dealt in halves
+  if constexpr (K::kFlip) {
+    const int t = full % S;
+    if (t > 0 && 2 * t <= S) {
+      full -= t;
+      tail = t;
+    }
+  }
+  const int nfull = full > r ? (full - r + S - 1) / S : 0;
+  int half_tile = -1, half = 0;      // this block's half of a leftover tile
+  if (r < 2 * tail) {
+    half = r < tail ? 0 : 1;
+    half_tile = lo + full + r - half * tail;
+    if (half == 1) {
+      Job t;
+      k.tile(half_tile, t);
+      if (!t.fb) half_tile = -1;
+    }
+  }
+  const int total = nfull + (half_tile >= 0 ? 1 : 0);
   if (total <= 0) return;
   const uint32_t lbase = uniform(lds_addr(lds));
   Pipe<K> p{k, lds, lbase, 0};
@@ -1181,7 +1205,13 @@ __device__ __forceinline__ void persistent(const K& k) {
   Ops<K, K, false> o{k, k, p, p};
   const auto tile_of = [&](int i) {
     Job j;
-    k.tile(lo + r + i * S, j);
+    if (i < nfull) {
+      k.tile(lo + r + i * S, j);
+    } else {
+      k.tile(half_tile, j);
+      j.u += half;
+      j.fb = false;
+    }
     j.kind = 0;
     return j;
   };
