@@ -37,6 +37,8 @@
 //     fp32 products).  Lane l of a 16x16 accumulator holds 4 consecutive A
 //     rows (4*(l/16) + 0..3) of B row l%16, so the output's contiguous
 //     dimension sits on the A side and each lane stores 4 adjacent elements.
+#include <atomic>
+
 #include "dmoe_device.h"
 #include "dmoe_internal.h"
 
@@ -256,19 +258,21 @@ gemm_up_kernel(const float* __restrict__ x_perm, const float* __restrict__ w1,
   }
 }
 
-// y_perm = act w2[e] for 64 rows and 64 hidden columns.  grid = (H/64, 2 max_tiles).
+// y_perm = act w2[e] for 64 rows and 64 hidden columns, or 32 when `narrow`
+// (only the first A half: twice the tiles for a product too small to fill
+// the CUs).  grid = (H/64 or H/32, 2 max_tiles).
 __global__ void __launch_bounds__(kGemmThreads)
 gemm_down_kernel(const float* __restrict__ act, const float* __restrict__ w2, int64_t H,
-                 int64_t F, const int32_t* __restrict__ tile_expert,
+                 int64_t F, const int32_t* __restrict__ tile_expert, int narrow,
                  float* __restrict__ y_perm) {
   GEMM_PROLOGUE
   int64_t p0;
   int e;
   if (!row_tile(tile_expert, p0, e)) return;
-  const int64_t h0 = (int64_t)blockIdx.x * kTileA;
+  const int64_t h0 = (int64_t)blockIdx.x * (narrow ? kHalfA : kTileA);
   const float* wb = w2 + (int64_t)e * F * H + h0;
   const Operand A{reinterpret_cast<const char*>(wb), reinterpret_cast<const char*>(wb + kHalfA),
-                  H * 4, kHalfA, h0 + kHalfA < H};
+                  H * 4, kHalfA, !narrow && h0 + kHalfA < H};
   const Operand B{reinterpret_cast<const char*>(act + p0 * F), nullptr, F * 4, kTileB, false};
   Acc acc;
   zero(acc);
@@ -336,14 +340,15 @@ __device__ __forceinline__ void down_dgrad_tile(const float* __restrict__ dy_per
 __global__ void __launch_bounds__(kGemmThreads)
 gemm_up_dgrad_kernel(const float* __restrict__ dh1, const float* __restrict__ dh3,
                      const float* __restrict__ w1, const float* __restrict__ w3, int64_t H,
-                     int64_t F, const int32_t* __restrict__ tile_expert, float* dx_perm) {
+                     int64_t F, const int32_t* __restrict__ tile_expert, int narrow,
+                     float* dx_perm) {
   GEMM_PROLOGUE
   int64_t p0;
   int e;
   if (!row_tile(tile_expert, p0, e)) return;
-  const int64_t h0 = (int64_t)blockIdx.x * kTileA;
+  const int64_t h0 = (int64_t)blockIdx.x * (narrow ? kHalfA : kTileA);
   const int64_t wofs = (int64_t)e * H * F + h0 * F;
-  const bool has1 = h0 + kHalfA < H;
+  const bool has1 = !narrow && h0 + kHalfA < H;
   const int ks = (int)(F / kKElems);
   Acc acc;
   zero(acc);
@@ -471,6 +476,24 @@ gemm_wgrad_up_kernel(const float* __restrict__ x_perm, const float* __restrict__
 
 static unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
 
+// Whether a row-tiled product of cols 64-column tiles per row tile should
+// run 32-column tiles instead: when its 64-column tiles would not give every
+// CU of the current device one.  Each output element is summed in the same
+// order either way.
+static bool narrow_tiles(unsigned cols, unsigned rows) {
+  static std::atomic<int> cache[64];   // compute units per device
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int cus = cache[dev].load(std::memory_order_relaxed);
+  if (cus <= 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cache[dev].store(cus, std::memory_order_relaxed);
+  }
+  return (int64_t)cols * rows < (int64_t)cus;
+}
+
 template <typename T> static const T* cp(const void* p) { return static_cast<const T*>(p); }
 template <typename T> static T* mp(void* p) { return static_cast<T*>(p); }
 
@@ -492,9 +515,10 @@ hipError_t launch_gemm_up(const Shape& s, const void* x_perm, const void* x, con
 hipError_t launch_gemm_down(const Shape& s, const void* act, const void* w2,
                             const MetaPtrs& m, void* y_perm, hipStream_t stream) {
   if (s.bf16) return launch_bf16_down(s, act, w2, m, y_perm, stream);
-  const dim3 grid(cdiv(s.H, kTileA), row_tiles(s));
+  const bool narrow = narrow_tiles(cdiv(s.H, kTileA), row_tiles(s));
+  const dim3 grid(cdiv(s.H, narrow ? kHalfA : kTileA), row_tiles(s));
   hipLaunchKernelGGL(gemm_down_kernel, grid, dim3(kGemmThreads), 0, stream,
-                     cp<float>(act), cp<float>(w2), s.H, s.F, m.tile_expert,
+                     cp<float>(act), cp<float>(w2), s.H, s.F, m.tile_expert, narrow ? 1 : 0,
                      mp<float>(y_perm));
   return hipGetLastError();
 }
@@ -521,10 +545,11 @@ hipError_t launch_gemm_up_dgrad(const Shape& s, const void* dh1, const void* dh3
                                 hipStream_t stream) {
   if (s.bf16)
     return launch_bf16_up_dgrad(s, dh1, dh3, w1, w3, x_perm, m, dx_perm, dw1, dw3, stream);
-  const dim3 grid(cdiv(s.H, kTileA), row_tiles(s));
+  const bool narrow = narrow_tiles(cdiv(s.H, kTileA), row_tiles(s));
+  const dim3 grid(cdiv(s.H, narrow ? kHalfA : kTileA), row_tiles(s));
   hipLaunchKernelGGL(gemm_up_dgrad_kernel, grid, dim3(kGemmThreads), 0, stream,
                      cp<float>(dh1), cp<float>(dh3), cp<float>(w1), cp<float>(w3), s.H,
-                     s.F, m.tile_expert, mp<float>(dx_perm));
+                     s.F, m.tile_expert, narrow ? 1 : 0, mp<float>(dx_perm));
   return hipGetLastError();
 }
 
