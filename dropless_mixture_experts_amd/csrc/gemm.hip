@@ -297,18 +297,18 @@ __device__ __forceinline__ void down_dgrad_tile(const float* __restrict__ dy_per
                                                 const float* h3, int64_t H, int64_t F,
                                                 const int32_t* __restrict__ tile_expert,
                                                 float* dh1, float* dh3, int bx, int by,
-                                                char* lds) {
+                                                bool narrow, char* lds) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wn = w & 1, wm = w >> 1;
   const int lr = (lane >> 4) * 4, lc = lane & 15;
   const int e = tile_expert[by / kBPerBlock];
   if (e < 0) return;
   const int64_t p0 = (int64_t)by * kTileB;
-  const int64_t fb = (int64_t)bx * kTileA;
+  const int64_t fb = (int64_t)bx * (narrow ? kHalfA : kTileA);
   const float* wb = w2 + (int64_t)e * F * H + fb * H;
   const Operand A{reinterpret_cast<const char*>(wb),
                   reinterpret_cast<const char*>(wb + kHalfA * H), H * 4, kHalfA,
-                  fb + kHalfA < F};
+                  !narrow && fb + kHalfA < F};
   const Operand B{reinterpret_cast<const char*>(dy_perm + p0 * H), nullptr, H * 4, kTileB, false};
   Acc acc;
   zero(acc);
@@ -389,17 +389,17 @@ __device__ __forceinline__ void wgrad_down_tile(const float* __restrict__ act,
                                                 int64_t F, const int32_t* __restrict__ tpe,
                                                 const int32_t* __restrict__ padded_bins,
                                                 float* __restrict__ dw2, int bx, int by, int e,
-                                                char* lds) {
+                                                bool narrow, char* lds) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wn = w & 1, wm = w >> 1;
   const int lr = (lane >> 4) * 4, lc = lane & 15;
-  const int64_t h0 = (int64_t)bx * kTileA, f0 = (int64_t)by * kTileB;
+  const int64_t h0 = (int64_t)bx * (narrow ? kHalfA : kTileA), f0 = (int64_t)by * kTileB;
   int64_t start;
   int n;
   expert_rows(e, tpe, padded_bins, start, n);
   const float* ab = dy_perm + start * H + h0;
   const Operand A{reinterpret_cast<const char*>(ab), reinterpret_cast<const char*>(ab + kHalfA),
-                  H * 4, kHalfA, h0 + kHalfA < H};
+                  H * 4, kHalfA, !narrow && h0 + kHalfA < H};
   const Operand B{reinterpret_cast<const char*>(act + start * F + f0), nullptr, F * 4, kTileB,
                   false};
   Acc acc;
@@ -418,8 +418,9 @@ __device__ __forceinline__ void wgrad_down_tile(const float* __restrict__ act,
 }
 
 // down dgrad + gate backward and dw2 in one launch (neither reads what the
-// other writes): blocks [0, nd) are dgrad tiles ((F/64) x (2 max_tiles),
-// x fastest), the rest dw2 tiles ((H/64) x (F/64) x E).
+// other writes): blocks [0, nd) are dgrad tiles ((F/cw) x (2 max_tiles),
+// x fastest), the rest dw2 tiles ((H/cw) x (F/64) x E), with cw = 64
+// columns, or 32 (the first A half) when `narrow`.
 __global__ void __launch_bounds__(kGemmThreads)
 gemm_down_dgrad_wgrad_down_kernel(const float* __restrict__ dy_perm,
                                   const float* __restrict__ w2, const float* h1,
@@ -427,17 +428,19 @@ gemm_down_dgrad_wgrad_down_kernel(const float* __restrict__ dy_perm,
                                   int64_t F, const int32_t* __restrict__ tile_expert,
                                   const int32_t* __restrict__ tpe,
                                   const int32_t* __restrict__ padded_bins, float* dh1,
-                                  float* dh3, float* __restrict__ dw2, int nd) {
+                                  float* dh3, float* __restrict__ dw2, int nd, int narrow) {
   __shared__ __attribute__((aligned(16))) char lds[2 * kLdsStage];
   const int b = (int)blockIdx.x;
+  const int cw = narrow ? kHalfA : kTileA;
   if (b < nd) {
-    const int fx = (int)((F + kTileA - 1) / kTileA);
-    down_dgrad_tile(dy_perm, w2, h1, h3, H, F, tile_expert, dh1, dh3, b % fx, b / fx, lds);
+    const int fx = (int)((F + cw - 1) / cw);
+    down_dgrad_tile(dy_perm, w2, h1, h3, H, F, tile_expert, dh1, dh3, b % fx, b / fx,
+                    narrow != 0, lds);
   } else {
-    const int hx = (int)((H + kTileA - 1) / kTileA), fy = (int)((F + kTileB - 1) / kTileB);
+    const int hx = (int)((H + cw - 1) / cw), fy = (int)((F + kTileB - 1) / kTileB);
     const int r = b - nd;
     wgrad_down_tile(act, dy_perm, H, F, tpe, padded_bins, dw2, r % hx, (r / hx) % fy,
-                    r / (hx * fy), lds);
+                    r / (hx * fy), narrow != 0, lds);
   }
 }
 
@@ -476,10 +479,9 @@ gemm_wgrad_up_kernel(const float* __restrict__ x_perm, const float* __restrict__
 
 static unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
 
-// Whether a row-tiled product of cols 64-column tiles per row tile should
-// run 32-column tiles instead: when its 64-column tiles would not give every
-// CU of the current device one.  Each output element is summed in the same
-// order either way.
+// Whether a launch of cols x rows 64-column tiles should run 32-column tiles
+// instead: when its 64-column tiles would not give every CU of the current
+// device one.  Each output element is summed in the same order either way.
 static bool narrow_tiles(unsigned cols, unsigned rows) {
   static std::atomic<int> cache[64];   // compute units per device
   int dev = 0;
@@ -530,12 +532,17 @@ hipError_t launch_gemm_down_dgrad_wgrad_down(const Shape& s, const void* dy_perm
   if (s.bf16)
     return launch_bf16_down_dgrad_wgrad_down(s, dy_perm, w2, h1, h3, act, m, dh1, dh3, dw2,
                                              stream);
-  const unsigned nd = cdiv(s.F, kTileA) * row_tiles(s);
-  const unsigned nw = cdiv(s.H, kTileA) * cdiv(s.F, kTileB) * (unsigned)s.E;
+  const bool narrow = narrow_tiles(cdiv(s.F, kTileA) * row_tiles(s) +
+                                       cdiv(s.H, kTileA) * cdiv(s.F, kTileB) * (unsigned)s.E,
+                                   1);
+  const int64_t cw = narrow ? kHalfA : kTileA;
+  const unsigned nd = cdiv(s.F, cw) * row_tiles(s);
+  const unsigned nw = cdiv(s.H, cw) * cdiv(s.F, kTileB) * (unsigned)s.E;
   hipLaunchKernelGGL(gemm_down_dgrad_wgrad_down_kernel, dim3(nd + nw), dim3(kGemmThreads), 0,
                      stream, cp<float>(dy_perm), cp<float>(w2), cp<float>(h1), cp<float>(h3),
                      cp<float>(act), s.H, s.F, m.tile_expert, m.tokens_per_expert,
-                     m.padded_bins, mp<float>(dh1), mp<float>(dh3), mp<float>(dw2), (int)nd);
+                     m.padded_bins, mp<float>(dh1), mp<float>(dh3), mp<float>(dw2), (int)nd,
+                     narrow ? 1 : 0);
   return hipGetLastError();
 }
 
