@@ -415,7 +415,10 @@ int dmoe_backward_fused_gather_timed(const dmoe_dims* dims, const void* x, const
  * dmoe_forward otherwise.  All pointers are device memory owned by the
  * caller; P_max = 128 * dmoe_max_tiles(dims).  Slot-order arrays have
  * T*k rows in entry order a = t*k + j.  Nothing is allocated, nothing
- * waits on the host, and argument errors return before any launch.
+ * waits on the host, and argument errors return before any launch.  No two
+ * array arguments of one call may overlap (each backward call computes its
+ * dgrad and its weight gradient in one launch, so a scratch array that
+ * aliased an input would be overwritten while it is read).
  *
  * dmoe_moa_map:     x [T, H] -> q [T*k, F].  x_perm [P_max, H] is written
  *                   (the padded copy of x, saved for dmoe_moa_map_backward);
