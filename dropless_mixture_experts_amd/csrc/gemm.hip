@@ -21,7 +21,10 @@
 //     gradient).  The A rows are two halves of 32 from two sources (w1 and
 //     w3 columns in the up projection, so the SiLU gate pairs them in
 //     registers; consecutive columns elsewhere).  Each wave owns 16 rows of
-//     each A half x 32 B rows: 2 x 2 MFMA 16x16 tiles.
+//     each A half x 32 B rows: 2 x 2 MFMA 16x16 tiles.  A launch whose 64 x
+//     64 tiles would leave CUs without one computes the first A half alone
+//     (32 x 64 tiles, twice as many; the down projection, the up dgrad and
+//     the merged down dgrad + dw2).
 //   * LDS holds both operands K-contiguous, 128 bytes of K per row per stage
 //     (32 fp32) plus 16 bytes of padding, which spreads the rows read by
 //     consecutive lanes over distinct banks.  32 K per stage halves the
